@@ -1,0 +1,193 @@
+"""The LoReS decode step, written out plainly.
+
+General recurrence ([LoReS] "Introduction and Theoretical Foundation",
+general recurrence form), per (sequence, head) unit:
+
+    S_t = S_{t-1} diag(alpha_t) (I - delta * beta_t k_t k_t^T) + beta_t v_t k_t^T
+    o_t = S_t q_t
+
+with S in R^{d_v x d_k}, decay alpha_t scalar or per key channel, write gate
+beta_t and delta in {0, 1}.  LoReS stores S quantized and, every step,
+dequantizes -> updates -> requantizes it ([LoReS] "Intra-State Quantization
+Approach", property 3), with one scale per value row ([LoReS] Section 4,
+scale grouping and Proposition 1: s_G = max |S_G| / r, r = 2^(b-1) - 1) and
+stochastic rounding ([LoReS] Section 4, Rounding).
+
+reference_step64 is the recurrence itself in fp64 matrix form.  decode_step
+is the same recurrence in the row form a kernel evaluates, with every fp32
+rounding the quantized path commits to (the readings are listed in the
+repository's design notes):
+
+  1  a_ij  = fl(s_i * alpha_j);  S'_ij = fl(c_ij * a_ij)          int heads
+     S'_ij = fl(X_ij * alpha_j)                                   bf16 / fp32 heads
+  2  delta = 1: r_i = fl(sum_j S'_ij k_j);  g_i = fl(beta * fl(v_i - r_i))
+     delta = 0: g_i = fl(beta * v_i)
+  3  U_ij = fma(g_i, k_j, S'_ij)
+       (real arithmetic: U = S' - delta*beta (S'k) k^T + beta v k^T, which is
+        S_{t-1} diag(alpha)(I - delta beta k k^T) + beta v k^T)
+  4  o_i  = fl(sum_j U_ij q_j)             (readout of the pre-requant state)
+  5  int heads, r = 127 (int8) or 7 (int4), bias B = 128 (int8) or 136 (int4):
+       m_i = max_j |U_ij|;  s'_i = fl(m_i / r);  inv_i = largest fp32 <= r / m_i
+       (inv_i = 0 for m_i = 0);  z_ij = fl(U_ij * inv_i + (B + n_ij 2^-16))
+       in one rounding;  e_ij = floor(z_ij);  c'_ij = e_ij - B  in [-r, r]
+     bf16 heads: bf16 bits of (f32bits(U_ij) + n_ij) >> 16   (rounding by noise)
+     fp32 heads: X'_ij = U_ij
+The dot products in 2 and 4 are accumulated in fp64 and rounded once.
+"""
+import numpy as np
+
+from . import exact
+from .exact import F32, F64, f32, fma32
+from .rng import noise16, noise16_iid, unit_key
+
+PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4 = 0, 1, 2, 3
+QMAX = {PREC_INT8: 127, PREC_INT4: 7}
+BIAS = {PREC_INT8: 128, PREC_INT4: 136}
+
+
+# ---------------------------------------------------------------------------
+# fp64 reference recurrence (the definition itself)
+# ---------------------------------------------------------------------------
+def reference_step64(S, q, k, v, alpha, beta, delta):
+    """One step of the general recurrence in fp64 for one unit.
+
+    S [dv, dk]; q, k [dk]; v [dv]; alpha scalar or [dk]; beta scalar.
+    Returns (S_t, o_t).
+    """
+    S = np.asarray(S, F64)
+    q, k, v = (np.asarray(a, F64) for a in (q, k, v))
+    dk = k.shape[0]
+    a = np.broadcast_to(np.asarray(alpha, F64), (dk,))
+    A = np.diag(a) @ (np.eye(dk) - delta * float(beta) * np.outer(k, k))
+    S_t = S @ A + float(beta) * np.outer(v, k)
+    return S_t, S_t @ q
+
+
+def transition64(k, alpha, beta, delta):
+    """A_t = diag(alpha_t)(I - delta beta_t k_t k_t^T) in fp64 (error propagation)."""
+    k = np.asarray(k, F64)
+    dk = k.shape[0]
+    a = np.broadcast_to(np.asarray(alpha, F64), (dk,))
+    return np.diag(a) @ (np.eye(dk) - delta * float(beta) * np.outer(k, k))
+
+
+# ---------------------------------------------------------------------------
+# state containers
+# ---------------------------------------------------------------------------
+def zero_state(prec, n, dv, dk):
+    if prec in QMAX:
+        return {"codes": np.zeros((n, dv, dk), np.int32), "scales": np.zeros((n, dv), F32)}
+    if prec == PREC_BF16:
+        return {"bits": np.zeros((n, dv, dk), np.uint16)}
+    return {"X": np.zeros((n, dv, dk), F32)}
+
+
+def dequant(prec, state):
+    """Stored state as fp32 values: fl(s_i * c_ij) for int heads, exact otherwise."""
+    if prec in QMAX:
+        return (state["scales"][:, :, None] * state["codes"].astype(F32)).astype(F32)
+    if prec == PREC_BF16:
+        return exact.bf16_to_f32(state["bits"])
+    return f32(state["X"]).copy()
+
+
+# ---------------------------------------------------------------------------
+# requantization
+# ---------------------------------------------------------------------------
+def quantize_rows(U, prec, n=None, rounding="sr"):
+    """Requantize U [N, dv, dk] (fp32) with one fresh scale per value row.
+
+    n: noise draws [N, dv, dk] (uint32 < 2^16), needed for rounding="sr".
+    rounding="rtn" rounds fl(U * inv) to nearest (ties to even) instead.
+    Returns the new state dict.
+    """
+    U = f32(U)
+    if prec in QMAX:
+        r = QMAX[prec]
+        m = np.max(np.abs(U), axis=2)
+        scales = exact.rn_div32(m, F32(r))
+        inv = exact.rd_div32(F32(r), m)
+        if rounding == "sr":
+            bias = (F32(BIAS[prec]) + n.astype(F32) * F32(2.0 ** -16)).astype(F32)
+            z = fma32(U, inv[:, :, None], bias)
+            codes = np.floor(z).astype(np.int32) - BIAS[prec]
+        elif rounding == "rtn":
+            y = (U * inv[:, :, None]).astype(F32)
+            codes = np.rint(y).astype(np.int32)
+        else:
+            raise ValueError(rounding)
+        return {"codes": codes, "scales": scales}
+    if prec == PREC_BF16:
+        bits = exact.f32_bits(U).astype(np.uint64)
+        if rounding == "sr":
+            bits = (bits + n.astype(np.uint64)) & np.uint64(0xFFFFFFFF)
+        elif rounding == "rtn":
+            lsb = (bits >> np.uint64(16)) & np.uint64(1)
+            bits = (bits + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFFFFFF)
+        else:
+            raise ValueError(rounding)
+        return {"bits": (bits >> np.uint64(16)).astype(np.uint16)}
+    return {"X": U.copy()}
+
+
+# ---------------------------------------------------------------------------
+# the decode step
+# ---------------------------------------------------------------------------
+def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
+                rounding="sr", noise="weyl"):
+    """One decode step for N units of one precision class.
+
+    q, k [N, dk] and v [N, dv]: fp32 values (bf16 inputs converted exactly);
+    alpha [N] (scalar decay) or [N, dk] (per key channel); beta [N];
+    b, h [N]: global sequence and head indices (they key the noise).
+    Returns (new_state, o [N, dv]).
+    """
+    q, k, v, beta = f32(q), f32(k), f32(v), f32(beta)
+    N, dk = k.shape
+    dv = v.shape[1]
+    alpha = f32(alpha)
+    a_row = alpha[:, None, None] if alpha.ndim == 1 else alpha[:, None, :]
+
+    # 1  dequantize and decay (key columns)
+    if prec in QMAX:
+        a = (state["scales"][:, :, None] * a_row).astype(F32)
+        Sp = (state["codes"].astype(F32) * a).astype(F32)
+    else:
+        Sp = (dequant(prec, state) * a_row).astype(F32)
+
+    # 2  delta projection and write gate
+    if delta:
+        r = exact.dot_rn32(Sp, k)
+        g = (beta[:, None] * (v - r).astype(F32)).astype(F32)
+    else:
+        g = (beta[:, None] * v).astype(F32)
+
+    # 3  rank-one write
+    U = fma32(g[:, :, None], k[:, None, :], Sp)
+
+    # 4  readout from the updated state
+    o = exact.dot_rn32(U, q)
+
+    # 5  requantize with fresh row scales
+    n = None
+    if prec != PREC_FP32 and rounding == "sr":
+        K = unit_key(seed, t, b, h)
+        n = (noise16 if noise == "weyl" else noise16_iid)(K, dv, dk)
+    return quantize_rows(U, prec, n, rounding), o
+
+
+def run_trajectory(prec, state, inputs, delta, seed, b, h, t0=1, rounding="sr",
+                   noise="weyl"):
+    """Apply decode_step for t = t0, t0+1, ... over inputs' leading time axis.
+
+    inputs: dict of arrays q [T, N, dk], k, v [T, N, dv], alpha [T, N(, dk)],
+    beta [T, N].  Returns (final_state, o [T, N, dv]).
+    """
+    outs = []
+    T = inputs["k"].shape[0]
+    for s in range(T):
+        state, o = decode_step(prec, state, inputs["q"][s], inputs["k"][s], inputs["v"][s],
+                               inputs["alpha"][s], inputs["beta"][s], delta, seed, t0 + s,
+                               b, h, rounding=rounding, noise=noise)
+        outs.append(o)
+    return state, np.stack(outs)

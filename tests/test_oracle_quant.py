@@ -1,0 +1,176 @@
+"""Pins for the oracle's requantizer (value-row scales, stochastic rounding).
+
+What the pages fix: one scale per value row, s = max|row| / r with
+r = 2^(b-1) - 1 ([LoReS] Section 4, scale grouping and Proposition 1), and
+rounding that is stochastic so errors do not reinforce across steps ([LoReS]
+Section 4, Rounding / Proposition 3).  The checks below follow from those
+definitions and from probability, not from the oracle's code:
+  * exhaustive enumeration of all 2^16 noise values: a value y rounds only to
+    floor(y) or floor(y)+1, up with probability frac(y) (to the 2^-16 grid),
+  * bf16 rounding: the mean over all 2^16 noise values is the input, exactly,
+  * zero rows, code range, one-step error bound, mean over seeds,
+  * Proposition 1's readout-error variances for value-axis and key-axis
+    scales under round-to-nearest (M_i^2 / 12r^2 and sum_j q_j^2 C_j^2 / 12r^2),
+    and the stochastic-rounding analogue M_i^2 / 6r^2 (derived: the variance
+    of a stochastic rounding with fraction f is f(1-f), mean 1/6),
+  * the per-row Weyl noise gives the same readout error as one independent
+    hash per element (within 10%).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import exact, rng, step
+
+F32 = np.float32
+QM = {step.PREC_INT8: 127, step.PREC_INT4: 7}
+
+
+def _row_with_all_noise(x, m):
+    """U [1, 1, 65537]: element 0 fixes the row max m, the rest all equal x."""
+    U = np.full((1, 1, 65537), x, F32)
+    U[0, 0, 0] = m
+    n = np.zeros((1, 1, 65537), np.uint32)
+    n[0, 0, 1:] = np.arange(65536, dtype=np.uint32)
+    return U, n
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+def test_sr_exhaustive_probability(prec):
+    r = QM[prec]
+    g = np.random.default_rng(10 + prec)
+    for trial in range(40):
+        m = F32(np.exp(g.uniform(-8, 4)))
+        x = F32(g.uniform(-1, 1) * m)
+        if trial == 0:
+            x = m                        # the row maximum itself
+        if trial == 1:
+            x = -m
+        U, n = _row_with_all_noise(x, m)
+        st = step.quantize_rows(U, prec, n)
+        inv = exact.rd_div32(F32(r), np.array([m], F32))[0]
+        y = Fraction(float(x)) * Fraction(float(inv))
+        fl = y.numerator // y.denominator
+        frac = y - fl
+        codes = st["codes"][0, 0, 1:]
+        assert codes.min() >= -r and codes.max() <= r
+        assert set(np.unique(codes).tolist()) <= {fl, fl + 1}
+        p_up = Fraction(int((codes == fl + 1).sum()), 65536)
+        assert abs(p_up - frac) <= Fraction(2, 65536), (x, m, float(p_up), float(frac))
+        mean = Fraction(int(codes.astype(np.int64).sum()), 65536)
+        assert abs(mean - y) <= Fraction(2, 65536)
+        # the stored scale is the correctly rounded m / r
+        assert st["scales"][0, 0] == exact.rn_div32(m, F32(r))
+
+
+def test_bf16_rounding_exactly_unbiased():
+    g = np.random.default_rng(11)
+    xs = np.concatenate([(g.standard_normal(30) * np.exp2(g.integers(-20, 20, 30))),
+                         [1.0, -1.0, 3.0e-39, 1e30, 0.0]]).astype(F32)
+    for x in xs:
+        U = np.full((1, 1, 65536), x, F32)
+        n = np.arange(65536, dtype=np.uint32).reshape(1, 1, -1)
+        vals = exact.bf16_to_f32(step.quantize_rows(U, step.PREC_BF16, n)["bits"])[0, 0]
+        uniq, counts = np.unique(vals, return_counts=True)
+        assert uniq.size <= 2
+        mean = sum(Fraction(float(v)) * int(c) for v, c in zip(uniq, counts)) / 65536
+        assert mean == Fraction(float(x)), x
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_BF16])
+def test_zero_rows_stay_zero(prec):
+    U = np.zeros((2, 3, 64), F32)
+    n = rng.noise16(rng.unit_key(0, 1, np.arange(2), 0), 3, 64)
+    st = step.quantize_rows(U, prec, n)
+    assert np.all(step.dequant(prec, st) == 0)
+    if prec != step.PREC_BF16:
+        assert np.all(st["codes"] == 0) and np.all(st["scales"] == 0)
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+def test_one_step_error_below_one_code(prec):
+    r = QM[prec]
+    g = np.random.default_rng(12)
+    U = (g.standard_normal((8, 64, 128)) * np.exp(g.uniform(-5, 5, (8, 64, 1)))).astype(F32)
+    U[0, 0, :] = 0
+    U[1, 1, 5] = 1e30
+    n = rng.noise16(rng.unit_key(5, 3, np.arange(8), 1), 64, 128)
+    st = step.quantize_rows(U, prec, n)
+    assert st["codes"].min() >= -r and st["codes"].max() <= r
+    X = step.dequant(prec, st).astype(np.float64)
+    s = st["scales"].astype(np.float64)[:, :, None]
+    assert np.all(np.abs(X - U) <= s * (1 + 1e-5))
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_BF16])
+def test_mean_over_seeds_is_unbiased(prec):
+    g = np.random.default_rng(13)
+    U = (g.standard_normal((1, 16, 64))).astype(F32)
+    acc = np.zeros(U.shape, np.float64)
+    acc2 = np.zeros(U.shape, np.float64)
+    S = 3000
+    for seed in range(S):
+        n = rng.noise16(rng.unit_key(seed, 1, 0, 0), 16, 64)
+        X = step.dequant(prec, step.quantize_rows(U, prec, n)).astype(np.float64)
+        acc += X
+        acc2 += X * X
+    mean = acc / S
+    var = np.maximum(acc2 / S - mean ** 2, 1e-30)
+    z = (mean - U) / np.sqrt(var / S)
+    nz = var > 1e-20
+    assert np.abs(z[nz]).max() < 5.5, np.abs(z[nz]).max()
+
+
+def _rtn_keyaxis(U, r):
+    """Round-to-nearest with one scale per key column (the comparison of Proposition 1)."""
+    C = np.max(np.abs(U), axis=1, keepdims=True).astype(F32)
+    s = (C / F32(r)).astype(F32)
+    inv = exact.rd_div32(F32(r), C)
+    codes = np.rint((U * inv).astype(F32))
+    return (codes * s).astype(F32)
+
+
+def test_proposition1_readout_error_variances():
+    g = np.random.default_rng(14)
+    N, dv, dk, r = 400, 32, 64, 127
+    # rows and columns with different ranges, so the two groupings differ
+    U = (g.standard_normal((N, dv, dk)) * np.exp(g.uniform(-2, 2, (N, dv, 1)))
+         * np.exp(g.uniform(-1, 1, (N, 1, dk)))).astype(F32)
+    q = g.standard_normal((N, dk))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    M = np.max(np.abs(U), axis=2).astype(np.float64)            # row ranges
+    C = np.max(np.abs(U), axis=1).astype(np.float64)            # column ranges
+
+    val = step.dequant(step.PREC_INT8, step.quantize_rows(U, step.PREC_INT8, rounding="rtn"))
+    e_val = np.einsum("nij,nj->ni", (val - U).astype(np.float64), q)
+    ratio_val = np.mean(e_val ** 2) / np.mean(M ** 2 / (12 * r * r))
+    assert abs(ratio_val - 1) < 0.05, ratio_val
+
+    key = _rtn_keyaxis(U, r)
+    e_key = np.einsum("nij,nj->ni", (key - U).astype(np.float64), q)
+    pred_key = np.einsum("nj,nj->n", q ** 2, C ** 2)[:, None] / (12 * r * r)
+    ratio_key = np.mean(e_key ** 2) / np.mean(np.broadcast_to(pred_key, e_key.shape))
+    assert abs(ratio_key - 1) < 0.05, ratio_key
+
+    n = rng.noise16(rng.unit_key(0, 1, np.arange(N), 0), dv, dk)
+    sr = step.dequant(step.PREC_INT8, step.quantize_rows(U, step.PREC_INT8, n))
+    e_sr = np.einsum("nij,nj->ni", (sr - U).astype(np.float64), q)
+    ratio_sr = np.mean(e_sr ** 2) / np.mean(M ** 2 / (6 * r * r))
+    assert abs(ratio_sr - 1) < 0.05, ratio_sr
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+def test_weyl_noise_matches_independent_noise_readout_error(prec):
+    g = np.random.default_rng(15)
+    N, dv, dk = 300, 32, 128
+    U = (g.standard_normal((N, dv, dk)) * np.exp(g.uniform(-2, 2, (N, dv, 1)))).astype(F32)
+    q = g.standard_normal((N, dk))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    K = rng.unit_key(9, 4, np.arange(N), 2)
+    errs = {}
+    for name, fn in (("weyl", rng.noise16), ("iid", rng.noise16_iid)):
+        X = step.dequant(prec, step.quantize_rows(U, prec, fn(K, dv, dk)))
+        e = np.einsum("nij,nj->ni", (X - U).astype(np.float64), q)
+        errs[name] = float(np.mean(e ** 2))
+    assert abs(errs["weyl"] / errs["iid"] - 1) < 0.10, errs

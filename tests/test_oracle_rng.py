@@ -1,0 +1,89 @@
+"""Pins for oracle.rng.
+
+mix64 and fmix32 are pinned by published test vectors (tests/golden/hash_vectors.json).
+The keying and the per-element draws are this implementation's own definition
+(the pages fix no generator), so they are checked for the properties the
+rounding needs: exact marginal uniformity, bit balance, fresh draws per step.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import rng
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "hash_vectors.json")
+
+
+def _gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def test_mix64_splitmix64_vectors():
+    g = _gold()["splitmix64_seed0_first_outputs"]
+    gamma = int(g["gamma"], 16)
+    state = 0
+    for want in g["outputs"]:
+        state = (state + gamma) & (2 ** 64 - 1)
+        assert int(rng.mix64(np.uint64(state))) == int(want, 16)
+
+
+def test_fmix32_murmur3_vectors():
+    for seed, want in _gold()["murmur3_x86_32_empty_input"]["vectors"]:
+        assert int(rng.fmix32(np.uint32(int(seed, 16)))) == int(want, 16)
+
+
+def test_fmix32_is_a_bijection_on_a_sample():
+    x = np.arange(1 << 20, dtype=np.uint32)
+    assert np.unique(rng.fmix32(x)).size == x.size
+
+
+def test_unit_key_depends_on_every_argument_without_collisions():
+    seeds, ts, bs, hs = np.meshgrid(np.arange(4), np.arange(1, 9), np.arange(16),
+                                    np.arange(16), indexing="ij")
+    K = rng.unit_key(seeds.ravel(), ts.ravel(), bs.ravel(), hs.ravel())
+    assert np.unique(K).size == K.size
+
+
+def test_noise16_range_and_shape():
+    K = rng.unit_key(0, 1, np.arange(5), 3)
+    n = rng.noise16(K, 64, 128)
+    assert n.shape == (5, 64, 128) and n.dtype == np.uint32
+    assert n.max() < 65536
+
+
+def test_noise16_marginal_uniformity_chi2():
+    # one element position, many keys: 256 buckets of the top byte
+    K = rng.unit_key(7, np.arange(1, 65537), 0, 0)
+    n = rng.noise16(K, 3, 8)
+    for (i, j) in [(0, 0), (1, 5), (2, 7)]:
+        counts = np.bincount((n[:, i, j] >> 8).astype(np.int64), minlength=256)
+        exp = n.shape[0] / 256.0
+        chi2 = float(((counts - exp) ** 2 / exp).sum())
+        # 255 dof: mean 255, sd ~22.6; 5 sd margin
+        assert chi2 < 255 + 5 * 22.6, chi2
+
+
+def test_noise16_bit_balance():
+    K = rng.unit_key(1, np.arange(1, 2049), 5, 9)
+    n = rng.noise16(K, 16, 32).ravel()
+    for bit in range(16):
+        p = float(((n >> bit) & 1).mean())
+        assert abs(p - 0.5) < 0.01, (bit, p)
+
+
+def test_noise16_fresh_each_step():
+    b = np.arange(4096)
+    n1 = rng.noise16(rng.unit_key(3, 10, b, 2), 4, 4).astype(np.float64)
+    n2 = rng.noise16(rng.unit_key(3, 11, b, 2), 4, 4).astype(np.float64)
+    for i in range(4):
+        for j in range(4):
+            c = np.corrcoef(n1[:, i, j], n2[:, i, j])[0, 1]
+            assert abs(c) < 5.0 / np.sqrt(b.size), c
+
+
+def test_noise16_iid_reference_range():
+    n = rng.noise16_iid(rng.unit_key(0, 1, 0, 0), 8, 16)
+    assert n.shape == (1, 8, 16) and n.max() < 65536
