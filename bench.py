@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the LoReS quantized recurrent-state decode step on one MI355X.
+
+A step is one decode step of the whole batch: every (sequence, head) state is
+dequantized, updated, read out and requantized in place.  Inputs for all
+timed steps are generated on the device before timing.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+
+Workloads (synthetic, shapes of the decode layers the method targets):
+  C2 (default) Gated-DeltaNet decode, B=64 H=32 d_k=d_v=128, bf16 q/k/v, int8 state
+  C3 Mamba-2 / SSD decode, B=256 H=128 d_v=64 d_k=128, no delta correction, int8
+  C4 KDA per-channel decay, B=128 H=32 d=128, 8 bf16 + 24 int8 heads
+  C5 large batch, B=2048 H=32 d=128, 16 int8 + 16 int4 heads
+  C1 is the tiny parity case (launch-bound; not a throughput workload).
+--mode copy times a plain device copy (the HBM calibration used for the
+rocprofv3 byte counters).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "state-updates/s (B*H*steps) and achieved HBM GB/s vs peak, quantized decode"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ["lores_step_impl.h", "lores_step_int8.hip", "lores_step_int4.hip",
+                  "lores_step_bf16.hip", "lores_step_fp32.hip", "lores_internal.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_linear_recurrence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def unit_bytes(prec, dk, dv, in_bytes, per_channel):
+    """Algorithmic bytes of one state update: the state read and written once,
+    plus q, k, v, alpha, beta read and o written."""
+    state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * dv, 3: dv * dk // 2 + 4 * dv}[prec]
+    io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
+    return 2 * state + io
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=2048)
+    return ap.parse_args(argv)
+
+
+def copy_mode(args, torch):
+    """Plain device-to-device copy of --copy-mib MiB, 10 times: the calibration
+    kernel for FETCH_SIZE / WRITE_SIZE counters and a measured copy bandwidth."""
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
+
+
+def cpu_baseline(w, inputs, head_prec, target_s, seed):
+    """Time the oracle (as it stands) on a bounded sample of the same workload:
+    the first units of the batch, step after step, until target_s has passed."""
+    import numpy as np
+    from oracle import step as ostep
+
+    n_units = min(w.B * w.H, 64)
+    units = [(u // w.H, u % w.H) for u in range(n_units)]
+    by_class = {}
+    for b, h in units:
+        by_class.setdefault(head_prec[h], []).append((b, h))
+    states = {c: ostep.zero_state(c, len(us), w.dv, w.dk) for c, us in by_class.items()}
+    T_in = inputs["k"].shape[0]
+    host = {}
+    for t in range(min(T_in, 64)):
+        host[t] = {k: v[t].float().cpu().numpy() for k, v in inputs.items()}
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        xin = host[steps % len(host)]
+        for c, us in by_class.items():
+            bs = np.array([b for b, _ in us])
+            hs = np.array([h for _, h in us])
+            states[c], _ = ostep.decode_step(c, states[c], xin["q"][bs, hs], xin["k"][bs, hs],
+                                             xin["v"][bs, hs], xin["alpha"][bs, hs],
+                                             xin["beta"][bs, hs], w.delta, seed, steps + 1, bs, hs)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {"value": n_units * steps / el, "unit": "state-updates/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_units} (sequence, head) units x {steps} decode steps of {w.key} "
+                      f"({el:.1f} s; NumPy oracle, single-threaded elementwise ops and "
+                      f"einsum, fp32-exact rounding emulation)"}
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main(argv=None):
+    args = parse(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the decode step has no cross-GPU exchange and its sharding "
+              "is described in DESIGN.md, but runs on more than one GPU are not part of it.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if args.mode == "copy":
+        copy_mode(args, torch)
+        return
+
+    import quantized_linear_recurrence_amd as lores
+    from workloads import get_workload, make_inputs
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    K, W = args.steps, args.warmup
+    T_in = min(w.T, max(K, W, 1))
+    print(f"[bench] generating {T_in} steps of {w.key} inputs on {dev}", file=sys.stderr, flush=True)
+    inputs = make_inputs(w, args.seed, dev, T=T_in)
+
+    # precision per head from the decay statistic of a calibration sample
+    if len(w.tiers) == 1:
+        head_prec = [w.tiers[0][1]] * w.H
+    else:
+        cal = inputs["alpha"][:min(T_in, 32)].float().cpu().numpy()
+        cal = cal.reshape(cal.shape[0] * cal.shape[1], w.H, -1)
+        head_prec = lores.lores_assign_precision(lores.lores_decay_stat(cal),
+                                                 [f for f, _ in w.tiers], [p for _, p in w.tiers])
+
+    in_bytes = 2 if w.in_bf16 else 4
+    step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel)
+                     for c in range(4))
+    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev)
+    o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
+
+    def step(t):
+        i = (t - 1) % T_in
+        lores.lores_decode_step(st, inputs["q"][i], inputs["k"][i], inputs["v"][i],
+                                inputs["alpha"][i], inputs["beta"][i], w.delta, args.seed, t, o=o)
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for t in range(1, W + 1):
+        step(t)
+    torch.cuda.synchronize()
+    # fresh state for the timed region
+    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(1, K + 1):
+        step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / K
+
+    # per-launch durations on the launch stream (events around each step)
+    n_lat = min(K, 256)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_lat)]
+    for i in range(n_lat):
+        evs[i][0].record()
+        step(K + 1 + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    per_launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    avg_launch_ms = sum(per_launch_ms) / n_lat
+    n_launches_per_step = sum(1 for c in range(4) if c in head_prec)
+    print(f"[bench] {ms_step * 1e3:.2f} us/step over the timed loop; "
+          f"{avg_launch_ms * 1e3:.2f} us average per step with per-step events "
+          f"({n_launches_per_step} kernel launch(es) per step)", file=sys.stderr, flush=True)
+
+    achieved = step_bytes / (avg_launch_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.key)
+    result = {
+        "metric": METRIC,
+        "value": w.B * w.H * K / (ms_total * 1e-3),
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.key} {w.name}",
+            "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "delta": w.delta,
+            "decay": w.decay, "inputs": "bf16" if w.in_bf16 else "fp32",
+            "state": {name: head_prec.count(c) for c, name in
+                      enumerate(["fp32", "bf16", "int8", "int4"]) if head_prec.count(c)},
+            "rounding": "stochastic", "parallelism": "single GPU",
+        },
+        "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": "lores_step_kernel (fused dequant-update-readout-requant)",
+            "launches_per_step": n_launches_per_step,
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, inputs, head_prec, args.cpu_seconds, args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

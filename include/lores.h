@@ -1,0 +1,199 @@
+/*
+ * lores.h - C ABI of the LoReS quantized recurrent-state decode step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method: "Quantizing Recurrent Language Models Is Easier Than You Think"
+ * (structured summary page).  Each (sequence, head) unit keeps a recurrent
+ * state S in R^{d_v x d_k} that every decode step updates in place:
+ *
+ *   S_t = S_{t-1} diag(alpha_t) (I - delta beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *   o_t = S_t q_t
+ *
+ * (section "Introduction and Theoretical Foundation", general recurrence form)
+ * while the state is stored quantized, dequantized, updated and requantized
+ * every step (section "Intra-State Quantization Approach", property 3), with
+ * one scale per value row (section "Intra-State Quantization (Section 4)",
+ * scale grouping and Proposition 1), stochastic rounding (same section,
+ * Rounding and Proposition 3) and a per-head precision chosen from the decay
+ * rate (same section, decay-based mixed precision).
+ *
+ * Conventions for every entry point:
+ *   - Return value: LORES_OK (0) or a negative LORES_E* code.  On error,
+ *     lores_last_error() (thread-local) describes it.  No C++ exception
+ *     crosses this boundary.  Validation happens before any GPU work, so a
+ *     call that fails validation launches nothing.
+ *   - "device" pointers point to HIP device memory owned by the caller; the
+ *     library never allocates or frees device memory.  "host" pointers point
+ *     to ordinary host memory, read or written synchronously.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; inputs must stay alive
+ *     and unmodified until that work has run.
+ *   - Calls on one lores_state handle are not re-entrant across streams.
+ */
+#ifndef LORES_H
+#define LORES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORES_SPEC_VERSION 1
+
+/* Per-head state precision. */
+enum {
+    LORES_FP32 = 0, /* unquantized fp32 state (the full-precision reference path) */
+    LORES_BF16 = 1, /* bfloat16 state, stochastic rounding from fp32               */
+    LORES_INT8 = 2, /* int8 codes in [-127, 127] + one fp32 scale per value row     */
+    LORES_INT4 = 3  /* int4 codes in [-7, 7]     + one fp32 scale per value row     */
+};
+
+/* Status codes. */
+enum {
+    LORES_OK = 0,
+    LORES_EINVAL = -1,      /* invalid argument (NULL, misaligned, out of range)  */
+    LORES_EUNSUPPORTED = -2,/* valid but not built (e.g. an unsupported d_k)      */
+    LORES_ESIZE = -3,       /* buffer too small                                     */
+    LORES_EHIP = -4,        /* a HIP runtime call failed                           */
+    LORES_ENOMEM = -5       /* host allocation failed                              */
+};
+
+/* Limits. */
+#define LORES_MAX_HEADS 512 /* heads per state                                   */
+#define LORES_MAX_DV 256    /* value rows per head                               */
+#define LORES_ROW_BLOCK 64  /* value rows per stored row block (one wavefront)   */
+
+/* Opaque host handle: dimensions, per-head precision, layout and the bound
+ * device buffer.  Created by lores_state_alloc, released by lores_state_free. */
+typedef struct lores_state lores_state;
+
+/*
+ * Packed state layout (version LORES_SPEC_VERSION), for inspection, tests and
+ * checkpointing.  The buffer holds one segment pair per precision class that
+ * has at least one head, in class order fp32, bf16, int8, int4, each segment
+ * starting on a 256-byte boundary:
+ *
+ *   codes  [B][H_c][n_chunk][d_v_pad][16 bytes]
+ *   scales [B][H_c][d_v_pad] fp32                 (int8 and int4 classes only)
+ *
+ * H_c = heads of class c, ordered by head index (head_slot below).
+ * d_v_pad = d_v rounded up to LORES_ROW_BLOCK; padding rows are never read
+ * or written by a step.  A row is cut into 16-byte chunks of E elements
+ * (E = 4 fp32, 8 bf16, 16 int8, 32 int4; n_chunk = d_k / E), stored
+ * chunk-major so one wavefront's 64 rows of a chunk are 1 KiB contiguous.
+ * Within a chunk, element e is:
+ *   fp32: word e, IEEE binary32        bf16: halfword e, bfloat16 bits
+ *   int8: byte e  = code + 128         (offset binary, 1..255)
+ *   int4: byte e/2, low nibble for even e, high nibble for odd e,
+ *         nibble = code + 8            (offset binary, 1..15)
+ * The value of an int element is scale[row] * code.  A row of all-zero bytes
+ * with scale 0 also reads as zero, so a zero-filled buffer is S = 0.
+ */
+typedef struct {
+    int32_t B, H, d_k, d_v, d_v_pad;
+    int32_t n_class[4];        /* heads per precision class                     */
+    int64_t codes_offset[4];   /* byte offset of class codes, -1 if no heads    */
+    int64_t scales_offset[4];  /* byte offset of class scales, -1 if none       */
+    int64_t unit_code_bytes[4];/* code bytes per (sequence, head) unit          */
+    uint64_t total_bytes;      /* bytes the caller's buffer must hold           */
+} lores_layout;
+
+/*
+ * lores_state_alloc - plan the packed layout and bind a caller-owned buffer.
+ *   B, H        sequences and heads (1 <= H <= LORES_MAX_HEADS, B >= 1)
+ *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128},
+ *               1 <= d_v <= LORES_MAX_DV
+ *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_INT4)
+ *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
+ *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
+ *               returns LORES_OK without creating a handle.  Otherwise *bytes
+ *               is the buffer size (LORES_ESIZE if too small).
+ *   stream      the buffer is cleared to S_0 = 0 asynchronously on it
+ *   out         host out: the new handle (owned by the caller; free it with
+ *               lores_state_free, which never touches device memory)
+ */
+int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                      const uint8_t *head_prec, void *d_buf, size_t *bytes,
+                      void *stream, lores_state **out);
+
+void lores_state_free(lores_state *st);
+
+/* Copy the layout of `st` into host struct *out. */
+int lores_state_layout(const lores_state *st, lores_layout *out);
+
+/* Host arrays [H]: precision and slot (index among heads of that class). */
+int lores_state_head_map(const lores_state *st, uint8_t *prec_out, int32_t *slot_out);
+
+/*
+ * lores_decay_stat - decay statistic per head for precision assignment:
+ * stat[h] = mean over n rows and `width` channels of log(alpha), computed in
+ * double.  Larger (closer to 0) means slower decay.
+ *   alpha  host [n][H][width] fp32, every value > 0
+ *   stat   host out [H] double
+ * (Decay-based mixed precision: section "Intra-State Quantization (Section 4)".)
+ */
+int lores_decay_stat(const float *alpha, int64_t n, int32_t H, int32_t width,
+                     double *stat);
+
+/*
+ * lores_assign_precision - decay-based mixed precision (same section): heads
+ * are ranked slowest-decaying first (larger stat first, ties to the lower head
+ * index) and dealt into tiers listed slowest first.  Tier k takes
+ * floor(tier_frac[k] * H + 0.5) heads (never more than remain); the last tier
+ * takes every remaining head.
+ *   stat       host [H] double (e.g. from lores_decay_stat)
+ *   tier_frac  host [n_tiers] double, each >= 0
+ *   tier_prec  host [n_tiers] precision codes
+ *   head_prec  host out [H]
+ * Host only and synchronous.
+ */
+int lores_assign_precision(const double *stat, int32_t H, const double *tier_frac,
+                           const uint8_t *tier_prec, int32_t n_tiers, uint8_t *head_prec);
+
+/*
+ * lores_decode_step - one decode step t for all B x H units, in place.
+ *   q, k        device [B][H][d_k]; fp32, or bfloat16 if in_bf16 != 0
+ *   v           device [B][H][d_v]; same dtype as q and k
+ *   alpha       device fp32 decay: [B][H] (scalar per head) or, if
+ *               alpha_per_channel != 0, [B][H][d_k] (one per key channel)
+ *   beta        device [B][H] fp32 write gate
+ *   delta       0 (no correction) or 1 (delta rule)
+ *   seed, t     key the stochastic rounding; t >= 1 (S_{t-1} -> S_t)
+ *   seq_base,   added to the local sequence and head index before keying the
+ *   head_base   rounding, so a shard of a larger batch reproduces the
+ *               unsharded result bit for bit
+ *   o           device out [B][H][d_v] fp32, the readout S_t q_t taken from
+ *               the updated state before requantization
+ * All device pointers must be 16-byte aligned.  Caller preconditions not
+ * checked: |q| = |k| = 1, decay in (0, 1], beta in (0, 2) when delta = 1,
+ * finite inputs.  Per element of an int head, with U the updated fp32 row:
+ *   scale' = fl(m / r), m = max|U_row|, r = 127 (int8) or 7 (int4);
+ *   code'  = floor(fl(U * inv + bias + u)) - bias, inv = the largest fp32 not
+ *            above r / m (0 if m = 0), bias = 128 (int8) or 136 (int4),
+ *            u = n * 2^-16 and n a 16-bit counter-based draw keyed on
+ *            (seed, t, sequence, head, row, column).
+ */
+int lores_decode_step(lores_state *st, const void *q, const void *k, const void *v,
+                      int32_t in_bf16, const float *alpha, int32_t alpha_per_channel,
+                      const float *beta, int32_t delta, uint64_t seed, uint64_t t,
+                      int64_t seq_base, int64_t head_base, float *o, void *stream);
+
+/*
+ * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32,
+ * value = scale * code for int heads, the stored value for bf16 / fp32 heads.
+ */
+int lores_dequant_state(const lores_state *st, float *out, void *stream);
+
+/* Thread-local description of the last error (empty string if none). */
+const char *lores_last_error(void);
+
+/* LORES_SPEC_VERSION of the library. */
+int lores_spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORES_H */

@@ -1,0 +1,329 @@
+// Host side of the LoReS C ABI: layout planning, argument validation,
+// decay-based precision assignment and kernel dispatch.  Every exported
+// function validates first and launches nothing on error; no exception
+// leaves this file.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "lores_internal.h"
+
+struct lores_state {
+    int32_t B, H, dk, dv, dv_pad, n_rb;
+    uint8_t prec[LORES_MAX_HEADS];
+    int32_t slot[LORES_MAX_HEADS];
+    int32_t n_class[4];
+    uint16_t heads[4][LORES_MAX_HEADS];
+    int64_t codes_off[4], scales_off[4], unit_bytes[4];
+    uint64_t total;
+    uint8_t *base;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return LORES_OK;
+}
+
+bool is_int_prec(int p) { return p == LORES_INT8 || p == LORES_INT4; }
+
+// 16-byte chunk = E elements; bytes per stored row = (d_k / E) * 16.
+int64_t row_bytes(int prec, int dk) {
+    static const int E[4] = {4, 8, 16, 32};
+    return (int64_t)(dk / E[prec]) * 16;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_dims(int32_t B, int32_t H, int32_t dk, int32_t dv) {
+    if (B < 1) return fail(LORES_EINVAL, "B must be >= 1 (got %d)", B);
+    if (H < 1 || H > LORES_MAX_HEADS)
+        return fail(LORES_EINVAL, "H must be in [1, %d] (got %d)", LORES_MAX_HEADS, H);
+    if (dk < 32 || dk % 32 != 0)
+        return fail(LORES_EINVAL, "d_k must be a positive multiple of 32 (got %d)", dk);
+    if (dk > 128) return fail(LORES_EUNSUPPORTED, "d_k > 128 is not built (got %d)", dk);
+    if (dv < 1 || dv > LORES_MAX_DV)
+        return fail(LORES_EINVAL, "d_v must be in [1, %d] (got %d)", LORES_MAX_DV, dv);
+    return LORES_OK;
+}
+
+// Fill st's layout from its dimensions and head_prec; returns status.
+int plan(lores_state *st, const uint8_t *head_prec) {
+    std::memset(st->n_class, 0, sizeof st->n_class);
+    for (int h = 0; h < st->H; ++h) {
+        const int p = head_prec[h];
+        if (p < 0 || p > 3) return fail(LORES_EINVAL, "head_prec[%d] = %d is not a precision code", h, p);
+        st->prec[h] = (uint8_t)p;
+        st->slot[h] = st->n_class[p];
+        st->heads[p][st->n_class[p]++] = (uint16_t)h;
+    }
+    st->dv_pad = (st->dv + LORES_ROW_BLOCK - 1) / LORES_ROW_BLOCK * LORES_ROW_BLOCK;
+    st->n_rb = st->dv_pad / LORES_ROW_BLOCK;
+    uint64_t off = 0;
+    for (int c = 0; c < 4; ++c) {
+        st->codes_off[c] = st->scales_off[c] = -1;
+        st->unit_bytes[c] = row_bytes(c, st->dk) * st->dv_pad;
+        if (!st->n_class[c]) continue;
+        const double units = (double)st->B * st->n_class[c];
+        if (units * st->unit_bytes[c] > 9.0e18) return fail(LORES_EINVAL, "state too large");
+        off = align256(off);
+        st->codes_off[c] = (int64_t)off;
+        off += (uint64_t)st->B * st->n_class[c] * st->unit_bytes[c];
+        if (is_int_prec(c)) {
+            off = align256(off);
+            st->scales_off[c] = (int64_t)off;
+            off += (uint64_t)st->B * st->n_class[c] * st->dv_pad * sizeof(float);
+        }
+        // one wavefront task per (unit, row block); groups of 4 tasks must fit a grid
+        if (units * st->n_rb / lores::kWavesPerGroup > 2147483647.0)
+            return fail(LORES_EINVAL, "too many (sequence, head) units for one launch");
+    }
+    st->total = align256(off);
+    return LORES_OK;
+}
+
+lores::ClassMeta make_meta(const lores_state *st, int c) {
+    lores::ClassMeta m;
+    std::memset(&m, 0, sizeof m);
+    m.B = st->B;
+    m.H = st->H;
+    m.Hc = st->n_class[c];
+    m.dv = st->dv;
+    m.dv_pad = st->dv_pad;
+    m.n_rb = st->n_rb;
+    m.unit_bytes = st->unit_bytes[c];
+    std::memcpy(m.heads, st->heads[c], sizeof m.heads);
+    return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lores_last_error(void) { return g_err.c_str(); }
+
+int lores_spec_version(void) { return LORES_SPEC_VERSION; }
+
+int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint8_t *head_prec,
+                      void *d_buf, size_t *bytes, void *stream, lores_state **out) {
+    try {
+        int rc = check_dims(B, H, d_k, d_v);
+        if (rc) return rc;
+        if (!head_prec) return fail(LORES_EINVAL, "head_prec is NULL");
+        if (!bytes) return fail(LORES_EINVAL, "bytes is NULL");
+        lores_state tmp;
+        tmp.B = B;
+        tmp.H = H;
+        tmp.dk = d_k;
+        tmp.dv = d_v;
+        tmp.base = nullptr;
+        rc = plan(&tmp, head_prec);
+        if (rc) return rc;
+        if (!d_buf) {
+            *bytes = (size_t)tmp.total;
+            return ok();
+        }
+        if (!out) return fail(LORES_EINVAL, "out is NULL");
+        if (!aligned(d_buf, 256)) return fail(LORES_EINVAL, "d_buf must be 256-byte aligned");
+        if (*bytes < tmp.total)
+            return fail(LORES_ESIZE, "buffer holds %zu bytes, the layout needs %llu", *bytes,
+                        (unsigned long long)tmp.total);
+        lores_state *st = new (std::nothrow) lores_state(tmp);
+        if (!st) return fail(LORES_ENOMEM, "host allocation of the state handle failed");
+        st->base = (uint8_t *)d_buf;
+        hipError_t e = lores::launch_fill_zero(d_buf, tmp.total, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete st;
+            return fail(LORES_EHIP, "zero fill launch failed: %s", hipGetErrorString(e));
+        }
+        *out = st;
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_state_alloc");
+    }
+}
+
+void lores_state_free(lores_state *st) { delete st; }
+
+int lores_state_layout(const lores_state *st, lores_layout *out) {
+    if (!st || !out) return fail(LORES_EINVAL, "NULL argument");
+    out->B = st->B;
+    out->H = st->H;
+    out->d_k = st->dk;
+    out->d_v = st->dv;
+    out->d_v_pad = st->dv_pad;
+    for (int c = 0; c < 4; ++c) {
+        out->n_class[c] = st->n_class[c];
+        out->codes_offset[c] = st->codes_off[c];
+        out->scales_offset[c] = st->scales_off[c];
+        out->unit_code_bytes[c] = st->unit_bytes[c];
+    }
+    out->total_bytes = st->total;
+    return ok();
+}
+
+int lores_state_head_map(const lores_state *st, uint8_t *prec_out, int32_t *slot_out) {
+    if (!st || !prec_out || !slot_out) return fail(LORES_EINVAL, "NULL argument");
+    for (int h = 0; h < st->H; ++h) {
+        prec_out[h] = st->prec[h];
+        slot_out[h] = st->slot[h];
+    }
+    return ok();
+}
+
+int lores_decay_stat(const float *alpha, int64_t n, int32_t H, int32_t width, double *stat) {
+    try {
+        if (!alpha || !stat) return fail(LORES_EINVAL, "NULL argument");
+        if (n < 1 || H < 1 || width < 1) return fail(LORES_EINVAL, "n, H and width must be >= 1");
+        std::vector<double> acc(H, 0.0);
+        for (int64_t i = 0; i < n; ++i) {
+            const float *row = alpha + i * (int64_t)H * width;
+            for (int h = 0; h < H; ++h) {
+                double s = 0.0;
+                for (int w = 0; w < width; ++w) {
+                    const float a = row[(int64_t)h * width + w];
+                    if (!(a > 0.0f)) return fail(LORES_EINVAL, "alpha must be > 0 (row %lld, head %d)", (long long)i, h);
+                    s += std::log((double)a);
+                }
+                acc[h] += s;
+            }
+        }
+        const double cnt = (double)n * width;
+        for (int h = 0; h < H; ++h) stat[h] = acc[h] / cnt;
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_decay_stat");
+    }
+}
+
+int lores_assign_precision(const double *stat, int32_t H, const double *tier_frac,
+                           const uint8_t *tier_prec, int32_t n_tiers, uint8_t *head_prec) {
+    try {
+        if (!stat || !tier_frac || !tier_prec || !head_prec) return fail(LORES_EINVAL, "NULL argument");
+        if (H < 1 || H > LORES_MAX_HEADS) return fail(LORES_EINVAL, "H must be in [1, %d]", LORES_MAX_HEADS);
+        if (n_tiers < 1) return fail(LORES_EINVAL, "n_tiers must be >= 1");
+        for (int k = 0; k < n_tiers; ++k) {
+            if (tier_prec[k] > 3) return fail(LORES_EINVAL, "tier_prec[%d] is not a precision code", k);
+            if (!(tier_frac[k] >= 0.0) || !std::isfinite(tier_frac[k]))
+                return fail(LORES_EINVAL, "tier_frac[%d] must be finite and >= 0", k);
+        }
+        for (int h = 0; h < H; ++h)
+            if (std::isnan(stat[h])) return fail(LORES_EINVAL, "stat[%d] is NaN", h);
+        std::vector<int> order(H);
+        std::iota(order.begin(), order.end(), 0);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int a, int b) { return stat[a] > stat[b]; });   // slowest first
+        int pos = 0;
+        for (int k = 0; k < n_tiers; ++k) {
+            int count;
+            if (k == n_tiers - 1) {
+                count = H - pos;
+            } else {
+                const double want = std::floor(tier_frac[k] * H + 0.5);
+                count = (int)std::min<double>(want, (double)(H - pos));
+            }
+            for (int i = 0; i < count; ++i) head_prec[order[pos + i]] = tier_prec[k];
+            pos += count;
+        }
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_assign_precision");
+    }
+}
+
+int lores_decode_step(lores_state *st, const void *q, const void *k, const void *v,
+                      int32_t in_bf16, const float *alpha, int32_t alpha_per_channel,
+                      const float *beta, int32_t delta, uint64_t seed, uint64_t t,
+                      int64_t seq_base, int64_t head_base, float *o, void *stream) {
+    try {
+        if (!st) return fail(LORES_EINVAL, "state handle is NULL");
+        if (!q || !k || !v || !alpha || !beta || !o)
+            return fail(LORES_EINVAL, "q, k, v, alpha, beta and o must be non-NULL device pointers");
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
+            !aligned(beta, 16) || !aligned(o, 16))
+            return fail(LORES_EINVAL, "device pointers must be 16-byte aligned");
+        if (in_bf16 != 0 && in_bf16 != 1) return fail(LORES_EINVAL, "in_bf16 must be 0 or 1");
+        if (alpha_per_channel != 0 && alpha_per_channel != 1)
+            return fail(LORES_EINVAL, "alpha_per_channel must be 0 or 1");
+        if (delta != 0 && delta != 1) return fail(LORES_EINVAL, "delta must be 0 or 1 (got %d)", delta);
+        if (t < 1) return fail(LORES_EINVAL, "t must be >= 1 (t = 0 is the initial state)");
+        if (seq_base < 0 || (uint64_t)seq_base + (uint64_t)st->B > (1ull << 32))
+            return fail(LORES_EINVAL, "seq_base + B must lie in [0, 2^32]");
+        if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
+            return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
+        const hipStream_t s = (hipStream_t)stream;
+        // int classes first: they carry most of the bytes of a mixed state
+        static const int order[4] = {LORES_INT8, LORES_INT4, LORES_BF16, LORES_FP32};
+        for (int oi = 0; oi < 4; ++oi) {
+            const int c = order[oi];
+            if (!st->n_class[c]) continue;
+            lores::ClassMeta m = make_meta(st, c);
+            m.seed = seed;
+            m.t = t;
+            m.seq_base = seq_base;
+            m.head_base = head_base;
+            lores::StepPtrs p;
+            p.q = q;
+            p.k = k;
+            p.v = v;
+            p.alpha = alpha;
+            p.beta = beta;
+            p.o = o;
+            p.codes = st->base + st->codes_off[c];
+            p.scales = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
+            hipError_t e;
+            switch (c) {
+                case LORES_FP32: e = lores::launch_step_fp32(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
+                case LORES_BF16: e = lores::launch_step_bf16(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
+                case LORES_INT8: e = lores::launch_step_int8(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
+                default: e = lores::launch_step_int4(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
+            }
+            if (e != hipSuccess)
+                return fail(LORES_EHIP, "decode-step launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_decode_step");
+    }
+}
+
+int lores_dequant_state(const lores_state *st, float *out, void *stream) {
+    try {
+        if (!st || !out) return fail(LORES_EINVAL, "NULL argument");
+        if (!aligned(out, 16)) return fail(LORES_EINVAL, "out must be 16-byte aligned");
+        for (int c = 0; c < 4; ++c) {
+            if (!st->n_class[c]) continue;
+            lores::ClassMeta m = make_meta(st, c);
+            const float *sc = is_int_prec(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
+            hipError_t e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
+                                                 (hipStream_t)stream);
+            if (e != hipSuccess) return fail(LORES_EHIP, "dequant launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_dequant_state");
+    }
+}
+
+}  // extern "C"

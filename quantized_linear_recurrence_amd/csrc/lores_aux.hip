@@ -1,0 +1,106 @@
+// Auxiliary kernels: packed state -> fp32 (lores_dequant_state) and the
+// zero fill that sets S_0 = 0 (a plain kernel rather than a memset node, so a
+// caller may capture it in a graph).
+#include "lores_step_impl.h"
+
+namespace lores {
+
+// value = scale * code for int heads (fl of the product), the stored value
+// for bf16 / fp32 heads.  Same wavefront-per-64-rows mapping as the step.
+template <int DK, int PREC>
+__global__ void __launch_bounds__(64 * kWavesPerGroup)
+lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
+                     float *__restrict__ out, const ClassMeta meta) {
+    constexpr int E = Prec<PREC>::E;
+    constexpr int NCH = DK / E;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long task = (long)blockIdx.x * kWavesPerGroup + wv;
+    const long ntask = (long)meta.B * meta.Hc * meta.n_rb;
+    if (task >= ntask) return;
+    const int rb = (int)(task % meta.n_rb);
+    const long unit = task / meta.n_rb;
+    const int slot = (int)(unit % meta.Hc);
+    const int b = (int)(unit / meta.Hc);
+    const int h = meta.heads[slot];
+    const long bh = (long)b * meta.H + h;
+    const int row = rb * 64 + lane;
+    if (row >= meta.dv) return;
+    const long dv_pad = meta.dv_pad;
+    const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * meta.unit_bytes) + row;
+    float s = 0.0f;
+    if constexpr (is_int<PREC>()) s = scales[unit * dv_pad + row];
+    float *orow = out + (bh * meta.dv + row) * DK;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const u32x4 v = cp[c * dv_pad];
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        float x[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if constexpr (PREC == LORES_INT8) {
+                x[e] = s * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
+            } else if constexpr (PREC == LORES_INT4) {
+                const uint32_t w = wd[e >> 3];
+                const uint32_t nib = (w >> (4 * (e & 7))) & 0xFu;
+                x[e] = s * ((float)nib - 8.0f);
+            } else if constexpr (PREC == LORES_BF16) {
+                const uint32_t w = wd[e >> 1];
+                x[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            } else {
+                x[e] = __uint_as_float(wd[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+        }
+    }
+}
+
+template <int PREC>
+static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales, float *out,
+                               const ClassMeta &m, hipStream_t s) {
+    const long ntask = (long)m.B * m.Hc * m.n_rb;
+    const dim3 grid((unsigned)((ntask + kWavesPerGroup - 1) / kWavesPerGroup));
+    const dim3 block(64 * kWavesPerGroup);
+    switch (dk) {
+        case 32: hipLaunchKernelGGL((lores_dequant_kernel<32, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
+                          float *out, const ClassMeta &m, hipStream_t s) {
+    switch (prec) {
+        case LORES_FP32: return dequant_prec<LORES_FP32>(dk, codes, scales, out, m, s);
+        case LORES_BF16: return dequant_prec<LORES_BF16>(dk, codes, scales, out, m, s);
+        case LORES_INT8: return dequant_prec<LORES_INT8>(dk, codes, scales, out, m, s);
+        case LORES_INT4: return dequant_prec<LORES_INT4>(dk, codes, scales, out, m, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// bytes is a multiple of 16 (segments are 256-byte aligned and padded).
+__global__ void __launch_bounds__(256) lores_fill_zero_kernel(u32x4 *__restrict__ p, uint64_t n) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s) {
+    const uint64_t n = bytes / 16;
+    if (n == 0) return hipSuccess;
+    uint64_t groups = (n + 255) / 256;
+    if (groups > 65536) groups = 65536;
+    hipLaunchKernelGGL(lores_fill_zero_kernel, dim3((unsigned)groups), dim3(256), 0, s,
+                       reinterpret_cast<u32x4 *>(buf), n);
+    return hipGetLastError();
+}
+
+}  // namespace lores

@@ -1,0 +1,365 @@
+// Fused LoReS decode step for gfx950: dequantize -> decay -> delta projection
+// -> rank-one write -> readout -> fresh row scale -> stochastic requantize ->
+// pack, in one pass over the state.
+//
+// Method: "Quantizing Recurrent Language Models Is Easier Than You Think",
+// general recurrence form (section "Introduction and Theoretical Foundation")
+//   S_t = S_{t-1} diag(alpha)(I - delta beta k k^T) + beta v k^T,  o_t = S_t q_t
+// evaluated row by row: with S' = S_{t-1} diag(alpha) and r_i = S'_i . k,
+//   U_i = S'_i + g_i k^T,  g_i = beta (v_i - r_i) (delta = 1) or beta v_i,
+// so every value row is independent once its own r_i is known.  The state is
+// requantized each step with one scale per value row and stochastic rounding
+// (section "Intra-State Quantization (Section 4)": scale grouping,
+// Proposition 1, Rounding, Proposition 3).
+//
+// Mapping: one wavefront per (sequence, head, block of 64 value rows); lane i
+// owns row i of the block for the whole step.  All lanes walk the key columns
+// in lock-step, so k_j, q_j and a per-channel alpha_j are wave-uniform and
+// are read with scalar loads into SGPRs; no LDS, no barriers, no cross-lane
+// reductions.  Codes are stored chunk-major (16-byte column chunks of 64
+// consecutive rows), so each chunk load or store of a wavefront is one
+// contiguous 1 KiB access.  The updated row U lives in d_k VGPRs between
+// the passes (dequant+r, update+readout+max, quantize+store).
+//
+// Arithmetic (must match the CPU oracle bit for bit where it decides codes):
+//   int heads   a = fl(s * alpha); S' = fl(c * a), computed as
+//               fma(c + off, a, -off * a) with the stored offset-binary code
+//               c + off (exact: the fma's exact value is c * a, and off * a
+//               is exact as off is a power of two)
+//   r, o        fp32 fma chains (summation order is free; the oracle rounds
+//               an fp64 sum once, and per-step parity absorbs the difference)
+//   g           fl(beta * fl(v - r))            (contraction disabled)
+//   U           fma(g, k_j, S'_j)
+//   s'          fl(m / r) (IEEE division);  inv = the largest fp32 <= r / m
+//   code        e = floor(fma(U, inv, bias + n 2^-16)), bias + n 2^-16 built by
+//               one byte permute of the noise word into a constant's mantissa;
+//               e is the stored offset-binary byte (int8) or, mod 16, the
+//               offset-binary nibble (int4, bias 136 = 128 + 8)
+//   bf16        bits of U plus the 16-bit draw, truncated to the high half
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lores_internal.h"
+
+namespace lores {
+
+// ---------------------------------------------------------------------------
+// counter-based noise: SplitMix64 finalizer (Steele, Lea, Flood 2014) and
+// MurmurHash3 32-bit finalizer (Appleby), as published.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+__device__ __forceinline__ uint32_t fmix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x85EBCA6Bu;
+    x ^= x >> 13;
+    x *= 0xC2B2AE35u;
+    x ^= x >> 16;
+    return x;
+}
+
+// Key of unit (b, h) at step t: fold of a three-level SplitMix64 chain.
+__device__ __forceinline__ uint32_t unit_key(uint64_t seed, uint64_t t, uint64_t b, uint64_t h) {
+    uint64_t z = mix64(mix64(mix64(seed) ^ t) ^ ((b << 32) | (h & 0xFFFFFFFFull)));
+    return (uint32_t)z ^ (uint32_t)(z >> 32);
+}
+
+constexpr uint32_t kPhi32 = 0x9E3779B9u;     // Weyl increment between noise words
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
+
+// ---------------------------------------------------------------------------
+// precision traits: elements per 16-byte chunk, quantizer constants
+// ---------------------------------------------------------------------------
+template <int PREC> struct Prec;
+template <> struct Prec<LORES_FP32> { static constexpr int E = 4; };
+template <> struct Prec<LORES_BF16> { static constexpr int E = 8; };
+template <> struct Prec<LORES_INT8> {
+    static constexpr int E = 16;
+    static constexpr float R = 127.0f;        // 2^(8-1) - 1
+    static constexpr float OFF = 128.0f;      // stored byte = code + 128
+    static constexpr uint32_t FBASE = 0x43000000u;  // 128.0f: mantissa takes n * 2^-16
+};
+template <> struct Prec<LORES_INT4> {
+    static constexpr int E = 32;
+    static constexpr float R = 7.0f;          // 2^(4-1) - 1
+    static constexpr float OFF = 8.0f;        // stored nibble = code + 8
+    static constexpr uint32_t FBASE = 0x43080000u;  // 136.0f = 128 + 8
+};
+
+template <int PREC> constexpr bool is_int() { return PREC == LORES_INT8 || PREC == LORES_INT4; }
+
+// bias + n * 2^-16 for the low (even column) or high (odd column) half of x.
+template <int PREC, bool HI>
+__device__ __forceinline__ float noise_bias(uint32_t x) {
+    // v_perm_b32 bytes: selector 0..3 pick x, 4..7 pick FBASE
+    return __uint_as_float(__builtin_amdgcn_perm(Prec<PREC>::FBASE, x, HI ? 0x07060302u : 0x07060100u));
+}
+
+// Largest fp32 not above r / m (0 for m = 0).
+__device__ __forceinline__ float rd_div(float r, float m) {
+    float q = r / m;                               // IEEE, correctly rounded
+    if (__builtin_fmaf(q, m, -r) > 0.0f) q = __uint_as_float(__float_as_uint(q) - 1u);
+    return m == 0.0f ? 0.0f : q;
+}
+
+// A wave-uniform zero the compiler cannot see through; its data dependence on
+// `dep` keeps scalar loads addressed with it from being hoisted above the
+// computation of `dep`.
+__device__ __forceinline__ long opaque_zero(float dep) {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z) : "v"(dep));
+    return z;
+}
+
+__device__ __forceinline__ long opaque_off(float dep) { return opaque_zero(dep); }
+
+// Input element j of a [.., DK] row at base index `base` (uniform).
+template <bool BF16IN>
+__device__ __forceinline__ float in_elem(const void *__restrict__ p, long base, int j) {
+    if constexpr (BF16IN) {
+        // base is even (a multiple of d_k), so the pair index splits
+        const uint32_t w = ((const uint32_t *)p)[(base >> 1) + (j >> 1)];
+        return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+        return ((const float *)p)[base + j];
+    }
+}
+
+template <bool BF16IN>
+__device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx) {
+    if constexpr (BF16IN) {
+        return __uint_as_float((uint32_t)((const uint16_t *)p)[idx] << 16);
+    } else {
+        return ((const float *)p)[idx];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the step kernel
+// ---------------------------------------------------------------------------
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
+__global__ void __launch_bounds__(64 * kWavesPerGroup)
+lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
+                  const void *__restrict__ vp, const float *__restrict__ alphap,
+                  const float *__restrict__ betap, float *__restrict__ op,
+                  uint8_t *__restrict__ codes, float *__restrict__ scales, const ClassMeta meta) {
+    constexpr int E = Prec<PREC>::E;
+    constexpr int NCH = DK / E;
+    static_assert(DK % E == 0, "d_k must be a whole number of 16-byte chunks");
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long task = (long)blockIdx.x * kWavesPerGroup + wv;
+    const long ntask = (long)meta.B * meta.Hc * meta.n_rb;
+    if (task >= ntask) return;
+    const int rb = (int)(task % meta.n_rb);
+    const long unit = task / meta.n_rb;               // b * Hc + slot
+    const int slot = (int)(unit % meta.Hc);
+    const int b = (int)(unit / meta.Hc);
+    const int h = meta.heads[slot];
+    const long bh = (long)b * meta.H + h;             // index into [B][H] inputs
+    const int row = rb * 64 + lane;
+    const bool active = row < meta.dv;
+    const long dv_pad = meta.dv_pad;
+
+    u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * meta.unit_bytes) + row;
+
+    // ---- load this row's chunks (1 KiB contiguous per wavefront and chunk)
+    u32x4 cw[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        cw[c] = active ? __builtin_nontemporal_load(cp + c * dv_pad) : u32x4{0u, 0u, 0u, 0u};
+
+    const float beta = betap[bh];
+    float alpha_s = 1.0f;
+    if constexpr (!PC) alpha_s = alphap[bh];
+    const long kbase = bh * DK;
+
+    float s = 0.0f, a = 0.0f, na = 0.0f;
+    if constexpr (is_int<PREC>()) {
+        s = active ? scales[unit * dv_pad + row] : 0.0f;
+        if constexpr (!PC) {
+            a = s * alpha_s;
+            na = a * -Prec<PREC>::OFF;
+        }
+    }
+
+    // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
+    // k and a per-channel alpha are read 16 columns at a time into SGPRs;
+    // each group's addresses depend (through opaque_zero) on the last element
+    // of the group two before, so a group is fetched one group ahead of use.
+    float U[DK];
+    float r = 0.0f;
+    constexpr bool kP1Loads = DELTA || PC;          // pass 1 reads k or alpha_j
+    long kb_cur = kbase, kb_next = kbase;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = c * E + e;
+            if (kP1Loads && (j & 15) == 0) {
+                kb_cur = kb_next;
+                // the r chain orders the groups; without it, the last element
+                kb_next = kbase + opaque_off(DELTA ? r : (j ? U[j - 1] : r));
+            }
+            float alpha_j = alpha_s;
+            if constexpr (PC) alpha_j = alphap[kb_cur + j];
+            float sp;
+            if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
+                float ub;
+                if constexpr (PREC == LORES_INT8) {
+                    ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+                } else {
+                    const uint32_t w = wd[e >> 3];
+                    const uint32_t nib = (e & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+                    ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
+                }
+                if constexpr (PC) {
+                    const float aj = s * alpha_j;
+                    sp = (ub - Prec<PREC>::OFF) * aj;
+                } else {
+                    sp = __builtin_fmaf(ub, a, na);
+                }
+            } else if constexpr (PREC == LORES_BF16) {
+                const uint32_t w = wd[e >> 1];
+                sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * alpha_j;
+            } else {
+                sp = __uint_as_float(wd[e]) * alpha_j;
+            }
+            U[j] = sp;
+            if constexpr (DELTA) r = __builtin_fmaf(sp, in_elem<BF16IN>(kp, kb_cur, j), r);
+        }
+    }
+
+    // ---- write gate
+    const float vi = active ? in_scalar<BF16IN>(vp, bh * meta.dv + row) : 0.0f;
+    const float g = DELTA ? beta * (vi - r) : beta * vi;
+
+    // ---- pass 2: rank-one write, readout, row abs-max
+    float o = 0.0f, m = 0.0f;
+    kb_next = kbase + opaque_off(g);
+#pragma unroll
+    for (int j = 0; j < DK; ++j) {
+        if ((j & 15) == 0) {
+            kb_cur = kb_next;
+            kb_next = kbase + opaque_off(o);     // the o chain orders the groups
+        }
+        U[j] = __builtin_fmaf(g, in_elem<BF16IN>(kp, kb_cur, j), U[j]);
+        o = __builtin_fmaf(U[j], in_elem<BF16IN>(qp, kb_cur, j), o);
+        m = fmaxf(m, fabsf(U[j]));
+    }
+    if (active) op[bh * meta.dv + row] = o;
+
+    // ---- pass 3: requantize and store in place
+    float inv = 0.0f;
+    if constexpr (is_int<PREC>()) {
+        const float snew = m / Prec<PREC>::R;
+        inv = rd_div(Prec<PREC>::R, m);
+        if (active) scales[unit * dv_pad + row] = snew;
+    }
+    uint32_t w = 0;
+    if constexpr (PREC != LORES_FP32) {
+        const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
+                                    (uint64_t)(meta.head_base + h));
+        w = fmix32(K ^ (uint32_t)row);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t ow[4];
+        if constexpr (PREC == LORES_INT8) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint32_t by[4];
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int j = c * E + q4 * 4 + 2 * p;
+                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
+                    by[2 * p] = (uint32_t)__builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x));
+                    by[2 * p + 1] = (uint32_t)__builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x));
+                }
+                ow[q4] = by[0] | (by[1] << 8) | (by[2] << 16) | (by[3] << 24);
+            }
+        } else if constexpr (PREC == LORES_INT4) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                uint32_t ev = 0, od = 0;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const int j = c * E + q4 * 8 + 2 * p;
+                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
+                    const uint32_t e0 = (uint32_t)__builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x));
+                    const uint32_t e1 = (uint32_t)__builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x));
+                    ev |= (e0 & 0xFFu) << (8 * p);
+                    od |= (e1 & 0xFFu) << (8 * p);
+                }
+                ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+            }
+        } else if constexpr (PREC == LORES_BF16) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int j = c * E + q4 * 2;
+                const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
+                const uint32_t b0 = __float_as_uint(U[j]) + (x & 0xFFFFu);
+                const uint32_t b1 = __float_as_uint(U[j + 1]) + (x >> 16);
+                ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+            }
+        } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+        }
+        if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
+hipError_t launch_one(const StepPtrs &p, const ClassMeta &m, hipStream_t s) {
+    const long ntask = (long)m.B * m.Hc * m.n_rb;
+    const long groups = (ntask + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL((lores_step_kernel<DK, PREC, PC, DELTA, BF16IN>), dim3((unsigned)groups),
+                       dim3(64 * kWavesPerGroup), 0, s, p.q, p.k, p.v, p.alpha, p.beta, p.o,
+                       p.codes, p.scales, m);
+    return hipGetLastError();
+}
+
+template <int DK, int PREC>
+hipError_t launch_dk(bool pc, bool delta, bool bf16, const StepPtrs &p, const ClassMeta &m,
+                     hipStream_t s) {
+    if (pc) {
+        if (delta) return bf16 ? launch_one<DK, PREC, true, true, true>(p, m, s)
+                               : launch_one<DK, PREC, true, true, false>(p, m, s);
+        return bf16 ? launch_one<DK, PREC, true, false, true>(p, m, s)
+                    : launch_one<DK, PREC, true, false, false>(p, m, s);
+    }
+    if (delta) return bf16 ? launch_one<DK, PREC, false, true, true>(p, m, s)
+                           : launch_one<DK, PREC, false, true, false>(p, m, s);
+    return bf16 ? launch_one<DK, PREC, false, false, true>(p, m, s)
+                : launch_one<DK, PREC, false, false, false>(p, m, s);
+}
+
+template <int PREC>
+hipError_t launch_prec(int dk, bool pc, bool delta, bool bf16, const StepPtrs &p,
+                       const ClassMeta &m, hipStream_t s) {
+    switch (dk) {
+        case 32: return launch_dk<32, PREC>(pc, delta, bf16, p, m, s);
+        case 64: return launch_dk<64, PREC>(pc, delta, bf16, p, m, s);
+        case 96: return launch_dk<96, PREC>(pc, delta, bf16, p, m, s);
+        case 128: return launch_dk<128, PREC>(pc, delta, bf16, p, m, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lores

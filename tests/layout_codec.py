@@ -1,0 +1,97 @@
+"""Host codec of the packed state layout documented in include/lores.h.
+
+Test infrastructure: it converts the oracle's state (signed codes and scales,
+bf16 bit patterns, fp32 values per unit) to the bytes of a device buffer and
+back, using only the offsets lores_state_layout reports and the layout rules
+the header states.  It holds none of the method's arithmetic.
+
+Units of class c are ordered [B][H_c]; slot s of class c is the s-th head of
+that class in head order.
+"""
+import numpy as np
+
+E = {0: 4, 1: 8, 2: 16, 3: 32}       # elements per 16-byte chunk
+OFFSET = {2: 128, 3: 8}              # offset-binary code offset
+
+
+def unit_index(b, slot, Hc):
+    return b * Hc + slot
+
+
+def class_units(head_prec, B, c):
+    """(b, h) of every unit of class c, in storage order."""
+    heads = [h for h, p in enumerate(head_prec) if p == c]
+    return [(b, h) for b in range(B) for h in heads]
+
+
+def pack_unit(c, dk, dv, dv_pad, state_unit):
+    """One unit's state -> (code bytes [n_chunk*dv_pad*16] uint8, scales [dv_pad] fp32 | None).
+
+    state_unit: {"codes": int [dv, dk], "scales": f32 [dv]} (int classes),
+                {"bits": uint16 [dv, dk]} (bf16) or {"X": f32 [dv, dk]} (fp32).
+    """
+    n_chunk = dk // E[c]
+    out = np.zeros((n_chunk, dv_pad, 16), np.uint8)
+    sc = None
+    if c in (2, 3):
+        codes = np.asarray(state_unit["codes"], np.int64)
+        assert codes.min() >= -(127 if c == 2 else 7) and codes.max() <= (127 if c == 2 else 7)
+        sc = np.zeros(dv_pad, np.float32)
+        sc[:dv] = state_unit["scales"]
+        off = (codes + OFFSET[c]).astype(np.uint8)              # [dv, dk]
+        if c == 2:
+            out[:, :dv, :] = off.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
+        else:
+            pairs = off.reshape(dv, n_chunk, 16, 2)
+            by = (pairs[..., 0] | (pairs[..., 1] << 4)).astype(np.uint8)
+            out[:, :dv, :] = by.transpose(1, 0, 2)
+    elif c == 1:
+        bits = np.asarray(state_unit["bits"], np.uint16).reshape(dv, n_chunk, 8)
+        out[:, :dv, :] = bits.view(np.uint8).reshape(dv, n_chunk, 16).transpose(1, 0, 2)
+    else:
+        X = np.ascontiguousarray(np.asarray(state_unit["X"], np.float32)).reshape(dv, n_chunk, 4)
+        out[:, :dv, :] = X.view(np.uint8).reshape(dv, n_chunk, 16).transpose(1, 0, 2)
+    return out.reshape(-1), sc
+
+
+def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None):
+    """Inverse of pack_unit."""
+    n_chunk = dk // E[c]
+    raw = np.asarray(code_bytes, np.uint8).reshape(n_chunk, dv_pad, 16)[:, :dv, :]
+    rows = np.ascontiguousarray(raw.transpose(1, 0, 2)).reshape(dv, n_chunk * 16)
+    if c == 2:
+        return {"codes": rows.astype(np.int32) - 128,
+                "scales": np.asarray(scales, np.float32)[:dv].copy()}
+    if c == 3:
+        lo = (rows & 0x0F).astype(np.int32)
+        hi = (rows >> 4).astype(np.int32)
+        codes = np.stack([lo, hi], axis=-1).reshape(dv, dk) - 8
+        return {"codes": codes, "scales": np.asarray(scales, np.float32)[:dv].copy()}
+    if c == 1:
+        return {"bits": rows.view(np.uint16).reshape(dv, dk).copy()}
+    return {"X": rows.view(np.float32).reshape(dv, dk).copy()}
+
+
+def unit_ranges(layout, c, unit):
+    """Byte ranges (code_start, code_len, scale_start | None, scale_len) of a unit."""
+    ub = layout["unit_code_bytes"][c]
+    cs = layout["codes_offset"][c] + unit * ub
+    if c in (2, 3):
+        dvp = layout["d_v_pad"]
+        return cs, ub, layout["scales_offset"][c] + unit * dvp * 4, dvp * 4
+    return cs, ub, None, 0
+
+
+def read_unit(buf_host, layout, c, unit):
+    """Decode unit `unit` of class c from a host copy (uint8 numpy) of the buffer."""
+    cs, cl, ss, sl = unit_ranges(layout, c, unit)
+    sc = buf_host[ss:ss + sl].view(np.float32) if ss is not None else None
+    return unpack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], buf_host[cs:cs + cl], sc)
+
+
+def write_unit(buf_host, layout, c, unit, state_unit):
+    cs, cl, ss, sl = unit_ranges(layout, c, unit)
+    code_bytes, sc = pack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], state_unit)
+    buf_host[cs:cs + cl] = code_bytes
+    if ss is not None:
+        buf_host[ss:ss + sl] = sc.view(np.uint8)

@@ -1,0 +1,219 @@
+"""GPU-versus-oracle parity harness (test infrastructure).
+
+Protocol: the oracle runs its own trajectory from its own initial state.
+Before every GPU step the oracle's current state of the compared units is
+written into the device buffer (the oracle never receives GPU data); the GPU
+step then runs over the whole batch in the production launch shape, and its
+outputs for the compared units are set against the oracle's step from the
+same state and inputs.  Units not compared keep whatever the GPU computed.
+
+Tolerances (per compared step):
+  codes   at most 1e-4 of codes differ, each by at most 1 (a different dot
+          product summation order can move a pre-rounding value across a
+          rounding threshold)
+  scales  relative difference <= 2^-20
+  bf16    at most 1e-4 of values differ, each by one bf16 ulp
+  o       max |o - o_ref| <= 1e-3 * readout scale (1e-5 for fp32 heads); the
+          readout scale of a unit is max_i |S_ref[i, :]|_2, which bounds |o_i|
+          for a unit-norm q
+  fp32    max |X - X_ref| <= 1e-5 * max_i |X_ref[i, :]|_2
+"""
+import sys
+
+import numpy as np
+import torch
+
+import quantized_linear_recurrence_amd as lores
+from oracle import assign as oassign
+from oracle import step as ostep
+from tests import layout_codec as lc
+from workloads import make_inputs
+
+F32 = np.float32
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def head_precisions(w, inputs, calib_steps=32):
+    """Decay-based precision per head (library) checked against the oracle."""
+    if len(w.tiers) == 1:
+        return [w.tiers[0][1]] * w.H
+    a = inputs["alpha"][:calib_steps].float().cpu().numpy()
+    a = a.reshape(a.shape[0] * a.shape[1], w.H, -1)
+    stat = lores.lores_decay_stat(a)
+    frac = [f for f, _ in w.tiers]
+    prec = [p for _, p in w.tiers]
+    got = lores.lores_assign_precision(stat, frac, prec)
+    want = oassign.assign_precision(oassign.decay_stat(a), frac, prec)
+    assert got == want, (got, want)
+    return got
+
+
+def random_unit_state(c, dv, dk, g):
+    if c in (2, 3):
+        r = 127 if c == 2 else 7
+        return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
+                "scales": np.exp(g.uniform(-7, -2, dv)).astype(F32)}
+    X = (g.standard_normal((dv, dk)) * 0.05).astype(F32)
+    if c == 1:
+        return {"bits": (X.view(np.uint32) >> 16).astype(np.uint16)}
+    return {"X": X}
+
+
+def _stack(states):
+    return {k: np.stack([s[k] for s in states]) for k in states[0]}
+
+
+def _unstack(st, n):
+    return [{k: v[i] for k, v in st.items()} for i in range(n)]
+
+
+class Stats:
+    def __init__(self):
+        self.codes = self.code_diff = 0
+        self.max_dc = 0
+        self.scale_rel = 0.0
+        self.bf16 = self.bf16_diff = 0
+        self.max_dbits = 0
+        self.o_err_q = 0.0
+        self.o_err_f = 0.0
+        self.x_err_f = 0.0
+        self.steps = 0
+
+    def summary(self):
+        return (f"steps={self.steps} code_flip={self.code_diff}/{self.codes} max|dc|={self.max_dc} "
+                f"scale_rel={self.scale_rel:.2e} bf16_flip={self.bf16_diff}/{self.bf16} "
+                f"max|dbits|={self.max_dbits} o_err_q={self.o_err_q:.2e} "
+                f"o_err_f32={self.o_err_f:.2e} x_err_f32={self.x_err_f:.2e}")
+
+    def check(self):
+        assert self.max_dc <= 1, self.summary()
+        assert self.code_diff <= max(1e-4 * self.codes, 0), self.summary()
+        assert self.scale_rel <= 2.0 ** -20, self.summary()
+        assert self.max_dbits <= 1, self.summary()
+        assert self.bf16_diff <= 1e-4 * self.bf16, self.summary()
+        assert self.o_err_q <= 1e-3, self.summary()
+        assert self.o_err_f <= 1e-5, self.summary()
+        assert self.x_err_f <= 1e-5, self.summary()
+
+
+def _readout_scale(X):
+    return np.maximum(np.linalg.norm(X.astype(np.float64), axis=-1).max(axis=-1), 1e-30)
+
+
+def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", inputs=None,
+               device="cuda"):
+    """Run T GPU steps with per-step resync to the oracle; returns Stats.
+
+    units: list of (b, h) to compare (default: all).  init: "zero" (S_0 = 0)
+    or "random" (random codes and scales, or random bf16 / fp32 values).
+    """
+    B = w.B if B is None else B
+    if inputs is None:
+        inputs = make_inputs(w, seed, device, T=T, B=B)
+    if head_prec is None:
+        head_prec = head_precisions(w, inputs)
+    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device)
+    lay = lores.lores_state_layout(st)
+    hprec, hslot = lores.lores_state_head_map(st)
+    assert list(hprec) == list(head_prec)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(w.H)]
+    g = np.random.default_rng(1234 + seed)
+    # oracle state per compared unit
+    ost = {}
+    for (b, h) in units:
+        c = head_prec[h]
+        if init == "zero":
+            s = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk).items()}
+        else:
+            s = random_unit_state(c, w.dv, w.dk, g)
+        ost[(b, h)] = s
+    by_class = {}
+    for (b, h) in units:
+        by_class.setdefault(head_prec[h], []).append((b, h))
+    buf_host = st.buf.cpu().numpy()
+    stats = Stats()
+    per_channel = w.per_channel
+    for t in range(1, T + 1):
+        # resync: install the oracle's state of the compared units
+        for (b, h), s in ost.items():
+            c = head_prec[h]
+            unit = b * lay["n_class"][c] + hslot[h]
+            lc.write_unit(buf_host, lay, c, unit, s)
+            cs, cl, ss, sl = lc.unit_ranges(lay, c, unit)
+            st.buf[cs:cs + cl].copy_(torch.from_numpy(buf_host[cs:cs + cl]))
+            if ss is not None:
+                st.buf[ss:ss + sl].copy_(torch.from_numpy(buf_host[ss:ss + sl]))
+        x = {k: v[t - 1] for k, v in inputs.items()}
+        o = lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], w.delta,
+                                    seed, t)
+        torch.cuda.synchronize()
+        buf_host = st.buf.cpu().numpy()
+        o_host = o.cpu().numpy()
+        xin = {k: v.float().cpu().numpy() for k, v in x.items()}
+        for c, us in by_class.items():
+            bs = np.array([b for b, _ in us])
+            hs = np.array([h for _, h in us])
+            prev = _stack([ost[u] for u in us])
+            q, k, v = xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs]
+            al, be = xin["alpha"][bs, hs], xin["beta"][bs, hs]
+            new, o_ref = ostep.decode_step(c, prev, q, k, v, al, be, w.delta, seed, t, bs, hs)
+            X_ref = ostep.dequant(c, new)
+            scale = _readout_scale(X_ref)
+            o_err = (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()
+            gpu = _stack([lc.read_unit(buf_host, lay, c, b * lay["n_class"][c] + hslot[h])
+                          for (b, h) in us])
+            if c in (2, 3):
+                d = np.abs(gpu["codes"].astype(np.int64) - new["codes"])
+                stats.codes += d.size
+                stats.code_diff += int((d > 0).sum())
+                stats.max_dc = max(stats.max_dc, int(d.max()))
+                rel = np.abs(gpu["scales"].astype(np.float64) - new["scales"]) / \
+                    np.maximum(np.abs(new["scales"]).astype(np.float64), 1e-38)
+                rel[(new["scales"] == 0) & (gpu["scales"] == 0)] = 0
+                stats.scale_rel = max(stats.scale_rel, float(rel.max()))
+                stats.o_err_q = max(stats.o_err_q, float(o_err))
+            elif c == 1:
+                d = np.abs(gpu["bits"].astype(np.int64) - new["bits"].astype(np.int64))
+                stats.bf16 += d.size
+                stats.bf16_diff += int((d > 0).sum())
+                stats.max_dbits = max(stats.max_dbits, int(d.max()))
+                stats.o_err_q = max(stats.o_err_q, float(o_err))
+            else:
+                xe = (np.abs(gpu["X"].astype(np.float64) - new["X"]).max(axis=(1, 2)) / scale).max()
+                stats.x_err_f = max(stats.x_err_f, float(xe))
+                stats.o_err_f = max(stats.o_err_f, float(o_err))
+            for i, u in enumerate(us):
+                ost[u] = {kk: vv[i] for kk, vv in new.items()}
+        stats.steps += 1
+    return stats
+
+
+def run_free_fp32(w, T, B=None, seed=0, device="cuda"):
+    """All heads fp32, no resync: the GPU trajectory against the oracle's over T steps.
+    Returns the worst o error relative to the readout scale."""
+    B = w.B if B is None else B
+    inputs = make_inputs(w, seed, device, T=T, B=B)
+    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, [0] * w.H, device=device)
+    bs = np.repeat(np.arange(B), w.H)
+    hs = np.tile(np.arange(w.H), B)
+    ost = ostep.zero_state(0, B * w.H, w.dv, w.dk)
+    worst = 0.0
+    for t in range(1, T + 1):
+        x = {k: v[t - 1] for k, v in inputs.items()}
+        o = lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], w.delta, 0, t)
+        xin = {k: v.float().cpu().numpy() for k, v in x.items()}
+        q = xin["q"].reshape(B * w.H, -1)
+        k = xin["k"].reshape(B * w.H, -1)
+        v = xin["v"].reshape(B * w.H, -1)
+        al = xin["alpha"].reshape(B * w.H, -1) if w.per_channel else xin["alpha"].reshape(-1)
+        be = xin["beta"].reshape(-1)
+        ost, o_ref = ostep.decode_step(0, ost, q, k, v, al, be, w.delta, 0, t, bs, hs)
+        scale = _readout_scale(ost["X"])
+        err = np.abs(o.cpu().numpy().reshape(B * w.H, -1) - o_ref).max(axis=1) / scale
+        worst = max(worst, float(err.max()))
+    return worst

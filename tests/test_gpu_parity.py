@@ -1,0 +1,89 @@
+"""GPU parity of the HIP decode step against the CPU oracle (through the C ABI).
+
+Every case prints its name before touching the GPU.  See tests/parity.py for
+the protocol and the tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_recurrence_amd as lores
+from tests.parity import log, run_free_fp32, run_parity
+from workloads import get_workload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+C1 = get_workload("C1")
+
+
+def _sample_units(B, H, n, seed=0):
+    g = np.random.default_rng(seed)
+    idx = g.choice(B * H, size=min(n, B * H), replace=False)
+    return sorted((int(i // H), int(i % H)) for i in idx)
+
+
+def test_c1_all_steps_int8():
+    log("case: C1 tiny gated delta rule, int8, all 128 steps, all units")
+    s = run_parity(C1, T=C1.T)
+    log(s.summary())
+    s.check()
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2, 3])
+@pytest.mark.parametrize("delta", [0, 1])
+def test_small_each_precision(prec, delta):
+    w = C1.scaled(B=2, H=3, T=12, delta=delta)
+    log(f"case: small B=2 H=3 d=64 prec={prec} delta={delta}, random initial state")
+    s = run_parity(w, T=w.T, head_prec=[prec] * w.H, init="random")
+    log(s.summary())
+    s.check()
+
+
+@pytest.mark.parametrize("dk,dv", [(96, 100), (32, 1), (128, 65), (64, 128)])
+@pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
+def test_ragged_mixed_precisions(dk, dv, decay):
+    w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=5, decay=decay)
+    log(f"case: ragged mixed B=3 H=4 dk={dk} dv={dv} decay={decay} heads fp32/bf16/int8/int4")
+    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3], init="random")
+    log(s.summary())
+    s.check()
+
+
+def test_bf16_inputs_small():
+    w = C1.scaled(B=2, H=4, T=8, in_bf16=True)
+    log("case: bf16 q/k/v inputs, mixed precisions")
+    s = run_parity(w, T=w.T, head_prec=[2, 3, 1, 0], init="random")
+    log(s.summary())
+    s.check()
+
+
+@pytest.mark.parametrize("key,T,n_units", [("C2", 3, 48), ("C3", 3, 48), ("C4", 3, 48),
+                                           ("C5", 2, 48)])
+def test_full_size_sampled_units(key, T, n_units):
+    w = get_workload(key)
+    log(f"case: {key} full batch B={w.B} H={w.H} d_v={w.dv} d_k={w.dk}, {n_units} sampled units, "
+        f"{T} steps")
+    s = run_parity(w, T=T, units=_sample_units(w.B, w.H, n_units), init="random")
+    log(s.summary())
+    s.check()
+
+
+def test_c5_seed_sweep():
+    w = get_workload("C5")
+    for seed in w.seeds:
+        log(f"case: C5 seed {seed}, 16 sampled units, 1 step")
+        s = run_parity(w, T=1, units=_sample_units(w.B, w.H, 16, seed=seed), seed=seed,
+                       init="random")
+        log(s.summary())
+        s.check()
+
+
+@pytest.mark.parametrize("delta,decay", [(1, "softplus_step"), (0, "softplus_step"),
+                                         (1, "kda_channel")])
+def test_fp32_path_free_running(delta, decay):
+    w = C1.scaled(B=2, H=2, T=128, delta=delta, decay=decay)
+    log(f"case: fp32 heads free-running 128 steps delta={delta} decay={decay}")
+    worst = run_free_fp32(w, T=w.T)
+    log(f"worst o error / readout scale = {worst:.2e}")
+    assert worst <= 1e-5

@@ -1,0 +1,49 @@
+"""The host codec of the packed layout: exhaustive round trips over every code
+value and every byte / nibble / halfword position (CPU only)."""
+import numpy as np
+import pytest
+
+from tests import layout_codec as lc
+
+
+@pytest.mark.parametrize("c,r", [(2, 127), (3, 7)])
+@pytest.mark.parametrize("dk,dv", [(32, 1), (64, 64), (96, 70), (128, 128)])
+def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
+    dv_pad = (dv + 63) // 64 * 64
+    vals = np.arange(-r, r + 1)
+    codes = np.resize(vals, dv * dk).reshape(dv, dk)
+    codes = np.roll(codes, 3, axis=1)                 # every value reaches every column
+    scales = np.linspace(0.5, 2, dv).astype(np.float32)
+    by, sc = lc.pack_unit(c, dk, dv, dv_pad, {"codes": codes, "scales": scales})
+    assert by.size == dv_pad * dk * (8 if c == 2 else 4) // 8
+    back = lc.unpack_unit(c, dk, dv, dv_pad, by, sc)
+    assert np.array_equal(back["codes"], codes) and np.array_equal(back["scales"], scales)
+
+
+def test_int8_byte_positions():
+    dk, dv = 32, 2
+    codes = np.zeros((dv, dk), np.int64)
+    codes[1, 17] = -127                               # row 1, chunk 1, byte 1
+    by, _ = lc.pack_unit(2, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
+    chunk = by.reshape(2, 64, 16)
+    assert chunk[1, 1, 1] == 1 and chunk[0, 0, 0] == 128
+
+
+def test_int4_nibble_positions():
+    dk, dv = 32, 1
+    codes = np.zeros((dv, dk), np.int64)
+    codes[0, 4] = 7                                   # byte 2, low nibble
+    codes[0, 5] = -7                                  # byte 2, high nibble
+    by, _ = lc.pack_unit(3, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
+    assert by.reshape(1, 64, 16)[0, 0, 2] == (15 | (1 << 4))
+
+
+def test_bf16_and_fp32_roundtrip():
+    g = np.random.default_rng(0)
+    for dk, dv in [(32, 3), (128, 65)]:
+        bits = g.integers(0, 65536, (dv, dk), dtype=np.uint16)
+        by, _ = lc.pack_unit(1, dk, dv, (dv + 63) // 64 * 64, {"bits": bits})
+        assert np.array_equal(lc.unpack_unit(1, dk, dv, (dv + 63) // 64 * 64, by)["bits"], bits)
+        X = g.standard_normal((dv, dk)).astype(np.float32)
+        by, _ = lc.pack_unit(0, dk, dv, (dv + 63) // 64 * 64, {"X": X})
+        assert np.array_equal(lc.unpack_unit(0, dk, dv, (dv + 63) // 64 * 64, by)["X"], X)
