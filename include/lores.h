@@ -166,7 +166,8 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
  *               unsharded result bit for bit
  *   o           device out [B][H][d_v] fp32, the readout S_t q_t taken from
  *               the updated state before requantization
- * All device pointers must be 16-byte aligned.  Caller preconditions not
+ * q, k, alpha, beta and o must be 4-byte aligned and v aligned to its
+ * element size (LORES_EINVAL otherwise).  Caller preconditions not
  * checked: |q| = |k| = 1, decay in (0, 1], beta in (0, 2) when delta = 1,
  * finite inputs.  Per element of an int head, with U the updated fp32 row:
  *   scale' = fl(m / r), m = max|U_row|, r = 127 (int8) or 7 (int4);

@@ -260,9 +260,12 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         if (!st) return fail(LORES_EINVAL, "state handle is NULL");
         if (!q || !k || !v || !alpha || !beta || !o)
             return fail(LORES_EINVAL, "q, k, v, alpha, beta and o must be non-NULL device pointers");
-        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(alpha, 16) ||
-            !aligned(beta, 16) || !aligned(o, 16))
-            return fail(LORES_EINVAL, "device pointers must be 16-byte aligned");
+        // q, k, alpha, beta are read as dwords (bf16 q and k as pairs), v one
+        // element per lane, o one fp32 per lane
+        if (!aligned(q, 4) || !aligned(k, 4) || !aligned(alpha, 4) || !aligned(beta, 4) ||
+            !aligned(o, 4) || !aligned(v, in_bf16 ? 2 : 4))
+            return fail(LORES_EINVAL, "q, k, alpha, beta and o must be 4-byte aligned, v aligned "
+                                      "to its element size");
         if (in_bf16 != 0 && in_bf16 != 1) return fail(LORES_EINVAL, "in_bf16 must be 0 or 1");
         if (alpha_per_channel != 0 && alpha_per_channel != 1)
             return fail(LORES_EINVAL, "alpha_per_channel must be 0 or 1");
