@@ -60,6 +60,10 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
     ap.add_argument("--copy-mib", type=int, default=2048)
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="how the timed steps are issued")
+    ap.add_argument("--spin-cycles", type=float, default=2.0e8,
+                    help="GPU spin before the per-step event loop")
     return ap.parse_args(argv)
 
 
@@ -180,40 +184,74 @@ def main(argv=None):
         lores.lores_decode_step(st, inputs["q"][i], inputs["k"][i], inputs["v"][i],
                                 inputs["alpha"][i], inputs["beta"][i], w.delta, args.seed, t, o=o)
 
-    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    n_launches_per_step = sum(1 for c in range(4) if c in head_prec)
+
+    def reset_state():
+        nonlocal st
+        st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf)
+
+    print(f"[bench] warmup {W} eager steps", file=sys.stderr, flush=True)
     for t in range(1, W + 1):
         step(t)
     torch.cuda.synchronize()
-    # fresh state for the timed region
-    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf)
-    torch.cuda.synchronize()
 
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for t in range(1, K + 1):
-        step(t)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # timed region: K steps captured once as a HIP graph (one kernel node per
+    # precision class and step), replayed after a warm replay from a fresh state
+    mode = args.launch
+    if mode == "graph":
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for t in range(1, K + 1):
+                    step(t)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+        except Exception as exc:            # graphs unavailable: time eager launches
+            print(f"[bench] graph capture failed ({exc}); timing eager launches",
+                  file=sys.stderr, flush=True)
+            mode = "eager"
+    reset_state()
+    print(f"[bench] timing {K} steps ({mode})", file=sys.stderr, flush=True)
+    if mode == "graph":
+        ms_total = timed(graph.replay)
+    else:
+        ms_total = timed(lambda: [step(t) for t in range(1, K + 1)])
     ms_step = ms_total / K
+    ms_eager = timed(lambda: [step(t) for t in range(1, min(K, 256) + 1)]) / min(K, 256)
 
-    # per-launch durations on the launch stream (events around each step)
+    # per-step kernel time on the launch stream: events around each step, with
+    # the queue first held behind a GPU spin so the host enqueues ahead of the GPU
     n_lat = min(K, 256)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_lat)]
+    torch.cuda.synchronize()
+    spin = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(args.spin_cycles))
+    spin.record()
+    h0 = time.perf_counter()
     for i in range(n_lat):
         evs[i][0].record()
         step(K + 1 + i)
         evs[i][1].record()
+    enqueue_s = time.perf_counter() - h0
+    spin_done = spin.query()          # False: the GPU was still spinning when enqueue ended
     torch.cuda.synchronize()
-    per_launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    per_launch_ms = [a.elapsed_time(b) for a, b in evs]
     avg_launch_ms = sum(per_launch_ms) / n_lat
-    n_launches_per_step = sum(1 for c in range(4) if c in head_prec)
-    print(f"[bench] {ms_step * 1e3:.2f} us/step over the timed loop; "
-          f"{avg_launch_ms * 1e3:.2f} us average per step with per-step events "
-          f"({n_launches_per_step} kernel launch(es) per step)", file=sys.stderr, flush=True)
+    print(f"[bench] {ms_step * 1e3:.2f} us/step ({mode}); {ms_eager * 1e3:.2f} us/step eager; "
+          f"{avg_launch_ms * 1e3:.2f} us per step inside events "
+          f"({n_launches_per_step} kernel launch(es) per step; host enqueue {enqueue_s * 1e3:.1f} ms, "
+          f"queue {'drained early' if spin_done else 'held'})", file=sys.stderr, flush=True)
 
     achieved = step_bytes / (avg_launch_ms * 1e-3) / 1e9
     traffic = load_traffic(w.key)
@@ -239,6 +277,9 @@ def main(argv=None):
             "rounding": "stochastic", "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,
+        "launch": mode,
+        "ms_per_step_eager": ms_eager,
+        "us_per_step_in_events": avg_launch_ms * 1e3,
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

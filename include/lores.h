@@ -102,7 +102,7 @@ typedef struct {
 
 /*
  * lores_state_alloc - plan the packed layout and bind a caller-owned buffer.
- *   B, H        sequences and heads (1 <= H <= LORES_MAX_HEADS, B >= 1)
+ *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
  *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128},
  *               1 <= d_v <= LORES_MAX_DV
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_INT4)

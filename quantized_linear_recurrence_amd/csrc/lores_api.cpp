@@ -57,7 +57,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int check_dims(int32_t B, int32_t H, int32_t dk, int32_t dv) {
-    if (B < 1) return fail(LORES_EINVAL, "B must be >= 1 (got %d)", B);
+    if (B < 1 || B > 65535) return fail(LORES_EINVAL, "B must be in [1, 65535] (got %d)", B);
     if (H < 1 || H > LORES_MAX_HEADS)
         return fail(LORES_EINVAL, "H must be in [1, %d] (got %d)", LORES_MAX_HEADS, H);
     if (dk < 32 || dk % 32 != 0)
@@ -95,9 +95,7 @@ int plan(lores_state *st, const uint8_t *head_prec) {
             st->scales_off[c] = (int64_t)off;
             off += (uint64_t)st->B * st->n_class[c] * st->dv_pad * sizeof(float);
         }
-        // one wavefront task per (unit, row block); groups of 4 tasks must fit a grid
-        if (units * st->n_rb / lores::kWavesPerGroup > 2147483647.0)
-            return fail(LORES_EINVAL, "too many (sequence, head) units for one launch");
+        // launch grid: y = sequence (at most 65535), x = groups of row-block tasks
     }
     st->total = align256(off);
     return LORES_OK;
@@ -113,7 +111,7 @@ lores::ClassMeta make_meta(const lores_state *st, int c) {
     m.dv_pad = st->dv_pad;
     m.n_rb = st->n_rb;
     m.unit_bytes = st->unit_bytes[c];
-    std::memcpy(m.heads, st->heads[c], sizeof m.heads);
+    for (int i = 0; i < st->n_class[c]; ++i) m.heads[i] = st->heads[c][i];
     return m;
 }
 

@@ -15,14 +15,13 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     constexpr int NCH = DK / E;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long task = (long)blockIdx.x * kWavesPerGroup + wv;
-    const long ntask = (long)meta.B * meta.Hc * meta.n_rb;
-    if (task >= ntask) return;
-    const int rb = (int)(task % meta.n_rb);
-    const long unit = task / meta.n_rb;
-    const int slot = (int)(unit % meta.Hc);
-    const int b = (int)(unit / meta.Hc);
-    const int h = meta.heads[slot];
+    const int task = blockIdx.x * kWavesPerGroup + wv;
+    if (task >= meta.Hc * meta.n_rb) return;
+    const int slot = task / meta.n_rb;
+    const int rb = task - slot * meta.n_rb;
+    const int b = blockIdx.y;
+    const long unit = (long)b * meta.Hc + slot;
+    const int h = (int)meta.heads[slot];
     const long bh = (long)b * meta.H + h;
     const int row = rb * 64 + lane;
     if (row >= meta.dv) return;
@@ -62,8 +61,7 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 template <int PREC>
 static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales, float *out,
                                const ClassMeta &m, hipStream_t s) {
-    const long ntask = (long)m.B * m.Hc * m.n_rb;
-    const dim3 grid((unsigned)((ntask + kWavesPerGroup - 1) / kWavesPerGroup));
+    const dim3 grid((m.Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
     switch (dk) {
         case 32: hipLaunchKernelGGL((lores_dequant_kernel<32, PREC>), grid, block, 0, s, codes, scales, out, m); break;

@@ -10,14 +10,15 @@
 namespace lores {
 
 // Per-launch description of one precision class of a state.  Passed by value
-// as a kernel argument (about 1.1 KiB), so the head table needs no device
-// allocation.
+// as a kernel argument (about 2.1 KiB), so the head table needs no device
+// allocation.  Launch grid: x = groups of kWavesPerGroup (head slot, row
+// block) tasks, y = sequence b.
 struct ClassMeta {
     int32_t B, H, Hc, dv, dv_pad, n_rb;
     int64_t unit_bytes;        // code bytes per (sequence, head) unit
     uint64_t seed, t;
     int64_t seq_base, head_base;
-    uint16_t heads[LORES_MAX_HEADS];   // slot -> head index of this class
+    uint32_t heads[LORES_MAX_HEADS];   // slot -> head index of this class (dwords: scalar loads)
 };
 
 // Pointers of one decode-step launch.

@@ -159,35 +159,52 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const long task = (long)blockIdx.x * kWavesPerGroup + wv;
-    const long ntask = (long)meta.B * meta.Hc * meta.n_rb;
-    if (task >= ntask) return;
-    const int rb = (int)(task % meta.n_rb);
-    const long unit = task / meta.n_rb;               // b * Hc + slot
-    const int slot = (int)(unit % meta.Hc);
-    const int b = (int)(unit / meta.Hc);
-    const int h = meta.heads[slot];
+    const int task = blockIdx.x * kWavesPerGroup + wv;      // (slot, row block) within b
+    if (task >= meta.Hc * meta.n_rb) return;
+    const int slot = meta.n_rb == 1 ? task : meta.n_rb == 2 ? task >> 1
+                   : meta.n_rb == 4 ? task >> 2 : task / 3;
+    const int rb = task - slot * meta.n_rb;
+    const int b = blockIdx.y;
+    const long unit = (long)b * meta.Hc + slot;
+    const int h = (int)meta.heads[slot];
     const long bh = (long)b * meta.H + h;             // index into [B][H] inputs
     const int row = rb * 64 + lane;
     const bool active = row < meta.dv;
     const long dv_pad = meta.dv_pad;
+    const long kbase = bh * DK;
+
+    // Warm L2 with this unit's k and q (and per-channel alpha) using one
+    // 16-byte vector load per lane, issued with the state loads; the scalar
+    // loads of the passes then find them near.  The value is kept alive by an
+    // empty asm at the end.
+    constexpr int kInB = BF16IN ? 2 : 4;
+    constexpr int kVecBytes = DK * kInB;              // bytes of k (and of q)
+    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
+    {
+        const int off = lane * 16;
+        const char *src = nullptr;
+        if (off < kVecBytes) src = (const char *)kp + kbase * kInB + off;
+        else if (off < 2 * kVecBytes) src = (const char *)qp + kbase * kInB + (off - kVecBytes);
+        else if (PC && off < 2 * kVecBytes + DK * 4)
+            src = (const char *)alphap + kbase * 4 + (off - 2 * kVecBytes);
+        if (src) warm = *reinterpret_cast<const u32x4 *>(src);
+    }
 
     u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * meta.unit_bytes) + row;
 
-    // ---- load this row's chunks (1 KiB contiguous per wavefront and chunk)
+    // ---- load this row's chunks (1 KiB contiguous per wavefront and chunk);
+    // padding rows (row >= d_v) lie inside the unit and are read, never written
     u32x4 cw[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-        cw[c] = active ? __builtin_nontemporal_load(cp + c * dv_pad) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
 
     const float beta = betap[bh];
     float alpha_s = 1.0f;
     if constexpr (!PC) alpha_s = alphap[bh];
-    const long kbase = bh * DK;
 
     float s = 0.0f, a = 0.0f, na = 0.0f;
     if constexpr (is_int<PREC>()) {
-        s = active ? scales[unit * dv_pad + row] : 0.0f;
+        s = scales[unit * dv_pad + row];
         if constexpr (!PC) {
             a = s * alpha_s;
             na = a * -Prec<PREC>::OFF;
@@ -243,7 +260,7 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
     }
 
     // ---- write gate
-    const float vi = active ? in_scalar<BF16IN>(vp, bh * meta.dv + row) : 0.0f;
+    const float vi = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
     const float g = DELTA ? beta * (vi - r) : beta * vi;
 
     // ---- pass 2: rank-one write, readout, row abs-max
@@ -320,6 +337,7 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         }
         if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
     }
+    asm volatile("" ::"v"(warm));
 }
 
 // ---------------------------------------------------------------------------
@@ -327,9 +345,8 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
 // ---------------------------------------------------------------------------
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
 hipError_t launch_one(const StepPtrs &p, const ClassMeta &m, hipStream_t s) {
-    const long ntask = (long)m.B * m.Hc * m.n_rb;
-    const long groups = (ntask + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((lores_step_kernel<DK, PREC, PC, DELTA, BF16IN>), dim3((unsigned)groups),
+    const int groups = (m.Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup;
+    hipLaunchKernelGGL((lores_step_kernel<DK, PREC, PC, DELTA, BF16IN>), dim3(groups, m.B),
                        dim3(64 * kWavesPerGroup), 0, s, p.q, p.k, p.v, p.alpha, p.beta, p.o,
                        p.codes, p.scales, m);
     return hipGetLastError();
