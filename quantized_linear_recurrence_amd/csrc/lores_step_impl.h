@@ -105,6 +105,34 @@ __device__ __forceinline__ float noise_bias(uint32_t x) {
     return __uint_as_float(__builtin_amdgcn_perm(Prec<PREC>::FBASE, x, HI ? 0x07060302u : 0x07060100u));
 }
 
+// x & m through an opaque VALU op: the compiler then keeps the byte structure
+// of the result and converts its bytes with v_cvt_f32_ubyte{0..3} instead of
+// re-deriving each nibble with a bit-field extract.
+__device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
+    uint32_t r;
+    asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
+    return r;
+}
+
+// Byte K of `word` := truncation of z (0 <= z < 256) to an integer; the other
+// bytes are kept.  One SDWA convert per element packs the codes for free.
+template <int K>
+__device__ __forceinline__ void cvt_u8_into(uint32_t &word, float z) {
+    if constexpr (K == 0) {
+        asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:BYTE_0 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+            : "+v"(word) : "v"(z));
+    } else if constexpr (K == 1) {
+        asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+            : "+v"(word) : "v"(z));
+    } else if constexpr (K == 2) {
+        asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+            : "+v"(word) : "v"(z));
+    } else {
+        asm("v_cvt_u32_f32_sdwa %0, %1 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+            : "+v"(word) : "v"(z));
+    }
+}
+
 // Largest fp32 not above r / m (0 for m = 0).
 __device__ __forceinline__ float rd_div(float r, float m) {
     float q = r / m;                               // IEEE, correctly rounded
@@ -238,8 +266,10 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                 if constexpr (PREC == LORES_INT8) {
                     ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
                 } else {
+                    // low nibbles (even elements) and high nibbles (odd) as bytes
                     const uint32_t w = wd[e >> 3];
-                    const uint32_t nib = (e & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+                    const uint32_t nib = (e & 1) ? and_opaque(w >> 4, 0x0F0F0F0Fu)
+                                                 : and_opaque(w, 0x0F0F0F0Fu);
                     ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
                 }
                 if constexpr (PC) {
@@ -297,29 +327,40 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         if constexpr (PREC == LORES_INT8) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                uint32_t by[4];
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {
-                    const int j = c * E + q4 * 4 + 2 * p;
-                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
-                    by[2 * p] = (uint32_t)__builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x));
-                    by[2 * p + 1] = (uint32_t)__builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x));
-                }
-                ow[q4] = by[0] | (by[1] << 8) | (by[2] << 16) | (by[3] << 24);
+                const int j = c * E + q4 * 4;
+                const uint32_t x0 = w + (uint32_t)(j >> 1) * kPhi32;
+                const uint32_t x1 = x0 + kPhi32;
+                const float z0 = __builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x0));
+                const float z1 = __builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x0));
+                const float z2 = __builtin_fmaf(U[j + 2], inv, noise_bias<PREC, false>(x1));
+                const float z3 = __builtin_fmaf(U[j + 3], inv, noise_bias<PREC, true>(x1));
+                uint32_t word = (uint32_t)z0;             // 1 <= z < 256: bytes 1..3 are 0
+                cvt_u8_into<1>(word, z1);
+                cvt_u8_into<2>(word, z2);
+                cvt_u8_into<3>(word, z3);
+                ow[q4] = word;
             }
         } else if constexpr (PREC == LORES_INT4) {
+            // e in [129, 143]; its low nibble is the offset-binary code c + 8
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
+                const int j = c * E + q4 * 8;
                 uint32_t ev = 0, od = 0;
+                float ze[4], zo[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const int j = c * E + q4 * 8 + 2 * p;
-                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
-                    const uint32_t e0 = (uint32_t)__builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x));
-                    const uint32_t e1 = (uint32_t)__builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x));
-                    ev |= (e0 & 0xFFu) << (8 * p);
-                    od |= (e1 & 0xFFu) << (8 * p);
+                    const uint32_t x = w + (uint32_t)((j >> 1) + p) * kPhi32;
+                    ze[p] = __builtin_fmaf(U[j + 2 * p], inv, noise_bias<PREC, false>(x));
+                    zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, noise_bias<PREC, true>(x));
                 }
+                ev = (uint32_t)ze[0];
+                od = (uint32_t)zo[0];
+                cvt_u8_into<1>(ev, ze[1]);
+                cvt_u8_into<1>(od, zo[1]);
+                cvt_u8_into<2>(ev, ze[2]);
+                cvt_u8_into<2>(od, zo[2]);
+                cvt_u8_into<3>(ev, ze[3]);
+                cvt_u8_into<3>(od, zo[3]);
                 ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
             }
         } else if constexpr (PREC == LORES_BF16) {
