@@ -101,21 +101,68 @@ int plan(lores_state *st, const uint8_t *head_prec) {
     return LORES_OK;
 }
 
-lores::ClassMeta make_meta(const lores_state *st, int c) {
-    lores::ClassMeta m;
+// Launch description for the classes in `cls` (one, or a fused pair).
+lores::StepMeta make_meta(const lores_state *st, const int *cls, int n_cls) {
+    lores::StepMeta m;
     std::memset(&m, 0, sizeof m);
     m.B = st->B;
     m.H = st->H;
-    m.Hc = st->n_class[c];
     m.dv = st->dv;
     m.dv_pad = st->dv_pad;
     m.n_rb = st->n_rb;
-    m.unit_bytes = st->unit_bytes[c];
-    for (int i = 0; i < st->n_class[c]; ++i) m.heads[i] = st->heads[c][i];
+    m.n_cls = n_cls;
+    int off = 0;
+    for (int i = 0; i < n_cls; ++i) {
+        const int c = cls[i];
+        lores::ClassDesc &d = m.cls[i];
+        d.prec = c;
+        d.Hc = st->n_class[c];
+        d.groups = (d.Hc * st->n_rb + lores::kWavesPerGroup - 1) / lores::kWavesPerGroup;
+        d.head_off = off;
+        d.unit_bytes = st->unit_bytes[c];
+        for (int k = 0; k < d.Hc; ++k) m.heads[off + k] = st->heads[c][k];
+        off += d.Hc;
+    }
+    // a launch of the two int classes pairs task p of one with task p of the
+    // other in one wavefront; `groups` then counts only the unpaired rest
+    if (n_cls == 2 && is_int_prec(cls[0]) && is_int_prec(cls[1])) {
+        const int n0 = m.cls[0].Hc * st->n_rb, n1 = m.cls[1].Hc * st->n_rb;
+        const int paired = n0 < n1 ? n0 : n1;
+        for (int i = 0; i < 2; ++i) {
+            const int rest = (i ? n1 : n0) - paired;
+            m.cls[i].groups = (rest + lores::kWavesPerGroup - 1) / lores::kWavesPerGroup;
+        }
+    }
     return m;
 }
 
 }  // namespace
+
+namespace lores {
+
+bool fusable_pair(int p0, int p1) {
+    return (p0 == LORES_INT8 && p1 == LORES_INT4) || (p0 == LORES_BF16 && p1 == LORES_INT8) ||
+           (p0 == LORES_BF16 && p1 == LORES_INT4);
+}
+
+hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, const StepPtrs &p,
+                       const StepMeta &m, hipStream_t s) {
+    if (p1 < 0) {
+        switch (p0) {
+            case LORES_FP32: return launch_step_fp32(dk, pc, delta, bf16, p, m, s);
+            case LORES_BF16: return launch_step_bf16(dk, pc, delta, bf16, p, m, s);
+            case LORES_INT8: return launch_step_int8(dk, pc, delta, bf16, p, m, s);
+            case LORES_INT4: return launch_step_int4(dk, pc, delta, bf16, p, m, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (p0 == LORES_INT8 && p1 == LORES_INT4) return launch_step_int8_int4(dk, pc, delta, bf16, p, m, s);
+    if (p0 == LORES_BF16 && p1 == LORES_INT8) return launch_step_bf16_int8(dk, pc, delta, bf16, p, m, s);
+    if (p0 == LORES_BF16 && p1 == LORES_INT4) return launch_step_bf16_int4(dk, pc, delta, bf16, p, m, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lores
 
 extern "C" {
 
@@ -274,32 +321,46 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
             return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
         const hipStream_t s = (hipStream_t)stream;
-        // int classes first: they carry most of the bytes of a mixed state
-        static const int order[4] = {LORES_INT8, LORES_INT4, LORES_BF16, LORES_FP32};
-        for (int oi = 0; oi < 4; ++oi) {
-            const int c = order[oi];
-            if (!st->n_class[c]) continue;
-            lores::ClassMeta m = make_meta(st, c);
+        // classes present; a fusable pair shares one launch, anything else
+        // gets one launch per class
+        int present[4], n = 0;
+        for (int c = 0; c < 4; ++c)
+            if (st->n_class[c]) present[n++] = c;
+        int groups[4][2], n_launch = 0, width[4];
+        if (n == 2 && lores::fusable_pair(present[0], present[1])) {
+            groups[0][0] = present[0];
+            groups[0][1] = present[1];
+            width[0] = 2;
+            n_launch = 1;
+        } else {
+            for (int i = 0; i < n; ++i) {
+                groups[i][0] = present[i];
+                width[i] = 1;
+            }
+            n_launch = n;
+        }
+        for (int l = 0; l < n_launch; ++l) {
+            lores::StepMeta m = make_meta(st, groups[l], width[l]);
             m.seed = seed;
             m.t = t;
             m.seq_base = seq_base;
             m.head_base = head_base;
             lores::StepPtrs p;
+            std::memset(&p, 0, sizeof p);
             p.q = q;
             p.k = k;
             p.v = v;
             p.alpha = alpha;
             p.beta = beta;
             p.o = o;
-            p.codes = st->base + st->codes_off[c];
-            p.scales = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
-            hipError_t e;
-            switch (c) {
-                case LORES_FP32: e = lores::launch_step_fp32(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
-                case LORES_BF16: e = lores::launch_step_bf16(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
-                case LORES_INT8: e = lores::launch_step_int8(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
-                default: e = lores::launch_step_int4(st->dk, alpha_per_channel, delta, in_bf16, p, m, s); break;
+            for (int i = 0; i < width[l]; ++i) {
+                const int c = groups[l][i];
+                p.codes[i] = st->base + st->codes_off[c];
+                p.scales[i] = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
             }
+            const int p1 = width[l] == 2 ? groups[l][1] : -1;
+            hipError_t e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16,
+                                              groups[l][0], p1, p, m, s);
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "decode-step launch failed: %s", hipGetErrorString(e));
         }
@@ -315,7 +376,7 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
         if (!aligned(out, 16)) return fail(LORES_EINVAL, "out must be 16-byte aligned");
         for (int c = 0; c < 4; ++c) {
             if (!st->n_class[c]) continue;
-            lores::ClassMeta m = make_meta(st, c);
+            lores::StepMeta m = make_meta(st, &c, 1);
             const float *sc = is_int_prec(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
                                                  (hipStream_t)stream);

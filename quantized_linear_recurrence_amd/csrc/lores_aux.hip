@@ -10,23 +10,24 @@ namespace lores {
 template <int DK, int PREC>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
-                     float *__restrict__ out, const ClassMeta meta) {
+                     float *__restrict__ out, const StepMeta meta) {
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = DK / E;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const ClassDesc &cd = meta.cls[0];
     const int task = blockIdx.x * kWavesPerGroup + wv;
-    if (task >= meta.Hc * meta.n_rb) return;
+    if (task >= cd.Hc * meta.n_rb) return;
     const int slot = task / meta.n_rb;
     const int rb = task - slot * meta.n_rb;
     const int b = blockIdx.y;
-    const long unit = (long)b * meta.Hc + slot;
-    const int h = (int)meta.heads[slot];
+    const long unit = (long)b * cd.Hc + slot;
+    const int h = (int)meta.heads[cd.head_off + slot];
     const long bh = (long)b * meta.H + h;
     const int row = rb * 64 + lane;
     if (row >= meta.dv) return;
     const long dv_pad = meta.dv_pad;
-    const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * meta.unit_bytes) + row;
+    const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * cd.unit_bytes) + row;
     float s = 0.0f;
     if constexpr (is_int<PREC>()) s = scales[unit * dv_pad + row];
     float *orow = out + (bh * meta.dv + row) * DK;
@@ -60,8 +61,8 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 
 template <int PREC>
 static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales, float *out,
-                               const ClassMeta &m, hipStream_t s) {
-    const dim3 grid((m.Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
+                               const StepMeta &m, hipStream_t s) {
+    const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
     switch (dk) {
         case 32: hipLaunchKernelGGL((lores_dequant_kernel<32, PREC>), grid, block, 0, s, codes, scales, out, m); break;
@@ -74,7 +75,7 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
 }
 
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                          float *out, const ClassMeta &m, hipStream_t s) {
+                          float *out, const StepMeta &m, hipStream_t s) {
     switch (prec) {
         case LORES_FP32: return dequant_prec<LORES_FP32>(dk, codes, scales, out, m, s);
         case LORES_BF16: return dequant_prec<LORES_BF16>(dk, codes, scales, out, m, s);

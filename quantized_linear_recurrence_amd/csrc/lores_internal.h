@@ -9,40 +9,56 @@
 
 namespace lores {
 
-// Per-launch description of one precision class of a state.  Passed by value
-// as a kernel argument (about 2.1 KiB), so the head table needs no device
-// allocation.  Launch grid: x = groups of kWavesPerGroup (head slot, row
-// block) tasks, y = sequence b.
-struct ClassMeta {
-    int32_t B, H, Hc, dv, dv_pad, n_rb;
-    int64_t unit_bytes;        // code bytes per (sequence, head) unit
-    uint64_t seed, t;
-    int64_t seq_base, head_base;
-    uint32_t heads[LORES_MAX_HEADS];   // slot -> head index of this class (dwords: scalar loads)
+// One precision class inside a decode-step launch.
+struct ClassDesc {
+    int32_t prec;          // LORES_* code
+    int32_t Hc;            // heads of the class
+    int32_t groups;        // work-groups along grid x: ceil(Hc * n_rb / kWavesPerGroup)
+    int32_t head_off;      // first entry of the class's head list in StepMeta::heads
+    int64_t unit_bytes;    // code bytes per (sequence, head) unit
 };
 
-// Pointers of one decode-step launch.
+// Description of one launch, passed by value as a kernel argument (about
+// 2.2 KiB), so no device allocation is needed.  Grid: x runs over the
+// work-groups of class 0 then class 1 (kWavesPerGroup (head slot, row block)
+// tasks each); y strides over sequences: a wavefront handles sequences
+// blockIdx.y, blockIdx.y + gridDim.y, ...
+struct StepMeta {
+    int32_t B, H, dv, dv_pad, n_rb, n_cls;
+    uint64_t seed, t;
+    int64_t seq_base, head_base;
+    ClassDesc cls[2];
+    uint32_t heads[LORES_MAX_HEADS];   // head indices, class by class (dwords: scalar loads)
+};
+
+// Pointers of one decode-step launch (codes / scales per class of the launch).
 struct StepPtrs {
     const void *q, *k, *v;
     const float *alpha, *beta;
     float *o;
-    uint8_t *codes;   // class code segment
-    float *scales;    // class scale segment (int classes), else nullptr
+    uint8_t *codes[2];
+    float *scales[2];        // int classes, else nullptr
 };
 
-// Launchers, one translation unit per precision class.  Each returns the
+// One launch covers one class or one of the fused pairs (int8, int4),
+// (bf16, int8), (bf16, int4); `p1` is -1 for a single class.  Returns the
 // launch status; `dk` is one of 32, 64, 96, 128.
-hipError_t launch_step_fp32(int dk, bool per_channel, bool delta, bool in_bf16,
-                            const StepPtrs &p, const ClassMeta &m, hipStream_t s);
-hipError_t launch_step_bf16(int dk, bool per_channel, bool delta, bool in_bf16,
-                            const StepPtrs &p, const ClassMeta &m, hipStream_t s);
-hipError_t launch_step_int8(int dk, bool per_channel, bool delta, bool in_bf16,
-                            const StepPtrs &p, const ClassMeta &m, hipStream_t s);
-hipError_t launch_step_int4(int dk, bool per_channel, bool delta, bool in_bf16,
-                            const StepPtrs &p, const ClassMeta &m, hipStream_t s);
+hipError_t launch_step(int dk, bool per_channel, bool delta, bool in_bf16, int p0, int p1,
+                       const StepPtrs &p, const StepMeta &m, hipStream_t s);
+bool fusable_pair(int p0, int p1);
 
+// Per-translation-unit launchers behind launch_step.
+hipError_t launch_step_fp32(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_bf16(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_int8_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_bf16_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_bf16_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+
+// Dequant uses the same StepMeta with one class.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                          float *out, const ClassMeta &m, hipStream_t s);
+                          float *out, const StepMeta &m, hipStream_t s);
 hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);
 
 // Tasks (one wavefront each) per 256-thread work-group.

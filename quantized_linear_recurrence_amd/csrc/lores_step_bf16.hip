@@ -1,11 +1,12 @@
-// Decode-step kernels for LORES_BF16 heads (see lores_step_impl.h).
+// Decode-step kernels for a state whose launch holds only LORES_BF16 heads
+// (see lores_step_impl.h).
 #include "lores_step_impl.h"
 
 namespace lores {
 
 hipError_t launch_step_bf16(int dk, bool per_channel, bool delta, bool in_bf16,
-                          const StepPtrs &p, const ClassMeta &m, hipStream_t s) {
-    return launch_prec<LORES_BF16>(dk, per_channel, delta, in_bf16, p, m, s);
+                          const StepPtrs &p, const StepMeta &m, hipStream_t s) {
+    return launch_classes<LORES_BF16, -1>(dk, per_channel, delta, in_bf16, p, m, s);
 }
 
 }  // namespace lores

@@ -1,11 +1,12 @@
-// Decode-step kernels for LORES_FP32 heads (see lores_step_impl.h).
+// Decode-step kernels for a state whose launch holds only LORES_FP32 heads
+// (see lores_step_impl.h).
 #include "lores_step_impl.h"
 
 namespace lores {
 
 hipError_t launch_step_fp32(int dk, bool per_channel, bool delta, bool in_bf16,
-                          const StepPtrs &p, const ClassMeta &m, hipStream_t s) {
-    return launch_prec<LORES_FP32>(dk, per_channel, delta, in_bf16, p, m, s);
+                          const StepPtrs &p, const StepMeta &m, hipStream_t s) {
+    return launch_classes<LORES_FP32, -1>(dk, per_channel, delta, in_bf16, p, m, s);
 }
 
 }  // namespace lores

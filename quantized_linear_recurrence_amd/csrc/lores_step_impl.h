@@ -173,249 +173,433 @@ __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx)
 }
 
 // ---------------------------------------------------------------------------
-// the step kernel
+// one (class, head slot, row block) stream of tasks
 // ---------------------------------------------------------------------------
+// A wavefront owns one (head slot, row block) of a class and walks the
+// sequences b = blockIdx.y, blockIdx.y + gridDim.y, ...  `issue` starts the
+// loads of one task (its chunks, row scale and v, plus one 16-byte load per
+// lane of its k and q, and per-channel alpha, that warms L2 for the scalar
+// loads of the passes); `run` computes and stores it and calls `mid` right
+// after pass 1, when the chunk registers are free, so the caller can start
+// the next task's loads there.
+constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
+
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
+struct TaskStream {
+    static constexpr int E = Prec<PREC>::E;
+    static constexpr int NCH = DK / E;
+    static_assert(DK % E == 0, "d_k must be a whole number of 16-byte chunks");
+    static constexpr int kInB = BF16IN ? 2 : 4;
+    static constexpr int kVecBytes = DK * kInB;      // bytes of k (and of q)
+
+    const void *__restrict__ qp;
+    const void *__restrict__ kp;
+    const void *__restrict__ vp;
+    const float *__restrict__ alphap;
+    const float *__restrict__ betap;
+    float *__restrict__ op;
+    uint8_t *__restrict__ codes;
+    float *__restrict__ scales;
+    const StepMeta &meta;
+    int Hc, slot, h, row;
+    long unit_bytes;
+    bool active;
+
+    __device__ __forceinline__ TaskStream(const void *q, const void *k, const void *v,
+                                          const float *alpha, const float *beta, float *o,
+                                          uint8_t *c, float *sc, const StepMeta &m,
+                                          const ClassDesc &cd, int task)
+        : qp(q), kp(k), vp(v), alphap(alpha), betap(beta), op(o), codes(c), scales(sc), meta(m) {
+        const int n_rb = m.n_rb;
+        slot = n_rb == 1 ? task : n_rb == 2 ? task >> 1 : n_rb == 4 ? task >> 2 : task / 3;
+        const int rb = task - slot * n_rb;
+        Hc = cd.Hc;
+        unit_bytes = cd.unit_bytes;
+        h = (int)m.heads[cd.head_off + slot];
+        row = rb * 64 + (threadIdx.x & 63);
+        active = row < m.dv;
+    }
+
+    __device__ __forceinline__ void issue(int b, u32x4 *cw, float &s_in, float &v_in,
+                                          u32x4 &warm) const {
+        const long dv_pad = meta.dv_pad;
+        const long unit = (long)b * Hc + slot;
+        const long bh = (long)b * meta.H + h;
+        // padding rows (row >= d_v) lie inside the unit and are read, never written
+        const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + row;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
+        if constexpr (is_int<PREC>()) s_in = scales[unit * dv_pad + row];
+        v_in = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
+        const int off = (threadIdx.x & 63) * 16;
+        const long kb = bh * DK;
+        const char *src = nullptr;
+        if (off < kVecBytes) src = (const char *)kp + kb * kInB + off;
+        else if (off < 2 * kVecBytes) src = (const char *)qp + kb * kInB + (off - kVecBytes);
+        else if (PC && off < 2 * kVecBytes + DK * 4)
+            src = (const char *)alphap + kb * 4 + (off - 2 * kVecBytes);
+        if (src) warm = *reinterpret_cast<const u32x4 *>(src);
+    }
+
+    template <class Mid>
+    __device__ __forceinline__ void run(int b, const u32x4 *cw, float s, float vi, Mid &&mid) const {
+        const long dv_pad = meta.dv_pad;
+        const long unit = (long)b * Hc + slot;
+        const long bh = (long)b * meta.H + h;           // index into [B][H] inputs
+        const long kbase = bh * DK;
+        u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * unit_bytes) + row;
+
+        const float beta = betap[bh];
+        float alpha_s = 1.0f;
+        if constexpr (!PC) alpha_s = alphap[bh];
+        float a = 0.0f, na = 0.0f;
+        if constexpr (is_int<PREC>() && !PC) {
+            a = s * alpha_s;
+            na = a * -Prec<PREC>::OFF;
+        }
+
+        // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
+        // k and a per-channel alpha are read 16 columns at a time into SGPRs;
+        // each group's addresses depend (through opaque_zero) on the r chain
+        // (or the last element) of the group two before, which keeps the
+        // compiler from hoisting every uniform load and spilling SGPRs.
+        float U[DK];
+        float r = 0.0f;
+        constexpr bool kP1Loads = DELTA || PC;          // pass 1 reads k or alpha_j
+        long kb_cur = kbase, kb_next = kbase;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int j = c * E + e;
+                if (kP1Loads && (j & 15) == 0) {
+                    kb_cur = kb_next;
+                    kb_next = kbase + opaque_off(DELTA ? r : (j ? U[j - 1] : r));
+                }
+                float alpha_j = alpha_s;
+                if constexpr (PC) alpha_j = alphap[kb_cur + j];
+                float sp;
+                if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
+                    float ub;
+                    if constexpr (PREC == LORES_INT8) {
+                        ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+                    } else {
+                        // low nibbles (even elements) and high nibbles (odd) as bytes
+                        const uint32_t w = wd[e >> 3];
+                        const uint32_t nib = (e & 1) ? and_opaque(w >> 4, 0x0F0F0F0Fu)
+                                                     : and_opaque(w, 0x0F0F0F0Fu);
+                        ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
+                    }
+                    if constexpr (PC) {
+                        const float aj = s * alpha_j;
+                        sp = (ub - Prec<PREC>::OFF) * aj;
+                    } else {
+                        sp = __builtin_fmaf(ub, a, na);
+                    }
+                } else if constexpr (PREC == LORES_BF16) {
+                    const uint32_t w = wd[e >> 1];
+                    sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * alpha_j;
+                } else {
+                    sp = __uint_as_float(wd[e]) * alpha_j;
+                }
+                U[j] = sp;
+                if constexpr (DELTA) r = __builtin_fmaf(sp, in_elem<BF16IN>(kp, kb_cur, j), r);
+            }
+        }
+
+        mid();                                           // the chunks are consumed
+
+        // ---- write gate
+        const float g = DELTA ? beta * (vi - r) : beta * vi;
+
+        // ---- pass 2: rank-one write, readout, row abs-max
+        float o = 0.0f, m = 0.0f;
+        kb_next = kbase + opaque_off(g);
+#pragma unroll
+        for (int j = 0; j < DK; ++j) {
+            if ((j & 15) == 0) {
+                kb_cur = kb_next;
+                kb_next = kbase + opaque_off(o);     // the o chain orders the groups
+            }
+            U[j] = __builtin_fmaf(g, in_elem<BF16IN>(kp, kb_cur, j), U[j]);
+            o = __builtin_fmaf(U[j], in_elem<BF16IN>(qp, kb_cur, j), o);
+            m = fmaxf(m, fabsf(U[j]));
+        }
+        if (active) op[bh * meta.dv + row] = o;
+
+        // ---- pass 3: requantize and store in place
+        float inv = 0.0f;
+        if constexpr (is_int<PREC>()) {
+            const float snew = m / Prec<PREC>::R;
+            inv = rd_div(Prec<PREC>::R, m);
+            if (active) scales[unit * dv_pad + row] = snew;
+        }
+        uint32_t w = 0;
+        if constexpr (PREC != LORES_FP32) {
+            const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
+                                        (uint64_t)(meta.head_base + h));
+            w = fmix32(K ^ (uint32_t)row);
+        }
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            uint32_t ow[4];
+            if constexpr (PREC == LORES_INT8) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 4;
+                    const uint32_t x0 = w + (uint32_t)(j >> 1) * kPhi32;
+                    const uint32_t x1 = x0 + kPhi32;
+                    const float z0 = __builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x0));
+                    const float z1 = __builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x0));
+                    const float z2 = __builtin_fmaf(U[j + 2], inv, noise_bias<PREC, false>(x1));
+                    const float z3 = __builtin_fmaf(U[j + 3], inv, noise_bias<PREC, true>(x1));
+                    uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
+                    cvt_u8_into<1>(word, z1);
+                    cvt_u8_into<2>(word, z2);
+                    cvt_u8_into<3>(word, z3);
+                    ow[q4] = word;
+                }
+            } else if constexpr (PREC == LORES_INT4) {
+                // e in [129, 143]; its low nibble is the offset-binary code c + 8
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 8;
+                    float ze[4], zo[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const uint32_t x = w + (uint32_t)((j >> 1) + p) * kPhi32;
+                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, noise_bias<PREC, false>(x));
+                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, noise_bias<PREC, true>(x));
+                    }
+                    uint32_t ev = (uint32_t)ze[0];
+                    uint32_t od = (uint32_t)zo[0];
+                    cvt_u8_into<1>(ev, ze[1]);
+                    cvt_u8_into<1>(od, zo[1]);
+                    cvt_u8_into<2>(ev, ze[2]);
+                    cvt_u8_into<2>(od, zo[2]);
+                    cvt_u8_into<3>(ev, ze[3]);
+                    cvt_u8_into<3>(od, zo[3]);
+                    ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+                }
+            } else if constexpr (PREC == LORES_BF16) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 2;
+                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
+                    const uint32_t b0 = __float_as_uint(U[j]) + (x & 0xFFFFu);
+                    const uint32_t b1 = __float_as_uint(U[j + 1]) + (x >> 16);
+                    ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                }
+            } else {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+            }
+            if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+        }
+    }
+};
+
+// One stream over all its sequences.  For int classes the next sequence's
+// loads are issued right after pass 1 (a second chunk set fits in the
+// registers); bf16 / fp32 rows are loaded at the top of each task.
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
+__device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN> &ts) {
+    using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN>;
+    constexpr bool kPrefetch = TS::NCH <= kMaxPrefetchChunks;
+    const int bstep = gridDim.y;
+    u32x4 cw[TS::NCH];
+    float s_in = 0.0f, v_in = 0.0f;
+    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
+    int b = blockIdx.y;
+    ts.issue(b, cw, s_in, v_in, warm);
+    while (true) {
+        const int bn = b + bstep;
+        const float s = s_in, vi = v_in;
+        ts.run(b, cw, s, vi, [&] {
+            asm volatile("" ::"v"(warm));
+            if constexpr (kPrefetch) {
+                if (bn < ts.meta.B) ts.issue(bn, cw, s_in, v_in, warm);
+            }
+        });
+        if (bn >= ts.meta.B) break;
+        b = bn;
+        if constexpr (!kPrefetch) ts.issue(b, cw, s_in, v_in, warm);
+    }
+}
+
+// Two streams of different int classes in one wavefront, alternating task by
+// task: every wavefront (so every SIMD) carries the same mix of the
+// VALU-heavier and the HBM-heavier class, and each task's pass 1 is followed
+// by the loads of the other stream's next task.
+template <int DK, int P0, int P1, bool PC, bool DELTA, bool BF16IN>
+__device__ __forceinline__ void run_paired(const TaskStream<DK, P0, PC, DELTA, BF16IN> &t0,
+                                           const TaskStream<DK, P1, PC, DELTA, BF16IN> &t1) {
+    static_assert(TaskStream<DK, P0, PC, DELTA, BF16IN>::NCH <= kMaxPrefetchChunks &&
+                      TaskStream<DK, P1, PC, DELTA, BF16IN>::NCH <= kMaxPrefetchChunks,
+                  "paired streams need prefetchable rows");
+    const int bstep = gridDim.y;
+    u32x4 cw[kMaxPrefetchChunks];
+    float s_in = 0.0f, v_in = 0.0f;
+    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
+    int b = blockIdx.y;
+    t0.issue(b, cw, s_in, v_in, warm);
+    while (true) {
+        const int bn = b + bstep;
+        float s = s_in, vi = v_in;
+        t0.run(b, cw, s, vi, [&] {
+            asm volatile("" ::"v"(warm));
+            t1.issue(b, cw, s_in, v_in, warm);
+        });
+        s = s_in;
+        vi = v_in;
+        t1.run(b, cw, s, vi, [&] {
+            asm volatile("" ::"v"(warm));
+            if (bn < t0.meta.B) t0.issue(bn, cw, s_in, v_in, warm);
+        });
+        if (bn >= t0.meta.B) break;
+        b = bn;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the step kernel: one class (P1 < 0) or a fused pair of classes
+// ---------------------------------------------------------------------------
+// Grid x, single class: groups of kWavesPerGroup tasks of class 0.  Fused
+// pair: first the paired groups (task p of class 0 with task p of class 1,
+// when both classes are prefetchable int classes), then the remaining tasks
+// of class 0, then those of class 1.  meta.cls[i].groups counts the groups
+// of the unpaired remainder of class i; the paired groups number
+// ceil(min(n0, n1) / kWavesPerGroup) when pairing applies, else 0.
+template <int P0, int P1, int DK>
+constexpr bool pairable() {
+    if constexpr (P1 < 0 || !is_int<P0>() || !is_int<P1>()) {
+        return false;
+    } else {
+        return DK / Prec<P0>::E <= kMaxPrefetchChunks && DK / Prec<P1>::E <= kMaxPrefetchChunks;
+    }
+}
+
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
-                  uint8_t *__restrict__ codes, float *__restrict__ scales, const ClassMeta meta) {
-    constexpr int E = Prec<PREC>::E;
-    constexpr int NCH = DK / E;
-    static_assert(DK % E == 0, "d_k must be a whole number of 16-byte chunks");
-
-    const int lane = threadIdx.x & 63;
+                  uint8_t *__restrict__ codes0, float *__restrict__ scales0,
+                  uint8_t *__restrict__ codes1, float *__restrict__ scales1, const StepMeta meta) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int task = blockIdx.x * kWavesPerGroup + wv;      // (slot, row block) within b
-    if (task >= meta.Hc * meta.n_rb) return;
-    const int slot = meta.n_rb == 1 ? task : meta.n_rb == 2 ? task >> 1
-                   : meta.n_rb == 4 ? task >> 2 : task / 3;
-    const int rb = task - slot * meta.n_rb;
-    const int b = blockIdx.y;
-    const long unit = (long)b * meta.Hc + slot;
-    const int h = (int)meta.heads[slot];
-    const long bh = (long)b * meta.H + h;             // index into [B][H] inputs
-    const int row = rb * 64 + lane;
-    const bool active = row < meta.dv;
-    const long dv_pad = meta.dv_pad;
-    const long kbase = bh * DK;
-
-    // Warm L2 with this unit's k and q (and per-channel alpha) using one
-    // 16-byte vector load per lane, issued with the state loads; the scalar
-    // loads of the passes then find them near.  The value is kept alive by an
-    // empty asm at the end.
-    constexpr int kInB = BF16IN ? 2 : 4;
-    constexpr int kVecBytes = DK * kInB;              // bytes of k (and of q)
-    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
-    {
-        const int off = lane * 16;
-        const char *src = nullptr;
-        if (off < kVecBytes) src = (const char *)kp + kbase * kInB + off;
-        else if (off < 2 * kVecBytes) src = (const char *)qp + kbase * kInB + (off - kVecBytes);
-        else if (PC && off < 2 * kVecBytes + DK * 4)
-            src = (const char *)alphap + kbase * 4 + (off - 2 * kVecBytes);
-        if (src) warm = *reinterpret_cast<const u32x4 *>(src);
-    }
-
-    u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * meta.unit_bytes) + row;
-
-    // ---- load this row's chunks (1 KiB contiguous per wavefront and chunk);
-    // padding rows (row >= d_v) lie inside the unit and are read, never written
-    u32x4 cw[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
-
-    const float beta = betap[bh];
-    float alpha_s = 1.0f;
-    if constexpr (!PC) alpha_s = alphap[bh];
-
-    float s = 0.0f, a = 0.0f, na = 0.0f;
-    if constexpr (is_int<PREC>()) {
-        s = scales[unit * dv_pad + row];
-        if constexpr (!PC) {
-            a = s * alpha_s;
-            na = a * -Prec<PREC>::OFF;
+    int gx = blockIdx.x;
+    const int n_rb = meta.n_rb;
+    if constexpr (P1 < 0) {
+        const int task = gx * kWavesPerGroup + wv;
+        if (task >= meta.cls[0].Hc * n_rb) return;
+        run_single(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op, codes0,
+                                                         scales0, meta, meta.cls[0], task));
+    } else {
+        const int n0 = meta.cls[0].Hc * n_rb, n1 = meta.cls[1].Hc * n_rb;
+        int paired = 0;
+        if constexpr (pairable<P0, P1, DK>()) {
+            paired = n0 < n1 ? n0 : n1;
+            const int pg = (paired + kWavesPerGroup - 1) / kWavesPerGroup;
+            if (gx < pg) {
+                const int task = gx * kWavesPerGroup + wv;
+                if (task >= paired) return;
+                run_paired(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
+                                                                 codes0, scales0, meta,
+                                                                 meta.cls[0], task),
+                           TaskStream<DK, P1, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
+                                                                 codes1, scales1, meta,
+                                                                 meta.cls[1], task));
+                return;
+            }
+            gx -= pg;
         }
-    }
-
-    // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
-    // k and a per-channel alpha are read 16 columns at a time into SGPRs;
-    // each group's addresses depend (through opaque_zero) on the last element
-    // of the group two before, so a group is fetched one group ahead of use.
-    float U[DK];
-    float r = 0.0f;
-    constexpr bool kP1Loads = DELTA || PC;          // pass 1 reads k or alpha_j
-    long kb_cur = kbase, kb_next = kbase;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = c * E + e;
-            if (kP1Loads && (j & 15) == 0) {
-                kb_cur = kb_next;
-                // the r chain orders the groups; without it, the last element
-                kb_next = kbase + opaque_off(DELTA ? r : (j ? U[j - 1] : r));
-            }
-            float alpha_j = alpha_s;
-            if constexpr (PC) alpha_j = alphap[kb_cur + j];
-            float sp;
-            if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
-                float ub;
-                if constexpr (PREC == LORES_INT8) {
-                    ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-                } else {
-                    // low nibbles (even elements) and high nibbles (odd) as bytes
-                    const uint32_t w = wd[e >> 3];
-                    const uint32_t nib = (e & 1) ? and_opaque(w >> 4, 0x0F0F0F0Fu)
-                                                 : and_opaque(w, 0x0F0F0F0Fu);
-                    ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
-                }
-                if constexpr (PC) {
-                    const float aj = s * alpha_j;
-                    sp = (ub - Prec<PREC>::OFF) * aj;
-                } else {
-                    sp = __builtin_fmaf(ub, a, na);
-                }
-            } else if constexpr (PREC == LORES_BF16) {
-                const uint32_t w = wd[e >> 1];
-                sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * alpha_j;
-            } else {
-                sp = __uint_as_float(wd[e]) * alpha_j;
-            }
-            U[j] = sp;
-            if constexpr (DELTA) r = __builtin_fmaf(sp, in_elem<BF16IN>(kp, kb_cur, j), r);
-        }
-    }
-
-    // ---- write gate
-    const float vi = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
-    const float g = DELTA ? beta * (vi - r) : beta * vi;
-
-    // ---- pass 2: rank-one write, readout, row abs-max
-    float o = 0.0f, m = 0.0f;
-    kb_next = kbase + opaque_off(g);
-#pragma unroll
-    for (int j = 0; j < DK; ++j) {
-        if ((j & 15) == 0) {
-            kb_cur = kb_next;
-            kb_next = kbase + opaque_off(o);     // the o chain orders the groups
-        }
-        U[j] = __builtin_fmaf(g, in_elem<BF16IN>(kp, kb_cur, j), U[j]);
-        o = __builtin_fmaf(U[j], in_elem<BF16IN>(qp, kb_cur, j), o);
-        m = fmaxf(m, fabsf(U[j]));
-    }
-    if (active) op[bh * meta.dv + row] = o;
-
-    // ---- pass 3: requantize and store in place
-    float inv = 0.0f;
-    if constexpr (is_int<PREC>()) {
-        const float snew = m / Prec<PREC>::R;
-        inv = rd_div(Prec<PREC>::R, m);
-        if (active) scales[unit * dv_pad + row] = snew;
-    }
-    uint32_t w = 0;
-    if constexpr (PREC != LORES_FP32) {
-        const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
-                                    (uint64_t)(meta.head_base + h));
-        w = fmix32(K ^ (uint32_t)row);
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        uint32_t ow[4];
-        if constexpr (PREC == LORES_INT8) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 4;
-                const uint32_t x0 = w + (uint32_t)(j >> 1) * kPhi32;
-                const uint32_t x1 = x0 + kPhi32;
-                const float z0 = __builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x0));
-                const float z1 = __builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x0));
-                const float z2 = __builtin_fmaf(U[j + 2], inv, noise_bias<PREC, false>(x1));
-                const float z3 = __builtin_fmaf(U[j + 3], inv, noise_bias<PREC, true>(x1));
-                uint32_t word = (uint32_t)z0;             // 1 <= z < 256: bytes 1..3 are 0
-                cvt_u8_into<1>(word, z1);
-                cvt_u8_into<2>(word, z2);
-                cvt_u8_into<3>(word, z3);
-                ow[q4] = word;
-            }
-        } else if constexpr (PREC == LORES_INT4) {
-            // e in [129, 143]; its low nibble is the offset-binary code c + 8
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 8;
-                uint32_t ev = 0, od = 0;
-                float ze[4], zo[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t x = w + (uint32_t)((j >> 1) + p) * kPhi32;
-                    ze[p] = __builtin_fmaf(U[j + 2 * p], inv, noise_bias<PREC, false>(x));
-                    zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, noise_bias<PREC, true>(x));
-                }
-                ev = (uint32_t)ze[0];
-                od = (uint32_t)zo[0];
-                cvt_u8_into<1>(ev, ze[1]);
-                cvt_u8_into<1>(od, zo[1]);
-                cvt_u8_into<2>(ev, ze[2]);
-                cvt_u8_into<2>(od, zo[2]);
-                cvt_u8_into<3>(ev, ze[3]);
-                cvt_u8_into<3>(od, zo[3]);
-                ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
-            }
-        } else if constexpr (PREC == LORES_BF16) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 2;
-                const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
-                const uint32_t b0 = __float_as_uint(U[j]) + (x & 0xFFFFu);
-                const uint32_t b1 = __float_as_uint(U[j + 1]) + (x >> 16);
-                ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-            }
+        if (gx < meta.cls[0].groups) {
+            const int task = paired + gx * kWavesPerGroup + wv;
+            if (task >= n0) return;
+            run_single(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
+                                                             codes0, scales0, meta, meta.cls[0],
+                                                             task));
         } else {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+            const int task = paired + (gx - meta.cls[0].groups) * kWavesPerGroup + wv;
+            if (task >= n1) return;
+            run_single(TaskStream<DK, P1, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
+                                                             codes1, scales1, meta, meta.cls[1],
+                                                             task));
         }
-        if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
     }
-    asm volatile("" ::"v"(warm));
 }
 
 // ---------------------------------------------------------------------------
-// launcher
+// launcher: the grid holds every (class, head slot, row block) group along x
+// and as many sequence strides along y as fit on the device at once
 // ---------------------------------------------------------------------------
-template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
-hipError_t launch_one(const StepPtrs &p, const ClassMeta &m, hipStream_t s) {
-    const int groups = (m.Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((lores_step_kernel<DK, PREC, PC, DELTA, BF16IN>), dim3(groups, m.B),
-                       dim3(64 * kWavesPerGroup), 0, s, p.q, p.k, p.v, p.alpha, p.beta, p.o,
-                       p.codes, p.scales, m);
+inline int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1>
+hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
+    auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1>;
+    static int per_cu = 0;                          // resident work-groups per CU
+    if (!per_cu) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern),
+                                                         64 * kWavesPerGroup, 0) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        per_cu = n;
+    }
+    int gx = m.cls[0].groups + (P1 < 0 ? 0 : m.cls[1].groups);
+    if constexpr (pairable<P0, P1, DK>()) {
+        const int n0 = m.cls[0].Hc * m.n_rb, n1 = m.cls[1].Hc * m.n_rb;
+        const int paired = n0 < n1 ? n0 : n1;
+        gx = (paired + kWavesPerGroup - 1) / kWavesPerGroup +
+             (n0 - paired + kWavesPerGroup - 1) / kWavesPerGroup +
+             (n1 - paired + kWavesPerGroup - 1) / kWavesPerGroup;
+    }
+    long resident = (long)per_cu * device_cu_count();
+    long gy = resident / gx;
+    if (gy < 1) gy = 1;
+    if (gy > m.B) gy = m.B;
+    hipLaunchKernelGGL(kern, dim3(gx, (unsigned)gy), dim3(64 * kWavesPerGroup), 0, s, p.q, p.k,
+                       p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.codes[1],
+                       p.scales[1], m);
     return hipGetLastError();
 }
 
-template <int DK, int PREC>
-hipError_t launch_dk(bool pc, bool delta, bool bf16, const StepPtrs &p, const ClassMeta &m,
+template <int DK, int P0, int P1>
+hipError_t launch_dk(bool pc, bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
                      hipStream_t s) {
     if (pc) {
-        if (delta) return bf16 ? launch_one<DK, PREC, true, true, true>(p, m, s)
-                               : launch_one<DK, PREC, true, true, false>(p, m, s);
-        return bf16 ? launch_one<DK, PREC, true, false, true>(p, m, s)
-                    : launch_one<DK, PREC, true, false, false>(p, m, s);
+        if (delta) return bf16 ? launch_one<DK, true, true, true, P0, P1>(p, m, s)
+                               : launch_one<DK, true, true, false, P0, P1>(p, m, s);
+        return bf16 ? launch_one<DK, true, false, true, P0, P1>(p, m, s)
+                    : launch_one<DK, true, false, false, P0, P1>(p, m, s);
     }
-    if (delta) return bf16 ? launch_one<DK, PREC, false, true, true>(p, m, s)
-                           : launch_one<DK, PREC, false, true, false>(p, m, s);
-    return bf16 ? launch_one<DK, PREC, false, false, true>(p, m, s)
-                : launch_one<DK, PREC, false, false, false>(p, m, s);
+    if (delta) return bf16 ? launch_one<DK, false, true, true, P0, P1>(p, m, s)
+                           : launch_one<DK, false, true, false, P0, P1>(p, m, s);
+    return bf16 ? launch_one<DK, false, false, true, P0, P1>(p, m, s)
+                : launch_one<DK, false, false, false, P0, P1>(p, m, s);
 }
 
-template <int PREC>
-hipError_t launch_prec(int dk, bool pc, bool delta, bool bf16, const StepPtrs &p,
-                       const ClassMeta &m, hipStream_t s) {
+template <int P0, int P1>
+hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs &p,
+                          const StepMeta &m, hipStream_t s) {
     switch (dk) {
-        case 32: return launch_dk<32, PREC>(pc, delta, bf16, p, m, s);
-        case 64: return launch_dk<64, PREC>(pc, delta, bf16, p, m, s);
-        case 96: return launch_dk<96, PREC>(pc, delta, bf16, p, m, s);
-        case 128: return launch_dk<128, PREC>(pc, delta, bf16, p, m, s);
+        case 32: return launch_dk<32, P0, P1>(pc, delta, bf16, p, m, s);
+        case 64: return launch_dk<64, P0, P1>(pc, delta, bf16, p, m, s);
+        case 96: return launch_dk<96, P0, P1>(pc, delta, bf16, p, m, s);
+        case 128: return launch_dk<128, P0, P1>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }
