@@ -140,27 +140,136 @@ __device__ __forceinline__ float rd_div(float r, float m) {
     return m == 0.0f ? 0.0f : q;
 }
 
-// A wave-uniform zero the compiler cannot see through; its data dependence on
-// `dep` keeps scalar loads addressed with it from being hoisted above the
-// computation of `dep`.
-__device__ __forceinline__ long opaque_zero(float dep) {
-    int z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z) : "v"(dep));
-    return z;
+// ---------------------------------------------------------------------------
+// k, q and a per-channel alpha as "row vectors": register i of a wavefront
+// holds element 16*i + (lane % 16) in every lane, so each 16-lane row holds
+// 16 consecutive elements, and DPP row_newbcast:e hands element 16*i + e to
+// all lanes as the first multiplicand of a v_fmac / v_mul at no extra cost.
+// Each block opens with s_nop 1: a DPP source read needs two wait states
+// after a VALU write of that register, which a copy the compiler might place
+// just before the block would otherwise violate.
+// ---------------------------------------------------------------------------
+#define LORES_V16(P) "v"(P[0]), "v"(P[1]), "v"(P[2]), "v"(P[3]), "v"(P[4]), "v"(P[5]), \
+    "v"(P[6]), "v"(P[7]), "v"(P[8]), "v"(P[9]), "v"(P[10]), "v"(P[11]), "v"(P[12]), \
+    "v"(P[13]), "v"(P[14]), "v"(P[15])
+#define LORES_PV16(P) "+v"(P[0]), "+v"(P[1]), "+v"(P[2]), "+v"(P[3]), "+v"(P[4]), \
+    "+v"(P[5]), "+v"(P[6]), "+v"(P[7]), "+v"(P[8]), "+v"(P[9]), "+v"(P[10]), "+v"(P[11]), \
+    "+v"(P[12]), "+v"(P[13]), "+v"(P[14]), "+v"(P[15])
+
+// r += sum_e x[e] * row element e of kv
+__device__ __forceinline__ void dot16(float &r, const float *x, float kv) {
+    asm("s_nop 1\n"
+        "v_fmac_f32_dpp %0, %17, %1 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %2 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %3 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %4 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %5 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %6 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %7 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %8 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %9 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %10 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %11 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %12 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %13 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %14 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %15 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %0, %17, %16 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : "+v"(r)
+        : LORES_V16(x), "v"(kv));
 }
 
-__device__ __forceinline__ long opaque_off(float dep) { return opaque_zero(dep); }
+// Forces the 16 values into registers at this point of the program; as a
+// volatile statement it also keeps later memory accesses after it.
+__device__ __forceinline__ void pin16(float *x) {
+    asm volatile("" : LORES_PV16(x));
+}
 
-// Input element j of a [.., DK] row at base index `base` (uniform).
-template <bool BF16IN>
-__device__ __forceinline__ float in_elem(const void *__restrict__ p, long base, int j) {
-    if constexpr (BF16IN) {
-        // base is even (a multiple of d_k), so the pair index splits
-        const uint32_t w = ((const uint32_t *)p)[(base >> 1) + (j >> 1)];
-        return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
-    } else {
-        return ((const float *)p)[base + j];
-    }
+// u[e] += g * row element e of kv, then o += u[e] * row element e of qv
+__device__ __forceinline__ void upd16(float *u, float &o, float g, float kv, float qv) {
+    asm("s_nop 1\n"
+        "v_fmac_f32_dpp %0, %18, %17 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %0 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %1, %18, %17 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %1 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %2, %18, %17 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %2 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %3, %18, %17 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %3 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %4, %18, %17 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %4 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %5, %18, %17 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %5 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %6, %18, %17 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %6 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %7, %18, %17 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %7 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %8, %18, %17 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %9, %18, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %10, %18, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %11, %18, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %12, %18, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %13, %18, %17 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %14, %18, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %15, %18, %17 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %16, %19, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : LORES_PV16(u), "+v"(o)
+        : "v"(g), "v"(kv), "v"(qv));
+}
+
+// y[e] = row element e of av * x
+__device__ __forceinline__ void scale16(float *y, float x, float av) {
+    asm("s_nop 1\n"
+        "v_mul_f32_dpp %0, %17, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %1, %17, %16 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %2, %17, %16 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %3, %17, %16 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %4, %17, %16 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %5, %17, %16 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %6, %17, %16 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %7, %17, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %8, %17, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %9, %17, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %10, %17, %16 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %11, %17, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %12, %17, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %13, %17, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %14, %17, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %15, %17, %16 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),
+          "=&v"(y[6]), "=&v"(y[7]), "=&v"(y[8]), "=&v"(y[9]), "=&v"(y[10]), "=&v"(y[11]),
+          "=&v"(y[12]), "=&v"(y[13]), "=&v"(y[14]), "=&v"(y[15])
+        : "v"(x), "v"(av));
+}
+
+// x[e] *= row element e of av
+__device__ __forceinline__ void mul16(float *x, float av) {
+    asm("s_nop 1\n"
+        "v_mul_f32_dpp %0, %16, %0 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %1, %16, %1 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %2, %16, %2 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %3, %16, %3 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %4, %16, %4 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %5, %16, %5 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %6, %16, %6 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %7, %16, %7 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %8, %16, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %9, %16, %9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %10, %16, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %11, %16, %11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %12, %16, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %13, %16, %13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %14, %16, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %15, %16, %15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : LORES_PV16(x)
+        : "v"(av));
 }
 
 template <bool BF16IN>
@@ -177,12 +286,20 @@ __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx)
 // ---------------------------------------------------------------------------
 // A wavefront owns one (head slot, row block) of a class and walks the
 // sequences b = blockIdx.y, blockIdx.y + gridDim.y, ...  `issue` starts the
-// loads of one task (its chunks, row scale and v, plus one 16-byte load per
-// lane of its k and q, and per-channel alpha, that warms L2 for the scalar
-// loads of the passes); `run` computes and stores it and calls `mid` right
-// after pass 1, when the chunk registers are free, so the caller can start
-// the next task's loads there.
+// loads of one task: its chunks, row scale and v, alpha and beta, and k and
+// q (and a per-channel alpha) as row vectors; `run` computes and stores the
+// task and calls `mid` right after pass 1, when the chunk registers are free,
+// so the caller can start the next task's loads there.
 constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
+
+// Per-task values loaded ahead of the task, besides its chunks: the row
+// scale and v of this lane's row, beta and a scalar alpha, and k, q and a
+// per-channel alpha as row vectors (NV registers each).
+template <int NV>
+struct TaskSide {
+    float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
+    float kv[NV], qv[NV], av[NV];
+};
 
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
 struct TaskStream {
@@ -220,8 +337,9 @@ struct TaskStream {
         active = row < m.dv;
     }
 
-    __device__ __forceinline__ void issue(int b, u32x4 *cw, float &s_in, float &v_in,
-                                          u32x4 &warm) const {
+    static constexpr int NV = DK / 16;            // row-vector registers per vector
+
+    __device__ __forceinline__ void issue(int b, u32x4 *cw, TaskSide<NV> &in) const {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;
@@ -229,29 +347,31 @@ struct TaskStream {
         const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + row;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
-        if constexpr (is_int<PREC>()) s_in = scales[unit * dv_pad + row];
-        v_in = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
-        const int off = (threadIdx.x & 63) * 16;
-        const long kb = bh * DK;
-        const char *src = nullptr;
-        if (off < kVecBytes) src = (const char *)kp + kb * kInB + off;
-        else if (off < 2 * kVecBytes) src = (const char *)qp + kb * kInB + (off - kVecBytes);
-        else if (PC && off < 2 * kVecBytes + DK * 4)
-            src = (const char *)alphap + kb * 4 + (off - 2 * kVecBytes);
-        if (src) warm = *reinterpret_cast<const u32x4 *>(src);
+        if constexpr (is_int<PREC>()) in.s = scales[unit * dv_pad + row];
+        in.v = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
+        in.beta = betap[bh];
+        in.alpha = PC ? 1.0f : alphap[bh];
+        // row vectors: register i holds element 16 i + lane % 16
+        const long kb = bh * DK + (threadIdx.x & 15);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            in.kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
+            in.qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
+            if constexpr (PC) in.av[i] = alphap[kb + 16 * i];
+        }
     }
 
     template <class Mid>
-    __device__ __forceinline__ void run(int b, const u32x4 *cw, float s, float vi, Mid &&mid) const {
+    __device__ __forceinline__ void run(int b, const u32x4 *cw, const TaskSide<NV> &in,
+                                        Mid &&mid) const {
+        const float s = in.s, vi = in.v;
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;           // index into [B][H] inputs
-        const long kbase = bh * DK;
         u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * unit_bytes) + row;
 
-        const float beta = betap[bh];
-        float alpha_s = 1.0f;
-        if constexpr (!PC) alpha_s = alphap[bh];
+        const float beta = in.beta;
+        const float alpha_s = in.alpha;
         float a = 0.0f, na = 0.0f;
         if constexpr (is_int<PREC>() && !PC) {
             a = s * alpha_s;
@@ -259,26 +379,18 @@ struct TaskStream {
         }
 
         // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
-        // k and a per-channel alpha are read 16 columns at a time into SGPRs;
-        // each group's addresses depend (through opaque_zero) on the r chain
-        // (or the last element) of the group two before, which keeps the
-        // compiler from hoisting every uniform load and spilling SGPRs.
         float U[DK];
         float r = 0.0f;
-        constexpr bool kP1Loads = DELTA || PC;          // pass 1 reads k or alpha_j
-        long kb_cur = kbase, kb_next = kbase;
+        float aj[16];                                    // s * alpha_j of one group (int, per channel)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int j = c * E + e;
-                if (kP1Loads && (j & 15) == 0) {
-                    kb_cur = kb_next;
-                    kb_next = kbase + opaque_off(DELTA ? r : (j ? U[j - 1] : r));
+                if constexpr (PC && is_int<PREC>()) {
+                    if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
-                float alpha_j = alpha_s;
-                if constexpr (PC) alpha_j = alphap[kb_cur + j];
                 float sp;
                 if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
@@ -291,20 +403,25 @@ struct TaskStream {
                                                      : and_opaque(w, 0x0F0F0F0Fu);
                         ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
                     }
-                    if constexpr (PC) {
-                        const float aj = s * alpha_j;
-                        sp = (ub - Prec<PREC>::OFF) * aj;
-                    } else {
-                        sp = __builtin_fmaf(ub, a, na);
-                    }
+                    if constexpr (PC) sp = (ub - Prec<PREC>::OFF) * aj[j & 15];
+                    else sp = __builtin_fmaf(ub, a, na);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
-                    sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16)) * alpha_j;
+                    sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    if constexpr (!PC) sp = sp * alpha_s;
                 } else {
-                    sp = __uint_as_float(wd[e]) * alpha_j;
+                    sp = __uint_as_float(wd[e]);
+                    if constexpr (!PC) sp = sp * alpha_s;
                 }
                 U[j] = sp;
-                if constexpr (DELTA) r = __builtin_fmaf(sp, in_elem<BF16IN>(kp, kb_cur, j), r);
+                if ((j & 15) == 15) {
+                    if constexpr (PC && !is_int<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
+                    if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
+                    // without the projection nothing orders pass 1 before the
+                    // next task's loads; materialize the group here so the
+                    // chunk registers are free when `mid` reuses them
+                    else pin16(&U[j - 15]);
+                }
             }
         }
 
@@ -315,16 +432,11 @@ struct TaskStream {
 
         // ---- pass 2: rank-one write, readout, row abs-max
         float o = 0.0f, m = 0.0f;
-        kb_next = kbase + opaque_off(g);
 #pragma unroll
-        for (int j = 0; j < DK; ++j) {
-            if ((j & 15) == 0) {
-                kb_cur = kb_next;
-                kb_next = kbase + opaque_off(o);     // the o chain orders the groups
-            }
-            U[j] = __builtin_fmaf(g, in_elem<BF16IN>(kp, kb_cur, j), U[j]);
-            o = __builtin_fmaf(U[j], in_elem<BF16IN>(qp, kb_cur, j), o);
-            m = fmaxf(m, fabsf(U[j]));
+        for (int gi = 0; gi < NV; ++gi) {
+            upd16(&U[16 * gi], o, g, in.kv[gi], in.qv[gi]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
         }
         if (active) op[bh * meta.dv + row] = o;
 
@@ -409,22 +521,20 @@ __device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA,
     constexpr bool kPrefetch = TS::NCH <= kMaxPrefetchChunks;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
-    float s_in = 0.0f, v_in = 0.0f;
-    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
+    TaskSide<TS::NV> in, nx;
     int b = blockIdx.y;
-    ts.issue(b, cw, s_in, v_in, warm);
+    ts.issue(b, cw, in);
     while (true) {
         const int bn = b + bstep;
-        const float s = s_in, vi = v_in;
-        ts.run(b, cw, s, vi, [&] {
-            asm volatile("" ::"v"(warm));
+        ts.run(b, cw, in, [&] {
             if constexpr (kPrefetch) {
-                if (bn < ts.meta.B) ts.issue(bn, cw, s_in, v_in, warm);
+                if (bn < ts.meta.B) ts.issue(bn, cw, nx);
             }
         });
         if (bn >= ts.meta.B) break;
         b = bn;
-        if constexpr (!kPrefetch) ts.issue(b, cw, s_in, v_in, warm);
+        if constexpr (kPrefetch) in = nx;
+        else ts.issue(b, cw, in);
     }
 }
 
@@ -440,22 +550,15 @@ __device__ __forceinline__ void run_paired(const TaskStream<DK, P0, PC, DELTA, B
                   "paired streams need prefetchable rows");
     const int bstep = gridDim.y;
     u32x4 cw[kMaxPrefetchChunks];
-    float s_in = 0.0f, v_in = 0.0f;
-    u32x4 warm = u32x4{0u, 0u, 0u, 0u};
+    TaskSide<TaskStream<DK, P0, PC, DELTA, BF16IN>::NV> in0;
+    TaskSide<TaskStream<DK, P1, PC, DELTA, BF16IN>::NV> in1;
     int b = blockIdx.y;
-    t0.issue(b, cw, s_in, v_in, warm);
+    t0.issue(b, cw, in0);
     while (true) {
         const int bn = b + bstep;
-        float s = s_in, vi = v_in;
-        t0.run(b, cw, s, vi, [&] {
-            asm volatile("" ::"v"(warm));
-            t1.issue(b, cw, s_in, v_in, warm);
-        });
-        s = s_in;
-        vi = v_in;
-        t1.run(b, cw, s, vi, [&] {
-            asm volatile("" ::"v"(warm));
-            if (bn < t0.meta.B) t0.issue(bn, cw, s_in, v_in, warm);
+        t0.run(b, cw, in0, [&] { t1.issue(b, cw, in1); });
+        t1.run(b, cw, in1, [&] {
+            if (bn < t0.meta.B) t0.issue(bn, cw, in0);
         });
         if (bn >= t0.meta.B) break;
         b = bn;
