@@ -182,6 +182,13 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
                       int64_t seq_base, int64_t head_base, float *o, void *stream);
 
 /*
+ * lores_step_launches - kernel launches one lores_decode_step on `st`
+ * enqueues (host out *n): one per precision class present, except that the
+ * pairs (int8, int4), (bf16, int8) and (bf16, int4) share a single launch.
+ */
+int lores_step_launches(const lores_state *st, int32_t *n);
+
+/*
  * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32,
  * value = scale * code for int heads, the stored value for bf16 / fp32 heads.
  */

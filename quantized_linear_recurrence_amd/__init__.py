@@ -20,7 +20,8 @@ from ._lib import (LORES_BF16, LORES_FP32, LORES_INT4, LORES_INT8, LoresLayout,
 __all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LoresError",
            "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_layout",
            "lores_state_head_map", "lores_decay_stat", "lores_assign_precision",
-           "lores_decode_step", "lores_dequant_state", "lores_last_error", "lores_spec_version"]
+           "lores_decode_step", "lores_step_launches", "lores_dequant_state",
+           "lores_last_error", "lores_spec_version"]
 
 
 class LoresError(RuntimeError):
@@ -139,6 +140,13 @@ def lores_state_head_map(state):
                                            prec.ctypes.data_as(ctypes.c_void_p),
                                            slot.ctypes.data_as(ctypes.c_void_p)))
     return prec, slot
+
+
+def lores_step_launches(state):
+    """Kernel launches one lores_decode_step on `state` enqueues."""
+    n = ctypes.c_int32(0)
+    _check(_lib.lib().lores_step_launches(ctypes.c_void_p(state.handle), ctypes.byref(n)))
+    return n.value
 
 
 def lores_decay_stat(alpha):

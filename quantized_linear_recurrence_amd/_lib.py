@@ -16,7 +16,8 @@ STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3:
 # every symbol include/lores.h declares
 EXPORTS = ("lores_state_alloc", "lores_state_free", "lores_state_layout", "lores_state_head_map",
            "lores_decay_stat", "lores_assign_precision", "lores_decode_step",
-           "lores_dequant_state", "lores_last_error", "lores_spec_version")
+           "lores_step_launches", "lores_dequant_state", "lores_last_error",
+           "lores_spec_version")
 
 
 class LoresLibraryMissing(RuntimeError):
@@ -60,6 +61,8 @@ def lib():
     L.lores_decode_step.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, u64, u64, i64, i64,
                                     vp, vp]
     L.lores_decode_step.restype = ctypes.c_int
+    L.lores_step_launches.argtypes = [vp, ctypes.POINTER(i32)]
+    L.lores_step_launches.restype = ctypes.c_int
     L.lores_dequant_state.argtypes = [vp, vp, vp]
     L.lores_dequant_state.restype = ctypes.c_int
     L.lores_last_error.argtypes = []

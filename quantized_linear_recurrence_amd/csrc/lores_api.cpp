@@ -297,6 +297,32 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
     }
 }
 
+// Launches of one decode step: the classes present, where a fusable pair
+// shares one launch and anything else gets one launch per class.
+static int plan_launches(const lores_state *st, int groups[4][2], int width[4]) {
+    int present[4], n = 0;
+    for (int c = 0; c < 4; ++c)
+        if (st->n_class[c]) present[n++] = c;
+    if (n == 2 && lores::fusable_pair(present[0], present[1])) {
+        groups[0][0] = present[0];
+        groups[0][1] = present[1];
+        width[0] = 2;
+        return 1;
+    }
+    for (int i = 0; i < n; ++i) {
+        groups[i][0] = present[i];
+        width[i] = 1;
+    }
+    return n;
+}
+
+int lores_step_launches(const lores_state *st, int32_t *n) {
+    if (!st || !n) return fail(LORES_EINVAL, "NULL argument");
+    int groups[4][2], width[4];
+    *n = plan_launches(st, groups, width);
+    return ok();
+}
+
 int lores_decode_step(lores_state *st, const void *q, const void *k, const void *v,
                       int32_t in_bf16, const float *alpha, int32_t alpha_per_channel,
                       const float *beta, int32_t delta, uint64_t seed, uint64_t t,
@@ -321,24 +347,8 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
             return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
         const hipStream_t s = (hipStream_t)stream;
-        // classes present; a fusable pair shares one launch, anything else
-        // gets one launch per class
-        int present[4], n = 0;
-        for (int c = 0; c < 4; ++c)
-            if (st->n_class[c]) present[n++] = c;
-        int groups[4][2], n_launch = 0, width[4];
-        if (n == 2 && lores::fusable_pair(present[0], present[1])) {
-            groups[0][0] = present[0];
-            groups[0][1] = present[1];
-            width[0] = 2;
-            n_launch = 1;
-        } else {
-            for (int i = 0; i < n; ++i) {
-                groups[i][0] = present[i];
-                width[i] = 1;
-            }
-            n_launch = n;
-        }
+        int groups[4][2], width[4];
+        const int n_launch = plan_launches(st, groups, width);
         for (int l = 0; l < n_launch; ++l) {
             lores::StepMeta m = make_meta(st, groups[l], width[l]);
             m.seed = seed;

@@ -108,8 +108,9 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
                device="cuda"):
     """Run T GPU steps with per-step resync to the oracle; returns Stats.
 
-    units: list of (b, h) to compare (default: all).  init: "zero" (S_0 = 0)
-    or "random" (random codes and scales, or random bf16 / fp32 values).
+    units: list of (b, h) to compare (default: all).  init: "zero" (S_0 = 0),
+    "random" (random codes and scales, or random bf16 / fp32 values) or a
+    function (prec, dv, dk, numpy Generator) -> one unit's state.
     """
     B = w.B if B is None else B
     if inputs is None:
@@ -127,7 +128,9 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
     ost = {}
     for (b, h) in units:
         c = head_prec[h]
-        if init == "zero":
+        if callable(init):
+            s = init(c, w.dv, w.dk, g)
+        elif init == "zero":
             s = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk).items()}
         else:
             s = random_unit_state(c, w.dv, w.dk, g)

@@ -1,0 +1,287 @@
+"""GPU tests of the C-ABI contract beyond step parity: launch grouping, shard
+invariance of the rounding keys, repeatability (eager and graph replays),
+dequantization of a packed state, error paths on a live handle, and states at
+the ends of the fp32 range.
+
+Every case prints its name before touching the GPU.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_recurrence_amd as lores
+from oracle import step as ostep
+from quantized_linear_recurrence_amd import _lib
+from tests import layout_codec as lc
+from tests.parity import log, random_unit_state, run_parity
+from workloads import get_workload, make_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+C1 = get_workload("C1")
+DEV = "cuda"
+
+
+def _install(st, states):
+    """Write {(b, h): unit state} into the device buffer of `st` through the codec."""
+    lay = lores.lores_state_layout(st)
+    _, slot = lores.lores_state_head_map(st)
+    buf = st.buf.cpu().numpy().copy()
+    for (b, h), s in states.items():
+        c = st.head_prec[h]
+        lc.write_unit(buf, lay, c, b * lay["n_class"][c] + slot[h], s)
+    st.buf.copy_(torch.from_numpy(buf))
+
+
+def _random_states(B, head_prec, dv, dk, seed):
+    g = np.random.default_rng(seed)
+    return {(b, h): random_unit_state(c, dv, dk, g)
+            for b in range(B) for h, c in enumerate(head_prec)}
+
+
+def _unit_bytes(st, buf_host, b, h):
+    """Raw code bytes and scales of one unit (bytes, for bit comparisons)."""
+    lay = lores.lores_state_layout(st)
+    _, slot = lores.lores_state_head_map(st)
+    c = st.head_prec[h]
+    cs, cl, ss, sl = lc.unit_ranges(lay, c, b * lay["n_class"][c] + slot[h])
+    out = [buf_host[cs:cs + cl]]
+    if ss is not None:
+        out.append(buf_host[ss:ss + sl])
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("prec,n", [([2, 2], 1), ([0], 1), ([2, 3], 1), ([1, 2], 1),
+                                    ([3, 1], 1), ([0, 2], 2), ([0, 1], 2), ([1, 2, 3], 3),
+                                    ([0, 1, 2, 3], 4)])
+def test_step_launches(prec, n):
+    log(f"case: launches per step for precisions {prec}")
+    st = lores.lores_state_alloc(2, len(prec), 64, 64, prec, device=DEV)
+    assert lores.lores_step_launches(st) == n
+
+
+@pytest.mark.parametrize("B,head_prec,dk,dv,seq_cuts,head_cuts", [
+    (6, [0, 1, 2, 3, 2, 3], 128, 96, [0, 2, 6], [0, 3, 6]),
+    (160, [2, 3] * 4, 128, 128, [0, 40, 160], [0, 4, 8]),
+    (9, [1, 2, 1, 2], 64, 33, [0, 1, 9], [0, 1, 4]),
+])
+def test_shard_invariance(B, head_prec, dk, dv, seq_cuts, head_cuts):
+    """A shard of sequences and heads, keyed with seq_base / head_base, gives
+    the unsharded result bit for bit (state bytes and o); the shards also run
+    in other launch shapes than the whole batch."""
+    H = len(head_prec)
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=3)
+    log(f"case: shard invariance B={B} H={H} dk={dk} dv={dv} precisions {head_prec} "
+        f"seq cuts {seq_cuts} head cuts {head_cuts}")
+    inp = make_inputs(w, 3, DEV)
+    init = _random_states(B, head_prec, dv, dk, seed=11)
+    full = lores.lores_state_alloc(B, H, dk, dv, head_prec, device=DEV)
+    _install(full, init)
+    shards = []
+    for b0, b1 in zip(seq_cuts[:-1], seq_cuts[1:]):
+        for h0, h1 in zip(head_cuts[:-1], head_cuts[1:]):
+            st = lores.lores_state_alloc(b1 - b0, h1 - h0, dk, dv, head_prec[h0:h1], device=DEV)
+            _install(st, {(b - b0, h - h0): init[(b, h)]
+                          for b in range(b0, b1) for h in range(h0, h1)})
+            shards.append((b0, b1, h0, h1, st))
+    for t in range(1, w.T + 1):
+        x = {k: v[t - 1] for k, v in inp.items()}
+        o_full = lores.lores_decode_step(full, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                         w.delta, 21, t)
+        for b0, b1, h0, h1, st in shards:
+            xs = {k: v[b0:b1, h0:h1].contiguous() for k, v in x.items()}
+            o_s = lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"],
+                                          w.delta, 21, t, seq_base=b0, head_base=h0)
+            assert torch.equal(o_s, o_full[b0:b1, h0:h1]), (t, b0, h0)
+    torch.cuda.synchronize()
+    fh = full.buf.cpu().numpy()
+    for b0, b1, h0, h1, st in shards:
+        sh = st.buf.cpu().numpy()
+        for b in range(b0, b1):
+            for h in range(h0, h1):
+                assert np.array_equal(_unit_bytes(st, sh, b - b0, h - h0),
+                                      _unit_bytes(full, fh, b, h)), (b, h)
+
+
+def test_key_changes_the_rounding():
+    """Another seed, step or base index moves the stochastic rounding: the
+    keys reach the noise (a sanity check against a constant key)."""
+    w = C1.scaled(B=2, H=2, dk=128, dv=64, T=1)
+    log("case: rounding keys, B=2 H=2 int8")
+    x = {k: v[0] for k, v in make_inputs(w, 0, DEV).items()}
+    init = _random_states(2, [2, 2], 64, 128, seed=5)
+    results = []
+    for seed, t, sb, hb in [(0, 1, 0, 0), (1, 1, 0, 0), (0, 2, 0, 0), (0, 1, 7, 0), (0, 1, 0, 7)]:
+        st = lores.lores_state_alloc(2, 2, 128, 64, [2, 2], device=DEV)
+        _install(st, init)
+        lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, seed, t,
+                                seq_base=sb, head_base=hb)
+        results.append(st.buf.cpu().numpy())
+    for r in results[1:]:
+        assert not np.array_equal(r, results[0])
+
+
+def test_repeatable_eager_and_graph():
+    """The same steps from the same state give the same bytes: twice eagerly,
+    and over several replays of a captured graph with eager work between."""
+    B, head_prec = 96, [2, 3] * 16
+    w = get_workload("C5").scaled(B=B, T=4)
+    log(f"case: repeatability B={B} H=32 d=128 int8/int4, 4 steps, eager x2 and graph x3")
+    inp = make_inputs(w, 0, DEV)
+    st = lores.lores_state_alloc(B, 32, 128, 128, head_prec, device=DEV)
+    _install(st, _random_states(B, head_prec, 128, 128, seed=2))
+    init = st.buf.clone()
+    outs = [torch.empty((B, 32, 128), dtype=torch.float32, device=DEV) for _ in range(w.T)]
+
+    def steps():
+        for t in range(1, w.T + 1):
+            x = {k: v[t - 1] for k, v in inp.items()}
+            lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], w.delta,
+                                    4, t, o=outs[t - 1])
+
+    steps()
+    torch.cuda.synchronize()
+    ref_buf = st.buf.clone()
+    ref_o = [o.clone() for o in outs]
+    st.buf.copy_(init)
+    steps()
+    torch.cuda.synchronize()
+    assert torch.equal(st.buf, ref_buf)
+    assert all(torch.equal(a, b) for a, b in zip(outs, ref_o))
+
+    graph = torch.cuda.CUDAGraph()
+    st.buf.copy_(init)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        steps()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.buf.copy_(init)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.buf, ref_buf), rep
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref_o)), rep
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (96, 65), (32, 1), (64, 200)])
+def test_dequant_matches_oracle(dk, dv):
+    """lores_dequant_state of a packed state (written through the codec)
+    equals the oracle's dequantization bit for bit."""
+    B, head_prec = 3, [0, 1, 2, 3, 3, 2]
+    log(f"case: dequant B={B} dk={dk} dv={dv} precisions {head_prec}")
+    st = lores.lores_state_alloc(B, len(head_prec), dk, dv, head_prec, device=DEV)
+    zero = lores.lores_dequant_state(st)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(zero).item() == 0
+    states = _random_states(B, head_prec, dv, dk, seed=dk + dv)
+    _install(st, states)
+    out = lores.lores_dequant_state(st).cpu().numpy()
+    for (b, h), s in states.items():
+        want = ostep.dequant(head_prec[h], {k: v[None] for k, v in s.items()})[0]
+        assert np.array_equal(out[b, h].view(np.uint32), want.view(np.uint32)), (b, h)
+
+
+def test_error_paths_live_handle():
+    """Invalid calls on a live handle fail with the documented code and
+    launch nothing."""
+    w = C1.scaled(B=2, H=2, dk=64, dv=64, T=1, in_bf16=True)
+    log("case: error paths on a live handle")
+    x = {k: v[0] for k, v in make_inputs(w, 0, DEV).items()}
+    st = lores.lores_state_alloc(2, 2, 64, 64, [2, 3], device=DEV)
+    _install(st, _random_states(2, [2, 3], 64, 64, seed=9))
+    before = st.buf.clone()
+    args = (x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, *args, 1, 0, 0)                # t = 0
+    assert "t must be" in lores.lores_last_error()
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, *args, 2, 0, 1)                # delta = 2
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, *args, 1, 0, 1, seq_base=(1 << 32) - 1)
+    with pytest.raises(ValueError):
+        lores.lores_decode_step(st, x["q"][:1], *args[1:], 1, 0, 1)   # wrong size (binding)
+
+    # misaligned bf16 q through the C ABI directly (2 bytes past an element pair)
+    L = _lib.lib()
+    o = torch.empty((2, 2, 64), dtype=torch.float32, device=DEV)
+    qq = torch.empty(2 * 2 * 64 + 1, dtype=torch.bfloat16, device=DEV)
+    vp = ctypes.c_void_p
+    rc = L.lores_decode_step(vp(st.handle), vp(qq.data_ptr() + 2), vp(x["k"].data_ptr()),
+                             vp(x["v"].data_ptr()), 1, vp(x["alpha"].data_ptr()), 0,
+                             vp(x["beta"].data_ptr()), 1, 0, 1, 0, 0, vp(o.data_ptr()),
+                             vp(torch.cuda.current_stream().cuda_stream))
+    assert rc == -1 and "aligned" in lores.lores_last_error()
+    rc = L.lores_decode_step(vp(st.handle), vp(x["q"].data_ptr()), vp(x["k"].data_ptr()),
+                             vp(x["v"].data_ptr()), 1, vp(x["alpha"].data_ptr()), 0,
+                             vp(x["beta"].data_ptr()), 1, 0, 1, 0, 0, vp(None),
+                             vp(torch.cuda.current_stream().cuda_stream))
+    assert rc == -1
+    torch.cuda.synchronize()
+    assert torch.equal(st.buf, before)
+
+    # buffers: too small, misaligned
+    need = lores.lores_state_alloc(2, 2, 64, 64, [2, 3])
+    with pytest.raises(lores.LoresError, match="ESIZE"):
+        lores.lores_state_alloc(2, 2, 64, 64, [2, 3],
+                                buf=torch.empty(need - 16, dtype=torch.uint8, device=DEV))
+    big = torch.empty(need + 512, dtype=torch.uint8, device=DEV)
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_state_alloc(2, 2, 64, 64, [2, 3], buf=big[16:16 + need])
+    with pytest.raises(lores.LoresError, match="EUNSUPPORTED|EINVAL"):
+        lores.lores_state_alloc(2, 2, 48, 64, [2, 3], device=DEV)
+
+
+def _scaled_state(lo, hi):
+    """Unit states with int scales exp(U(lo, hi)) and bf16 / fp32 values of that size."""
+    def init(c, dv, dk, g):
+        if c in (2, 3):
+            r = 127 if c == 2 else 7
+            return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
+                    "scales": np.exp(g.uniform(lo, hi, dv)).astype(np.float32)}
+        X = (g.standard_normal((dv, dk)) * np.exp(g.uniform(lo, hi, (dv, 1)))).astype(np.float32)
+        if c == 1:
+            return {"bits": (X.view(np.uint32) >> 16).astype(np.uint16)}
+        return {"X": X}
+    return init
+
+
+@pytest.mark.parametrize("name,lo,hi,v_scale", [
+    ("huge", 60.0, 78.0, 1.0),            # scales ~1e26..1e34, |U| up to ~1e36
+    ("tiny", -90.0, -84.0, 1e-37),        # r / m above the fp32 range for some rows
+    ("subnormal", -100.0, -95.0, 1e-41),  # scales and values below the normal range
+])
+def test_extreme_magnitudes(name, lo, hi, v_scale):
+    w = C1.scaled(B=2, H=4, dk=128, dv=64, T=3)
+    log(f"case: extreme magnitudes ({name}) B=2 H=4 precisions fp32/bf16/int8/int4")
+    inp = make_inputs(w, 1, DEV)
+    inp["v"] = inp["v"] * v_scale
+    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3], init=_scaled_state(lo, hi), inputs=inp)
+    log(s.summary())
+    s.check()
+
+
+def test_zero_rows():
+    """Rows that stay zero (zero state, zero write) keep scale 0 and code 0."""
+    w = C1.scaled(B=2, H=2, dk=64, dv=64, T=2)
+    log("case: zero rows, int8 / int4")
+    inp = make_inputs(w, 0, DEV)
+    inp["v"] = torch.zeros_like(inp["v"])
+    st = lores.lores_state_alloc(2, 2, 64, 64, [2, 3], device=DEV)
+    for t in (1, 2):
+        x = {k: v[t - 1] for k, v in inp.items()}
+        o = lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, 0, t)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+    assert torch.count_nonzero(lores.lores_dequant_state(st)).item() == 0
+    lay = lores.lores_state_layout(st)
+    buf = st.buf.cpu().numpy()
+    for c in (2, 3):
+        for u in range(2):
+            s = lc.read_unit(buf, lay, c, u)
+            assert not s["codes"].any() and not s["scales"].any()
