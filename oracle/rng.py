@@ -19,16 +19,16 @@ Keying and draws (this implementation's definition):
   unit key  K = lo32(z) ^ hi32(z),
             z = mix64(mix64(mix64(seed) ^ t) ^ ((b << 32) | h))      once per unit
   row word  w_i = fmix32(K ^ i)
-  noise     x = w_i + floor(j / 2) * 0x9E3779B9  (mod 2^32)
-            n_ij = low 16 bits of x for even j, high 16 bits for odd j
+  noise     n_ij = (lo16(w_i) + j * 0x9E37) mod 2^16
   n_ij is a 16-bit integer; the int quantizer uses u_ij = n_ij * 2^-16 in
   [0, 1) and the bf16 rounding adds n_ij below the kept bits.
 
-Each n_ij is exactly uniform on {0, ..., 65535} when w_i is (x is then uniform
-mod 2^32), so every element's rounding is unbiased on its own; within a row the
-draws form a Weyl (golden-ratio) sequence rather than independent draws.
-noise16_iid is the reference with one hash per element, kept to check that
-this choice does not change the readout error statistics.
+Each n_ij is exactly uniform on {0, ..., 65535} when w_i is, so every
+element's rounding is unbiased on its own; within a row the draws form a
+16-bit Weyl sequence with the golden-ratio step 0x9E37 (about 0.618 * 2^16)
+rather than independent draws.  noise16_iid is the reference with one hash
+per element, kept to check that this choice does not change the readout
+error statistics.
 
 PARITY UNPINNED by the pages (they fix no generator): mix64 and fmix32 are
 pinned by published test vectors; the keying and the draws only by
@@ -38,7 +38,7 @@ import numpy as np
 
 U32 = np.uint32
 U64 = np.uint64
-PHI32 = U32(0x9E3779B9)
+PSI16 = U32(0x9E37)
 
 
 def mix64(z):
@@ -75,11 +75,10 @@ def noise16(K, dv, dk):
     K = np.asarray(K, dtype=U32).reshape(-1)
     i = np.arange(dv, dtype=U32)
     w = fmix32(K[:, None] ^ i[None, :])                       # [N, dv]
-    j = np.arange(dk)
-    step = (j // 2).astype(U32)
+    j = np.arange(dk, dtype=U32)
     with np.errstate(over="ignore"):
-        x = w[:, :, None] + step[None, None, :] * PHI32          # mod 2^32
-    return np.where((j % 2) == 0, x & U32(0xFFFF), x >> U32(16)).astype(U32)
+        x = (w[:, :, None] & U32(0xFFFF)) + j[None, None, :] * PSI16
+    return (x & U32(0xFFFF)).astype(U32)
 
 
 def noise16_iid(K, dv, dk):

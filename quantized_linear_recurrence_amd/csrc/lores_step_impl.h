@@ -73,7 +73,9 @@ __device__ __forceinline__ uint32_t unit_key(uint64_t seed, uint64_t t, uint64_t
     return (uint32_t)z ^ (uint32_t)(z >> 32);
 }
 
-constexpr uint32_t kPhi32 = 0x9E3779B9u;     // Weyl increment between noise words
+// The draws of row i: n_ij = (lo16(w_i) + j * kPsi16) mod 2^16, a 16-bit
+// Weyl sequence with the golden-ratio step.
+constexpr uint32_t kPsi16 = 0x9E37u;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 
@@ -98,11 +100,22 @@ template <> struct Prec<LORES_INT4> {
 
 template <int PREC> constexpr bool is_int() { return PREC == LORES_INT8 || PREC == LORES_INT4; }
 
-// bias + n * 2^-16 for the low (even column) or high (odd column) half of x.
-template <int PREC, bool HI>
-__device__ __forceinline__ float noise_bias(uint32_t x) {
-    // v_perm_b32 bytes: selector 0..3 pick x, 4..7 pick FBASE
-    return __uint_as_float(__builtin_amdgcn_perm(Prec<PREC>::FBASE, x, HI ? 0x07060302u : 0x07060100u));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Both 16-bit halves of x advanced by those of inc, each mod 2^16 (one
+// v_pk_add_u16): the noise sequence steps in the low half while the high
+// half, the sign, exponent and top mantissa bits of the bias, is kept.
+__device__ __forceinline__ uint32_t step16(uint32_t x, uint32_t inc) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) + __builtin_bit_cast(u16x2, inc));
+}
+
+// A wave-uniform constant the compiler cannot see through: with it as the
+// step, the noise stays one add per column instead of every column being
+// re-derived from the first with a constant of its own.
+__device__ __forceinline__ uint32_t opaque_uniform(uint32_t v) {
+    uint32_t r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
 }
 
 // x & m through an opaque VALU op: the compiler then keeps the byte structure
@@ -447,12 +460,19 @@ struct TaskStream {
             inv = rd_div(Prec<PREC>::R, m);
             if (active) scales[unit * dv_pad + row] = snew;
         }
-        uint32_t w = 0;
+        // int: x holds the fma addend bias + n_ij * 2^-16 of the current
+        // column (in [128, 256), where one fp32 ulp is 2^-16: the draw is the
+        // low 16 mantissa bits); bf16: x holds the draws of columns j, j + 1
+        uint32_t x = 0;
         if constexpr (PREC != LORES_FP32) {
             const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
                                         (uint64_t)(meta.head_base + h));
-            w = fmix32(K ^ (uint32_t)row);
+            const uint32_t n0 = fmix32(K ^ (uint32_t)row) & 0xFFFFu;
+            if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
+            else x = n0 | (((n0 + kPsi16) & 0xFFFFu) << 16);
         }
+        const uint32_t psi = opaque_uniform(is_int<PREC>() ? kPsi16
+                                                            : ((2 * kPsi16) & 0xFFFFu) * 0x00010001u);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             uint32_t ow[4];
@@ -460,12 +480,13 @@ struct TaskStream {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 4;
-                    const uint32_t x0 = w + (uint32_t)(j >> 1) * kPhi32;
-                    const uint32_t x1 = x0 + kPhi32;
-                    const float z0 = __builtin_fmaf(U[j], inv, noise_bias<PREC, false>(x0));
-                    const float z1 = __builtin_fmaf(U[j + 1], inv, noise_bias<PREC, true>(x0));
-                    const float z2 = __builtin_fmaf(U[j + 2], inv, noise_bias<PREC, false>(x1));
-                    const float z3 = __builtin_fmaf(U[j + 3], inv, noise_bias<PREC, true>(x1));
+                    float z[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
+                        x = step16(x, psi);
+                    }
+                    const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
                     uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
                     cvt_u8_into<1>(word, z1);
                     cvt_u8_into<2>(word, z2);
@@ -480,9 +501,10 @@ struct TaskStream {
                     float ze[4], zo[4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        const uint32_t x = w + (uint32_t)((j >> 1) + p) * kPhi32;
-                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, noise_bias<PREC, false>(x));
-                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, noise_bias<PREC, true>(x));
+                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
+                        x = step16(x, psi);
+                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
+                        x = step16(x, psi);
                     }
                     uint32_t ev = (uint32_t)ze[0];
                     uint32_t od = (uint32_t)zo[0];
@@ -498,9 +520,10 @@ struct TaskStream {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 2;
-                    const uint32_t x = w + (uint32_t)(j >> 1) * kPhi32;
-                    const uint32_t b0 = __float_as_uint(U[j]) + (x & 0xFFFFu);
-                    const uint32_t b1 = __float_as_uint(U[j + 1]) + (x >> 16);
+                    const uint32_t k2 = (uint32_t)(j >> 1) * ((2 * kPsi16) & 0xFFFFu);
+                    const uint32_t xj = step16(x, (k2 & 0xFFFFu) * 0x00010001u);
+                    const uint32_t b0 = __float_as_uint(U[j]) + (xj & 0xFFFFu);
+                    const uint32_t b1 = __float_as_uint(U[j + 1]) + (xj >> 16);
                     ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
                 }
             } else {
@@ -508,6 +531,9 @@ struct TaskStream {
                 for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
             }
             if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+            // keep the next chunk's draws after this store: unpinned, the
+            // whole (cheap, input-independent) chain is computed up front
+            // and held in registers
         }
     }
 };

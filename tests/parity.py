@@ -12,7 +12,11 @@ Tolerances (per compared step):
           product summation order can move a pre-rounding value across a
           rounding threshold)
   scales  relative difference <= 2^-20
-  bf16    at most 1e-4 of values differ, each by one bf16 ulp
+  bf16    at most 1e-4 of values differ, each by one bf16 ulp, or, where the
+          update cancelled to a value far below its row's magnitude (a bf16
+          ulp there is tiny), by at most one ulp plus 2^-16 of the row's
+          absolute maximum: a different summation order of r moves g by a
+          few fp32 ulps and U by about 2^-19 of the row's magnitude
   o       max |o - o_ref| <= 1e-3 * readout scale (1e-5 for fp32 heads); the
           readout scale of a unit is max_i |S_ref[i, :]|_2, which bounds |o_i|
           for a unit-norm q
@@ -78,6 +82,8 @@ class Stats:
         self.scale_rel = 0.0
         self.bf16 = self.bf16_diff = 0
         self.max_dbits = 0
+        self.bf16_far = 0               # differing by more than one ulp
+        self.bf16_far_rel = 0.0         # their worst excess over one ulp / row max
         self.o_err_q = 0.0
         self.o_err_f = 0.0
         self.x_err_f = 0.0
@@ -86,18 +92,23 @@ class Stats:
     def summary(self):
         return (f"steps={self.steps} code_flip={self.code_diff}/{self.codes} max|dc|={self.max_dc} "
                 f"scale_rel={self.scale_rel:.2e} bf16_flip={self.bf16_diff}/{self.bf16} "
-                f"max|dbits|={self.max_dbits} o_err_q={self.o_err_q:.2e} "
+                f"max|dbits|={self.max_dbits} far={self.bf16_far} "
+                f"far_rel={self.bf16_far_rel:.2e} o_err_q={self.o_err_q:.2e} "
                 f"o_err_f32={self.o_err_f:.2e} x_err_f32={self.x_err_f:.2e}")
 
     def check(self):
         assert self.max_dc <= 1, self.summary()
         assert self.code_diff <= max(1e-4 * self.codes, 0), self.summary()
         assert self.scale_rel <= 2.0 ** -20, self.summary()
-        assert self.max_dbits <= 1, self.summary()
+        assert self.bf16_far_rel <= 2.0 ** -16, self.summary()
         assert self.bf16_diff <= 1e-4 * self.bf16, self.summary()
         assert self.o_err_q <= 1e-3, self.summary()
         assert self.o_err_f <= 1e-5, self.summary()
         assert self.x_err_f <= 1e-5, self.summary()
+
+
+def bf16_values(bits):
+    return (np.asarray(bits, np.uint32) << np.uint32(16)).view(F32)
 
 
 def _readout_scale(X):
@@ -185,6 +196,16 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
                 stats.bf16 += d.size
                 stats.bf16_diff += int((d > 0).sum())
                 stats.max_dbits = max(stats.max_dbits, int(d.max()))
+                far = d > 1
+                if far.any():
+                    xg = bf16_values(gpu["bits"]).astype(np.float64)
+                    xr = X_ref.astype(np.float64)
+                    ulp = np.abs(bf16_values(new["bits"] | np.uint16(1)).astype(np.float64)
+                                 - bf16_values(new["bits"] & np.uint16(0xFFFE)).astype(np.float64))
+                    rowmax = np.abs(xr).max(axis=2, keepdims=True)
+                    excess = (np.abs(xg - xr) - ulp) / np.maximum(rowmax, 1e-300)
+                    stats.bf16_far += int(far.sum())
+                    stats.bf16_far_rel = max(stats.bf16_far_rel, float(excess[far].max()))
                 stats.o_err_q = max(stats.o_err_q, float(o_err))
             else:
                 xe = (np.abs(gpu["X"].astype(np.float64) - new["X"]).max(axis=(1, 2)) / scale).max()
