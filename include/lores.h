@@ -50,6 +50,12 @@ enum {
     LORES_INT4 = 3  /* int4 codes in [-7, 7]     + one fp32 scale per value row     */
 };
 
+/* Rounding of the requantization (per state; lores_state_set_rounding). */
+enum {
+    LORES_ROUND_STOCHASTIC = 0, /* default: the counter-based draw n below              */
+    LORES_ROUND_NEAREST = 1     /* the same quantizer with the draw fixed at n = 2^15 */
+};
+
 /* Status codes. */
 enum {
     LORES_OK = 0,
@@ -123,6 +129,22 @@ void lores_state_free(lores_state *st);
 /* Copy the layout of `st` into host struct *out. */
 int lores_state_layout(const lores_state *st, lores_layout *out);
 
+/*
+ * lores_state_set_rounding - rounding of every later requantization of `st`
+ * (host only; takes effect for calls enqueued afterwards).
+ *   LORES_ROUND_STOCHASTIC  stochastic rounding (the default), as described
+ *                           at lores_decode_step
+ *   LORES_ROUND_NEAREST     the same formula with u = 1/2 (n = 2^15): codes
+ *                           floor(fl(U * inv + bias + 1/2)) - bias, i.e. round
+ *                           to nearest, ties upward, after the fp32 rounding of
+ *                           the sum; bf16 heads keep the high half of
+ *                           f32bits(U) + 2^15 (nearest, ties away from zero)
+ * Round-to-nearest is the deterministic baseline the stochastic rounding is
+ * compared with ("Intra-State Quantization (Section 4)", Rounding and
+ * Proposition 3).  LORES_EINVAL for any other mode.
+ */
+int lores_state_set_rounding(lores_state *st, int32_t mode);
+
 /* Host arrays [H]: precision and slot (index among heads of that class). */
 int lores_state_head_map(const lores_state *st, uint8_t *prec_out, int32_t *slot_out);
 
@@ -193,6 +215,24 @@ int lores_step_launches(const lores_state *st, int32_t *n);
  * value = scale * code for int heads, the stored value for bf16 / fp32 heads.
  */
 int lores_dequant_state(const lores_state *st, float *out, void *stream);
+
+/*
+ * lores_quant_state - fp32 state -> packed state of `st`, in place of its
+ * contents: the requantization of lores_decode_step applied to X itself
+ * (int heads: fresh row scale and codes; bf16 heads: rounded; fp32 heads:
+ * copied), with the state's rounding mode and draws keyed on step index 0,
+ * which lores_decode_step never uses (t >= 1).  This hands a state built
+ * elsewhere (a prefill, a checkpoint) to decoding: S_0 = Q(X).
+ * ("Intra-State Quantization Approach": the state is held quantized between
+ * steps; "Intra-State Quantization (Section 4)", scale grouping and Rounding.)
+ *   X          device [B][H][d_v][d_k] fp32, 16-byte aligned (the layout
+ *              lores_dequant_state writes), finite
+ *   seed, seq_base, head_base   as for lores_decode_step
+ * LORES_EINVAL on a NULL or misaligned X or out-of-range bases; nothing is
+ * launched then.
+ */
+int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t seq_base,
+                      int64_t head_base, void *stream);
 
 /* Thread-local description of the last error (empty string if none). */
 const char *lores_last_error(void);

@@ -98,10 +98,17 @@ def quantize_rows(U, prec, n=None, rounding="sr"):
     """Requantize U [N, dv, dk] (fp32) with one fresh scale per value row.
 
     n: noise draws [N, dv, dk] (uint32 < 2^16), needed for rounding="sr".
-    rounding="rtn" rounds fl(U * inv) to nearest (ties to even) instead.
+    rounding="nearest" is the same quantizer with every draw fixed at 2^15
+    (u = 1/2): round to nearest, ties upward after the fp32 rounding of the
+    sum (bf16: ties away from zero) -- the library's round-to-nearest mode.
+    rounding="rtn" is the textbook form: fl(U * inv) rounded to nearest, ties
+    to even (bf16: ties to even), used by the error-propagation checks.
     Returns the new state dict.
     """
     U = f32(U)
+    if rounding == "nearest":
+        n = np.full(U.shape, 1 << 15, dtype=np.uint32)
+        rounding = "sr"
     if prec in QMAX:
         r = QMAX[prec]
         m = np.max(np.abs(U), axis=2)
@@ -170,10 +177,25 @@ def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
 
     # 5  requantize with fresh row scales
     n = None
-    if prec != PREC_FP32 and rounding == "sr":
+    if prec != PREC_FP32 and rounding == "sr":  # "nearest" and "rtn" need no draws
         K = unit_key(seed, t, b, h)
         n = (noise16 if noise == "weyl" else noise16_iid)(K, dv, dk)
     return quantize_rows(U, prec, n, rounding), o
+
+
+def quant_state(prec, X, seed, b, h, rounding="sr"):
+    """Quantize fp32 states X [N, dv, dk] of one precision class: the
+    requantization of a decode step applied to X itself, with draws keyed on
+    step index 0 (decode steps use t >= 1).  b, h [N]: global indices.
+
+    The state is stored quantized between steps ("Intra-State Quantization
+    Approach"); this is how a state built elsewhere enters that form."""
+    X = f32(X)
+    N, dv, dk = X.shape
+    n = None
+    if prec != PREC_FP32 and rounding == "sr":
+        n = noise16(unit_key(seed, 0, b, h), dv, dk)
+    return quantize_rows(X, prec, n, rounding)
 
 
 def run_trajectory(prec, state, inputs, delta, seed, b, h, t0=1, rounding="sr",

@@ -14,13 +14,14 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (LORES_BF16, LORES_FP32, LORES_INT4, LORES_INT8, LoresLayout,
-                   LoresLibraryMissing)
+from ._lib import (LORES_BF16, LORES_FP32, LORES_INT4, LORES_INT8, LORES_ROUND_NEAREST,
+                   LORES_ROUND_STOCHASTIC, LoresLayout, LoresLibraryMissing)
 
-__all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LoresError",
+__all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LORES_ROUND_STOCHASTIC",
+           "LORES_ROUND_NEAREST", "LoresError", "lores_state_set_rounding",
            "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_layout",
            "lores_state_head_map", "lores_decay_stat", "lores_assign_precision",
-           "lores_decode_step", "lores_step_launches", "lores_dequant_state",
+           "lores_decode_step", "lores_step_launches", "lores_quant_state", "lores_dequant_state",
            "lores_last_error", "lores_spec_version"]
 
 
@@ -83,6 +84,7 @@ class LoresState:
         self.device = buf.device
         self.B, self.H, self.d_k, self.d_v = B, H, d_k, d_v
         self.head_prec = list(head_prec)
+        self.rounding = LORES_ROUND_STOCHASTIC
 
     @property
     def handle(self):
@@ -142,6 +144,12 @@ def lores_state_head_map(state):
     return prec, slot
 
 
+def lores_state_set_rounding(state, mode):
+    """LORES_ROUND_STOCHASTIC (default) or LORES_ROUND_NEAREST for later steps."""
+    _check(_lib.lib().lores_state_set_rounding(ctypes.c_void_p(state.handle), int(mode)))
+    state.rounding = int(mode)
+
+
 def lores_step_launches(state):
     """Kernel launches one lores_decode_step on `state` enqueues."""
     n = ctypes.c_int32(0)
@@ -195,6 +203,16 @@ def lores_decode_step(state, q, k, v, alpha, beta, delta, seed, t, o=None, seq_b
                                         int(seq_base), int(head_base), o_ptr,
                                         _stream_ptr(stream, dev)))
     return o
+
+
+def lores_quant_state(state, X, seed, seq_base=0, head_base=0, stream=None):
+    """fp32 [B, H, d_v, d_k] -> the packed state (requantized, draws keyed at t = 0)."""
+    import torch
+    shape = (state.B, state.H, state.d_v, state.d_k)
+    ptr = _dev_ptr(X, "X", torch.float32, int(np.prod(shape)), state.device)
+    _check(_lib.lib().lores_quant_state(ctypes.c_void_p(state.handle), ptr, int(seed),
+                                        int(seq_base), int(head_base),
+                                        _stream_ptr(stream, state.device)))
 
 
 def lores_dequant_state(state, out=None, stream=None):

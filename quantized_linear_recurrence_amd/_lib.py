@@ -9,6 +9,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblores.so")
 
 LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4 = 0, 1, 2, 3
+LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST = 0, 1
 LORES_OK, LORES_EINVAL, LORES_EUNSUPPORTED, LORES_ESIZE, LORES_EHIP, LORES_ENOMEM = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3: "LORES_ESIZE",
                 -4: "LORES_EHIP", -5: "LORES_ENOMEM"}
@@ -16,8 +17,9 @@ STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3:
 # every symbol include/lores.h declares
 EXPORTS = ("lores_state_alloc", "lores_state_free", "lores_state_layout", "lores_state_head_map",
            "lores_decay_stat", "lores_assign_precision", "lores_decode_step",
-           "lores_step_launches", "lores_dequant_state", "lores_last_error",
-           "lores_spec_version")
+           "lores_step_launches", "lores_state_set_rounding", "lores_quant_state",
+           "lores_dequant_state",
+           "lores_last_error", "lores_spec_version")
 
 
 class LoresLibraryMissing(RuntimeError):
@@ -61,8 +63,12 @@ def lib():
     L.lores_decode_step.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, i32, u64, u64, i64, i64,
                                     vp, vp]
     L.lores_decode_step.restype = ctypes.c_int
+    L.lores_state_set_rounding.argtypes = [vp, i32]
+    L.lores_state_set_rounding.restype = ctypes.c_int
     L.lores_step_launches.argtypes = [vp, ctypes.POINTER(i32)]
     L.lores_step_launches.restype = ctypes.c_int
+    L.lores_quant_state.argtypes = [vp, vp, u64, i64, i64, vp]
+    L.lores_quant_state.restype = ctypes.c_int
     L.lores_dequant_state.argtypes = [vp, vp, vp]
     L.lores_dequant_state.restype = ctypes.c_int
     L.lores_last_error.argtypes = []

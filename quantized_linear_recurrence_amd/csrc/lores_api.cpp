@@ -23,6 +23,7 @@ struct lores_state {
     int64_t codes_off[4], scales_off[4], unit_bytes[4];
     uint64_t total;
     uint8_t *base;
+    int32_t rounding;        // LORES_ROUND_*
 };
 
 namespace {
@@ -111,6 +112,7 @@ lores::StepMeta make_meta(const lores_state *st, const int *cls, int n_cls) {
     m.dv_pad = st->dv_pad;
     m.n_rb = st->n_rb;
     m.n_cls = n_cls;
+    m.rounding = st->rounding;
     int off = 0;
     for (int i = 0; i < n_cls; ++i) {
         const int c = cls[i];
@@ -183,6 +185,7 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         tmp.dk = d_k;
         tmp.dv = d_v;
         tmp.base = nullptr;
+        tmp.rounding = LORES_ROUND_STOCHASTIC;
         rc = plan(&tmp, head_prec);
         if (rc) return rc;
         if (!d_buf) {
@@ -225,6 +228,15 @@ int lores_state_layout(const lores_state *st, lores_layout *out) {
         out->unit_code_bytes[c] = st->unit_bytes[c];
     }
     out->total_bytes = st->total;
+    return ok();
+}
+
+int lores_state_set_rounding(lores_state *st, int32_t mode) {
+    if (!st) return fail(LORES_EINVAL, "state handle is NULL");
+    if (mode != LORES_ROUND_STOCHASTIC && mode != LORES_ROUND_NEAREST)
+        return fail(LORES_EINVAL, "rounding mode must be LORES_ROUND_STOCHASTIC (0) or "
+                                  "LORES_ROUND_NEAREST (1), got %d", mode);
+    st->rounding = mode;
     return ok();
 }
 
@@ -377,6 +389,34 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         return ok();
     } catch (...) {
         return fail(LORES_EINVAL, "internal error in lores_decode_step");
+    }
+}
+
+int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t seq_base,
+                      int64_t head_base, void *stream) {
+    try {
+        if (!st || !X) return fail(LORES_EINVAL, "NULL argument");
+        if (!aligned(X, 16)) return fail(LORES_EINVAL, "X must be 16-byte aligned");
+        if (seq_base < 0 || (uint64_t)seq_base + (uint64_t)st->B > (1ull << 32))
+            return fail(LORES_EINVAL, "seq_base + B must lie in [0, 2^32]");
+        if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
+            return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
+        for (int c = 0; c < 4; ++c) {
+            if (!st->n_class[c]) continue;
+            lores::StepMeta m = make_meta(st, &c, 1);
+            m.seed = seed;
+            m.t = 0;
+            m.seq_base = seq_base;
+            m.head_base = head_base;
+            float *sc = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
+            hipError_t e = lores::launch_quant(c, st->dk, X, st->base + st->codes_off[c], sc, m,
+                                               (hipStream_t)stream);
+            if (e != hipSuccess)
+                return fail(LORES_EHIP, "quantize launch failed: %s", hipGetErrorString(e));
+        }
+        return ok();
+    } catch (...) {
+        return fail(LORES_EINVAL, "internal error in lores_quant_state");
     }
 }
 

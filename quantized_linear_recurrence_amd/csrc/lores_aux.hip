@@ -1,6 +1,7 @@
-// Auxiliary kernels: packed state -> fp32 (lores_dequant_state) and the
-// zero fill that sets S_0 = 0 (a plain kernel rather than a memset node, so a
-// caller may capture it in a graph).
+// Auxiliary kernels: packed state -> fp32 (lores_dequant_state), fp32 ->
+// packed state (lores_quant_state) and the zero fill that sets S_0 = 0 (a
+// plain kernel rather than a memset node, so a caller may capture it in a
+// graph).
 #include "lores_step_impl.h"
 
 namespace lores {
@@ -56,6 +57,72 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
         }
+    }
+}
+
+// fp32 rows -> packed rows of one class with the step's own requantization
+// (requantize_row), keyed at meta.t.  Same wavefront-per-64-rows mapping.
+template <int DK, int PREC>
+__global__ void __launch_bounds__(64 * kWavesPerGroup)
+lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
+                   float *__restrict__ scales, const StepMeta meta) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const ClassDesc &cd = meta.cls[0];
+    const int task = blockIdx.x * kWavesPerGroup + wv;
+    if (task >= cd.Hc * meta.n_rb) return;
+    const int slot = task / meta.n_rb;
+    const int rb = task - slot * meta.n_rb;
+    const int b = blockIdx.y;
+    const long unit = (long)b * cd.Hc + slot;
+    const int h = (int)meta.heads[cd.head_off + slot];
+    const long bh = (long)b * meta.H + h;
+    const int row = rb * 64 + lane;
+    const bool active = row < meta.dv;
+    const long dv_pad = meta.dv_pad;
+    // padding lanes read the last real row and store nothing
+    const float *xrow = X + (bh * meta.dv + (active ? row : meta.dv - 1)) * DK;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    float U[DK];
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < DK; c += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(xrow + c);
+        U[c] = v.x;
+        U[c + 1] = v.y;
+        U[c + 2] = v.z;
+        U[c + 3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
+    u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * cd.unit_bytes) + row;
+    requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+                             is_int<PREC>() ? scales + unit * dv_pad + row : nullptr);
+}
+
+template <int PREC>
+static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scales,
+                             const StepMeta &m, hipStream_t s) {
+    const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
+    const dim3 block(64 * kWavesPerGroup);
+    switch (dk) {
+        case 32: hipLaunchKernelGGL((lores_quant_kernel<32, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
+                        const StepMeta &m, hipStream_t s) {
+    switch (prec) {
+        case LORES_FP32: return quant_prec<LORES_FP32>(dk, X, codes, scales, m, s);
+        case LORES_BF16: return quant_prec<LORES_BF16>(dk, X, codes, scales, m, s);
+        case LORES_INT8: return quant_prec<LORES_INT8>(dk, X, codes, scales, m, s);
+        case LORES_INT4: return quant_prec<LORES_INT4>(dk, X, codes, scales, m, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

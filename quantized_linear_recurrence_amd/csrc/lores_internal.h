@@ -25,6 +25,8 @@ struct ClassDesc {
 // blockIdx.y, blockIdx.y + gridDim.y, ...
 struct StepMeta {
     int32_t B, H, dv, dv_pad, n_rb, n_cls;
+    int32_t rounding;                  // LORES_ROUND_*
+    int32_t pad_;
     uint64_t seed, t;
     int64_t seq_base, head_base;
     ClassDesc cls[2];
@@ -59,6 +61,8 @@ hipError_t launch_step_bf16_int4(int, bool, bool, bool, const StepPtrs &, const 
 // Dequant uses the same StepMeta with one class.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
                           float *out, const StepMeta &m, hipStream_t s);
+hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
+                        const StepMeta &m, hipStream_t s);
 hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);
 
 // Tasks (one wavefront each) per 256-thread work-group.

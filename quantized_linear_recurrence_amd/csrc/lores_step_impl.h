@@ -102,6 +102,7 @@ template <int PREC> constexpr bool is_int() { return PREC == LORES_INT8 || PREC 
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
+
 // Both 16-bit halves of x advanced by those of inc, each mod 2^16 (one
 // v_pk_add_u16): the noise sequence steps in the low half while the high
 // half, the sign, exponent and top mantissa bits of the bias, is kept.
@@ -295,6 +296,107 @@ __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx)
 }
 
 // ---------------------------------------------------------------------------
+// requantization of one row (one lane): fresh scale, rounding, packing and
+// store of the row's 16-byte chunks (chunk c at cp + c * dv_pad).  Shared by
+// the step and by the fp32 -> packed state entry.
+// ---------------------------------------------------------------------------
+template <int DK, int PREC>
+__device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, const StepMeta &meta,
+                                               int b, int h, int row, bool active, u32x4 *cp,
+                                               long dv_pad, float *scale_out) {
+    constexpr int E = Prec<PREC>::E;
+    constexpr int NCH = DK / E;
+    float inv = 0.0f;
+    if constexpr (is_int<PREC>()) {
+        const float snew = m / Prec<PREC>::R;
+        inv = rd_div(Prec<PREC>::R, m);
+        if (active) *scale_out = snew;
+    }
+    // int: x holds the fma addend bias + n_ij * 2^-16 of the current
+    // column (in [128, 256), where one fp32 ulp is 2^-16: the draw is the
+    // low 16 mantissa bits); bf16: x holds the draws of columns 0 and 1.
+    // Round-to-nearest is the constant draw 2^15 (first draw 2^15, step 0).
+    const bool nearest = meta.rounding == LORES_ROUND_NEAREST;
+    uint32_t x = 0;
+    if constexpr (PREC != LORES_FP32) {
+        const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
+                                    (uint64_t)(meta.head_base + h));
+        uint32_t n0 = fmix32(K ^ (uint32_t)row) & 0xFFFFu;
+        if (nearest) n0 = 0x8000u;
+        const uint32_t n1 = nearest ? n0 : (n0 + kPsi16) & 0xFFFFu;
+        if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
+        else x = n0 | (n1 << 16);
+    }
+    const uint32_t psi = opaque_uniform(nearest ? 0u : kPsi16);
+    const uint32_t psi2 = opaque_uniform(nearest ? 0u : ((2 * kPsi16) & 0xFFFFu) * 0x00010001u);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t ow[4];
+        if constexpr (PREC == LORES_INT8) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int j = c * E + q4 * 4;
+                float z[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
+                    x = step16(x, psi);
+                }
+                const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
+                uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
+                cvt_u8_into<1>(word, z1);
+                cvt_u8_into<2>(word, z2);
+                cvt_u8_into<3>(word, z3);
+                ow[q4] = word;
+            }
+        } else if constexpr (PREC == LORES_INT4) {
+            // e in [129, 143]; its low nibble is the offset-binary code c + 8
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int j = c * E + q4 * 8;
+                float ze[4], zo[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
+                    x = step16(x, psi);
+                    zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
+                    x = step16(x, psi);
+                }
+                uint32_t ev = (uint32_t)ze[0];
+                uint32_t od = (uint32_t)zo[0];
+                cvt_u8_into<1>(ev, ze[1]);
+                cvt_u8_into<1>(od, zo[1]);
+                cvt_u8_into<2>(ev, ze[2]);
+                cvt_u8_into<2>(od, zo[2]);
+                cvt_u8_into<3>(ev, ze[3]);
+                cvt_u8_into<3>(od, zo[3]);
+                ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+            }
+        } else if constexpr (PREC == LORES_BF16) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int j = c * E + q4 * 2;
+                // draws of columns j, j + 1: those of columns 0, 1 plus
+                // (j / 2) * 2 psi in each half (one v_pk_mad_u16)
+                const u16x2 kk = {(unsigned short)(j >> 1), (unsigned short)(j >> 1)};
+                const uint32_t xj = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(u16x2, x) + kk * __builtin_bit_cast(u16x2, psi2));
+                const uint32_t b0 = __float_as_uint(U[j]) + (xj & 0xFFFFu);
+                const uint32_t b1 = __float_as_uint(U[j + 1]) + (xj >> 16);
+                ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+            }
+        } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+        }
+        if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+        // keep the next chunk's draws after this store: unpinned, the
+        // whole (cheap, input-independent) chain is computed up front
+        // and held in registers
+    }
+}
+
+// ---------------------------------------------------------------------------
 // one (class, head slot, row block) stream of tasks
 // ---------------------------------------------------------------------------
 // A wavefront owns one (head slot, row block) of a class and walks the
@@ -454,113 +556,44 @@ struct TaskStream {
         if (active) op[bh * meta.dv + row] = o;
 
         // ---- pass 3: requantize and store in place
-        float inv = 0.0f;
-        if constexpr (is_int<PREC>()) {
-            const float snew = m / Prec<PREC>::R;
-            inv = rd_div(Prec<PREC>::R, m);
-            if (active) scales[unit * dv_pad + row] = snew;
-        }
-        // int: x holds the fma addend bias + n_ij * 2^-16 of the current
-        // column (in [128, 256), where one fp32 ulp is 2^-16: the draw is the
-        // low 16 mantissa bits); bf16: x holds the draws of columns j, j + 1
-        uint32_t x = 0;
-        if constexpr (PREC != LORES_FP32) {
-            const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
-                                        (uint64_t)(meta.head_base + h));
-            const uint32_t n0 = fmix32(K ^ (uint32_t)row) & 0xFFFFu;
-            if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
-            else x = n0 | (((n0 + kPsi16) & 0xFFFFu) << 16);
-        }
-        const uint32_t psi = opaque_uniform(is_int<PREC>() ? kPsi16
-                                                            : ((2 * kPsi16) & 0xFFFFu) * 0x00010001u);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            uint32_t ow[4];
-            if constexpr (PREC == LORES_INT8) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int j = c * E + q4 * 4;
-                    float z[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
-                        x = step16(x, psi);
-                    }
-                    const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
-                    uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
-                    cvt_u8_into<1>(word, z1);
-                    cvt_u8_into<2>(word, z2);
-                    cvt_u8_into<3>(word, z3);
-                    ow[q4] = word;
-                }
-            } else if constexpr (PREC == LORES_INT4) {
-                // e in [129, 143]; its low nibble is the offset-binary code c + 8
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int j = c * E + q4 * 8;
-                    float ze[4], zo[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
-                        x = step16(x, psi);
-                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
-                        x = step16(x, psi);
-                    }
-                    uint32_t ev = (uint32_t)ze[0];
-                    uint32_t od = (uint32_t)zo[0];
-                    cvt_u8_into<1>(ev, ze[1]);
-                    cvt_u8_into<1>(od, zo[1]);
-                    cvt_u8_into<2>(ev, ze[2]);
-                    cvt_u8_into<2>(od, zo[2]);
-                    cvt_u8_into<3>(ev, ze[3]);
-                    cvt_u8_into<3>(od, zo[3]);
-                    ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
-                }
-            } else if constexpr (PREC == LORES_BF16) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int j = c * E + q4 * 2;
-                    const uint32_t k2 = (uint32_t)(j >> 1) * ((2 * kPsi16) & 0xFFFFu);
-                    const uint32_t xj = step16(x, (k2 & 0xFFFFu) * 0x00010001u);
-                    const uint32_t b0 = __float_as_uint(U[j]) + (xj & 0xFFFFu);
-                    const uint32_t b1 = __float_as_uint(U[j + 1]) + (xj >> 16);
-                    ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-                }
-            } else {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
-            }
-            if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
-            // keep the next chunk's draws after this store: unpinned, the
-            // whole (cheap, input-independent) chain is computed up front
-            // and held in registers
-        }
+        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+                                 is_int<PREC>() ? scales + unit * dv_pad + row : nullptr);
     }
 };
 
 // One stream over all its sequences.  For int classes the next sequence's
 // loads are issued right after pass 1 (a second chunk set fits in the
-// registers); bf16 / fp32 rows are loaded at the top of each task.
+// registers); bf16 / fp32 rows are loaded at the top of each task.  The loop
+// body holds two tasks, so the prefetched per-task values alternate between
+// two register sets instead of being copied.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
 __device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN> &ts) {
     using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN>;
     constexpr bool kPrefetch = TS::NCH <= kMaxPrefetchChunks;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
-    TaskSide<TS::NV> in, nx;
+    TaskSide<TS::NV> in0, in1;        // alternate, so no copy between tasks
     int b = blockIdx.y;
-    ts.issue(b, cw, in);
+    ts.issue(b, cw, in0);
     while (true) {
-        const int bn = b + bstep;
-        ts.run(b, cw, in, [&] {
+        int bn = b + bstep;
+        ts.run(b, cw, in0, [&] {
             if constexpr (kPrefetch) {
-                if (bn < ts.meta.B) ts.issue(bn, cw, nx);
+                if (bn < ts.meta.B) ts.issue(bn, cw, in1);
             }
         });
         if (bn >= ts.meta.B) break;
         b = bn;
-        if constexpr (kPrefetch) in = nx;
-        else ts.issue(b, cw, in);
+        bn = b + bstep;
+        if constexpr (!kPrefetch) ts.issue(b, cw, in1);
+        ts.run(b, cw, in1, [&] {
+            if constexpr (kPrefetch) {
+                if (bn < ts.meta.B) ts.issue(bn, cw, in0);
+            }
+        });
+        if (bn >= ts.meta.B) break;
+        b = bn;
+        if constexpr (!kPrefetch) ts.issue(b, cw, in0);
     }
 }
 

@@ -116,12 +116,14 @@ def _readout_scale(X):
 
 
 def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", inputs=None,
-               device="cuda"):
+               device="cuda", rounding="sr"):
     """Run T GPU steps with per-step resync to the oracle; returns Stats.
 
     units: list of (b, h) to compare (default: all).  init: "zero" (S_0 = 0),
     "random" (random codes and scales, or random bf16 / fp32 values) or a
     function (prec, dv, dk, numpy Generator) -> one unit's state.
+    rounding: "sr" (stochastic, the default) or "nearest" (the library's
+    round-to-nearest mode, set on the state through the C ABI).
     """
     B = w.B if B is None else B
     if inputs is None:
@@ -129,6 +131,8 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
     if head_prec is None:
         head_prec = head_precisions(w, inputs)
     st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device)
+    if rounding == "nearest":
+        lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
     lay = lores.lores_state_layout(st)
     hprec, hslot = lores.lores_state_head_map(st)
     assert list(hprec) == list(head_prec)
@@ -175,7 +179,8 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
             prev = _stack([ost[u] for u in us])
             q, k, v = xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs]
             al, be = xin["alpha"][bs, hs], xin["beta"][bs, hs]
-            new, o_ref = ostep.decode_step(c, prev, q, k, v, al, be, w.delta, seed, t, bs, hs)
+            new, o_ref = ostep.decode_step(c, prev, q, k, v, al, be, w.delta, seed, t, bs, hs,
+                                           rounding=rounding)
             X_ref = ostep.dequant(c, new)
             scale = _readout_scale(X_ref)
             o_err = (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()

@@ -124,6 +124,28 @@ def test_key_changes_the_rounding():
         assert not np.array_equal(r, results[0])
 
 
+def test_nearest_rounding_ignores_the_keys():
+    """In round-to-nearest mode the seed, step and base indices no longer
+    reach the result; an invalid mode is rejected."""
+    w = C1.scaled(B=2, H=3, dk=128, dv=64, T=1)
+    log("case: nearest mode is key-independent, B=2 H=3 int8/int4/bf16")
+    x = {k: v[0] for k, v in make_inputs(w, 0, DEV).items()}
+    prec = [2, 3, 1]
+    init = _random_states(2, prec, 64, 128, seed=6)
+    results = []
+    for seed, t, sb, hb in [(0, 1, 0, 0), (1, 1, 0, 0), (0, 2, 0, 0), (0, 1, 7, 0), (0, 1, 0, 7)]:
+        st = lores.lores_state_alloc(2, 3, 128, 64, prec, device=DEV)
+        lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
+        _install(st, init)
+        lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, seed, t,
+                                seq_base=sb, head_base=hb)
+        results.append(st.buf.cpu().numpy())
+    for r in results[1:]:
+        assert np.array_equal(r, results[0])
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_state_set_rounding(st, 2)
+
+
 def test_repeatable_eager_and_graph():
     """The same steps from the same state give the same bytes: twice eagerly,
     and over several replays of a captured graph with eager work between."""
@@ -235,6 +257,91 @@ def test_error_paths_live_handle():
         lores.lores_state_alloc(2, 2, 64, 64, [2, 3], buf=big[16:16 + need])
     with pytest.raises(lores.LoresError, match="EUNSUPPORTED|EINVAL"):
         lores.lores_state_alloc(2, 2, 48, 64, [2, 3], device=DEV)
+
+
+@pytest.mark.parametrize("dk,dv,rounding", [(128, 128, "sr"), (96, 65, "sr"), (32, 1, "sr"),
+                                             (64, 200, "nearest"), (128, 64, "nearest")])
+def test_quant_state_matches_oracle(dk, dv, rounding):
+    """lores_quant_state equals the oracle's quantization of the same fp32
+    state bit for bit (no summation is involved), for every precision, with
+    zero rows and rows of very different magnitude; base indices key it."""
+    B, head_prec = 3, [0, 1, 2, 3, 3, 2]
+    H = len(head_prec)
+    log(f"case: quant state B={B} dk={dk} dv={dv} rounding={rounding} precisions {head_prec}")
+    g = np.random.default_rng(dk * 7 + dv)
+    X = (g.standard_normal((B, H, dv, dk)) * np.exp(g.uniform(-6, 6, (B, H, dv, 1)))).astype(np.float32)
+    X[0, :, 0, :] = 0.0                                    # zero rows
+    st = lores.lores_state_alloc(B, H, dk, dv, head_prec, device=DEV)
+    if rounding == "nearest":
+        lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
+    seed, sb, hb = 77, 5, 9
+    lores.lores_quant_state(st, torch.from_numpy(X).to(DEV), seed, seq_base=sb, head_base=hb)
+    torch.cuda.synchronize()
+    lay = lores.lores_state_layout(st)
+    _, slot = lores.lores_state_head_map(st)
+    buf = st.buf.cpu().numpy()
+    for h, c in enumerate(head_prec):
+        bs = np.arange(B)
+        want = ostep.quant_state(c, X[:, h], seed, bs + sb, np.full(B, h + hb), rounding=rounding)
+        for b in range(B):
+            got = lc.read_unit(buf, lay, c, b * lay["n_class"][c] + slot[h])
+            for key, val in got.items():
+                assert np.array_equal(np.asarray(val).view(np.uint8),
+                                      np.ascontiguousarray(want[key][b]).astype(val.dtype).view(np.uint8)), \
+                    (b, h, key)
+    # the round trip through lores_dequant_state is the oracle's dequantization
+    out = lores.lores_dequant_state(st).cpu().numpy()
+    for h, c in enumerate(head_prec):
+        want = ostep.dequant(c, ostep.quant_state(c, X[:, h], seed, np.arange(B) + sb,
+                                                  np.full(B, h + hb), rounding=rounding))
+        assert np.array_equal(out[:, h].view(np.uint32), want.view(np.uint32)), h
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_quant_state(st, torch.from_numpy(X).to(DEV), seed, seq_base=-1)
+
+
+def test_quant_state_then_step():
+    """A state handed over by lores_quant_state steps on like any other: the
+    GPU's quantize-then-step matches the oracle's (quantization bit-exact,
+    the step to the parity tolerances)."""
+    B, H, dk, dv, prec, seed = 2, 4, 128, 64, [0, 1, 2, 3], 11
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=1)
+    log("case: quant state, then one decode step, precisions fp32/bf16/int8/int4")
+    g = np.random.default_rng(3)
+    X = (g.standard_normal((B, H, dv, dk)) * 0.1).astype(np.float32)
+    x = {k: v[0] for k, v in make_inputs(w, 4, DEV).items()}
+    st = lores.lores_state_alloc(B, H, dk, dv, prec, device=DEV)
+    lores.lores_quant_state(st, torch.from_numpy(X).to(DEV), seed)
+    o = lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, seed, 1)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    xin = {k: v.float().cpu().numpy() for k, v in x.items()}
+    lay = lores.lores_state_layout(st)
+    _, slot = lores.lores_state_head_map(st)
+    buf = st.buf.cpu().numpy()
+    bs = np.arange(B)
+    for h, c in enumerate(prec):
+        s0 = ostep.quant_state(c, X[:, h], seed, bs, np.full(B, h))
+        new, o_ref = ostep.decode_step(c, s0, xin["q"][:, h], xin["k"][:, h], xin["v"][:, h],
+                                       xin["alpha"][:, h], xin["beta"][:, h], 1, seed, 1, bs,
+                                       np.full(B, h))
+        X_ref = ostep.dequant(c, new).astype(np.float64)
+        scale = np.linalg.norm(X_ref, axis=-1).max(axis=-1)
+        tol = 1e-5 if c == 0 else 1e-3
+        assert np.all(np.abs(o[:, h] - o_ref).max(axis=1) <= tol * scale), h
+        gpu = [lc.read_unit(buf, lay, c, b * lay["n_class"][c] + slot[h]) for b in range(B)]
+        X_gpu = np.stack([ostep.dequant(c, {k: v[None] for k, v in u.items()})[0] for u in gpu])
+        # one code (or one bf16 ulp plus the cancellation allowance) per element
+        err = np.abs(X_gpu.astype(np.float64) - X_ref)
+        rowmax = np.abs(X_ref).max(axis=2, keepdims=True)
+        if c in (2, 3):
+            step_size = rowmax / (127 if c == 2 else 7)
+            assert np.all(err <= step_size * (1 + 1e-6)), h
+            d = np.abs(np.stack([u["codes"] for u in gpu]).astype(np.int64) - new["codes"])
+            assert d.max() <= 1 and (d > 0).sum() <= max(1, 1e-4 * d.size), h
+        elif c == 1:
+            assert np.all(err <= np.abs(X_ref) * 2.0 ** -7 + rowmax * 2.0 ** -16), h
+        else:
+            assert np.all(err <= 1e-5 * rowmax), h
 
 
 def _scaled_state(lo, hi):

@@ -50,6 +50,24 @@ def test_ragged_mixed_precisions(dk, dv, decay):
     s.check()
 
 
+@pytest.mark.parametrize("delta", [0, 1])
+def test_nearest_rounding_each_precision(delta):
+    w = C1.scaled(B=3, H=4, dk=128, dv=80, T=6, delta=delta, decay="kda_channel")
+    log(f"case: round-to-nearest mode B=3 H=4 d_k=128 d_v=80 delta={delta}, heads fp32/bf16/int8/int4")
+    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3], init="random", rounding="nearest")
+    log(s.summary())
+    s.check()
+
+
+def test_nearest_rounding_fused_pair_full_size():
+    w = get_workload("C5")
+    log("case: round-to-nearest mode, C5 full batch (fused int8 + int4), 32 sampled units, 2 steps")
+    s = run_parity(w, T=2, units=_sample_units(w.B, w.H, 32, seed=5), init="random",
+                   rounding="nearest")
+    log(s.summary())
+    s.check()
+
+
 def test_bf16_inputs_small():
     w = C1.scaled(B=2, H=4, T=8, in_bf16=True)
     log("case: bf16 q/k/v inputs, mixed precisions")

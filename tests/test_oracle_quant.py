@@ -174,3 +174,44 @@ def test_weyl_noise_matches_independent_noise_readout_error(prec):
         e = np.einsum("nij,nj->ni", (X - U).astype(np.float64), q)
         errs[name] = float(np.mean(e ** 2))
     assert abs(errs["weyl"] / errs["iid"] - 1) < 0.10, errs
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+def test_nearest_mode_is_round_to_nearest(prec):
+    """rounding="nearest" (the draw fixed at 2^15) rounds y = U * inv to the
+    nearest code: |c - y| <= 1/2 (+ the 2^-16 rounding of the sum), and it
+    agrees with the textbook ties-to-even rounding except within 2^-15 of a
+    tie."""
+    g = np.random.default_rng(41)
+    U = (g.standard_normal((50, 16, 64)) * np.exp(g.uniform(-3, 3, (50, 16, 1)))).astype(F32)
+    st = step.quantize_rows(U, prec, rounding="nearest")
+    r = {step.PREC_INT8: 127, step.PREC_INT4: 7}[prec]
+    m = np.abs(U).max(axis=2)
+    inv = exact.rd_div32(F32(r), m).astype(np.float64)
+    y = U.astype(np.float64) * inv[:, :, None]
+    c = st["codes"].astype(np.float64)
+    assert np.all(np.abs(c - y) <= 0.5 + 2.0 ** -15)
+    assert np.all(np.abs(c) <= r)
+    rtn = step.quantize_rows(U, prec, rounding="rtn")["codes"]
+    near_tie = np.abs(np.abs(y - np.floor(y)) - 0.5) <= 2.0 ** -15
+    assert np.array_equal(st["codes"][~near_tie], rtn[~near_tie])
+    # exact ties go up
+    U2 = np.zeros((1, 1, 4), F32)
+    U2[0, 0] = [r, 0.5 * r / r * 1.0, -0.5, 0.0]        # y = r, 0.5, -0.5, 0
+    c2 = step.quantize_rows(U2, prec, rounding="nearest")["codes"][0, 0]
+    assert list(c2) == [r, 1, 0, 0]
+
+
+def test_nearest_mode_bf16_is_round_to_nearest():
+    g = np.random.default_rng(42)
+    U = (g.standard_normal((4, 8, 256)) * np.exp(g.uniform(-20, 20, (4, 8, 1)))).astype(F32)
+    near = step.quantize_rows(U, step.PREC_BF16, rounding="nearest")["bits"]
+    rne = step.quantize_rows(U, step.PREC_BF16, rounding="rtn")["bits"]
+    low = exact.f32_bits(U) & np.uint32(0xFFFF)
+    tie = low == 0x8000
+    assert np.array_equal(near[~tie], rne[~tie])
+    # at a tie the magnitude rounds up (away from zero)
+    x = np.array([[[exact.bits_f32(np.uint32(0x3F808000)), exact.bits_f32(np.uint32(0xBF818000))]]],
+                 F32)
+    got = step.quantize_rows(x, step.PREC_BF16, rounding="nearest")["bits"][0, 0]
+    assert list(got) == [0x3F81, 0xBF82]
