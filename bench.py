@@ -14,7 +14,9 @@ Workloads (synthetic, shapes of the decode layers the method targets):
   C5 large batch, B=2048 H=32 d=128, 16 int8 + 16 int4 heads
   C1 is the tiny parity case (launch-bound; not a throughput workload).
 --mode copy times a plain device copy (the HBM calibration used for the
-rocprofv3 byte counters).
+rocprofv3 byte counters); --mode error runs the error-accumulation harness
+(quantized state against an fp32 twin over a long horizon) and prints its
+report instead.
 """
 import argparse
 import hashlib
@@ -59,7 +61,9 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "error"])
+    ap.add_argument("--error-steps", type=int, default=2048,
+                    help="horizon of the error-accumulation harness (--mode error)")
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="how the timed steps are issued")
@@ -151,6 +155,15 @@ def main(argv=None):
     import torch
     if args.mode == "copy":
         copy_mode(args, torch)
+        return
+    if args.mode == "error":
+        from quantized_linear_recurrence_amd import error_harness
+        t0 = time.perf_counter()
+        rows = error_harness.run_suite(T=args.error_steps, seed=args.seed)
+        print(json.dumps({"mode": "error", "metric": "relative state error vs an fp32 twin",
+                          "T": args.error_steps, "B": 32, "H": 12, "d_k": 128, "d_v": 128,
+                          "delta": 0, "inputs": "random unit k, q; random v; beta 0.5",
+                          "seconds": time.perf_counter() - t0, "results": rows}), flush=True)
         return
 
     import quantized_linear_recurrence_amd as lores

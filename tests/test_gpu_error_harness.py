@@ -1,0 +1,64 @@
+"""GPU runs of the error-accumulation harness: the quantized state against an
+fp32 twin through the same kernel over long horizons, checked for the trends
+the pages derive (error propagation through the decay, Proposition 2; the
+rounding comparison, Proposition 3; decay-based precision)."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_recurrence_amd as lores
+from quantized_linear_recurrence_amd import error_harness as eh
+from tests.parity import log
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SR, NEAR = lores.LORES_ROUND_STOCHASTIC, lores.LORES_ROUND_NEAREST
+
+
+def _run(prec, lo, hi, rnd, T=1024, H=12):
+    return eh.error_trajectory(prec if callable(prec) else [prec] * H, B=32, T=T, delta=0,
+                               alpha_lo=lo, alpha_hi=hi, beta=0.5, drift=100.0, rounding=rnd,
+                               seed=1)
+
+
+def test_error_grows_with_decay_and_horizon():
+    log("case: harness int4 stochastic, decay in [0.9, 1), T=1024")
+    res = _run(3, 0.9, 1.0, SR)
+    s = eh.summarize(res, bins=3)
+    log(str([(round(r["alpha_range"][0], 3), round(r["rel_err_T"], 4)) for r in s]))
+    # slower decay keeps more of every past local error
+    assert s[2]["rel_err_T"] > 1.5 * s[0]["rel_err_T"]
+    slowest = res["rel_err"][-1]
+    assert slowest[-1] > 2.0 * slowest[0]                 # accumulated, not one step's error
+
+
+def test_int8_error_far_below_int4():
+    log("case: harness int8 vs int4 stochastic, decay in [0.9, 1), T=512")
+    e8 = np.mean([e[-1] for e in _run(2, 0.9, 1.0, SR, T=512)["rel_err"]])
+    e4 = np.mean([e[-1] for e in _run(3, 0.9, 1.0, SR, T=512)["rel_err"]])
+    log(f"int8 {e8:.4f} int4 {e4:.4f}")
+    assert e8 < e4 / 8                                    # 127 vs 7 levels per sign
+
+
+def test_nearest_rounding_stagnates_on_slow_heads():
+    log("case: harness int4 stochastic vs nearest, decay in [0.99, 1), T=2048")
+    s_sr = eh.summarize(_run(3, 0.99, 1.0, SR, T=2048), bins=3)[-1]
+    s_nr = eh.summarize(_run(3, 0.99, 1.0, NEAR, T=2048), bins=3)[-1]
+    log(f"stochastic {s_sr['rel_err_T']:.3f} (x{s_sr['growth_T4_to_T']:.2f} from T/4), "
+        f"nearest {s_nr['rel_err_T']:.3f} (x{s_nr['growth_T4_to_T']:.2f})")
+    assert s_nr["rel_err_T"] > 1.15 * s_sr["rel_err_T"]
+    assert s_nr["growth_T4_to_T"] > s_sr["growth_T4_to_T"]
+
+
+def test_decay_assigned_mixed_precision_sits_between():
+    log("case: harness decay-assigned int8 (slowest half) + int4 vs uniform, T=512")
+    H = 12
+    mixed = _run(eh.decay_assigned(H, [(0.5, 2), (0.5, 3)]), 0.9, 1.0, SR, T=512)
+    assert mixed["head_prec"] == [3] * 6 + [2] * 6       # heads are sorted fastest first
+    assert abs(eh.effective_bits(mixed["head_prec"]) - 6.25) < 1e-9
+    em = np.mean([e[-1] for e in mixed["rel_err"]])
+    e8 = np.mean([e[-1] for e in _run(2, 0.9, 1.0, SR, T=512)["rel_err"]])
+    e4 = np.mean([e[-1] for e in _run(3, 0.9, 1.0, SR, T=512)["rel_err"]])
+    log(f"int8 {e8:.4f} mixed {em:.4f} int4 {e4:.4f}")
+    assert e8 < em < e4
