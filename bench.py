@@ -12,6 +12,7 @@ Workloads (synthetic, shapes of the decode layers the method targets):
   C3 Mamba-2 / SSD decode, B=256 H=128 d_v=64 d_k=128, no delta correction, int8
   C4 KDA per-channel decay, B=128 H=32 d=128, 8 bf16 + 24 int8 heads
   C5 large batch, B=2048 H=32 d=128, 16 int8 + 16 int4 heads
+  C5i6 the same shape with the slowest half of the heads in int6 (5.25 bits)
   C1 is the tiny parity case (launch-bound; not a throughput workload).
 --mode copy times a plain device copy (the HBM calibration used for the
 rocprofv3 byte counters); --mode error runs the error-accumulation harness
@@ -46,7 +47,8 @@ def kernel_source_hash():
 def unit_bytes(prec, dk, dv, in_bytes, per_channel):
     """Algorithmic bytes of one state update: the state read and written once,
     plus q, k, v, alpha, beta read and o written."""
-    state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * dv, 3: dv * dk // 2 + 4 * dv}[prec]
+    state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * dv, 3: dv * dk // 2 + 4 * dv,
+             4: 6 * dv * dk // 8 + 4 * dv}[prec]
     io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
     return 2 * state + io
 
@@ -56,7 +58,7 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C5i6"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -187,7 +189,7 @@ def main(argv=None):
 
     in_bytes = 2 if w.in_bf16 else 4
     step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel)
-                     for c in range(4))
+                     for c in range(5))
     st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev)
     o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
 
@@ -269,7 +271,7 @@ def main(argv=None):
             "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "delta": w.delta,
             "decay": w.decay, "inputs": "bf16" if w.in_bf16 else "fp32",
             "state": {name: head_prec.count(c) for c, name in
-                      enumerate(["fp32", "bf16", "int8", "int4"]) if head_prec.count(c)},
+                      enumerate(["fp32", "bf16", "int8", "int4", "int6"]) if head_prec.count(c)},
             "rounding": "stochastic", "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,

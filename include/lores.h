@@ -40,15 +40,17 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 1
+#define LORES_SPEC_VERSION 2
 
 /* Per-head state precision. */
 enum {
     LORES_FP32 = 0, /* unquantized fp32 state (the full-precision reference path) */
     LORES_BF16 = 1, /* bfloat16 state, stochastic rounding from fp32               */
     LORES_INT8 = 2, /* int8 codes in [-127, 127] + one fp32 scale per value row     */
-    LORES_INT4 = 3  /* int4 codes in [-7, 7]     + one fp32 scale per value row     */
+    LORES_INT4 = 3, /* int4 codes in [-7, 7]     + one fp32 scale per value row     */
+    LORES_INT6 = 4  /* int6 codes in [-31, 31]   + one fp32 scale per value row     */
 };
+#define LORES_NUM_PREC 5
 
 /* Rounding of the requantization (per state; lores_state_set_rounding). */
 enum {
@@ -78,11 +80,11 @@ typedef struct lores_state lores_state;
 /*
  * Packed state layout (version LORES_SPEC_VERSION), for inspection, tests and
  * checkpointing.  The buffer holds one segment pair per precision class that
- * has at least one head, in class order fp32, bf16, int8, int4, each segment
- * starting on a 256-byte boundary:
+ * has at least one head, in class order fp32, bf16, int8, int4, int6, each
+ * segment starting on a 256-byte boundary:
  *
  *   codes  [B][H_c][n_chunk][d_v_pad][16 bytes]
- *   scales [B][H_c][d_v_pad] fp32                 (int8 and int4 classes only)
+ *   scales [B][H_c][d_v_pad] fp32                 (int8, int4 and int6 classes)
  *
  * H_c = heads of class c, ordered by head index (head_slot below).
  * d_v_pad = d_v rounded up to LORES_ROW_BLOCK; padding rows are never read
@@ -94,15 +96,19 @@ typedef struct lores_state lores_state;
  *   int8: byte e  = code + 128         (offset binary, 1..255)
  *   int4: byte e/2, low nibble for even e, high nibble for odd e,
  *         nibble = code + 8            (offset binary, 1..15)
+ * int6 rows are a little-endian bit stream over the row's chunks (chunk c
+ * holds row bytes 16c .. 16c + 15): element j is bits 6j .. 6j + 5, value
+ * code + 32 (offset binary, 1..63); n_chunk = ceil(6 d_k / 128), the bits
+ * after the last element are zero.
  * The value of an int element is scale[row] * code.  A row of all-zero bytes
  * with scale 0 also reads as zero, so a zero-filled buffer is S = 0.
  */
 typedef struct {
     int32_t B, H, d_k, d_v, d_v_pad;
-    int32_t n_class[4];        /* heads per precision class                     */
-    int64_t codes_offset[4];   /* byte offset of class codes, -1 if no heads    */
-    int64_t scales_offset[4];  /* byte offset of class scales, -1 if none       */
-    int64_t unit_code_bytes[4];/* code bytes per (sequence, head) unit          */
+    int32_t n_class[LORES_NUM_PREC];        /* heads per precision class        */
+    int64_t codes_offset[LORES_NUM_PREC];   /* byte offset of class codes, -1   */
+    int64_t scales_offset[LORES_NUM_PREC];  /* byte offset of class scales, -1  */
+    int64_t unit_code_bytes[LORES_NUM_PREC];/* code bytes per (sequence, head)  */
     uint64_t total_bytes;      /* bytes the caller's buffer must hold           */
 } lores_layout;
 
@@ -111,7 +117,7 @@ typedef struct {
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
  *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128},
  *               1 <= d_v <= LORES_MAX_DV
- *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_INT4)
+ *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_INT6)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
  *               returns LORES_OK without creating a handle.  Otherwise *bytes
@@ -192,9 +198,10 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
  * element size (LORES_EINVAL otherwise).  Caller preconditions not
  * checked: |q| = |k| = 1, decay in (0, 1], beta in (0, 2) when delta = 1,
  * finite inputs.  Per element of an int head, with U the updated fp32 row:
- *   scale' = fl(m / r), m = max|U_row|, r = 127 (int8) or 7 (int4);
+ *   scale' = fl(m / r), m = max|U_row|, r = 127 (int8), 31 (int6) or 7 (int4);
  *   code'  = floor(fl(U * inv + bias + u)) - bias, inv = the largest fp32 not
- *            above r / m (0 if m = 0), bias = 128 (int8) or 136 (int4),
+ *            above r / m (0 if m = 0), bias = 128 (int8), 160 (int6) or 136
+ *            (int4),
  *            u = n * 2^-16 and n a 16-bit counter-based draw keyed on
  *            (seed, t, sequence, head, row, column).
  */
@@ -206,7 +213,8 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
 /*
  * lores_step_launches - kernel launches one lores_decode_step on `st`
  * enqueues (host out *n): one per precision class present, except that the
- * pairs (int8, int4), (bf16, int8) and (bf16, int4) share a single launch.
+ * pairs (int8, int4), (int4, int6), (bf16, int8) and (bf16, int4) share a
+ * single launch.
  */
 int lores_step_launches(const lores_state *st, int32_t *n);
 

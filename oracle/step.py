@@ -26,7 +26,8 @@ repository's design notes):
        (real arithmetic: U = S' - delta*beta (S'k) k^T + beta v k^T, which is
         S_{t-1} diag(alpha)(I - delta beta k k^T) + beta v k^T)
   4  o_i  = fl(sum_j U_ij q_j)             (readout of the pre-requant state)
-  5  int heads, r = 127 (int8) or 7 (int4), bias B = 128 (int8) or 136 (int4):
+  5  int heads, r = 2^(b-1) - 1 = 127 (int8), 31 (int6) or 7 (int4), bias
+     B = 128 (int8), 160 (int6) or 136 (int4):
        m_i = max_j |U_ij|;  s'_i = fl(m_i / r);  inv_i = largest fp32 <= r / m_i
        (inv_i = 0 for m_i = 0);  z_ij = fl(U_ij * inv_i + (B + n_ij 2^-16))
        in one rounding;  e_ij = floor(z_ij);  c'_ij = e_ij - B  in [-r, r]
@@ -40,9 +41,9 @@ from . import exact
 from .exact import F32, F64, f32, fma32
 from .rng import noise16, noise16_iid, unit_key
 
-PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4 = 0, 1, 2, 3
-QMAX = {PREC_INT8: 127, PREC_INT4: 7}
-BIAS = {PREC_INT8: 128, PREC_INT4: 136}
+PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4, PREC_INT6 = 0, 1, 2, 3, 4
+QMAX = {PREC_INT8: 127, PREC_INT4: 7, PREC_INT6: 31}
+BIAS = {PREC_INT8: 128, PREC_INT4: 136, PREC_INT6: 160}
 
 
 # ---------------------------------------------------------------------------

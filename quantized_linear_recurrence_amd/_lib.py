@@ -8,7 +8,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblores.so")
 
-LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4 = 0, 1, 2, 3
+LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4, LORES_INT6 = 0, 1, 2, 3, 4
+NUM_PREC = 5
 LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST = 0, 1
 LORES_OK, LORES_EINVAL, LORES_EUNSUPPORTED, LORES_ESIZE, LORES_EHIP, LORES_ENOMEM = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3: "LORES_ESIZE",
@@ -29,8 +30,9 @@ class LoresLibraryMissing(RuntimeError):
 class LoresLayout(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("d_k", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("d_v_pad", ctypes.c_int32),
-                ("n_class", ctypes.c_int32 * 4), ("codes_offset", ctypes.c_int64 * 4),
-                ("scales_offset", ctypes.c_int64 * 4), ("unit_code_bytes", ctypes.c_int64 * 4),
+                ("n_class", ctypes.c_int32 * NUM_PREC), ("codes_offset", ctypes.c_int64 * NUM_PREC),
+                ("scales_offset", ctypes.c_int64 * NUM_PREC),
+                ("unit_code_bytes", ctypes.c_int64 * NUM_PREC),
                 ("total_bytes", ctypes.c_uint64)]
 
 

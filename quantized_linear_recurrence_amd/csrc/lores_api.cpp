@@ -18,9 +18,9 @@ struct lores_state {
     int32_t B, H, dk, dv, dv_pad, n_rb;
     uint8_t prec[LORES_MAX_HEADS];
     int32_t slot[LORES_MAX_HEADS];
-    int32_t n_class[4];
-    uint16_t heads[4][LORES_MAX_HEADS];
-    int64_t codes_off[4], scales_off[4], unit_bytes[4];
+    int32_t n_class[LORES_NUM_PREC];
+    uint16_t heads[LORES_NUM_PREC][LORES_MAX_HEADS];
+    int64_t codes_off[LORES_NUM_PREC], scales_off[LORES_NUM_PREC], unit_bytes[LORES_NUM_PREC];
     uint64_t total;
     uint8_t *base;
     int32_t rounding;        // LORES_ROUND_*
@@ -45,12 +45,13 @@ int ok() {
     return LORES_OK;
 }
 
-bool is_int_prec(int p) { return p == LORES_INT8 || p == LORES_INT4; }
+bool is_int_prec(int p) { return p == LORES_INT8 || p == LORES_INT4 || p == LORES_INT6; }
 
-// 16-byte chunk = E elements; bytes per stored row = (d_k / E) * 16.
+// Bytes per stored row: d_k elements of 32, 16, 8, 4 or 6 bits in whole
+// 16-byte chunks (only int6 rows can end in a partly used chunk).
 int64_t row_bytes(int prec, int dk) {
-    static const int E[4] = {4, 8, 16, 32};
-    return (int64_t)(dk / E[prec]) * 16;
+    static const int bits[LORES_NUM_PREC] = {32, 16, 8, 4, 6};
+    return (int64_t)((dk * bits[prec] + 127) / 128) * 16;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~(uint64_t)255; }
@@ -74,7 +75,8 @@ int plan(lores_state *st, const uint8_t *head_prec) {
     std::memset(st->n_class, 0, sizeof st->n_class);
     for (int h = 0; h < st->H; ++h) {
         const int p = head_prec[h];
-        if (p < 0 || p > 3) return fail(LORES_EINVAL, "head_prec[%d] = %d is not a precision code", h, p);
+        if (p < 0 || p >= LORES_NUM_PREC)
+            return fail(LORES_EINVAL, "head_prec[%d] = %d is not a precision code", h, p);
         st->prec[h] = (uint8_t)p;
         st->slot[h] = st->n_class[p];
         st->heads[p][st->n_class[p]++] = (uint16_t)h;
@@ -82,7 +84,7 @@ int plan(lores_state *st, const uint8_t *head_prec) {
     st->dv_pad = (st->dv + LORES_ROW_BLOCK - 1) / LORES_ROW_BLOCK * LORES_ROW_BLOCK;
     st->n_rb = st->dv_pad / LORES_ROW_BLOCK;
     uint64_t off = 0;
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < LORES_NUM_PREC; ++c) {
         st->codes_off[c] = st->scales_off[c] = -1;
         st->unit_bytes[c] = row_bytes(c, st->dk) * st->dv_pad;
         if (!st->n_class[c]) continue;
@@ -143,8 +145,8 @@ lores::StepMeta make_meta(const lores_state *st, const int *cls, int n_cls) {
 namespace lores {
 
 bool fusable_pair(int p0, int p1) {
-    return (p0 == LORES_INT8 && p1 == LORES_INT4) || (p0 == LORES_BF16 && p1 == LORES_INT8) ||
-           (p0 == LORES_BF16 && p1 == LORES_INT4);
+    return (p0 == LORES_INT8 && p1 == LORES_INT4) || (p0 == LORES_INT4 && p1 == LORES_INT6) ||
+           (p0 == LORES_BF16 && p1 == LORES_INT8) || (p0 == LORES_BF16 && p1 == LORES_INT4);
 }
 
 hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, const StepPtrs &p,
@@ -155,10 +157,12 @@ hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, c
             case LORES_BF16: return launch_step_bf16(dk, pc, delta, bf16, p, m, s);
             case LORES_INT8: return launch_step_int8(dk, pc, delta, bf16, p, m, s);
             case LORES_INT4: return launch_step_int4(dk, pc, delta, bf16, p, m, s);
+            case LORES_INT6: return launch_step_int6(dk, pc, delta, bf16, p, m, s);
             default: return hipErrorInvalidValue;
         }
     }
     if (p0 == LORES_INT8 && p1 == LORES_INT4) return launch_step_int8_int4(dk, pc, delta, bf16, p, m, s);
+    if (p0 == LORES_INT4 && p1 == LORES_INT6) return launch_step_int4_int6(dk, pc, delta, bf16, p, m, s);
     if (p0 == LORES_BF16 && p1 == LORES_INT8) return launch_step_bf16_int8(dk, pc, delta, bf16, p, m, s);
     if (p0 == LORES_BF16 && p1 == LORES_INT4) return launch_step_bf16_int4(dk, pc, delta, bf16, p, m, s);
     return hipErrorInvalidValue;
@@ -221,7 +225,7 @@ int lores_state_layout(const lores_state *st, lores_layout *out) {
     out->d_k = st->dk;
     out->d_v = st->dv;
     out->d_v_pad = st->dv_pad;
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < LORES_NUM_PREC; ++c) {
         out->n_class[c] = st->n_class[c];
         out->codes_offset[c] = st->codes_off[c];
         out->scales_offset[c] = st->scales_off[c];
@@ -281,7 +285,8 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
         if (H < 1 || H > LORES_MAX_HEADS) return fail(LORES_EINVAL, "H must be in [1, %d]", LORES_MAX_HEADS);
         if (n_tiers < 1) return fail(LORES_EINVAL, "n_tiers must be >= 1");
         for (int k = 0; k < n_tiers; ++k) {
-            if (tier_prec[k] > 3) return fail(LORES_EINVAL, "tier_prec[%d] is not a precision code", k);
+            if (tier_prec[k] >= LORES_NUM_PREC)
+                return fail(LORES_EINVAL, "tier_prec[%d] is not a precision code", k);
             if (!(tier_frac[k] >= 0.0) || !std::isfinite(tier_frac[k]))
                 return fail(LORES_EINVAL, "tier_frac[%d] must be finite and >= 0", k);
         }
@@ -311,9 +316,10 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
 
 // Launches of one decode step: the classes present, where a fusable pair
 // shares one launch and anything else gets one launch per class.
-static int plan_launches(const lores_state *st, int groups[4][2], int width[4]) {
-    int present[4], n = 0;
-    for (int c = 0; c < 4; ++c)
+static int plan_launches(const lores_state *st, int groups[LORES_NUM_PREC][2],
+                         int width[LORES_NUM_PREC]) {
+    int present[LORES_NUM_PREC], n = 0;
+    for (int c = 0; c < LORES_NUM_PREC; ++c)
         if (st->n_class[c]) present[n++] = c;
     if (n == 2 && lores::fusable_pair(present[0], present[1])) {
         groups[0][0] = present[0];
@@ -330,7 +336,7 @@ static int plan_launches(const lores_state *st, int groups[4][2], int width[4]) 
 
 int lores_step_launches(const lores_state *st, int32_t *n) {
     if (!st || !n) return fail(LORES_EINVAL, "NULL argument");
-    int groups[4][2], width[4];
+    int groups[LORES_NUM_PREC][2], width[LORES_NUM_PREC];
     *n = plan_launches(st, groups, width);
     return ok();
 }
@@ -359,7 +365,7 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
             return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
         const hipStream_t s = (hipStream_t)stream;
-        int groups[4][2], width[4];
+        int groups[LORES_NUM_PREC][2], width[LORES_NUM_PREC];
         const int n_launch = plan_launches(st, groups, width);
         for (int l = 0; l < n_launch; ++l) {
             lores::StepMeta m = make_meta(st, groups[l], width[l]);
@@ -401,7 +407,7 @@ int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t se
             return fail(LORES_EINVAL, "seq_base + B must lie in [0, 2^32]");
         if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
             return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < LORES_NUM_PREC; ++c) {
             if (!st->n_class[c]) continue;
             lores::StepMeta m = make_meta(st, &c, 1);
             m.seed = seed;
@@ -424,7 +430,7 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
     try {
         if (!st || !out) return fail(LORES_EINVAL, "NULL argument");
         if (!aligned(out, 16)) return fail(LORES_EINVAL, "out must be 16-byte aligned");
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < LORES_NUM_PREC; ++c) {
             if (!st->n_class[c]) continue;
             lores::StepMeta m = make_meta(st, &c, 1);
             const float *sc = is_int_prec(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;

@@ -13,7 +13,7 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                      float *__restrict__ out, const StepMeta meta) {
     constexpr int E = Prec<PREC>::E;
-    constexpr int NCH = DK / E;
+    constexpr int NCH = row_chunks<DK, PREC>();
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ClassDesc &cd = meta.cls[0];
@@ -32,30 +32,43 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     float s = 0.0f;
     if constexpr (is_int<PREC>()) s = scales[unit * dv_pad + row];
     float *orow = out + (bh * meta.dv + row) * DK;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (PREC == LORES_INT6) {
+        u32x4 cw[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const u32x4 v = cp[c * dv_pad];
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-        float x[E];
+        for (int c = 0; c < NCH; ++c) cw[c] = cp[c * dv_pad];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if constexpr (PREC == LORES_INT8) {
-                x[e] = s * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
-            } else if constexpr (PREC == LORES_INT4) {
-                const uint32_t w = wd[e >> 3];
-                const uint32_t nib = (w >> (4 * (e & 7))) & 0xFu;
-                x[e] = s * ((float)nib - 8.0f);
-            } else if constexpr (PREC == LORES_BF16) {
-                const uint32_t w = wd[e >> 1];
-                x[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-            } else {
-                x[e] = __uint_as_float(wd[e]);
-            }
+        for (int j = 0; j < DK; j += 4) {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = s * ((float)int6_field(cw, j + e) - 32.0f);
+            *reinterpret_cast<f32x4 *>(orow + j) = f32x4{x[0], x[1], x[2], x[3]};
         }
+    } else {
 #pragma unroll
-        for (int e = 0; e < E; e += 4) {
-            typedef float f32x4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+        for (int c = 0; c < NCH; ++c) {
+            const u32x4 v = cp[c * dv_pad];
+            const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+            float x[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if constexpr (PREC == LORES_INT8) {
+                    x[e] = s * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
+                } else if constexpr (PREC == LORES_INT4) {
+                    const uint32_t w = wd[e >> 3];
+                    const uint32_t nib = (w >> (4 * (e & 7))) & 0xFu;
+                    x[e] = s * ((float)nib - 8.0f);
+                } else if constexpr (PREC == LORES_BF16) {
+                    const uint32_t w = wd[e >> 1];
+                    x[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                } else {
+                    x[e] = __uint_as_float(wd[e]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < E; e += 4) {
+                *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+            }
         }
     }
 }
@@ -122,6 +135,7 @@ hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float 
         case LORES_BF16: return quant_prec<LORES_BF16>(dk, X, codes, scales, m, s);
         case LORES_INT8: return quant_prec<LORES_INT8>(dk, X, codes, scales, m, s);
         case LORES_INT4: return quant_prec<LORES_INT4>(dk, X, codes, scales, m, s);
+        case LORES_INT6: return quant_prec<LORES_INT6>(dk, X, codes, scales, m, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -148,6 +162,7 @@ hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *s
         case LORES_BF16: return dequant_prec<LORES_BF16>(dk, codes, scales, out, m, s);
         case LORES_INT8: return dequant_prec<LORES_INT8>(dk, codes, scales, out, m, s);
         case LORES_INT4: return dequant_prec<LORES_INT4>(dk, codes, scales, out, m, s);
+        case LORES_INT6: return dequant_prec<LORES_INT6>(dk, codes, scales, out, m, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -43,7 +43,7 @@ struct StepPtrs {
 };
 
 // One launch covers one class or one of the fused pairs (int8, int4),
-// (bf16, int8), (bf16, int4); `p1` is -1 for a single class.  Returns the
+// (int4, int6), (bf16, int8), (bf16, int4); `p1` is -1 for a single class.  Returns the
 // launch status; `dk` is one of 32, 64, 96, 128.
 hipError_t launch_step(int dk, bool per_channel, bool delta, bool in_bf16, int p0, int p1,
                        const StepPtrs &p, const StepMeta &m, hipStream_t s);
@@ -54,7 +54,9 @@ hipError_t launch_step_fp32(int, bool, bool, bool, const StepPtrs &, const StepM
 hipError_t launch_step_bf16(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int8_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_int4_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_bf16_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_bf16_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 

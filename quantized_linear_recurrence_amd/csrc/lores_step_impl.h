@@ -83,22 +83,61 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chu
 // precision traits: elements per 16-byte chunk, quantizer constants
 // ---------------------------------------------------------------------------
 template <int PREC> struct Prec;
-template <> struct Prec<LORES_FP32> { static constexpr int E = 4; };
-template <> struct Prec<LORES_BF16> { static constexpr int E = 8; };
+template <> struct Prec<LORES_FP32> { static constexpr int E = 4, BITS = 32; };
+template <> struct Prec<LORES_BF16> { static constexpr int E = 8, BITS = 16; };
 template <> struct Prec<LORES_INT8> {
-    static constexpr int E = 16;
+    static constexpr int E = 16, BITS = 8;
     static constexpr float R = 127.0f;        // 2^(8-1) - 1
     static constexpr float OFF = 128.0f;      // stored byte = code + 128
     static constexpr uint32_t FBASE = 0x43000000u;  // 128.0f: mantissa takes n * 2^-16
 };
 template <> struct Prec<LORES_INT4> {
-    static constexpr int E = 32;
+    static constexpr int E = 32, BITS = 4;
     static constexpr float R = 7.0f;          // 2^(4-1) - 1
     static constexpr float OFF = 8.0f;        // stored nibble = code + 8
     static constexpr uint32_t FBASE = 0x43080000u;  // 136.0f = 128 + 8
 };
+// int6 rows are a bit stream (element j at bits 6j .. 6j + 5), not E
+// elements per chunk; the stored field is floor(z) - 128 = code + 32.
+template <> struct Prec<LORES_INT6> {
+    static constexpr int E = 0, BITS = 6;
+    static constexpr float R = 31.0f;         // 2^(6-1) - 1
+    static constexpr float OFF = 32.0f;       // stored field = code + 32
+    static constexpr uint32_t FBASE = 0x43200000u;  // 160.0f = 128 + 32
+};
 
-template <int PREC> constexpr bool is_int() { return PREC == LORES_INT8 || PREC == LORES_INT4; }
+template <int PREC> constexpr bool is_int() {
+    return PREC == LORES_INT8 || PREC == LORES_INT4 || PREC == LORES_INT6;
+}
+
+// 16-byte chunks per stored row of d_k elements
+template <int DK, int PREC> constexpr int row_chunks() {
+    return (DK * Prec<PREC>::BITS + 127) / 128;
+}
+
+// Field j (6 bits) of an int6 row held in chunk registers cw.
+__device__ __forceinline__ uint32_t int6_field(const u32x4 *cw, int j) {
+    const int bit = 6 * j, w = bit >> 5, o = bit & 31;
+    const uint32_t lo = cw[w >> 2][w & 3];
+    if (o <= 26) return __builtin_amdgcn_ubfe(lo, o, 6);
+    const uint32_t hi = cw[(w + 1) >> 2][(w + 1) & 3];
+    return __builtin_amdgcn_alignbit(hi, lo, o) & 63u;
+}
+
+// For each word w of an int6 row: the sum, over the fields that touch w, of
+// the bit 7 that each stored byte floor(z) carries (floor(z) = 128 + field),
+// shifted like the field.  Packing adds floor(z) << offset and subtracts it.
+template <int DK>
+struct Int6Stray {
+    uint32_t k[4 * ((6 * DK + 127) / 128)];   // the row's words
+    constexpr Int6Stray() : k{} {
+        for (int j = 0; j < DK; ++j) {
+            const int bit = 6 * j, w = bit >> 5, o = bit & 31;
+            k[w] += 128u << o;
+            if (o > 26) k[w + 1] += 128u >> (32 - o);
+        }
+    }
+};
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -305,7 +344,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                                                int b, int h, int row, bool active, u32x4 *cp,
                                                long dv_pad, float *scale_out) {
     constexpr int E = Prec<PREC>::E;
-    constexpr int NCH = DK / E;
+    constexpr int NCH = row_chunks<DK, PREC>();
     float inv = 0.0f;
     if constexpr (is_int<PREC>()) {
         const float snew = m / Prec<PREC>::R;
@@ -329,70 +368,105 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
     }
     const uint32_t psi = opaque_uniform(nearest ? 0u : kPsi16);
     const uint32_t psi2 = opaque_uniform(nearest ? 0u : ((2 * kPsi16) & 0xFFFFu) * 0x00010001u);
+    if constexpr (PREC == LORES_INT6) {
+        // floor(z) = 128 + field; add it shifted into place and take the
+        // fields' bit 7 back out with one constant per word (folded into the
+        // initial value), so no field needs a mask.  Chunk by chunk: a chunk
+        // is stored as soon as its four words are complete, and the draw
+        // register is pinned after each store, so the compiler cannot compute
+        // every element's sum up front and hold them all.
+        constexpr Int6Stray<DK> stray;
+        int j = 0;
+        uint32_t carry = 0;                  // high bits of a field crossing into the next chunk
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        uint32_t ow[4];
-        if constexpr (PREC == LORES_INT8) {
+        for (int c = 0; c < NCH; ++c) {
+            uint32_t acc[4];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 4;
-                float z[4];
+            for (int k = 0; k < 4; ++k) acc[k] = 0u - stray.k[4 * c + k];
+            acc[0] += carry;
+            carry = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
-                    x = step16(x, psi);
+            for (; j < DK && 6 * j < 128 * (c + 1); ++j) {
+                const float z = __builtin_fmaf(U[j], inv, __uint_as_float(x));
+                x = step16(x, psi);
+                const uint32_t e = (uint32_t)z;
+                const int bit = 6 * j - 128 * c, w = bit >> 5, o = bit & 31;
+                acc[w] += e << o;
+                if (o > 26) {
+                    if (w < 3) acc[w + 1] += e >> (32 - o);
+                    else carry = e >> (32 - o);
                 }
-                const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
-                uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
-                cvt_u8_into<1>(word, z1);
-                cvt_u8_into<2>(word, z2);
-                cvt_u8_into<3>(word, z3);
-                ow[q4] = word;
             }
-        } else if constexpr (PREC == LORES_INT4) {
-            // e in [129, 143]; its low nibble is the offset-binary code c + 8
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 8;
-                float ze[4], zo[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
-                    x = step16(x, psi);
-                    zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
-                    x = step16(x, psi);
-                }
-                uint32_t ev = (uint32_t)ze[0];
-                uint32_t od = (uint32_t)zo[0];
-                cvt_u8_into<1>(ev, ze[1]);
-                cvt_u8_into<1>(od, zo[1]);
-                cvt_u8_into<2>(ev, ze[2]);
-                cvt_u8_into<2>(od, zo[2]);
-                cvt_u8_into<3>(ev, ze[3]);
-                cvt_u8_into<3>(od, zo[3]);
-                ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
-            }
-        } else if constexpr (PREC == LORES_BF16) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j = c * E + q4 * 2;
-                // draws of columns j, j + 1: those of columns 0, 1 plus
-                // (j / 2) * 2 psi in each half (one v_pk_mad_u16)
-                const u16x2 kk = {(unsigned short)(j >> 1), (unsigned short)(j >> 1)};
-                const uint32_t xj = __builtin_bit_cast(
-                    uint32_t, __builtin_bit_cast(u16x2, x) + kk * __builtin_bit_cast(u16x2, psi2));
-                const uint32_t b0 = __float_as_uint(U[j]) + (xj & 0xFFFFu);
-                const uint32_t b1 = __float_as_uint(U[j + 1]) + (xj >> 16);
-                ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-            }
-        } else {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+            if (active)
+                __builtin_nontemporal_store(u32x4{acc[0], acc[1], acc[2], acc[3]}, cp + c * dv_pad);
+            asm volatile("" : "+v"(x));
         }
-        if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
-        // keep the next chunk's draws after this store: unpinned, the
-        // whole (cheap, input-independent) chain is computed up front
-        // and held in registers
+    } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            uint32_t ow[4];
+            if constexpr (PREC == LORES_INT8) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 4;
+                    float z[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
+                        x = step16(x, psi);
+                    }
+                    const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
+                    uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
+                    cvt_u8_into<1>(word, z1);
+                    cvt_u8_into<2>(word, z2);
+                    cvt_u8_into<3>(word, z3);
+                    ow[q4] = word;
+                }
+            } else if constexpr (PREC == LORES_INT4) {
+                // e in [129, 143]; its low nibble is the offset-binary code c + 8
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 8;
+                    float ze[4], zo[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
+                        x = step16(x, psi);
+                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
+                        x = step16(x, psi);
+                    }
+                    uint32_t ev = (uint32_t)ze[0];
+                    uint32_t od = (uint32_t)zo[0];
+                    cvt_u8_into<1>(ev, ze[1]);
+                    cvt_u8_into<1>(od, zo[1]);
+                    cvt_u8_into<2>(ev, ze[2]);
+                    cvt_u8_into<2>(od, zo[2]);
+                    cvt_u8_into<3>(ev, ze[3]);
+                    cvt_u8_into<3>(od, zo[3]);
+                    ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+                }
+            } else if constexpr (PREC == LORES_BF16) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 2;
+                    // draws of columns j, j + 1: those of columns 0, 1 plus
+                    // (j / 2) * 2 psi in each half (one v_pk_mad_u16)
+                    const u16x2 kk = {(unsigned short)(j >> 1), (unsigned short)(j >> 1)};
+                    const uint32_t xj = __builtin_bit_cast(
+                        uint32_t, __builtin_bit_cast(u16x2, x) + kk * __builtin_bit_cast(u16x2, psi2));
+                    const uint32_t b0 = __float_as_uint(U[j]) + (xj & 0xFFFFu);
+                    const uint32_t b1 = __float_as_uint(U[j + 1]) + (xj >> 16);
+                    ow[q4] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+                }
+            } else {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
+            }
+            if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+            // keep the next chunk's draws after this store: unpinned, the
+            // whole (cheap, input-independent) chain is computed up front
+            // and held in registers
+        }
     }
 }
 
@@ -419,8 +493,8 @@ struct TaskSide {
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
 struct TaskStream {
     static constexpr int E = Prec<PREC>::E;
-    static constexpr int NCH = DK / E;
-    static_assert(DK % E == 0, "d_k must be a whole number of 16-byte chunks");
+    static constexpr int NCH = row_chunks<DK, PREC>();
+    static_assert(PREC == LORES_INT6 || DK % E == 0, "d_k must be a whole number of 16-byte chunks");
     static constexpr int kInB = BF16IN ? 2 : 4;
     static constexpr int kVecBytes = DK * kInB;      // bytes of k (and of q)
 
@@ -497,6 +571,28 @@ struct TaskStream {
         float U[DK];
         float r = 0.0f;
         float aj[16];                                    // s * alpha_j of one group (int, per channel)
+        // after each group of 16 columns: per-channel decay of float heads,
+        // then the group's share of r
+        auto group_done = [&](int j) {
+            if constexpr (PC && !is_int<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
+            if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
+            // without the projection nothing orders pass 1 before the
+            // next task's loads; materialize the group here so the
+            // chunk registers are free when `mid` reuses them
+            else pin16(&U[j - 15]);
+        };
+        if constexpr (PREC == LORES_INT6) {
+#pragma unroll
+            for (int j = 0; j < DK; ++j) {
+                if constexpr (PC) {
+                    if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
+                }
+                const float ub = (float)int6_field(cw, j);
+                if constexpr (PC) U[j] = (ub - Prec<PREC>::OFF) * aj[j & 15];
+                else U[j] = __builtin_fmaf(ub, a, na);
+                if ((j & 15) == 15) group_done(j);
+            }
+        } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
@@ -529,15 +625,9 @@ struct TaskStream {
                     if constexpr (!PC) sp = sp * alpha_s;
                 }
                 U[j] = sp;
-                if ((j & 15) == 15) {
-                    if constexpr (PC && !is_int<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
-                    if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
-                    // without the projection nothing orders pass 1 before the
-                    // next task's loads; materialize the group here so the
-                    // chunk registers are free when `mid` reuses them
-                    else pin16(&U[j - 15]);
-                }
+                if ((j & 15) == 15) group_done(j);
             }
+        }
         }
 
         mid();                                           // the chunks are consumed
@@ -638,7 +728,7 @@ constexpr bool pairable() {
     if constexpr (P1 < 0 || !is_int<P0>() || !is_int<P1>()) {
         return false;
     } else {
-        return DK / Prec<P0>::E <= kMaxPrefetchChunks && DK / Prec<P1>::E <= kMaxPrefetchChunks;
+        return row_chunks<DK, P0>() <= kMaxPrefetchChunks && row_chunks<DK, P1>() <= kMaxPrefetchChunks;
     }
 }
 

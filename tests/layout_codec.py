@@ -10,8 +10,31 @@ that class in head order.
 """
 import numpy as np
 
-E = {0: 4, 1: 8, 2: 16, 3: 32}       # elements per 16-byte chunk
-OFFSET = {2: 128, 3: 8}              # offset-binary code offset
+E = {0: 4, 1: 8, 2: 16, 3: 32}       # elements per 16-byte chunk (int6: a bit stream, below)
+OFFSET = {2: 128, 3: 8, 4: 32}       # offset-binary code offset
+QMAX = {2: 127, 3: 7, 4: 31}
+INT_CLASSES = (2, 3, 4)
+
+
+def n_chunks(c, dk):
+    """16-byte chunks per row: d_k elements of 32, 16, 8, 4 or 6 bits, the
+    last chunk zero-padded."""
+    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6}[c]
+    return (dk * bits + 127) // 128
+
+
+def _pack6(vals):
+    """[dv, dk] values 0..63 -> [dv, n_bytes] bytes of the little-endian bit
+    stream: value j at bits [6j, 6j + 6)."""
+    dv, dk = vals.shape
+    bits = ((vals[:, :, None].astype(np.uint16) >> np.arange(6)) & 1).astype(np.uint8)
+    return np.packbits(bits.reshape(dv, dk * 6), axis=1, bitorder="little")
+
+
+def _unpack6(rows, dk):
+    dv = rows.shape[0]
+    bits = np.unpackbits(rows, axis=1, bitorder="little")[:, :dk * 6].reshape(dv, dk, 6)
+    return (bits.astype(np.int32) << np.arange(6)).sum(axis=2)
 
 
 def unit_index(b, slot, Hc):
@@ -30,17 +53,22 @@ def pack_unit(c, dk, dv, dv_pad, state_unit):
     state_unit: {"codes": int [dv, dk], "scales": f32 [dv]} (int classes),
                 {"bits": uint16 [dv, dk]} (bf16) or {"X": f32 [dv, dk]} (fp32).
     """
-    n_chunk = dk // E[c]
+    n_chunk = n_chunks(c, dk)
     out = np.zeros((n_chunk, dv_pad, 16), np.uint8)
     sc = None
-    if c in (2, 3):
+    if c in INT_CLASSES:
         codes = np.asarray(state_unit["codes"], np.int64)
-        assert codes.min() >= -(127 if c == 2 else 7) and codes.max() <= (127 if c == 2 else 7)
+        assert codes.min() >= -QMAX[c] and codes.max() <= QMAX[c]
         sc = np.zeros(dv_pad, np.float32)
         sc[:dv] = state_unit["scales"]
         off = (codes + OFFSET[c]).astype(np.uint8)              # [dv, dk]
         if c == 2:
             out[:, :dv, :] = off.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
+        elif c == 4:
+            row = np.zeros((dv, n_chunk * 16), np.uint8)
+            packed = _pack6(off)
+            row[:, :packed.shape[1]] = packed
+            out[:, :dv, :] = row.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
         else:
             pairs = off.reshape(dv, n_chunk, 16, 2)
             by = (pairs[..., 0] | (pairs[..., 1] << 4)).astype(np.uint8)
@@ -56,11 +84,14 @@ def pack_unit(c, dk, dv, dv_pad, state_unit):
 
 def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None):
     """Inverse of pack_unit."""
-    n_chunk = dk // E[c]
+    n_chunk = n_chunks(c, dk)
     raw = np.asarray(code_bytes, np.uint8).reshape(n_chunk, dv_pad, 16)[:, :dv, :]
     rows = np.ascontiguousarray(raw.transpose(1, 0, 2)).reshape(dv, n_chunk * 16)
     if c == 2:
         return {"codes": rows.astype(np.int32) - 128,
+                "scales": np.asarray(scales, np.float32)[:dv].copy()}
+    if c == 4:
+        return {"codes": _unpack6(rows, dk) - 32,
                 "scales": np.asarray(scales, np.float32)[:dv].copy()}
     if c == 3:
         lo = (rows & 0x0F).astype(np.int32)
@@ -76,7 +107,7 @@ def unit_ranges(layout, c, unit):
     """Byte ranges (code_start, code_len, scale_start | None, scale_len) of a unit."""
     ub = layout["unit_code_bytes"][c]
     cs = layout["codes_offset"][c] + unit * ub
-    if c in (2, 3):
+    if c in INT_CLASSES:
         dvp = layout["d_v_pad"]
         return cs, ub, layout["scales_offset"][c] + unit * dvp * 4, dvp * 4
     return cs, ub, None, 0

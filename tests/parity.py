@@ -57,8 +57,8 @@ def head_precisions(w, inputs, calib_steps=32):
 
 
 def random_unit_state(c, dv, dk, g):
-    if c in (2, 3):
-        r = 127 if c == 2 else 7
+    if c in (2, 3, 4):
+        r = {2: 127, 3: 7, 4: 31}[c]
         return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
                 "scales": np.exp(g.uniform(-7, -2, dv)).astype(F32)}
     X = (g.standard_normal((dv, dk)) * 0.05).astype(F32)
@@ -186,7 +186,7 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
             o_err = (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()
             gpu = _stack([lc.read_unit(buf_host, lay, c, b * lay["n_class"][c] + hslot[h])
                           for (b, h) in us])
-            if c in (2, 3):
+            if c in (2, 3, 4):
                 d = np.abs(gpu["codes"].astype(np.int64) - new["codes"])
                 stats.codes += d.size
                 stats.code_diff += int((d > 0).sum())

@@ -56,7 +56,8 @@ def _unit_bytes(st, buf_host, b, h):
 
 @pytest.mark.parametrize("prec,n", [([2, 2], 1), ([0], 1), ([2, 3], 1), ([1, 2], 1),
                                     ([3, 1], 1), ([0, 2], 2), ([0, 1], 2), ([1, 2, 3], 3),
-                                    ([0, 1, 2, 3], 4)])
+                                    ([0, 1, 2, 3], 4), ([4], 1), ([4, 3], 1), ([2, 4], 2),
+                                    ([0, 1, 2, 3, 4], 5)])
 def test_step_launches(prec, n):
     log(f"case: launches per step for precisions {prec}")
     st = lores.lores_state_alloc(2, len(prec), 64, 64, prec, device=DEV)
@@ -67,6 +68,7 @@ def test_step_launches(prec, n):
     (6, [0, 1, 2, 3, 2, 3], 128, 96, [0, 2, 6], [0, 3, 6]),
     (160, [2, 3] * 4, 128, 128, [0, 40, 160], [0, 4, 8]),
     (9, [1, 2, 1, 2], 64, 33, [0, 1, 9], [0, 1, 4]),
+    (130, [4, 3] * 4, 128, 96, [0, 66, 130], [0, 2, 8]),
 ])
 def test_shard_invariance(B, head_prec, dk, dv, seq_cuts, head_cuts):
     """A shard of sequences and heads, keyed with seq_base / head_base, gives
@@ -195,7 +197,7 @@ def test_repeatable_eager_and_graph():
 def test_dequant_matches_oracle(dk, dv):
     """lores_dequant_state of a packed state (written through the codec)
     equals the oracle's dequantization bit for bit."""
-    B, head_prec = 3, [0, 1, 2, 3, 3, 2]
+    B, head_prec = 3, [0, 1, 2, 3, 3, 2, 4]
     log(f"case: dequant B={B} dk={dk} dv={dv} precisions {head_prec}")
     st = lores.lores_state_alloc(B, len(head_prec), dk, dv, head_prec, device=DEV)
     zero = lores.lores_dequant_state(st)
@@ -265,7 +267,7 @@ def test_quant_state_matches_oracle(dk, dv, rounding):
     """lores_quant_state equals the oracle's quantization of the same fp32
     state bit for bit (no summation is involved), for every precision, with
     zero rows and rows of very different magnitude; base indices key it."""
-    B, head_prec = 3, [0, 1, 2, 3, 3, 2]
+    B, head_prec = 3, [0, 1, 2, 3, 3, 2, 4]
     H = len(head_prec)
     log(f"case: quant state B={B} dk={dk} dv={dv} rounding={rounding} precisions {head_prec}")
     g = np.random.default_rng(dk * 7 + dv)
@@ -333,8 +335,8 @@ def test_quant_state_then_step():
         # one code (or one bf16 ulp plus the cancellation allowance) per element
         err = np.abs(X_gpu.astype(np.float64) - X_ref)
         rowmax = np.abs(X_ref).max(axis=2, keepdims=True)
-        if c in (2, 3):
-            step_size = rowmax / (127 if c == 2 else 7)
+        if c in (2, 3, 4):
+            step_size = rowmax / {2: 127, 3: 7, 4: 31}[c]
             assert np.all(err <= step_size * (1 + 1e-6)), h
             d = np.abs(np.stack([u["codes"] for u in gpu]).astype(np.int64) - new["codes"])
             assert d.max() <= 1 and (d > 0).sum() <= max(1, 1e-4 * d.size), h
@@ -347,8 +349,8 @@ def test_quant_state_then_step():
 def _scaled_state(lo, hi):
     """Unit states with int scales exp(U(lo, hi)) and bf16 / fp32 values of that size."""
     def init(c, dv, dk, g):
-        if c in (2, 3):
-            r = 127 if c == 2 else 7
+        if c in (2, 3, 4):
+            r = {2: 127, 3: 7, 4: 31}[c]
             return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
                     "scales": np.exp(g.uniform(lo, hi, dv)).astype(np.float32)}
         X = (g.standard_normal((dv, dk)) * np.exp(g.uniform(lo, hi, (dv, 1)))).astype(np.float32)

@@ -6,7 +6,7 @@ import pytest
 from tests import layout_codec as lc
 
 
-@pytest.mark.parametrize("c,r", [(2, 127), (3, 7)])
+@pytest.mark.parametrize("c,r", [(2, 127), (3, 7), (4, 31)])
 @pytest.mark.parametrize("dk,dv", [(32, 1), (64, 64), (96, 70), (128, 128)])
 def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
     dv_pad = (dv + 63) // 64 * 64
@@ -15,7 +15,7 @@ def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
     codes = np.roll(codes, 3, axis=1)                 # every value reaches every column
     scales = np.linspace(0.5, 2, dv).astype(np.float32)
     by, sc = lc.pack_unit(c, dk, dv, dv_pad, {"codes": codes, "scales": scales})
-    assert by.size == dv_pad * dk * (8 if c == 2 else 4) // 8
+    assert by.size == dv_pad * 16 * -(-(dk * {2: 8, 3: 4, 4: 6}[c]) // 128)
     back = lc.unpack_unit(c, dk, dv, dv_pad, by, sc)
     assert np.array_equal(back["codes"], codes) and np.array_equal(back["scales"], scales)
 
@@ -47,3 +47,18 @@ def test_bf16_and_fp32_roundtrip():
         X = g.standard_normal((dv, dk)).astype(np.float32)
         by, _ = lc.pack_unit(0, dk, dv, (dv + 63) // 64 * 64, {"X": X})
         assert np.array_equal(lc.unpack_unit(0, dk, dv, (dv + 63) // 64 * 64, by)["X"], X)
+
+
+def test_int6_bit_positions():
+    """Element j occupies bits 6j .. 6j + 5 of the row's little-endian bytes,
+    across 16-byte chunk boundaries; the padding bits stay zero."""
+    dk, dv = 96, 1                                    # 576 bits: 4.5 chunks -> 5
+    codes = np.full((dv, dk), -32 + 32, np.int64)     # stored 32 everywhere ...
+    codes[0, 21] = 31                                 # bits 126..131: straddles chunks 0 and 1
+    codes[0, 5] = -31                                 # bits 30..35: straddles words 0 and 1
+    by, _ = lc.pack_unit(4, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
+    row = by.reshape(5, 64, 16)[:, 0, :].reshape(-1)  # the row's 80 bytes, chunk after chunk
+    bits = np.unpackbits(row, bitorder="little")
+    val = lambda j: int(sum(int(bits[6 * j + i]) << i for i in range(6)))
+    assert val(21) == 63 and val(5) == 1 and val(0) == 32 and val(95) == 32
+    assert not bits[576:].any()

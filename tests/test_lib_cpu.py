@@ -38,21 +38,21 @@ def test_library_exports_every_declared_symbol(lores_lib):
 
 
 def test_spec_version(lores_lib):
-    assert lores.lores_spec_version() == 1
+    assert lores.lores_spec_version() == 2
 
 
 def _layout_bytes(B, H, dk, dv, head_prec):
     """Segment sizes as include/lores.h documents them."""
-    E = {0: 4, 1: 8, 2: 16, 3: 32}
+    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6}
     dvp = (dv + 63) // 64 * 64
     off = 0
-    for c in range(4):
+    for c in range(5):
         hc = sum(1 for p in head_prec if p == c)
         if not hc:
             continue
         off = (off + 255) // 256 * 256
-        off += B * hc * (dk // E[c]) * 16 * dvp
-        if c in (2, 3):
+        off += B * hc * -(-(dk * bits[c]) // 128) * 16 * dvp     # whole 16-byte chunks per row
+        if c in (2, 3, 4):
             off = (off + 255) // 256 * 256
             off += B * hc * dvp * 4
     return (off + 255) // 256 * 256
@@ -61,7 +61,8 @@ def _layout_bytes(B, H, dk, dv, head_prec):
 @pytest.mark.parametrize("B,H,dk,dv,prec", [
     (1, 2, 64, 64, [2, 2]), (64, 32, 128, 128, [2] * 32), (256, 128, 128, 64, [2] * 128),
     (128, 32, 128, 128, [1] * 8 + [2] * 24), (2048, 32, 128, 128, [2] * 16 + [3] * 16),
-    (3, 4, 96, 100, [0, 1, 2, 3]), (1, 1, 32, 1, [3])])
+    (3, 4, 96, 100, [0, 1, 2, 3]), (1, 1, 32, 1, [3]), (2048, 32, 128, 128, [4] * 16 + [3] * 16),
+    (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4])])
 def test_size_query_matches_documented_layout(lores_lib, B, H, dk, dv, prec):
     assert lores.lores_state_alloc(B, H, dk, dv, prec) == _layout_bytes(B, H, dk, dv, prec)
 

@@ -24,7 +24,7 @@ import pytest
 from oracle import exact, rng, step
 
 F32 = np.float32
-QM = {step.PREC_INT8: 127, step.PREC_INT4: 7}
+QM = {step.PREC_INT8: 127, step.PREC_INT4: 7, step.PREC_INT6: 31}    # 2^(b-1) - 1
 
 
 def _row_with_all_noise(x, m):
@@ -36,7 +36,7 @@ def _row_with_all_noise(x, m):
     return U, n
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
 def test_sr_exhaustive_probability(prec):
     r = QM[prec]
     g = np.random.default_rng(10 + prec)
@@ -78,7 +78,7 @@ def test_bf16_rounding_exactly_unbiased():
         assert mean == Fraction(float(x)), x
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_BF16])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6, step.PREC_BF16])
 def test_zero_rows_stay_zero(prec):
     U = np.zeros((2, 3, 64), F32)
     n = rng.noise16(rng.unit_key(0, 1, np.arange(2), 0), 3, 64)
@@ -88,7 +88,7 @@ def test_zero_rows_stay_zero(prec):
         assert np.all(st["codes"] == 0) and np.all(st["scales"] == 0)
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
 def test_one_step_error_below_one_code(prec):
     r = QM[prec]
     g = np.random.default_rng(12)
@@ -103,7 +103,7 @@ def test_one_step_error_below_one_code(prec):
     assert np.all(np.abs(X - U) <= s * (1 + 1e-5))
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_BF16])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6, step.PREC_BF16])
 def test_mean_over_seeds_is_unbiased(prec):
     g = np.random.default_rng(13)
     U = (g.standard_normal((1, 16, 64))).astype(F32)
@@ -160,7 +160,7 @@ def test_proposition1_readout_error_variances():
     assert abs(ratio_sr - 1) < 0.05, ratio_sr
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
 def test_weyl_noise_matches_independent_noise_readout_error(prec):
     g = np.random.default_rng(15)
     N, dv, dk = 300, 32, 128
@@ -176,7 +176,7 @@ def test_weyl_noise_matches_independent_noise_readout_error(prec):
     assert abs(errs["weyl"] / errs["iid"] - 1) < 0.10, errs
 
 
-@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
 def test_nearest_mode_is_round_to_nearest(prec):
     """rounding="nearest" (the draw fixed at 2^15) rounds y = U * inv to the
     nearest code: |c - y| <= 1/2 (+ the 2^-16 rounding of the sum), and it
@@ -185,7 +185,7 @@ def test_nearest_mode_is_round_to_nearest(prec):
     g = np.random.default_rng(41)
     U = (g.standard_normal((50, 16, 64)) * np.exp(g.uniform(-3, 3, (50, 16, 1)))).astype(F32)
     st = step.quantize_rows(U, prec, rounding="nearest")
-    r = {step.PREC_INT8: 127, step.PREC_INT4: 7}[prec]
+    r = QM[prec]
     m = np.abs(U).max(axis=2)
     inv = exact.rd_div32(F32(r), m).astype(np.float64)
     y = U.astype(np.float64) * inv[:, :, None]

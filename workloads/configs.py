@@ -7,12 +7,12 @@ The recurrence and its constraints (unit-norm q and k, beta in (0, 2), decay in
 (0, 1], delta in {0, 1}) are those of "Quantizing Recurrent Language Models Is
 Easier Than You Think", Introduction, general recurrence form.
 
-Precision codes match the C ABI: 0 = fp32, 1 = bf16, 2 = int8, 3 = int4.
+Precision codes match the C ABI: 0 = fp32, 1 = bf16, 2 = int8, 3 = int4, 4 = int6.
 Tiers are listed slowest-decaying first, as (fraction of heads, precision).
 """
 from dataclasses import dataclass, field
 
-PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4 = 0, 1, 2, 3
+PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4, PREC_INT6 = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -60,6 +60,11 @@ WORKLOADS = {
     "C5": Workload("C5", "gdn-b2048-h32-d128-int8+int4", B=2048, H=32, dk=128, dv=128,
                    T=64, delta=1, decay="uniform_head", alpha_lo=0.7, alpha_hi=1.0,
                    tiers=((0.5, PREC_INT8), (0.5, PREC_INT4)), seeds=tuple(range(8))),
+    # The same shape with the slowest-decaying half in int6 instead of int8:
+    # the int4 / int6 mix, 5.25 bits per element with the row scales.
+    "C5i6": Workload("C5i6", "gdn-b2048-h32-d128-int6+int4", B=2048, H=32, dk=128, dv=128,
+                     T=64, delta=1, decay="uniform_head", alpha_lo=0.7, alpha_hi=1.0,
+                     tiers=((0.5, PREC_INT6), (0.5, PREC_INT4))),
 }
 
 
