@@ -62,3 +62,24 @@ def test_decay_assigned_mixed_precision_sits_between():
     e4 = np.mean([e[-1] for e in _run(3, 0.9, 1.0, SR, T=512)["rel_err"]])
     log(f"int8 {e8:.4f} mixed {em:.4f} int4 {e4:.4f}")
     assert e8 < em < e4
+
+
+def test_int6_and_the_five_bit_mix():
+    """int6 sits between int8 and int4, and promoting the slowest-decaying
+    half of int4 heads to int6 (5.25 effective bits) recovers most of the
+    int4 error on the slow heads, where it accumulates."""
+    log("case: harness int6, int4 and the decay-assigned int6 + int4 mix, T=512")
+    H = 12
+    e = {}
+    for name, prec in (("int8", 2), ("int6", 4), ("int4", 3),
+                       ("mix", eh.decay_assigned(H, [(0.5, 4), (0.5, 3)]))):
+        res = _run(prec, 0.9, 1.0, SR, T=512)
+        e[name] = res
+    mean = {k: float(np.mean([x[-1] for x in r["rel_err"]])) for k, r in e.items()}
+    log(str({k: round(v, 4) for k, v in mean.items()}))
+    assert mean["int8"] < mean["int6"] < mean["mix"] < mean["int4"]
+    assert abs(eh.effective_bits(e["mix"]["head_prec"]) - 5.25) < 1e-9
+    slow = slice(6, 12)                                  # heads sorted fastest first
+    slow_mix = np.mean([x[-1] for x in e["mix"]["rel_err"][slow]])
+    slow_int4 = np.mean([x[-1] for x in e["int4"]["rel_err"][slow]])
+    assert slow_mix < slow_int4 / 2
