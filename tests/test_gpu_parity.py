@@ -106,3 +106,17 @@ def test_fp32_path_free_running(delta, decay):
     worst = run_free_fp32(w, T=w.T)
     log(f"worst o error / readout scale = {worst:.2e}")
     assert worst <= 1e-5
+
+
+@pytest.mark.parametrize("B,H,dv,prec", [
+    (65535, 1, 64, [2]),                                  # the largest batch (grid y limit)
+    (3, 512, 256, [0, 1, 2, 3, 4] * 102 + [2, 3]),        # the most heads, the tallest state
+])
+def test_maximum_sizes(B, H, dv, prec):
+    w = C1.scaled(B=B, H=H, dk=128, dv=dv, T=2)
+    log(f"case: maximum sizes B={B} H={H} d_v={dv} d_k=128, sampled units")
+    units = _sample_units(B, H, 40, seed=B + H)
+    units += [(B - 1, H - 1), (0, 0), (B - 1, 0), (0, H - 1)]
+    s = run_parity(w, T=w.T, units=sorted(set(units)), head_prec=prec, init="random")
+    log(s.summary())
+    s.check()
