@@ -528,6 +528,8 @@ struct TaskStream {
 
     static constexpr int NV = DK / 16;            // row-vector registers per vector
 
+    // Loads of task b: chunks [C0, C1) and, with C0 = 0, the per-task values.
+    template <int C0 = 0, int C1 = NCH>
     __device__ __forceinline__ void issue(int b, u32x4 *cw, TaskSide<NV> &in) const {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
@@ -535,7 +537,8 @@ struct TaskStream {
         // padding rows (row >= d_v) lie inside the unit and are read, never written
         const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + row;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
+        for (int c = C0; c < C1; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
+        if constexpr (C0 != 0) return;
         if constexpr (is_int<PREC>()) in.s = scales[unit * dv_pad + row];
         in.v = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
         in.beta = betap[bh];
@@ -651,39 +654,39 @@ struct TaskStream {
     }
 };
 
-// One stream over all its sequences.  For int classes the next sequence's
-// loads are issued right after pass 1 (a second chunk set fits in the
-// registers); bf16 / fp32 rows are loaded at the top of each task.  The loop
-// body holds two tasks, so the prefetched per-task values alternate between
-// two register sets instead of being copied.
+// One stream over all its sequences.  Right after pass 1 of a task (when
+// the chunk registers are free) the next sequence's per-task values and
+// first chunks are loaded: all of an int row, the first kMaxPrefetchChunks
+// of a bf16 row (the rest are loaded as that task starts), none of an fp32
+// row.  The loop body holds two tasks, so the prefetched per-task values
+// alternate between two register sets instead of being copied.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
 __device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN> &ts) {
     using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN>;
-    constexpr bool kPrefetch = TS::NCH <= kMaxPrefetchChunks;
+    // fp32 rows (32 chunks at d_k = 128) leave no registers for a prefetch
+    // beside U: only their per-task values are loaded ahead
+    constexpr int P = TS::NCH <= kMaxPrefetchChunks ? TS::NCH
+                    : PREC == LORES_BF16 ? kMaxPrefetchChunks : 0;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
-    TaskSide<TS::NV> in0, in1;        // alternate, so no copy between tasks
+    TaskSide<TS::NV> in0, in1;
     int b = blockIdx.y;
     ts.issue(b, cw, in0);
     while (true) {
         int bn = b + bstep;
         ts.run(b, cw, in0, [&] {
-            if constexpr (kPrefetch) {
-                if (bn < ts.meta.B) ts.issue(bn, cw, in1);
-            }
+            if (bn < ts.meta.B) ts.template issue<0, P>(bn, cw, in1);
         });
         if (bn >= ts.meta.B) break;
         b = bn;
         bn = b + bstep;
-        if constexpr (!kPrefetch) ts.issue(b, cw, in1);
+        if constexpr (P < TS::NCH) ts.template issue<P, TS::NCH>(b, cw, in1);
         ts.run(b, cw, in1, [&] {
-            if constexpr (kPrefetch) {
-                if (bn < ts.meta.B) ts.issue(bn, cw, in0);
-            }
+            if (bn < ts.meta.B) ts.template issue<0, P>(bn, cw, in0);
         });
         if (bn >= ts.meta.B) break;
         b = bn;
-        if constexpr (!kPrefetch) ts.issue(b, cw, in0);
+        if constexpr (P < TS::NCH) ts.template issue<P, TS::NCH>(b, cw, in0);
     }
 }
 
