@@ -167,6 +167,15 @@ __device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
     return r;
 }
 
+// Byte 2 of the fp32 patterns of z[0..3] into bytes 0..3 (three v_perm_b32).
+__device__ __forceinline__ uint32_t gather_byte2(const float *z) {
+    // selector bytes: 0-3 pick the second operand's bytes, 4-7 the first's,
+    // 0x0c gives zero
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(z[1]), __float_as_uint(z[0]), 0x0c0c0602u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(z[3]), __float_as_uint(z[2]), 0x0c0c0602u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 // Byte K of `word` := truncation of z (0 <= z < 256) to an integer; the other
 // bytes are kept.  One SDWA convert per element packs the codes for free.
 template <int K>
@@ -423,7 +432,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                     ow[q4] = word;
                 }
             } else if constexpr (PREC == LORES_INT4) {
-                // e in [129, 143]; its low nibble is the offset-binary code c + 8
+                // floor(z) in [129, 143]: floor(z) - 128 is the offset-binary code c + 8
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 8;
@@ -435,15 +444,12 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                         zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
                         x = step16(x, psi);
                     }
-                    uint32_t ev = (uint32_t)ze[0];
-                    uint32_t od = (uint32_t)zo[0];
-                    cvt_u8_into<1>(ev, ze[1]);
-                    cvt_u8_into<1>(od, zo[1]);
-                    cvt_u8_into<2>(ev, ze[2]);
-                    cvt_u8_into<2>(od, zo[2]);
-                    cvt_u8_into<3>(ev, ze[3]);
-                    cvt_u8_into<3>(od, zo[3]);
-                    ow[q4] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+                    // z lies in [128, 256), where bits 16..22 of its fp32
+                    // pattern are floor(z) - 128 = code + 8 (<= 15) and bit
+                    // 23 is 0: byte 2 of each z is its stored nibble
+                    const uint32_t ev = gather_byte2(ze);
+                    const uint32_t od = gather_byte2(zo);
+                    ow[q4] = ev | (od << 4);
                 }
             } else if constexpr (PREC == LORES_BF16) {
 #pragma unroll
