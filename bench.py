@@ -17,7 +17,8 @@ Workloads (synthetic, shapes of the decode layers the method targets):
 --mode copy times a plain device copy (the HBM calibration used for the
 rocprofv3 byte counters); --mode error runs the error-accumulation harness
 (quantized state against an fp32 twin over a long horizon) and prints its
-report instead.
+report instead; --mode sweep times the step kernel per state precision at the
+large-batch shape (which classes are HBM-bound and which VALU-bound).
 """
 import argparse
 import hashlib
@@ -48,7 +49,7 @@ def unit_bytes(prec, dk, dv, in_bytes, per_channel):
     """Algorithmic bytes of one state update: the state read and written once,
     plus q, k, v, alpha, beta read and o written."""
     state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * dv, 3: dv * dk // 2 + 4 * dv,
-             4: 6 * dv * dk // 8 + 4 * dv}[prec]
+             4: 6 * dv * dk // 8 + 4 * dv, 5: dv * dk + 4 * dv}[prec]
     io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
     return 2 * state + io
 
@@ -63,7 +64,7 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "error"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy", "error", "sweep"])
     ap.add_argument("--error-steps", type=int, default=2048,
                     help="horizon of the error-accumulation harness (--mode error)")
     ap.add_argument("--copy-mib", type=int, default=2048)
@@ -92,6 +93,65 @@ def copy_mode(args, torch):
     ms = e0.elapsed_time(e1) / reps
     print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
+
+
+SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta)
+    ("int8+int4 (C5)", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1),
+    ("int8+int4 (C5), delta 0", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 0),
+    ("int8", 2048, 32, 128, 128, [2] * 32, 1),
+    ("int8, delta 0", 2048, 32, 128, 128, [2] * 32, 0),
+    ("int6", 2048, 32, 128, 128, [4] * 32, 1),
+    ("fp8 (E4M3)", 2048, 32, 128, 128, [5] * 32, 1),
+    ("int4", 2048, 32, 128, 128, [3] * 32, 1),
+    ("int4, delta 0", 2048, 32, 128, 128, [3] * 32, 0),
+    ("bf16", 1024, 32, 128, 128, [1] * 32, 1),
+    ("int8, d_v 64 (C3 shape), delta 0", 256, 128, 128, 64, [2] * 128, 0),
+]
+
+
+def sweep_mode(args, torch):
+    """Achieved HBM throughput of the step kernel per state precision at the
+    large-batch shape: which classes sit on the HBM roof and which on the
+    VALU roof.  Random unit-norm q, k; v ~ N(0, 1); alpha in [0.7, 1);
+    fp32 inputs; 64 steps in a captured graph after 8 warm-up steps."""
+    import quantized_linear_recurrence_amd as lores
+    dev = torch.device("cuda:0")
+    rows = []
+    for label, B, H, dk, dv, prec, delta in SWEEP:
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed)
+
+        def unit(x):
+            return x / x.norm(dim=-1, keepdim=True)
+        q = unit(torch.randn(B, H, dk, generator=g, device=dev))
+        k = unit(torch.randn(B, H, dk, generator=g, device=dev))
+        v = torch.randn(B, H, dv, generator=g, device=dev)
+        alpha = (0.7 + 0.3 * torch.rand(B, H, generator=g, device=dev)).contiguous()
+        beta = (2 * torch.sigmoid(torch.randn(B, H, generator=g, device=dev))).contiguous()
+        st = lores.lores_state_alloc(B, H, dk, dv, prec, device=dev)
+        o = torch.empty(B, H, dv, device=dev)
+        for t in range(1, 9):
+            lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, t, o=o)
+        steps = 64
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for t in range(1, steps + 1):
+                lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, 100 + t, o=o)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        nbytes = sum(B * prec.count(c) * unit_bytes(c, dk, dv, 4, False) for c in range(6))
+        gbs = nbytes / us / 1e3
+        rows.append({"state": label, "B": B, "H": H, "d_k": dk, "d_v": dv, "delta": delta,
+                     "us_per_step": us, "GBps": gbs, "frac": gbs / HBM_PEAK_GBPS})
+        print(f"[sweep] {label:34s} {us:8.1f} us/step {gbs:7.0f} GB/s  {gbs / HBM_PEAK_GBPS:.3f}",
+              file=sys.stderr, flush=True)
+    print(json.dumps({"mode": "sweep", "rows": rows}), flush=True)
 
 
 def cpu_baseline(w, inputs, head_prec, target_s, seed):
@@ -158,6 +218,9 @@ def main(argv=None):
     if args.mode == "copy":
         copy_mode(args, torch)
         return
+    if args.mode == "sweep":
+        sweep_mode(args, torch)
+        return
     if args.mode == "error":
         from quantized_linear_recurrence_amd import error_harness
         t0 = time.perf_counter()
@@ -189,7 +252,7 @@ def main(argv=None):
 
     in_bytes = 2 if w.in_bf16 else 4
     step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel)
-                     for c in range(5))
+                     for c in range(6))
     st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev)
     o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
 
@@ -271,7 +334,7 @@ def main(argv=None):
             "B": w.B, "H": w.H, "d_k": w.dk, "d_v": w.dv, "delta": w.delta,
             "decay": w.decay, "inputs": "bf16" if w.in_bf16 else "fp32",
             "state": {name: head_prec.count(c) for c, name in
-                      enumerate(["fp32", "bf16", "int8", "int4", "int6"]) if head_prec.count(c)},
+                      enumerate(["fp32", "bf16", "int8", "int4", "int6", "fp8"]) if head_prec.count(c)},
             "rounding": "stochastic", "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 2
+#define LORES_SPEC_VERSION 3
 
 /* Per-head state precision. */
 enum {
@@ -48,9 +48,10 @@ enum {
     LORES_BF16 = 1, /* bfloat16 state, stochastic rounding from fp32               */
     LORES_INT8 = 2, /* int8 codes in [-127, 127] + one fp32 scale per value row     */
     LORES_INT4 = 3, /* int4 codes in [-7, 7]     + one fp32 scale per value row     */
-    LORES_INT6 = 4  /* int6 codes in [-31, 31]   + one fp32 scale per value row     */
+    LORES_INT6 = 4, /* int6 codes in [-31, 31]   + one fp32 scale per value row     */
+    LORES_FP8 = 5   /* E4M3 (OCP fp8) values     + one fp32 scale per value row     */
 };
-#define LORES_NUM_PREC 5
+#define LORES_NUM_PREC 6
 
 /* Rounding of the requantization (per state; lores_state_set_rounding). */
 enum {
@@ -80,11 +81,11 @@ typedef struct lores_state lores_state;
 /*
  * Packed state layout (version LORES_SPEC_VERSION), for inspection, tests and
  * checkpointing.  The buffer holds one segment pair per precision class that
- * has at least one head, in class order fp32, bf16, int8, int4, int6, each
- * segment starting on a 256-byte boundary:
+ * has at least one head, in class order fp32, bf16, int8, int4, int6, fp8,
+ * each segment starting on a 256-byte boundary:
  *
  *   codes  [B][H_c][n_chunk][d_v_pad][16 bytes]
- *   scales [B][H_c][d_v_pad] fp32                 (int8, int4 and int6 classes)
+ *   scales [B][H_c][d_v_pad] fp32                 (int8, int4, int6, fp8 classes)
  *
  * H_c = heads of class c, ordered by head index (head_slot below).
  * d_v_pad = d_v rounded up to LORES_ROW_BLOCK; padding rows are never read
@@ -94,6 +95,8 @@ typedef struct lores_state lores_state;
  * Within a chunk, element e is:
  *   fp32: word e, IEEE binary32        bf16: halfword e, bfloat16 bits
  *   int8: byte e  = code + 128         (offset binary, 1..255)
+ *   fp8:  byte e  = E4M3 byte (OCP: sign, 4 exponent bits with bias 7,
+ *         3 mantissa bits; never the NaN pattern), value scale * E4M3 value
  *   int4: byte e/2, low nibble for even e, high nibble for odd e,
  *         nibble = code + 8            (offset binary, 1..15)
  * int6 rows are a little-endian bit stream over the row's chunks (chunk c
@@ -117,7 +120,7 @@ typedef struct {
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
  *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128},
  *               1 <= d_v <= LORES_MAX_DV
- *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_INT6)
+ *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
  *               returns LORES_OK without creating a handle.  Otherwise *bytes
@@ -202,6 +205,10 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
  *   code'  = floor(fl(U * inv + bias + u)) - bias, inv = the largest fp32 not
  *            above r / m (0 if m = 0), bias = 128 (int8), 160 (int6) or 136
  *            (int4),
+ * fp8 heads: scale' = fl(m / 448), y = fl(U * inv) with inv the largest fp32
+ *            not above 448 / m; the E4M3 byte of y is the sign and the top
+ *            7 magnitude bits of f32bits(fl(y * 2^-120)) + (n << 4), which
+ *            rounds stochastically on the E4M3 grid (subnormals included),
  *            u = n * 2^-16 and n a 16-bit counter-based draw keyed on
  *            (seed, t, sequence, head, row, column).
  */

@@ -19,6 +19,7 @@ rounding the quantized path commits to (the readings are listed in the
 repository's design notes):
 
   1  a_ij  = fl(s_i * alpha_j);  S'_ij = fl(c_ij * a_ij)          int heads
+     S'_ij = fl(v_ij * a_ij), v_ij the E4M3 value                 fp8 heads
      S'_ij = fl(X_ij * alpha_j)                                   bf16 / fp32 heads
   2  delta = 1: r_i = fl(sum_j S'_ij k_j);  g_i = fl(beta * fl(v_i - r_i))
      delta = 0: g_i = fl(beta * v_i)
@@ -26,7 +27,9 @@ repository's design notes):
        (real arithmetic: U = S' - delta*beta (S'k) k^T + beta v k^T, which is
         S_{t-1} diag(alpha)(I - delta beta k k^T) + beta v k^T)
   4  o_i  = fl(sum_j U_ij q_j)             (readout of the pre-requant state)
-  5  int heads, r = 2^(b-1) - 1 = 127 (int8), 31 (int6) or 7 (int4), bias
+  5  fp8 heads: s'_i = fl(m_i / 448), inv_i = largest fp32 <= 448 / m_i,
+       y_ij = fl(U_ij * inv_i), bytes = e4m3_encode(y_ij, n_ij)
+     int heads, r = 2^(b-1) - 1 = 127 (int8), 31 (int6) or 7 (int4), bias
      B = 128 (int8), 160 (int6) or 136 (int4):
        m_i = max_j |U_ij|;  s'_i = fl(m_i / r);  inv_i = largest fp32 <= r / m_i
        (inv_i = 0 for m_i = 0);  z_ij = fl(U_ij * inv_i + (B + n_ij 2^-16))
@@ -41,9 +44,43 @@ from . import exact
 from .exact import F32, F64, f32, fma32
 from .rng import noise16, noise16_iid, unit_key
 
-PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4, PREC_INT6 = 0, 1, 2, 3, 4
+PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4, PREC_INT6, PREC_FP8 = 0, 1, 2, 3, 4, 5
 QMAX = {PREC_INT8: 127, PREC_INT4: 7, PREC_INT6: 31}
 BIAS = {PREC_INT8: 128, PREC_INT4: 136, PREC_INT6: 160}
+FP8_MAX = 448.0          # largest finite E4M3 value
+
+
+# ---------------------------------------------------------------------------
+# E4M3 (OCP 8-bit floating point: 1 sign, 4 exponent bits with bias 7, 3
+# mantissa bits; exponent 0 holds subnormals; S.1111.111 is NaN, so the
+# largest finite magnitude is 1.75 * 2^8 = 448).  The pages compare this
+# format with value-grouped INT8 ("Intra-State Quantization (Section 4)",
+# Format).
+# ---------------------------------------------------------------------------
+def e4m3_decode(b):
+    """E4M3 bytes -> fp32 values, from the format's definition."""
+    b = np.asarray(b, np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(F64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return (sign * mag).astype(F32)
+
+
+def e4m3_encode(y, n):
+    """Stochastic rounding of fp32 values |y| <= 448 to E4M3 bytes with the
+    16-bit draws n.  ys = fl(y * 2^-120) puts the E4M3 normal range on the
+    fp32 normal range starting at 2^-126 and the E4M3 subnormals on fp32
+    denormals, so in both ranges the E4M3 grid is the fp32 bit pattern with
+    its low 20 bits dropped; the draw is added just below the kept bits
+    (bits 4..19) before dropping them.  The byte is the sign and the next 7
+    bits.  n = 2^15 for every element is round to nearest, ties upward in
+    magnitude."""
+    ys = (f32(y) * F32(2.0 ** -120)).astype(F32)
+    t = exact.f32_bits(ys).astype(np.uint64) + (np.asarray(n, np.uint64) << np.uint64(4))
+    u = (t >> np.uint64(20)) & np.uint64(0xFFF)
+    return ((u & np.uint64(0x7F)) | ((u >> np.uint64(4)) & np.uint64(0x80))).astype(np.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -76,6 +113,8 @@ def transition64(k, alpha, beta, delta):
 # state containers
 # ---------------------------------------------------------------------------
 def zero_state(prec, n, dv, dk):
+    if prec == PREC_FP8:
+        return {"fp8": np.zeros((n, dv, dk), np.uint8), "scales": np.zeros((n, dv), F32)}
     if prec in QMAX:
         return {"codes": np.zeros((n, dv, dk), np.int32), "scales": np.zeros((n, dv), F32)}
     if prec == PREC_BF16:
@@ -84,7 +123,10 @@ def zero_state(prec, n, dv, dk):
 
 
 def dequant(prec, state):
-    """Stored state as fp32 values: fl(s_i * c_ij) for int heads, exact otherwise."""
+    """Stored state as fp32 values: fl(s_i * c_ij) for int heads, fl(s_i *
+    E4M3 value) for fp8 heads, exact otherwise."""
+    if prec == PREC_FP8:
+        return (state["scales"][:, :, None] * e4m3_decode(state["fp8"])).astype(F32)
     if prec in QMAX:
         return (state["scales"][:, :, None] * state["codes"].astype(F32)).astype(F32)
     if prec == PREC_BF16:
@@ -110,6 +152,15 @@ def quantize_rows(U, prec, n=None, rounding="sr"):
     if rounding == "nearest":
         n = np.full(U.shape, 1 << 15, dtype=np.uint32)
         rounding = "sr"
+    if prec == PREC_FP8:
+        # the row maximum maps to the largest E4M3 value
+        if rounding != "sr":
+            raise ValueError(rounding)
+        m = np.max(np.abs(U), axis=2)
+        scales = exact.rn_div32(m, F32(FP8_MAX))
+        inv = exact.rd_div32(F32(FP8_MAX), m)
+        y = (U * inv[:, :, None]).astype(F32)
+        return {"fp8": e4m3_encode(y, n), "scales": scales}
     if prec in QMAX:
         r = QMAX[prec]
         m = np.max(np.abs(U), axis=2)
@@ -157,7 +208,10 @@ def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
     a_row = alpha[:, None, None] if alpha.ndim == 1 else alpha[:, None, :]
 
     # 1  dequantize and decay (key columns)
-    if prec in QMAX:
+    if prec == PREC_FP8:
+        a = (state["scales"][:, :, None] * a_row).astype(F32)
+        Sp = (e4m3_decode(state["fp8"]) * a).astype(F32)
+    elif prec in QMAX:
         a = (state["scales"][:, :, None] * a_row).astype(F32)
         Sp = (state["codes"].astype(F32) * a).astype(F32)
     else:

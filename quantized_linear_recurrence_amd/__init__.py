@@ -14,10 +14,11 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (LORES_BF16, LORES_FP32, LORES_INT4, LORES_INT6, LORES_INT8, LORES_ROUND_NEAREST,
+from ._lib import (LORES_BF16, LORES_FP8, LORES_FP32, LORES_INT4, LORES_INT6, LORES_INT8,
+                   LORES_ROUND_NEAREST,
                    LORES_ROUND_STOCHASTIC, LoresLayout, LoresLibraryMissing)
 
-__all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LORES_INT6",
+__all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LORES_INT6", "LORES_FP8",
            "LORES_ROUND_STOCHASTIC",
            "LORES_ROUND_NEAREST", "LoresError", "lores_state_set_rounding",
            "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_layout",

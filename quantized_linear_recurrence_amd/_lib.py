@@ -8,8 +8,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblores.so")
 
-LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4, LORES_INT6 = 0, 1, 2, 3, 4
-NUM_PREC = 5
+LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4, LORES_INT6, LORES_FP8 = 0, 1, 2, 3, 4, 5
+NUM_PREC = 6
 LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST = 0, 1
 LORES_OK, LORES_EINVAL, LORES_EUNSUPPORTED, LORES_ESIZE, LORES_EHIP, LORES_ENOMEM = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3: "LORES_ESIZE",

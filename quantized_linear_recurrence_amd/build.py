@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "liblores.so")
 ARCH = "gfx950"
 
 SOURCES = ["lores_api.cpp", "lores_aux.hip", "lores_step_int8.hip", "lores_step_int4.hip",
-           "lores_step_int6.hip", "lores_step_bf16.hip", "lores_step_fp32.hip",
+           "lores_step_int6.hip", "lores_step_fp8.hip", "lores_step_bf16.hip", "lores_step_fp32.hip",
            "lores_step_int8_int4.hip", "lores_step_int4_int6.hip", "lores_step_bf16_int8.hip",
            "lores_step_bf16_int4.hip"]
 

@@ -47,10 +47,13 @@ int ok() {
 
 bool is_int_prec(int p) { return p == LORES_INT8 || p == LORES_INT4 || p == LORES_INT6; }
 
+// classes stored with one fp32 scale per value row
+bool has_scales(int p) { return is_int_prec(p) || p == LORES_FP8; }
+
 // Bytes per stored row: d_k elements of 32, 16, 8, 4 or 6 bits in whole
 // 16-byte chunks (only int6 rows can end in a partly used chunk).
 int64_t row_bytes(int prec, int dk) {
-    static const int bits[LORES_NUM_PREC] = {32, 16, 8, 4, 6};
+    static const int bits[LORES_NUM_PREC] = {32, 16, 8, 4, 6, 8};
     return (int64_t)((dk * bits[prec] + 127) / 128) * 16;
 }
 
@@ -93,7 +96,7 @@ int plan(lores_state *st, const uint8_t *head_prec) {
         off = align256(off);
         st->codes_off[c] = (int64_t)off;
         off += (uint64_t)st->B * st->n_class[c] * st->unit_bytes[c];
-        if (is_int_prec(c)) {
+        if (has_scales(c)) {
             off = align256(off);
             st->scales_off[c] = (int64_t)off;
             off += (uint64_t)st->B * st->n_class[c] * st->dv_pad * sizeof(float);
@@ -158,6 +161,7 @@ hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, c
             case LORES_INT8: return launch_step_int8(dk, pc, delta, bf16, p, m, s);
             case LORES_INT4: return launch_step_int4(dk, pc, delta, bf16, p, m, s);
             case LORES_INT6: return launch_step_int6(dk, pc, delta, bf16, p, m, s);
+            case LORES_FP8: return launch_step_fp8(dk, pc, delta, bf16, p, m, s);
             default: return hipErrorInvalidValue;
         }
     }
@@ -384,7 +388,7 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             for (int i = 0; i < width[l]; ++i) {
                 const int c = groups[l][i];
                 p.codes[i] = st->base + st->codes_off[c];
-                p.scales[i] = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
+                p.scales[i] = has_scales(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
             }
             const int p1 = width[l] == 2 ? groups[l][1] : -1;
             hipError_t e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16,
@@ -414,7 +418,7 @@ int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t se
             m.t = 0;
             m.seq_base = seq_base;
             m.head_base = head_base;
-            float *sc = is_int_prec(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
+            float *sc = has_scales(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e = lores::launch_quant(c, st->dk, X, st->base + st->codes_off[c], sc, m,
                                                (hipStream_t)stream);
             if (e != hipSuccess)
@@ -433,7 +437,7 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
         for (int c = 0; c < LORES_NUM_PREC; ++c) {
             if (!st->n_class[c]) continue;
             lores::StepMeta m = make_meta(st, &c, 1);
-            const float *sc = is_int_prec(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
+            const float *sc = has_scales(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
                                                  (hipStream_t)stream);
             if (e != hipSuccess) return fail(LORES_EHIP, "dequant launch failed: %s", hipGetErrorString(e));

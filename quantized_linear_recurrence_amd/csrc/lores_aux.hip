@@ -30,7 +30,7 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     const long dv_pad = meta.dv_pad;
     const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * cd.unit_bytes) + row;
     float s = 0.0f;
-    if constexpr (is_int<PREC>()) s = scales[unit * dv_pad + row];
+    if constexpr (has_scale<PREC>()) s = scales[unit * dv_pad + row];
     float *orow = out + (bh * meta.dv + row) * DK;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     if constexpr (PREC == LORES_INT6) {
@@ -52,7 +52,9 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
             float x[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                if constexpr (PREC == LORES_INT8) {
+                if constexpr (PREC == LORES_FP8) {
+                    x[e] = s * fp8_value(wd[e >> 2], e & 3);
+                } else if constexpr (PREC == LORES_INT8) {
                     x[e] = s * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
                 } else if constexpr (PREC == LORES_INT4) {
                     const uint32_t w = wd[e >> 3];
@@ -110,7 +112,7 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
     u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * cd.unit_bytes) + row;
     requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
-                             is_int<PREC>() ? scales + unit * dv_pad + row : nullptr);
+                             has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
 }
 
 template <int PREC>
@@ -136,6 +138,7 @@ hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float 
         case LORES_INT8: return quant_prec<LORES_INT8>(dk, X, codes, scales, m, s);
         case LORES_INT4: return quant_prec<LORES_INT4>(dk, X, codes, scales, m, s);
         case LORES_INT6: return quant_prec<LORES_INT6>(dk, X, codes, scales, m, s);
+        case LORES_FP8: return quant_prec<LORES_FP8>(dk, X, codes, scales, m, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -163,6 +166,7 @@ hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *s
         case LORES_INT8: return dequant_prec<LORES_INT8>(dk, codes, scales, out, m, s);
         case LORES_INT4: return dequant_prec<LORES_INT4>(dk, codes, scales, out, m, s);
         case LORES_INT6: return dequant_prec<LORES_INT6>(dk, codes, scales, out, m, s);
+        case LORES_FP8: return dequant_prec<LORES_FP8>(dk, codes, scales, out, m, s);
         default: return hipErrorInvalidValue;
     }
 }

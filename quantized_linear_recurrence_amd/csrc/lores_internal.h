@@ -55,6 +55,7 @@ hipError_t launch_step_bf16(int, bool, bool, bool, const StepPtrs &, const StepM
 hipError_t launch_step_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_fp8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int8_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_int4_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_bf16_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);

@@ -106,8 +106,29 @@ template <> struct Prec<LORES_INT6> {
     static constexpr uint32_t FBASE = 0x43200000u;  // 160.0f = 128 + 32
 };
 
+// E4M3 (OCP fp8) values with a value-row scale: the row maximum maps to
+// 448, the largest finite E4M3 value.
+template <> struct Prec<LORES_FP8> {
+    static constexpr int E = 16, BITS = 8;
+    static constexpr float R = 448.0f;
+};
+
 template <int PREC> constexpr bool is_int() {
     return PREC == LORES_INT8 || PREC == LORES_INT4 || PREC == LORES_INT6;
+}
+
+// classes stored with one fp32 scale per value row
+template <int PREC> constexpr bool has_scale() { return is_int<PREC>() || PREC == LORES_FP8; }
+
+// E4M3 byte `sel` of w as fp32 (hardware decode; gfx950 decodes the OCP
+// E4M3 format).  sel is a constant once the callers' loops are unrolled.
+__device__ __forceinline__ float fp8_value(uint32_t w, int sel) {
+    switch (sel) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+    }
 }
 
 // 16-byte chunks per stored row of d_k elements
@@ -355,7 +376,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = row_chunks<DK, PREC>();
     float inv = 0.0f;
-    if constexpr (is_int<PREC>()) {
+    if constexpr (has_scale<PREC>()) {
         const float snew = m / Prec<PREC>::R;
         inv = rd_div(Prec<PREC>::R, m);
         if (active) *scale_out = snew;
@@ -373,7 +394,8 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
         if (nearest) n0 = 0x8000u;
         const uint32_t n1 = nearest ? n0 : (n0 + kPsi16) & 0xFFFFu;
         if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
-        else x = n0 | (n1 << 16);
+        else if constexpr (PREC == LORES_BF16) x = n0 | (n1 << 16);
+        else x = n0;                                     // fp8: the draw alone
     }
     const uint32_t psi = opaque_uniform(nearest ? 0u : kPsi16);
     const uint32_t psi2 = opaque_uniform(nearest ? 0u : ((2 * kPsi16) & 0xFFFFu) * 0x00010001u);
@@ -450,6 +472,27 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                     const uint32_t ev = gather_byte2(ze);
                     const uint32_t od = gather_byte2(zo);
                     ow[q4] = ev | (od << 4);
+                }
+            } else if constexpr (PREC == LORES_FP8) {
+                // y = U * inv in [-448, 448]; fl(y * 2^-120) puts the E4M3
+                // grid on the fp32 pattern with its low 20 bits dropped (E4M3
+                // subnormals on fp32 denormals): add the draw at bits 4..19,
+                // keep the sign and the next 7 bits
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j = c * E + q4 * 4;
+                    uint32_t by[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = U[j + e] * inv;
+                        const uint32_t t = __float_as_uint(y * 0x1p-120f) + (x << 4);
+                        x = step16(x, psi);
+                        const uint32_t u = t >> 20;
+                        by[e] = (u & 0x7Fu) | ((u >> 4) & 0x80u);
+                    }
+                    ow[q4] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(by[3], by[2], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(by[1], by[0], 0x0c0c0400u),
+                                                   0x05040100u);
                 }
             } else if constexpr (PREC == LORES_BF16) {
 #pragma unroll
@@ -545,7 +588,7 @@ struct TaskStream {
 #pragma unroll
         for (int c = C0; c < C1; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
         if constexpr (C0 != 0) return;
-        if constexpr (is_int<PREC>()) in.s = scales[unit * dv_pad + row];
+        if constexpr (has_scale<PREC>()) in.s = scales[unit * dv_pad + row];
         in.v = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
         in.beta = betap[bh];
         in.alpha = PC ? 1.0f : alphap[bh];
@@ -574,6 +617,8 @@ struct TaskStream {
         if constexpr (is_int<PREC>() && !PC) {
             a = s * alpha_s;
             na = a * -Prec<PREC>::OFF;
+        } else if constexpr (PREC == LORES_FP8 && !PC) {
+            a = s * alpha_s;
         }
 
         // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
@@ -583,7 +628,7 @@ struct TaskStream {
         // after each group of 16 columns: per-channel decay of float heads,
         // then the group's share of r
         auto group_done = [&](int j) {
-            if constexpr (PC && !is_int<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
+            if constexpr (PC && !has_scale<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
             if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
             // without the projection nothing orders pass 1 before the
             // next task's loads; materialize the group here so the
@@ -608,11 +653,16 @@ struct TaskStream {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int j = c * E + e;
-                if constexpr (PC && is_int<PREC>()) {
+                if constexpr (PC && has_scale<PREC>()) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
                 float sp;
-                if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
+                if constexpr (PREC == LORES_FP8) {
+                    // the E4M3 value (hardware decode of byte e & 3), times s * alpha
+                    const float v = fp8_value(wd[e >> 2], e & 3);
+                    if constexpr (PC) sp = v * aj[j & 15];
+                    else sp = v * a;
+                } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
                     if constexpr (PREC == LORES_INT8) {
                         ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
@@ -656,7 +706,7 @@ struct TaskStream {
 
         // ---- pass 3: requantize and store in place
         requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
-                                 is_int<PREC>() ? scales + unit * dv_pad + row : nullptr);
+                                 has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
     }
 };
 

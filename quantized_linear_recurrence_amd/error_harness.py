@@ -126,7 +126,7 @@ def summarize(res, bins=3):
 # bits per stored element including the fp32 row scale (d_k = 128)
 def effective_bits(head_prec, d_k=128):
     per = {LORES_FP32: 32.0, 1: 16.0, 2: 8.0 + 32.0 / d_k, 3: 4.0 + 32.0 / d_k,
-           4: 6.0 + 32.0 / d_k}
+           4: 6.0 + 32.0 / d_k, 5: 8.0 + 32.0 / d_k}
     return float(np.mean([per[p] for p in head_prec]))
 
 
@@ -146,13 +146,14 @@ def decay_assigned(H, tiers):
 
 def run_suite(T=2048, B=32, H=12, d=128, seed=1, device="cuda"):
     """The harness's report: random writes (drift 100), scalar decay, delta
-    = 0, two decay regimes; int8, int6 and int4 states and the decay-assigned
+    = 0, two decay regimes; int8, E4M3, int6 and int4 states and the decay-assigned
     mixes that keep the slowest half of the heads at 8 or 6 bits (6.25 and
     5.25 effective bits); stochastic and nearest rounding."""
     names = {0: "stochastic", 1: "nearest"}
     rows = []
     for lo, hi in ((0.9, 1.0), (0.99, 1.0)):
-        for label, prec in (("int8", [2] * H), ("int6", [4] * H), ("int4", [3] * H),
+        for label, prec in (("int8", [2] * H), ("fp8 (E4M3)", [5] * H), ("int6", [4] * H),
+                            ("int4", [3] * H),
                             ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)])),
                             ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]))):
             for rnd in (LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST):

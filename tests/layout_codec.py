@@ -14,12 +14,13 @@ E = {0: 4, 1: 8, 2: 16, 3: 32}       # elements per 16-byte chunk (int6: a bit s
 OFFSET = {2: 128, 3: 8, 4: 32}       # offset-binary code offset
 QMAX = {2: 127, 3: 7, 4: 31}
 INT_CLASSES = (2, 3, 4)
+SCALED_CLASSES = (2, 3, 4, 5)        # classes with one fp32 scale per value row
 
 
 def n_chunks(c, dk):
     """16-byte chunks per row: d_k elements of 32, 16, 8, 4 or 6 bits, the
     last chunk zero-padded."""
-    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6}[c]
+    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}[c]
     return (dk * bits + 127) // 128
 
 
@@ -56,7 +57,12 @@ def pack_unit(c, dk, dv, dv_pad, state_unit):
     n_chunk = n_chunks(c, dk)
     out = np.zeros((n_chunk, dv_pad, 16), np.uint8)
     sc = None
-    if c in INT_CLASSES:
+    if c == 5:
+        sc = np.zeros(dv_pad, np.float32)
+        sc[:dv] = state_unit["scales"]
+        by = np.asarray(state_unit["fp8"], np.uint8)
+        out[:, :dv, :] = by.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
+    elif c in INT_CLASSES:
         codes = np.asarray(state_unit["codes"], np.int64)
         assert codes.min() >= -QMAX[c] and codes.max() <= QMAX[c]
         sc = np.zeros(dv_pad, np.float32)
@@ -90,6 +96,8 @@ def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None):
     if c == 2:
         return {"codes": rows.astype(np.int32) - 128,
                 "scales": np.asarray(scales, np.float32)[:dv].copy()}
+    if c == 5:
+        return {"fp8": rows.copy(), "scales": np.asarray(scales, np.float32)[:dv].copy()}
     if c == 4:
         return {"codes": _unpack6(rows, dk) - 32,
                 "scales": np.asarray(scales, np.float32)[:dv].copy()}
@@ -107,7 +115,7 @@ def unit_ranges(layout, c, unit):
     """Byte ranges (code_start, code_len, scale_start | None, scale_len) of a unit."""
     ub = layout["unit_code_bytes"][c]
     cs = layout["codes_offset"][c] + unit * ub
-    if c in INT_CLASSES:
+    if c in SCALED_CLASSES:
         dvp = layout["d_v_pad"]
         return cs, ub, layout["scales_offset"][c] + unit * dvp * 4, dvp * 4
     return cs, ub, None, 0

@@ -12,6 +12,9 @@ Tolerances (per compared step):
           product summation order can move a pre-rounding value across a
           rounding threshold)
   scales  relative difference <= 2^-20
+  fp8     at most 1e-4 of bytes differ, each value within one E4M3 step
+          (1/8 of the larger magnitude, or the subnormal step) of the
+          oracle's, plus 2^-16 of the row's absolute maximum
   bf16    at most 1e-4 of values differ, each by one bf16 ulp, or, where the
           update cancelled to a value far below its row's magnitude (a bf16
           ulp there is tiny), by at most one ulp plus 2^-16 of the row's
@@ -57,6 +60,10 @@ def head_precisions(w, inputs, calib_steps=32):
 
 
 def random_unit_state(c, dv, dk, g):
+    if c == 5:
+        by = g.integers(0, 256, (dv, dk)).astype(np.uint8)
+        by[(by & 0x7F) == 0x7F] ^= 0x01                  # no NaN patterns
+        return {"fp8": by, "scales": np.exp(g.uniform(-7, -2, dv)).astype(F32)}
     if c in (2, 3, 4):
         r = {2: 127, 3: 7, 4: 31}[c]
         return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
@@ -82,6 +89,8 @@ class Stats:
         self.scale_rel = 0.0
         self.bf16 = self.bf16_diff = 0
         self.max_dbits = 0
+        self.fp8 = self.fp8_diff = 0
+        self.fp8_excess = 0.0           # worst excess over one E4M3 step / row max
         self.bf16_far = 0               # differing by more than one ulp
         self.bf16_far_rel = 0.0         # their worst excess over one ulp / row max
         self.o_err_q = 0.0
@@ -93,7 +102,8 @@ class Stats:
         return (f"steps={self.steps} code_flip={self.code_diff}/{self.codes} max|dc|={self.max_dc} "
                 f"scale_rel={self.scale_rel:.2e} bf16_flip={self.bf16_diff}/{self.bf16} "
                 f"max|dbits|={self.max_dbits} far={self.bf16_far} "
-                f"far_rel={self.bf16_far_rel:.2e} o_err_q={self.o_err_q:.2e} "
+                f"far_rel={self.bf16_far_rel:.2e} fp8_flip={self.fp8_diff}/{self.fp8} "
+                f"fp8_excess={self.fp8_excess:.2e} o_err_q={self.o_err_q:.2e} "
                 f"o_err_f32={self.o_err_f:.2e} x_err_f32={self.x_err_f:.2e}")
 
     def check(self):
@@ -101,6 +111,8 @@ class Stats:
         assert self.code_diff <= max(1e-4 * self.codes, 0), self.summary()
         assert self.scale_rel <= 2.0 ** -20, self.summary()
         assert self.bf16_far_rel <= 2.0 ** -16, self.summary()
+        assert self.fp8_diff <= 1e-4 * self.fp8, self.summary()
+        assert self.fp8_excess <= 2.0 ** -16, self.summary()
         assert self.bf16_diff <= 1e-4 * self.bf16, self.summary()
         assert self.o_err_q <= 1e-3, self.summary()
         assert self.o_err_f <= 1e-5, self.summary()
@@ -191,6 +203,25 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
                 stats.codes += d.size
                 stats.code_diff += int((d > 0).sum())
                 stats.max_dc = max(stats.max_dc, int(d.max()))
+                rel = np.abs(gpu["scales"].astype(np.float64) - new["scales"]) / \
+                    np.maximum(np.abs(new["scales"]).astype(np.float64), 1e-38)
+                rel[(new["scales"] == 0) & (gpu["scales"] == 0)] = 0
+                stats.scale_rel = max(stats.scale_rel, float(rel.max()))
+                stats.o_err_q = max(stats.o_err_q, float(o_err))
+            elif c == 5:
+                # E4M3 has a value-relative grid like bf16: a differing value
+                # must lie within one E4M3 step of the oracle's value, plus the
+                # cancellation allowance of the bf16 rule
+                Xg = ostep.dequant(c, gpu).astype(np.float64)
+                Xr = X_ref.astype(np.float64)
+                diff = gpu["fp8"] != new["fp8"]
+                stats.fp8 += diff.size
+                stats.fp8_diff += int(diff.sum())
+                if diff.any():
+                    rowmax = np.abs(Xr).max(axis=2, keepdims=True)
+                    step = np.maximum(np.abs(Xr), np.abs(Xg)) / 8 + rowmax / 448 * 2.0 ** -9
+                    excess = (np.abs(Xg - Xr) - step) / np.maximum(rowmax, 1e-300)
+                    stats.fp8_excess = max(stats.fp8_excess, float(excess[diff].max()))
                 rel = np.abs(gpu["scales"].astype(np.float64) - new["scales"]) / \
                     np.maximum(np.abs(new["scales"]).astype(np.float64), 1e-38)
                 rel[(new["scales"] == 0) & (gpu["scales"] == 0)] = 0

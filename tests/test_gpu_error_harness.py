@@ -83,3 +83,14 @@ def test_int6_and_the_five_bit_mix():
     slow_mix = np.mean([x[-1] for x in e["mix"]["rel_err"][slow]])
     slow_int4 = np.mean([x[-1] for x in e["int4"]["rel_err"][slow]])
     assert slow_mix < slow_int4 / 2
+
+
+def test_int8_beats_e4m3_at_the_same_bits():
+    """Value-row-scaled int8 keeps a uniform grid down to zero; E4M3 spends
+    bits on an exponent, so its grid is coarse at the large values a row
+    scale maps near 448.  Over the horizon int8 accumulates less error."""
+    log("case: harness int8 vs E4M3, stochastic, decay in [0.9, 1), T=512")
+    e8 = np.mean([e[-1] for e in _run(2, 0.9, 1.0, SR, T=512)["rel_err"]])
+    ef = np.mean([e[-1] for e in _run(5, 0.9, 1.0, SR, T=512)["rel_err"]])
+    log(f"int8 {e8:.4f} fp8 {ef:.4f}")
+    assert e8 < ef

@@ -30,7 +30,7 @@ def test_c1_all_steps_int8():
     s.check()
 
 
-@pytest.mark.parametrize("prec", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("prec", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("delta", [0, 1])
 def test_small_each_precision(prec, delta):
     w = C1.scaled(B=2, H=3, T=12, delta=delta)
@@ -43,19 +43,20 @@ def test_small_each_precision(prec, delta):
 @pytest.mark.parametrize("dk,dv", [(96, 100), (32, 1), (128, 65), (64, 128)])
 @pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
 def test_ragged_mixed_precisions(dk, dv, decay):
-    w = C1.scaled(B=3, H=5, dk=dk, dv=dv, T=5, decay=decay)
-    log(f"case: ragged mixed B=3 H=5 dk={dk} dv={dv} decay={decay} heads fp32/bf16/int8/int4/int6")
-    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3, 4], init="random")
+    w = C1.scaled(B=3, H=6, dk=dk, dv=dv, T=5, decay=decay)
+    log(f"case: ragged mixed B=3 H=6 dk={dk} dv={dv} decay={decay} "
+        "heads fp32/bf16/int8/int4/int6/fp8")
+    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3, 4, 5], init="random")
     log(s.summary())
     s.check()
 
 
 @pytest.mark.parametrize("delta", [0, 1])
 def test_nearest_rounding_each_precision(delta):
-    w = C1.scaled(B=3, H=5, dk=128, dv=80, T=6, delta=delta, decay="kda_channel")
-    log(f"case: round-to-nearest mode B=3 H=5 d_k=128 d_v=80 delta={delta}, "
-        "heads fp32/bf16/int8/int4/int6")
-    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3, 4], init="random", rounding="nearest")
+    w = C1.scaled(B=3, H=6, dk=128, dv=80, T=6, delta=delta, decay="kda_channel")
+    log(f"case: round-to-nearest mode B=3 H=6 d_k=128 d_v=80 delta={delta}, "
+        "heads fp32/bf16/int8/int4/int6/fp8")
+    s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3, 4, 5], init="random", rounding="nearest")
     log(s.summary())
     s.check()
 

@@ -62,3 +62,15 @@ def test_int6_bit_positions():
     val = lambda j: int(sum(int(bits[6 * j + i]) << i for i in range(6)))
     assert val(21) == 63 and val(5) == 1 and val(0) == 32 and val(95) == 32
     assert not bits[576:].any()
+
+
+def test_fp8_bytes_roundtrip():
+    dk, dv = 64, 70
+    g = np.random.default_rng(3)
+    by = g.integers(0, 256, (dv, dk)).astype(np.uint8)
+    sc = np.linspace(0.1, 3, dv).astype(np.float32)
+    packed, psc = lc.pack_unit(5, dk, dv, 128, {"fp8": by, "scales": sc})
+    assert packed.size == 128 * dk
+    back = lc.unpack_unit(5, dk, dv, 128, packed, psc)
+    assert np.array_equal(back["fp8"], by) and np.array_equal(back["scales"], sc)
+    assert packed.reshape(dk // 16, 128, 16)[1, 3, 5] == by[3, 16 + 5]   # chunk 1, row 3, byte 5

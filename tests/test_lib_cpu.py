@@ -38,21 +38,21 @@ def test_library_exports_every_declared_symbol(lores_lib):
 
 
 def test_spec_version(lores_lib):
-    assert lores.lores_spec_version() == 2
+    assert lores.lores_spec_version() == 3
 
 
 def _layout_bytes(B, H, dk, dv, head_prec):
     """Segment sizes as include/lores.h documents them."""
-    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6}
+    bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}
     dvp = (dv + 63) // 64 * 64
     off = 0
-    for c in range(5):
+    for c in range(6):
         hc = sum(1 for p in head_prec if p == c)
         if not hc:
             continue
         off = (off + 255) // 256 * 256
         off += B * hc * -(-(dk * bits[c]) // 128) * 16 * dvp     # whole 16-byte chunks per row
-        if c in (2, 3, 4):
+        if c in (2, 3, 4, 5):                      # one fp32 scale per value row
             off = (off + 255) // 256 * 256
             off += B * hc * dvp * 4
     return (off + 255) // 256 * 256
@@ -62,7 +62,7 @@ def _layout_bytes(B, H, dk, dv, head_prec):
     (1, 2, 64, 64, [2, 2]), (64, 32, 128, 128, [2] * 32), (256, 128, 128, 64, [2] * 128),
     (128, 32, 128, 128, [1] * 8 + [2] * 24), (2048, 32, 128, 128, [2] * 16 + [3] * 16),
     (3, 4, 96, 100, [0, 1, 2, 3]), (1, 1, 32, 1, [3]), (2048, 32, 128, 128, [4] * 16 + [3] * 16),
-    (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4])])
+    (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4]), (4, 6, 64, 100, [5, 4, 3, 2, 1, 0])])
 def test_size_query_matches_documented_layout(lores_lib, B, H, dk, dv, prec):
     assert lores.lores_state_alloc(B, H, dk, dv, prec) == _layout_bytes(B, H, dk, dv, prec)
 

@@ -215,3 +215,88 @@ def test_nearest_mode_bf16_is_round_to_nearest():
                  F32)
     got = step.quantize_rows(x, step.PREC_BF16, rounding="nearest")["bits"][0, 0]
     assert list(got) == [0x3F81, 0xBF82]
+
+
+# ---------------------------------------------------------------------------
+# E4M3 (fp8) heads
+# ---------------------------------------------------------------------------
+def _e4m3_values():
+    """Every finite E4M3 byte and its value, enumerated from the format's
+    definition (sign, 4-bit exponent with bias 7, 3-bit mantissa,
+    exponent 0 = subnormal, S.1111.111 = NaN)."""
+    out = {}
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue
+        v = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+        out[b] = -v if s else v
+    return out
+
+
+def test_e4m3_decode_matches_the_format():
+    table = _e4m3_values()
+    got = step.e4m3_decode(np.arange(256))
+    for b, v in table.items():
+        assert Fraction(float(got[b])) == v, b
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert max(table.values()) == 448
+
+
+def test_e4m3_encode_is_exact_on_the_grid_and_never_overflows():
+    table = _e4m3_values()
+    bytes_ = np.array(sorted(table), np.int64)
+    vals = step.e4m3_decode(bytes_)
+    for n in (0, 1 << 15, 65535):
+        enc = step.e4m3_encode(vals, np.full(vals.shape, n, np.uint32))
+        back = step.e4m3_decode(enc)
+        assert np.array_equal(back, vals) or np.array_equal(np.abs(back), np.abs(vals))
+    # the largest magnitude never rounds past 448, whatever the draw
+    enc = step.e4m3_encode(np.array([448.0, -448.0, 447.99], np.float32), np.full(3, 65535, np.uint32))
+    assert np.all(np.abs(step.e4m3_decode(enc)) <= 448)
+
+
+def test_e4m3_sr_exhaustive_probability():
+    """For values across the normal and subnormal ranges and the boundary,
+    the 2^16 draws round to the two neighbouring grid values with P(up) equal
+    to the position between them, within 2^-16."""
+    grid = sorted(set(abs(v) for v in _e4m3_values().values()))
+    g = np.random.default_rng(44)
+    xs = [Fraction(1, 1024) * 3 + Fraction(1, 5000), Fraction(1, 64) - Fraction(1, 100000),
+          Fraction(1, 64) + Fraction(1, 3000), Fraction(3, 7), Fraction(300, 1)]
+    xs += [Fraction(float(x)) for x in g.uniform(0, 448, 6)]
+    for x in xs:
+        xf = np.float32(float(x))
+        if float(xf) > 448:
+            continue
+        for sgn in (1, -1):
+            y = np.full(65536, sgn * xf, np.float32)
+            vals = step.e4m3_decode(step.e4m3_encode(y, np.arange(65536, dtype=np.uint32)))
+            ax = Fraction(float(abs(xf)))
+            lo = max(v for v in grid if v <= ax)
+            hi = min(v for v in grid if v >= ax)
+            got = set(Fraction(float(abs(v))) for v in np.unique(np.abs(vals)))
+            assert got <= {lo, hi}, (x, got)
+            if hi == lo:
+                continue
+            p_up = Fraction(int((np.abs(vals) == np.float32(float(hi))).sum()), 65536)
+            assert abs(p_up - (ax - lo) / (hi - lo)) <= Fraction(2, 65536), (float(ax), float(p_up))
+            assert np.all(np.sign(vals[vals != 0]) == sgn)
+
+
+def test_fp8_rows_scale_to_448_and_round_to_nearest():
+    g = np.random.default_rng(45)
+    U = (g.standard_normal((20, 8, 64)) * np.exp(g.uniform(-5, 5, (20, 8, 1)))).astype(F32)
+    st = step.quantize_rows(U, step.PREC_FP8, rounding="nearest")
+    X = step.dequant(step.PREC_FP8, st)
+    m = np.abs(U).max(axis=2)
+    assert np.array_equal(st["scales"], exact.rn_div32(m, F32(448)))
+    vals = step.e4m3_decode(st["fp8"]).astype(np.float64)
+    inv = exact.rd_div32(F32(448), m).astype(np.float64)
+    y = U.astype(np.float64) * inv[:, :, None]
+    # nearest: within half of the local grid spacing (E4M3 keeps 3 mantissa bits)
+    spacing = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(vals), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(vals - y) <= 0.5 * spacing * (1 + 1e-6) + 2.0 ** -24 * np.abs(y))
+    # every nonzero row reaches 448 (its maximum maps there)
+    assert np.all(np.abs(vals).max(axis=2) == 448)
+    assert X.dtype == np.float32
