@@ -208,10 +208,10 @@ def main(argv=None):
     args = parse(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the decode step has no cross-GPU exchange and its sharding "
-              "is described in DESIGN.md, but runs on more than one GPU are not part of it.",
-              file=sys.stderr, flush=True)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the decode step exchanges nothing between GPUs, so a sharded run is this "
+              "single-GPU step on each GPU's share of sequences or heads, and multi-GPU "
+              "runs are not supported here.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch

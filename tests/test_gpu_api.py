@@ -193,6 +193,45 @@ def test_repeatable_eager_and_graph():
         assert all(torch.equal(a, b) for a, b in zip(outs, ref_o)), rep
 
 
+def test_two_states_on_two_streams():
+    """Two independent states stepped concurrently on two streams give the
+    bytes and outputs of the same steps run one after the other: the library
+    keeps no state outside its handles and launches on the stream it is given."""
+    log("case: two states, two streams, 6 steps each, int8/int4 and bf16/int6")
+    cfg = [(64, [2, 3] * 8, 128, 128), (48, [1, 4] * 6, 64, 96)]
+    runs = {}
+    for mode in ("sequential", "concurrent"):
+        states, outs, inps = [], [], []
+        for i, (B, prec, dk, dv) in enumerate(cfg):
+            w = C1.scaled(B=B, H=len(prec), dk=dk, dv=dv, T=6)
+            inps.append(make_inputs(w, 10 + i, DEV))
+            st = lores.lores_state_alloc(B, len(prec), dk, dv, prec, device=DEV)
+            _install(st, _random_states(B, prec, dv, dk, seed=20 + i))
+            states.append((st, w))
+            outs.append([torch.empty((B, len(prec), dv), device=DEV) for _ in range(w.T)])
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+        def run(i):
+            st, w = states[i]
+            for t in range(1, w.T + 1):
+                x = {k: v[t - 1] for k, v in inps[i].items()}
+                lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1,
+                                        3, t, o=outs[i][t - 1], stream=streams[i])
+        if mode == "sequential":
+            run(0)
+            torch.cuda.synchronize()
+            run(1)
+        else:
+            run(0)
+            run(1)
+        torch.cuda.synchronize()
+        runs[mode] = ([st.buf.clone() for st, _ in states], [[o.clone() for o in oo] for oo in outs])
+    for i in range(2):
+        assert torch.equal(runs["sequential"][0][i], runs["concurrent"][0][i]), i
+        assert all(torch.equal(a, b) for a, b in zip(runs["sequential"][1][i], runs["concurrent"][1][i]))
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 128), (96, 65), (32, 1), (64, 200)])
 def test_dequant_matches_oracle(dk, dv):
     """lores_dequant_state of a packed state (written through the codec)
