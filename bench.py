@@ -32,15 +32,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-updates/s (B*H*steps) and achieved HBM GB/s vs peak, quantized decode"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCES = ["lores_step_impl.h", "lores_internal.h", "lores_step_fp32.hip",
-                  "lores_step_bf16.hip", "lores_step_int8.hip", "lores_step_int4.hip",
-                  "lores_step_int8_int4.hip", "lores_step_bf16_int8.hip", "lores_step_bf16_int4.hip"]
+CSRC = os.path.join(ROOT, "quantized_linear_recurrence_amd", "csrc")
 
 
 def kernel_source_hash():
+    """Hash of the step kernel's sources (its header and every step
+    translation unit): a stored HBM byte count is used only while it matches."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "quantized_linear_recurrence_amd", "csrc", f), "rb") as fh:
+    names = sorted(f for f in os.listdir(CSRC) if f.startswith("lores_step") or f == "lores_internal.h")
+    for f in names:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 

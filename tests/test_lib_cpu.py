@@ -38,7 +38,9 @@ def test_library_exports_every_declared_symbol(lores_lib):
 
 
 def test_spec_version(lores_lib):
-    assert lores.lores_spec_version() == 3
+    hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
+    v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 3
 
 
 def _layout_bytes(B, H, dk, dv, head_prec):
