@@ -11,7 +11,10 @@ beta_t and delta in {0, 1}.  LoReS stores S quantized and, every step,
 dequantizes -> updates -> requantizes it ([LoReS] "Intra-State Quantization
 Approach", property 3), with one scale per value row ([LoReS] Section 4,
 scale grouping and Proposition 1: s_G = max |S_G| / r, r = 2^(b-1) - 1) and
-stochastic rounding ([LoReS] Section 4, Rounding).
+stochastic rounding ([LoReS] Section 4, Rounding).  The comparison grouping
+of the same section, one scale per key column (axis="key"), is the same
+quantizer with the group G taken down a column instead of along a row; the
+PACE abstract argues for it at four bits.
 
 reference_step64 is the recurrence itself in fp64 matrix form.  decode_step
 is the same recurrence in the row form a kernel evaluates, with every fp32
@@ -20,6 +23,7 @@ repository's design notes):
 
   1  a_ij  = fl(s_i * alpha_j);  S'_ij = fl(c_ij * a_ij)          int heads
      S'_ij = fl(v_ij * a_ij), v_ij the E4M3 value                 fp8 heads
+     (key-column scales: a_ij = fl(s_j * alpha_j), the same otherwise)
      S'_ij = fl(X_ij * alpha_j)                                   bf16 / fp32 heads
   2  delta = 1: r_i = fl(sum_j S'_ij k_j);  g_i = fl(beta * fl(v_i - r_i))
      delta = 0: g_i = fl(beta * v_i)
@@ -36,6 +40,8 @@ repository's design notes):
        in one rounding;  e_ij = floor(z_ij);  c'_ij = e_ij - B  in [-r, r]
      bf16 heads: bf16 bits of (f32bits(U_ij) + n_ij) >> 16   (rounding by noise)
      fp32 heads: X'_ij = U_ij
+     (key-column scales: m_j = max_i |U_ij| over the unit's d_v rows, and
+      s'_j, inv_j from m_j; the draws n_ij are the same)
 The dot products in 2 and 4 are accumulated in fp64 and rounded once.
 """
 import numpy as np
@@ -48,6 +54,20 @@ PREC_FP32, PREC_BF16, PREC_INT8, PREC_INT4, PREC_INT6, PREC_FP8 = 0, 1, 2, 3, 4,
 QMAX = {PREC_INT8: 127, PREC_INT4: 7, PREC_INT6: 31}
 BIAS = {PREC_INT8: 128, PREC_INT4: 136, PREC_INT6: 160}
 FP8_MAX = 448.0          # largest finite E4M3 value
+AXES = ("value", "key")  # one scale per value row / per key column
+SCALED = (PREC_INT8, PREC_INT4, PREC_INT6, PREC_FP8)
+
+
+def _check_axis(axis):
+    if axis not in AXES:
+        raise ValueError(f"axis must be 'value' or 'key', got {axis!r}")
+
+
+def _spread(scales, axis):
+    """Scales [N, d_v] (value rows) or [N, d_k] (key columns) shaped to
+    broadcast against states [N, d_v, d_k]."""
+    _check_axis(axis)
+    return scales[:, :, None] if axis == "value" else scales[:, None, :]
 
 
 # ---------------------------------------------------------------------------
@@ -112,23 +132,25 @@ def transition64(k, alpha, beta, delta):
 # ---------------------------------------------------------------------------
 # state containers
 # ---------------------------------------------------------------------------
-def zero_state(prec, n, dv, dk):
+def zero_state(prec, n, dv, dk, axis="value"):
+    _check_axis(axis)
+    ns = dv if axis == "value" else dk
     if prec == PREC_FP8:
-        return {"fp8": np.zeros((n, dv, dk), np.uint8), "scales": np.zeros((n, dv), F32)}
+        return {"fp8": np.zeros((n, dv, dk), np.uint8), "scales": np.zeros((n, ns), F32)}
     if prec in QMAX:
-        return {"codes": np.zeros((n, dv, dk), np.int32), "scales": np.zeros((n, dv), F32)}
+        return {"codes": np.zeros((n, dv, dk), np.int32), "scales": np.zeros((n, ns), F32)}
     if prec == PREC_BF16:
         return {"bits": np.zeros((n, dv, dk), np.uint16)}
     return {"X": np.zeros((n, dv, dk), F32)}
 
 
-def dequant(prec, state):
+def dequant(prec, state, axis="value"):
     """Stored state as fp32 values: fl(s_i * c_ij) for int heads, fl(s_i *
-    E4M3 value) for fp8 heads, exact otherwise."""
+    E4M3 value) for fp8 heads (s_j with key-column scales), exact otherwise."""
     if prec == PREC_FP8:
-        return (state["scales"][:, :, None] * e4m3_decode(state["fp8"])).astype(F32)
+        return (_spread(state["scales"], axis) * e4m3_decode(state["fp8"])).astype(F32)
     if prec in QMAX:
-        return (state["scales"][:, :, None] * state["codes"].astype(F32)).astype(F32)
+        return (_spread(state["scales"], axis) * state["codes"].astype(F32)).astype(F32)
     if prec == PREC_BF16:
         return exact.bf16_to_f32(state["bits"])
     return f32(state["X"]).copy()
@@ -137,8 +159,10 @@ def dequant(prec, state):
 # ---------------------------------------------------------------------------
 # requantization
 # ---------------------------------------------------------------------------
-def quantize_rows(U, prec, n=None, rounding="sr"):
-    """Requantize U [N, dv, dk] (fp32) with one fresh scale per value row.
+def quantize_rows(U, prec, n=None, rounding="sr", axis="value"):
+    """Requantize U [N, dv, dk] (fp32) with one fresh scale per value row
+    (axis="value") or per key column (axis="key": the maximum runs over the
+    d_v rows of each column).
 
     n: noise draws [N, dv, dk] (uint32 < 2^16), needed for rounding="sr".
     rounding="nearest" is the same quantizer with every draw fixed at 2^15
@@ -149,6 +173,8 @@ def quantize_rows(U, prec, n=None, rounding="sr"):
     Returns the new state dict.
     """
     U = f32(U)
+    _check_axis(axis)
+    gaxis = 2 if axis == "value" else 1           # the axis a scale group runs along
     if rounding == "nearest":
         n = np.full(U.shape, 1 << 15, dtype=np.uint32)
         rounding = "sr"
@@ -156,22 +182,22 @@ def quantize_rows(U, prec, n=None, rounding="sr"):
         # the row maximum maps to the largest E4M3 value
         if rounding != "sr":
             raise ValueError(rounding)
-        m = np.max(np.abs(U), axis=2)
+        m = np.max(np.abs(U), axis=gaxis)
         scales = exact.rn_div32(m, F32(FP8_MAX))
         inv = exact.rd_div32(F32(FP8_MAX), m)
-        y = (U * inv[:, :, None]).astype(F32)
+        y = (U * _spread(inv, axis)).astype(F32)
         return {"fp8": e4m3_encode(y, n), "scales": scales}
     if prec in QMAX:
         r = QMAX[prec]
-        m = np.max(np.abs(U), axis=2)
+        m = np.max(np.abs(U), axis=gaxis)
         scales = exact.rn_div32(m, F32(r))
         inv = exact.rd_div32(F32(r), m)
         if rounding == "sr":
             bias = (F32(BIAS[prec]) + n.astype(F32) * F32(2.0 ** -16)).astype(F32)
-            z = fma32(U, inv[:, :, None], bias)
+            z = fma32(U, _spread(inv, axis), bias)
             codes = np.floor(z).astype(np.int32) - BIAS[prec]
         elif rounding == "rtn":
-            y = (U * inv[:, :, None]).astype(F32)
+            y = (U * _spread(inv, axis)).astype(F32)
             codes = np.rint(y).astype(np.int32)
         else:
             raise ValueError(rounding)
@@ -193,12 +219,13 @@ def quantize_rows(U, prec, n=None, rounding="sr"):
 # the decode step
 # ---------------------------------------------------------------------------
 def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
-                rounding="sr", noise="weyl"):
+                rounding="sr", noise="weyl", axis="value"):
     """One decode step for N units of one precision class.
 
     q, k [N, dk] and v [N, dv]: fp32 values (bf16 inputs converted exactly);
     alpha [N] (scalar decay) or [N, dk] (per key channel); beta [N];
     b, h [N]: global sequence and head indices (they key the noise).
+    axis: "value" (one scale per value row) or "key" (one per key column).
     Returns (new_state, o [N, dv]).
     """
     q, k, v, beta = f32(q), f32(k), f32(v), f32(beta)
@@ -209,10 +236,10 @@ def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
 
     # 1  dequantize and decay (key columns)
     if prec == PREC_FP8:
-        a = (state["scales"][:, :, None] * a_row).astype(F32)
+        a = (_spread(state["scales"], axis) * a_row).astype(F32)
         Sp = (e4m3_decode(state["fp8"]) * a).astype(F32)
     elif prec in QMAX:
-        a = (state["scales"][:, :, None] * a_row).astype(F32)
+        a = (_spread(state["scales"], axis) * a_row).astype(F32)
         Sp = (state["codes"].astype(F32) * a).astype(F32)
     else:
         Sp = (dequant(prec, state) * a_row).astype(F32)
@@ -230,15 +257,15 @@ def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
     # 4  readout from the updated state
     o = exact.dot_rn32(U, q)
 
-    # 5  requantize with fresh row scales
+    # 5  requantize with fresh scales
     n = None
     if prec != PREC_FP32 and rounding == "sr":  # "nearest" and "rtn" need no draws
         K = unit_key(seed, t, b, h)
         n = (noise16 if noise == "weyl" else noise16_iid)(K, dv, dk)
-    return quantize_rows(U, prec, n, rounding), o
+    return quantize_rows(U, prec, n, rounding, axis), o
 
 
-def quant_state(prec, X, seed, b, h, rounding="sr"):
+def quant_state(prec, X, seed, b, h, rounding="sr", axis="value"):
     """Quantize fp32 states X [N, dv, dk] of one precision class: the
     requantization of a decode step applied to X itself, with draws keyed on
     step index 0 (decode steps use t >= 1).  b, h [N]: global indices.
@@ -250,11 +277,11 @@ def quant_state(prec, X, seed, b, h, rounding="sr"):
     n = None
     if prec != PREC_FP32 and rounding == "sr":
         n = noise16(unit_key(seed, 0, b, h), dv, dk)
-    return quantize_rows(X, prec, n, rounding)
+    return quantize_rows(X, prec, n, rounding, axis)
 
 
 def run_trajectory(prec, state, inputs, delta, seed, b, h, t0=1, rounding="sr",
-                   noise="weyl"):
+                   noise="weyl", axis="value"):
     """Apply decode_step for t = t0, t0+1, ... over inputs' leading time axis.
 
     inputs: dict of arrays q [T, N, dk], k, v [T, N, dv], alpha [T, N(, dk)],
@@ -265,6 +292,6 @@ def run_trajectory(prec, state, inputs, delta, seed, b, h, t0=1, rounding="sr",
     for s in range(T):
         state, o = decode_step(prec, state, inputs["q"][s], inputs["k"][s], inputs["v"][s],
                                inputs["alpha"][s], inputs["beta"][s], delta, seed, t0 + s,
-                               b, h, rounding=rounding, noise=noise)
+                               b, h, rounding=rounding, noise=noise, axis=axis)
         outs.append(o)
     return state, np.stack(outs)

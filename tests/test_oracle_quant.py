@@ -122,15 +122,6 @@ def test_mean_over_seeds_is_unbiased(prec):
     assert np.abs(z[nz]).max() < 5.5, np.abs(z[nz]).max()
 
 
-def _rtn_keyaxis(U, r):
-    """Round-to-nearest with one scale per key column (the comparison of Proposition 1)."""
-    C = np.max(np.abs(U), axis=1, keepdims=True).astype(F32)
-    s = (C / F32(r)).astype(F32)
-    inv = exact.rd_div32(F32(r), C)
-    codes = np.rint((U * inv).astype(F32))
-    return (codes * s).astype(F32)
-
-
 def test_proposition1_readout_error_variances():
     g = np.random.default_rng(14)
     N, dv, dk, r = 400, 32, 64, 127
@@ -147,7 +138,8 @@ def test_proposition1_readout_error_variances():
     ratio_val = np.mean(e_val ** 2) / np.mean(M ** 2 / (12 * r * r))
     assert abs(ratio_val - 1) < 0.05, ratio_val
 
-    key = _rtn_keyaxis(U, r)
+    key = step.dequant(step.PREC_INT8, step.quantize_rows(U, step.PREC_INT8, rounding="rtn",
+                                                          axis="key"), axis="key")
     e_key = np.einsum("nij,nj->ni", (key - U).astype(np.float64), q)
     pred_key = np.einsum("nj,nj->n", q ** 2, C ** 2)[:, None] / (12 * r * r)
     ratio_key = np.mean(e_key ** 2) / np.mean(np.broadcast_to(pred_key, e_key.shape))
