@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 3
+#define LORES_SPEC_VERSION 4
 
 /* Per-head state precision. */
 enum {
@@ -57,6 +57,16 @@ enum {
 enum {
     LORES_ROUND_STOCHASTIC = 0, /* default: the counter-based draw n below              */
     LORES_ROUND_NEAREST = 1     /* the same quantizer with the draw fixed at n = 2^15 */
+};
+
+/* Scale grouping of the scaled classes (int8, int4, int6, fp8), fixed when
+ * the state is allocated (lores_state_alloc_axis).  The pages compare one
+ * scale per value row with one per key column ("Intra-State Quantization
+ * (Section 4)", Scale Grouping and Proposition 1); value rows are their
+ * choice and the default here. */
+enum {
+    LORES_SCALE_VALUE = 0, /* one fp32 scale per value row: s_i = max_j |S_ij| / r  */
+    LORES_SCALE_KEY = 1    /* one fp32 scale per key column: s_j = max_i |S_ij| / r */
 };
 
 /* Status codes. */
@@ -86,6 +96,7 @@ typedef struct lores_state lores_state;
  *
  *   codes  [B][H_c][n_chunk][d_v_pad][16 bytes]
  *   scales [B][H_c][d_v_pad] fp32                 (int8, int4, int6, fp8 classes)
+ *          [B][H_c][d_k] fp32                     (the same, key-column scales)
  *
  * H_c = heads of class c, ordered by head index (head_slot below).
  * d_v_pad = d_v rounded up to LORES_ROW_BLOCK; padding rows are never read
@@ -103,8 +114,9 @@ typedef struct lores_state lores_state;
  * holds row bytes 16c .. 16c + 15): element j is bits 6j .. 6j + 5, value
  * code + 32 (offset binary, 1..63); n_chunk = ceil(6 d_k / 128), the bits
  * after the last element are zero.
- * The value of an int element is scale[row] * code.  A row of all-zero bytes
- * with scale 0 also reads as zero, so a zero-filled buffer is S = 0.
+ * The value of an int element is scale[row] * code (scale[column] * code
+ * with key-column scales).  A row of all-zero bytes with scale 0 also reads
+ * as zero, so a zero-filled buffer is S = 0.
  */
 typedef struct {
     int32_t B, H, d_k, d_v, d_v_pad;
@@ -113,6 +125,8 @@ typedef struct {
     int64_t scales_offset[LORES_NUM_PREC];  /* byte offset of class scales, -1  */
     int64_t unit_code_bytes[LORES_NUM_PREC];/* code bytes per (sequence, head)  */
     uint64_t total_bytes;      /* bytes the caller's buffer must hold           */
+    int32_t scale_axis;        /* LORES_SCALE_VALUE or LORES_SCALE_KEY          */
+    int32_t unit_scales;       /* fp32 scales per (sequence, head): d_v_pad or d_k */
 } lores_layout;
 
 /*
@@ -132,6 +146,24 @@ typedef struct {
 int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                       const uint8_t *head_prec, void *d_buf, size_t *bytes,
                       void *stream, lores_state **out);
+
+/*
+ * lores_state_alloc_axis - lores_state_alloc with a choice of scale grouping
+ * for every scaled head (int8, int4, int6, fp8): LORES_SCALE_VALUE is
+ * lores_state_alloc itself; LORES_SCALE_KEY keeps one scale per key column,
+ * s_j = fl(m_j / r) with m_j the maximum of |S_ij| over the unit's d_v rows,
+ * and the same codes, rounding and draws otherwise (the comparison grouping
+ * of "Intra-State Quantization (Section 4)", Scale Grouping and Proposition
+ * 1).  A step then dequantizes S'_ij = fl(c_ij * fl(s_j * alpha_j)).
+ * LORES_SCALE_KEY is built for d_k in {64, 128} and d_v in [1, 128] or
+ * [193, 256] (a unit's row blocks must share one work-group of four
+ * wavefronts); other shapes return LORES_EUNSUPPORTED.  A key-column state
+ * runs one launch per precision class (no fused pairs).  LORES_EINVAL for
+ * any other scale_axis.
+ */
+int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                           const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
+                           size_t *bytes, void *stream, lores_state **out);
 
 void lores_state_free(lores_state *st);
 
@@ -221,13 +253,14 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
  * lores_step_launches - kernel launches one lores_decode_step on `st`
  * enqueues (host out *n): one per precision class present, except that the
  * pairs (int8, int4), (int4, int6), (bf16, int8) and (bf16, int4) share a
- * single launch.
+ * single launch when the state keeps value-row scales.
  */
 int lores_step_launches(const lores_state *st, int32_t *n);
 
 /*
  * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32,
- * value = scale * code for int heads, the stored value for bf16 / fp32 heads.
+ * value = scale * code for int heads (the row's or the column's scale), the
+ * stored value for bf16 / fp32 heads.
  */
 int lores_dequant_state(const lores_state *st, float *out, void *stream);
 
@@ -235,7 +268,8 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream);
  * lores_quant_state - fp32 state -> packed state of `st`, in place of its
  * contents: the requantization of lores_decode_step applied to X itself
  * (int heads: fresh row scale and codes; bf16 heads: rounded; fp32 heads:
- * copied), with the state's rounding mode and draws keyed on step index 0,
+ * copied; key-column states take the column maxima of X), with the state's
+ * rounding mode and draws keyed on step index 0,
  * which lores_decode_step never uses (t >= 1).  This hands a state built
  * elsewhere (a prefill, a checkpoint) to decoding: S_0 = Q(X).
  * ("Intra-State Quantization Approach": the state is held quantized between

@@ -15,13 +15,14 @@ import numpy as np
 
 from . import _lib
 from ._lib import (LORES_BF16, LORES_FP8, LORES_FP32, LORES_INT4, LORES_INT6, LORES_INT8,
-                   LORES_ROUND_NEAREST,
-                   LORES_ROUND_STOCHASTIC, LoresLayout, LoresLibraryMissing)
+                   LORES_ROUND_NEAREST, LORES_ROUND_STOCHASTIC, LORES_SCALE_KEY,
+                   LORES_SCALE_VALUE, LoresLayout, LoresLibraryMissing)
 
 __all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LORES_INT6", "LORES_FP8",
-           "LORES_ROUND_STOCHASTIC",
-           "LORES_ROUND_NEAREST", "LoresError", "lores_state_set_rounding",
-           "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_layout",
+           "LORES_ROUND_STOCHASTIC", "LORES_ROUND_NEAREST", "LORES_SCALE_VALUE", "LORES_SCALE_KEY",
+           "LoresError", "lores_state_set_rounding",
+           "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_alloc_axis",
+           "lores_state_layout",
            "lores_state_head_map", "lores_decay_stat", "lores_assign_precision",
            "lores_decode_step", "lores_step_launches", "lores_quant_state", "lores_dequant_state",
            "lores_last_error", "lores_spec_version"]
@@ -80,13 +81,14 @@ class LoresState:
     is freed when this object is garbage-collected.
     """
 
-    def __init__(self, handle, buf, B, H, d_k, d_v, head_prec):
+    def __init__(self, handle, buf, B, H, d_k, d_v, head_prec, scale_axis=LORES_SCALE_VALUE):
         self._h = handle
         self.buf = buf
         self.device = buf.device
         self.B, self.H, self.d_k, self.d_v = B, H, d_k, d_v
         self.head_prec = list(head_prec)
         self.rounding = LORES_ROUND_STOCHASTIC
+        self.scale_axis = scale_axis
 
     @property
     def handle(self):
@@ -102,19 +104,23 @@ class LoresState:
             self._h = None
 
 
-def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=None):
+def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=None,
+                      scale_axis=LORES_SCALE_VALUE):
     """Plan the packed layout; size query if device and buf are both None.
 
     Returns the byte size (size query) or a LoresState whose buffer (a new
     torch uint8 tensor on `device`, or the given `buf`) is cleared to S_0 = 0
-    on `stream`.
+    on `stream`.  scale_axis: LORES_SCALE_VALUE (one scale per value row,
+    lores_state_alloc) or LORES_SCALE_KEY (one per key column,
+    lores_state_alloc_axis).
     """
     L = _lib.lib()
     hp, hp_ptr = _host_array(head_prec, np.uint8)
     if hp.size != H:
         raise ValueError(f"head_prec must have H = {H} entries")
     nbytes = ctypes.c_size_t(0)
-    _check(L.lores_state_alloc(B, H, d_k, d_v, hp_ptr, None, ctypes.byref(nbytes), None, None))
+    _check(L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis), None,
+                                    ctypes.byref(nbytes), None, None))
     if device is None and buf is None:
         return nbytes.value
     import torch
@@ -123,9 +129,13 @@ def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=N
     device = buf.device
     size = ctypes.c_size_t(buf.numel() * buf.element_size())
     out = ctypes.c_void_p()
-    _check(L.lores_state_alloc(B, H, d_k, d_v, hp_ptr, ctypes.c_void_p(buf.data_ptr()),
-                               ctypes.byref(size), _stream_ptr(stream, device), ctypes.byref(out)))
-    return LoresState(out.value, buf, B, H, d_k, d_v, hp.tolist())
+    _check(L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis),
+                                    ctypes.c_void_p(buf.data_ptr()), ctypes.byref(size),
+                                    _stream_ptr(stream, device), ctypes.byref(out)))
+    return LoresState(out.value, buf, B, H, d_k, d_v, hp.tolist(), int(scale_axis))
+
+
+lores_state_alloc_axis = lores_state_alloc
 
 
 def lores_state_layout(state):
@@ -134,7 +144,8 @@ def lores_state_layout(state):
     return {"B": lay.B, "H": lay.H, "d_k": lay.d_k, "d_v": lay.d_v, "d_v_pad": lay.d_v_pad,
             "n_class": list(lay.n_class), "codes_offset": list(lay.codes_offset),
             "scales_offset": list(lay.scales_offset),
-            "unit_code_bytes": list(lay.unit_code_bytes), "total_bytes": lay.total_bytes}
+            "unit_code_bytes": list(lay.unit_code_bytes), "total_bytes": lay.total_bytes,
+            "scale_axis": lay.scale_axis, "unit_scales": lay.unit_scales}
 
 
 def lores_state_head_map(state):

@@ -24,6 +24,7 @@ struct lores_state {
     uint64_t total;
     uint8_t *base;
     int32_t rounding;        // LORES_ROUND_*
+    int32_t axis;            // LORES_SCALE_*
 };
 
 namespace {
@@ -73,7 +74,12 @@ int check_dims(int32_t B, int32_t H, int32_t dk, int32_t dv) {
     return LORES_OK;
 }
 
-// Fill st's layout from its dimensions and head_prec; returns status.
+// fp32 scales per (sequence, head) unit of a scaled class
+int64_t unit_scales(const lores_state *st) {
+    return st->axis == LORES_SCALE_KEY ? st->dk : st->dv_pad;
+}
+
+// Fill st's layout from its dimensions, head_prec and axis; returns status.
 int plan(lores_state *st, const uint8_t *head_prec) {
     std::memset(st->n_class, 0, sizeof st->n_class);
     for (int h = 0; h < st->H; ++h) {
@@ -99,7 +105,7 @@ int plan(lores_state *st, const uint8_t *head_prec) {
         if (has_scales(c)) {
             off = align256(off);
             st->scales_off[c] = (int64_t)off;
-            off += (uint64_t)st->B * st->n_class[c] * st->dv_pad * sizeof(float);
+            off += (uint64_t)st->B * st->n_class[c] * unit_scales(st) * sizeof(float);
         }
         // launch grid: y = sequence (at most 65535), x = groups of row-block tasks
     }
@@ -153,7 +159,17 @@ bool fusable_pair(int p0, int p1) {
 }
 
 hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, const StepPtrs &p,
-                       const StepMeta &m, hipStream_t s) {
+                       const StepMeta &m, hipStream_t s, bool key) {
+    if (key) {
+        if (p1 >= 0) return hipErrorInvalidValue;
+        switch (p0) {
+            case LORES_INT8: return launch_step_key_int8(dk, pc, delta, bf16, p, m, s);
+            case LORES_INT4: return launch_step_key_int4(dk, pc, delta, bf16, p, m, s);
+            case LORES_INT6: return launch_step_key_int6(dk, pc, delta, bf16, p, m, s);
+            case LORES_FP8: return launch_step_key_fp8(dk, pc, delta, bf16, p, m, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     if (p1 < 0) {
         switch (p0) {
             case LORES_FP32: return launch_step_fp32(dk, pc, delta, bf16, p, m, s);
@@ -180,13 +196,26 @@ const char *lores_last_error(void) { return g_err.c_str(); }
 
 int lores_spec_version(void) { return LORES_SPEC_VERSION; }
 
-int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint8_t *head_prec,
-                      void *d_buf, size_t *bytes, void *stream, lores_state **out) {
+int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                           const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
+                           size_t *bytes, void *stream, lores_state **out) {
     try {
         int rc = check_dims(B, H, d_k, d_v);
         if (rc) return rc;
         if (!head_prec) return fail(LORES_EINVAL, "head_prec is NULL");
         if (!bytes) return fail(LORES_EINVAL, "bytes is NULL");
+        if (scale_axis != LORES_SCALE_VALUE && scale_axis != LORES_SCALE_KEY)
+            return fail(LORES_EINVAL, "scale_axis must be LORES_SCALE_VALUE (0) or "
+                                      "LORES_SCALE_KEY (1), got %d", scale_axis);
+        if (scale_axis == LORES_SCALE_KEY) {
+            if (d_k != 64 && d_k != 128)
+                return fail(LORES_EUNSUPPORTED, "key-column scales are built for d_k = 64 and "
+                                                "128 (got %d)", d_k);
+            if (d_v > 128 && d_v <= 192)
+                return fail(LORES_EUNSUPPORTED, "key-column scales need d_v <= 128 or d_v > 192 "
+                                                "(three row blocks do not fill a work-group; got %d)",
+                            d_v);
+        }
         lores_state tmp;
         tmp.B = B;
         tmp.H = H;
@@ -194,6 +223,7 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         tmp.dv = d_v;
         tmp.base = nullptr;
         tmp.rounding = LORES_ROUND_STOCHASTIC;
+        tmp.axis = scale_axis;
         rc = plan(&tmp, head_prec);
         if (rc) return rc;
         if (!d_buf) {
@@ -220,6 +250,12 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
     }
 }
 
+int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint8_t *head_prec,
+                      void *d_buf, size_t *bytes, void *stream, lores_state **out) {
+    return lores_state_alloc_axis(B, H, d_k, d_v, head_prec, LORES_SCALE_VALUE, d_buf, bytes,
+                                  stream, out);
+}
+
 void lores_state_free(lores_state *st) { delete st; }
 
 int lores_state_layout(const lores_state *st, lores_layout *out) {
@@ -236,6 +272,8 @@ int lores_state_layout(const lores_state *st, lores_layout *out) {
         out->unit_code_bytes[c] = st->unit_bytes[c];
     }
     out->total_bytes = st->total;
+    out->scale_axis = st->axis;
+    out->unit_scales = (int32_t)unit_scales(st);
     return ok();
 }
 
@@ -325,7 +363,7 @@ static int plan_launches(const lores_state *st, int groups[LORES_NUM_PREC][2],
     int present[LORES_NUM_PREC], n = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c)
         if (st->n_class[c]) present[n++] = c;
-    if (n == 2 && lores::fusable_pair(present[0], present[1])) {
+    if (n == 2 && st->axis == LORES_SCALE_VALUE && lores::fusable_pair(present[0], present[1])) {
         groups[0][0] = present[0];
         groups[0][1] = present[1];
         width[0] = 2;
@@ -391,8 +429,9 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
                 p.scales[i] = has_scales(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
             }
             const int p1 = width[l] == 2 ? groups[l][1] : -1;
+            const bool key = st->axis == LORES_SCALE_KEY && has_scales(groups[l][0]);
             hipError_t e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16,
-                                              groups[l][0], p1, p, m, s);
+                                              groups[l][0], p1, p, m, s, key);
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "decode-step launch failed: %s", hipGetErrorString(e));
         }
@@ -420,7 +459,8 @@ int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t se
             m.head_base = head_base;
             float *sc = has_scales(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e = lores::launch_quant(c, st->dk, X, st->base + st->codes_off[c], sc, m,
-                                               (hipStream_t)stream);
+                                               (hipStream_t)stream,
+                                               st->axis == LORES_SCALE_KEY && has_scales(c));
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "quantize launch failed: %s", hipGetErrorString(e));
         }
@@ -439,7 +479,8 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
             lores::StepMeta m = make_meta(st, &c, 1);
             const float *sc = has_scales(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
-                                                 (hipStream_t)stream);
+                                                 (hipStream_t)stream,
+                                                 st->axis == LORES_SCALE_KEY && has_scales(c));
             if (e != hipSuccess) return fail(LORES_EHIP, "dequant launch failed: %s", hipGetErrorString(e));
         }
         return ok();

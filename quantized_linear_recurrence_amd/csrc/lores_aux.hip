@@ -8,7 +8,8 @@ namespace lores {
 
 // value = scale * code for int heads (fl of the product), the stored value
 // for bf16 / fp32 heads.  Same wavefront-per-64-rows mapping as the step.
-template <int DK, int PREC>
+// KEY: the scale of element j is the unit's key-column scale s_j.
+template <int DK, int PREC, bool KEY = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                      float *__restrict__ out, const StepMeta meta) {
@@ -30,7 +31,12 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     const long dv_pad = meta.dv_pad;
     const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * cd.unit_bytes) + row;
     float s = 0.0f;
-    if constexpr (has_scale<PREC>()) s = scales[unit * dv_pad + row];
+    if constexpr (has_scale<PREC>() && !KEY) s = scales[unit * dv_pad + row];
+    // the scale of element j (wave-uniform loads for key columns)
+    auto sc = [&](int j) {
+        if constexpr (KEY) return scales[unit * DK + j];
+        else return s;
+    };
     float *orow = out + (bh * meta.dv + row) * DK;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     if constexpr (PREC == LORES_INT6) {
@@ -41,7 +47,7 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
         for (int j = 0; j < DK; j += 4) {
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = s * ((float)int6_field(cw, j + e) - 32.0f);
+            for (int e = 0; e < 4; ++e) x[e] = sc(j + e) * ((float)int6_field(cw, j + e) - 32.0f);
             *reinterpret_cast<f32x4 *>(orow + j) = f32x4{x[0], x[1], x[2], x[3]};
         }
     } else {
@@ -53,13 +59,13 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 if constexpr (PREC == LORES_FP8) {
-                    x[e] = s * fp8_value(wd[e >> 2], e & 3);
+                    x[e] = sc(c * E + e) * fp8_value(wd[e >> 2], e & 3);
                 } else if constexpr (PREC == LORES_INT8) {
-                    x[e] = s * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
+                    x[e] = sc(c * E + e) * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
                 } else if constexpr (PREC == LORES_INT4) {
                     const uint32_t w = wd[e >> 3];
                     const uint32_t nib = (w >> (4 * (e & 7))) & 0xFu;
-                    x[e] = s * ((float)nib - 8.0f);
+                    x[e] = sc(c * E + e) * ((float)nib - 8.0f);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
                     x[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
@@ -77,7 +83,9 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 
 // fp32 rows -> packed rows of one class with the step's own requantization
 // (requantize_row), keyed at meta.t.  Same wavefront-per-64-rows mapping.
-template <int DK, int PREC>
+// KEY: key-column scales from the column maxima of the unit's rows (the
+// unit's row blocks are consecutive wavefronts of one work-group).
+template <int DK, int PREC, bool KEY = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
                    float *__restrict__ scales, const StepMeta meta) {
@@ -85,7 +93,10 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ClassDesc &cd = meta.cls[0];
     const int task = blockIdx.x * kWavesPerGroup + wv;
-    if (task >= cd.Hc * meta.n_rb) return;
+    if (task >= cd.Hc * meta.n_rb) {
+        if constexpr (KEY) lds_barrier();          // the work-group's one barrier
+        return;
+    }
     const int slot = task / meta.n_rb;
     const int rb = task - slot * meta.n_rb;
     const int b = blockIdx.y;
@@ -108,18 +119,40 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
         U[c + 2] = v.z;
         U[c + 3] = v.w;
     }
-#pragma unroll
-    for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
     u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * cd.unit_bytes) + row;
-    requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
-                             has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+    if constexpr (KEY) {
+        __shared__ float cmax[kWavesPerGroup * DK];
+        float cm[DK / 64], snew[DK / 16], inv[DK / 16];
+        col_absmax<DK>(U, cm);
+        key_scales<DK>(cm, cmax, wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv);
+        if (rb == 0 && lane < 16) {
+#pragma unroll
+            for (int i = 0; i < DK / 16; ++i) scales[unit * DK + 16 * i + lane] = snew[i];
+        }
+        requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr, inv);
+    } else {
+#pragma unroll
+        for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
+        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+                                 has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+    }
 }
 
 template <int PREC>
 static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scales,
-                             const StepMeta &m, hipStream_t s) {
+                             const StepMeta &m, hipStream_t s, bool key) {
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
+    if constexpr (has_scale<PREC>()) {
+        if (key) {
+            switch (dk) {
+                case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), grid, block, 0, s, X, codes, scales, m); break;
+                case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), grid, block, 0, s, X, codes, scales, m); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (dk) {
         case 32: hipLaunchKernelGGL((lores_quant_kernel<32, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC>), grid, block, 0, s, X, codes, scales, m); break;
@@ -131,23 +164,33 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
 }
 
 hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
-                        const StepMeta &m, hipStream_t s) {
+                        const StepMeta &m, hipStream_t s, bool key) {
     switch (prec) {
-        case LORES_FP32: return quant_prec<LORES_FP32>(dk, X, codes, scales, m, s);
-        case LORES_BF16: return quant_prec<LORES_BF16>(dk, X, codes, scales, m, s);
-        case LORES_INT8: return quant_prec<LORES_INT8>(dk, X, codes, scales, m, s);
-        case LORES_INT4: return quant_prec<LORES_INT4>(dk, X, codes, scales, m, s);
-        case LORES_INT6: return quant_prec<LORES_INT6>(dk, X, codes, scales, m, s);
-        case LORES_FP8: return quant_prec<LORES_FP8>(dk, X, codes, scales, m, s);
+        case LORES_FP32: return quant_prec<LORES_FP32>(dk, X, codes, scales, m, s, key);
+        case LORES_BF16: return quant_prec<LORES_BF16>(dk, X, codes, scales, m, s, key);
+        case LORES_INT8: return quant_prec<LORES_INT8>(dk, X, codes, scales, m, s, key);
+        case LORES_INT4: return quant_prec<LORES_INT4>(dk, X, codes, scales, m, s, key);
+        case LORES_INT6: return quant_prec<LORES_INT6>(dk, X, codes, scales, m, s, key);
+        case LORES_FP8: return quant_prec<LORES_FP8>(dk, X, codes, scales, m, s, key);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int PREC>
 static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales, float *out,
-                               const StepMeta &m, hipStream_t s) {
+                               const StepMeta &m, hipStream_t s, bool key) {
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
+    if constexpr (has_scale<PREC>()) {
+        if (key) {
+            switch (dk) {
+                case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (dk) {
         case 32: hipLaunchKernelGGL((lores_dequant_kernel<32, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC>), grid, block, 0, s, codes, scales, out, m); break;
@@ -159,14 +202,14 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
 }
 
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                          float *out, const StepMeta &m, hipStream_t s) {
+                          float *out, const StepMeta &m, hipStream_t s, bool key) {
     switch (prec) {
-        case LORES_FP32: return dequant_prec<LORES_FP32>(dk, codes, scales, out, m, s);
-        case LORES_BF16: return dequant_prec<LORES_BF16>(dk, codes, scales, out, m, s);
-        case LORES_INT8: return dequant_prec<LORES_INT8>(dk, codes, scales, out, m, s);
-        case LORES_INT4: return dequant_prec<LORES_INT4>(dk, codes, scales, out, m, s);
-        case LORES_INT6: return dequant_prec<LORES_INT6>(dk, codes, scales, out, m, s);
-        case LORES_FP8: return dequant_prec<LORES_FP8>(dk, codes, scales, out, m, s);
+        case LORES_FP32: return dequant_prec<LORES_FP32>(dk, codes, scales, out, m, s, key);
+        case LORES_BF16: return dequant_prec<LORES_BF16>(dk, codes, scales, out, m, s, key);
+        case LORES_INT8: return dequant_prec<LORES_INT8>(dk, codes, scales, out, m, s, key);
+        case LORES_INT4: return dequant_prec<LORES_INT4>(dk, codes, scales, out, m, s, key);
+        case LORES_INT6: return dequant_prec<LORES_INT6>(dk, codes, scales, out, m, s, key);
+        case LORES_FP8: return dequant_prec<LORES_FP8>(dk, codes, scales, out, m, s, key);
         default: return hipErrorInvalidValue;
     }
 }

@@ -46,7 +46,7 @@ struct StepPtrs {
 // (int4, int6), (bf16, int8), (bf16, int4); `p1` is -1 for a single class.  Returns the
 // launch status; `dk` is one of 32, 64, 96, 128.
 hipError_t launch_step(int dk, bool per_channel, bool delta, bool in_bf16, int p0, int p1,
-                       const StepPtrs &p, const StepMeta &m, hipStream_t s);
+                       const StepPtrs &p, const StepMeta &m, hipStream_t s, bool key = false);
 bool fusable_pair(int p0, int p1);
 
 // Per-translation-unit launchers behind launch_step.
@@ -60,12 +60,17 @@ hipError_t launch_step_int8_int4(int, bool, bool, bool, const StepPtrs &, const 
 hipError_t launch_step_int4_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_bf16_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_bf16_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+// key-column scales (one class per launch, d_k = 64 or 128)
+hipError_t launch_step_key_int8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_key_int4(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_key_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
+hipError_t launch_step_key_fp8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 
-// Dequant uses the same StepMeta with one class.
+// Dequant uses the same StepMeta with one class; `key`: key-column scales.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                          float *out, const StepMeta &m, hipStream_t s);
+                          float *out, const StepMeta &m, hipStream_t s, bool key);
 hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
-                        const StepMeta &m, hipStream_t s);
+                        const StepMeta &m, hipStream_t s, bool key);
 hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);
 
 // Tasks (one wavefront each) per 256-thread work-group.

@@ -355,6 +355,183 @@ __device__ __forceinline__ void mul16(float *x, float av) {
         : "v"(av));
 }
 
+// ---------------------------------------------------------------------------
+// key-column scales: one scale per key column of a (sequence, head) unit,
+// s_j = max_i |U_ij| / r over all d_v rows, the comparison grouping of the
+// pages' scale-grouping section.  The column maximum of a wavefront's 64
+// rows is a butterfly across lanes; the unit's row blocks (wavefronts of one
+// work-group) then combine theirs through LDS.  The column factors (s_j
+// alpha_j for the dequantization, r / m_j for the requantization) are row
+// vectors like k and q, consumed through DPP row_newbcast.
+// ---------------------------------------------------------------------------
+
+// z[e] += row element E0 + e of inv * u[e] for e < 4 (one rounding each)
+#define LORES_FMAC4(E0, E1, E2, E3)                                                          \
+    asm("s_nop 1\n"                                                                          \
+        "v_fmac_f32_dpp %0, %4, %5 row_newbcast:" #E0 " row_mask:0xf bank_mask:0xf\n"        \
+        "v_fmac_f32_dpp %1, %4, %6 row_newbcast:" #E1 " row_mask:0xf bank_mask:0xf\n"        \
+        "v_fmac_f32_dpp %2, %4, %7 row_newbcast:" #E2 " row_mask:0xf bank_mask:0xf\n"        \
+        "v_fmac_f32_dpp %3, %4, %8 row_newbcast:" #E3 " row_mask:0xf bank_mask:0xf\n"        \
+        : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3])                                    \
+        : "v"(inv), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]))
+__device__ __forceinline__ void fmac4_col(float *z, float inv, const float *u, int e0) {
+    switch (e0) {
+        case 0: LORES_FMAC4(0, 1, 2, 3); break;
+        case 4: LORES_FMAC4(4, 5, 6, 7); break;
+        case 8: LORES_FMAC4(8, 9, 10, 11); break;
+        default: LORES_FMAC4(12, 13, 14, 15); break;
+    }
+}
+#undef LORES_FMAC4
+
+// y[e] = row element E0 + e of inv * u[e] for e < 4
+#define LORES_MUL4(E0, E1, E2, E3)                                                           \
+    asm("s_nop 1\n"                                                                          \
+        "v_mul_f32_dpp %0, %4, %5 row_newbcast:" #E0 " row_mask:0xf bank_mask:0xf\n"         \
+        "v_mul_f32_dpp %1, %4, %6 row_newbcast:" #E1 " row_mask:0xf bank_mask:0xf\n"         \
+        "v_mul_f32_dpp %2, %4, %7 row_newbcast:" #E2 " row_mask:0xf bank_mask:0xf\n"         \
+        "v_mul_f32_dpp %3, %4, %8 row_newbcast:" #E3 " row_mask:0xf bank_mask:0xf\n"         \
+        : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3])                                \
+        : "v"(inv), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]))
+__device__ __forceinline__ void mul4_col(float *y, float inv, const float *u, int e0) {
+    switch (e0) {
+        case 0: LORES_MUL4(0, 1, 2, 3); break;
+        case 4: LORES_MUL4(4, 5, 6, 7); break;
+        case 8: LORES_MUL4(8, 9, 10, 11); break;
+        default: LORES_MUL4(12, 13, 14, 15); break;
+    }
+}
+#undef LORES_MUL4
+
+// max(|x|, |z|) (values are finite: no NaN quieting needed)
+__device__ __forceinline__ float absmax(float x, float z) {
+    float y;
+    asm("v_max_f32_e64 %0, |%1|, |%2|" : "=v"(y) : "v"(x), "v"(z));
+    return y;
+}
+
+// y[p] = max(|s[p]|, |o[p] of the partner lane|) for p < 8; the partner is
+// lane ^ 7 within 8 (row_half_mirror), lane ^ 1 (quad_perm [1,0,3,2]),
+// lane ^ 2 (quad_perm [2,3,0,1]) or lane ^ 8 (row_ror:8)
+#define LORES_DPP_HALF_MIRROR "row_half_mirror"
+#define LORES_DPP_XOR1 "quad_perm:[1,0,3,2]"
+#define LORES_DPP_XOR2 "quad_perm:[2,3,0,1]"
+#define LORES_DPP_XOR8 "row_ror:8"
+#define LORES_XMAX8(CTRL)                                                                     \
+    asm("s_nop 1\n"                                                                           \
+        "v_max_f32_dpp %0, |%8|, |%16| " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
+        "v_max_f32_dpp %1, |%9|, |%17| " CTRL " row_mask:0xf bank_mask:0xf\n"                 \
+        "v_max_f32_dpp %2, |%10|, |%18| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        "v_max_f32_dpp %3, |%11|, |%19| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        "v_max_f32_dpp %4, |%12|, |%20| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        "v_max_f32_dpp %5, |%13|, |%21| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        "v_max_f32_dpp %6, |%14|, |%22| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        "v_max_f32_dpp %7, |%15|, |%23| " CTRL " row_mask:0xf bank_mask:0xf\n"                \
+        : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]),      \
+          "=&v"(y[6]), "=&v"(y[7])                                                            \
+        : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "v"(o[5]), "v"(o[6]),        \
+          "v"(o[7]), "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]), "v"(s[4]), "v"(s[5]),        \
+          "v"(s[6]), "v"(s[7]))
+#define LORES_XMAX1(CTRL)                                                                     \
+    asm("s_nop 1\n"                                                                           \
+        "v_max_f32_dpp %0, |%1|, |%2| " CTRL " row_mask:0xf bank_mask:0xf\n"                  \
+        : "=&v"(y) : "v"(o), "v"(s))
+
+// One level of the column-maximum butterfly for one pair of registers (a, b):
+// lanes whose bit `mask` is clear keep column a, the others column b, each
+// combined with the partner lane across that bit.
+template <int LEVEL>
+__device__ __forceinline__ float xmax_pair(float a, float b, bool hi) {
+    const float s = hi ? b : a, o = hi ? a : b;
+    float y;
+    if constexpr (LEVEL == 4) LORES_XMAX1(LORES_DPP_XOR1);
+    else if constexpr (LEVEL == 5) LORES_XMAX1(LORES_DPP_XOR2);
+    else LORES_XMAX1(LORES_DPP_XOR8);
+    return y;
+}
+
+// Column maxima of |U| over the 64 rows (lanes) of a wavefront.  Six
+// levels, each pairing registers (2p, 2p + 1) and lanes across one bit:
+// lane ^ 7 within 8 (bit 2 selects), lane ^ 32 and lane ^ 16 (v_permlane32 /
+// v_permlane16 swaps; bits 5, 4), lane ^ 1, lane ^ 2, lane ^ 8 (bits 0, 1, 3).
+// Depth first, 16 columns at a time, so only a few partial results are live.
+// Register t of lane L then holds the maximum of column key_col(t, L).
+__device__ __forceinline__ int key_col(int t, int L) {
+    return 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + (L & 1) * 8 +
+           ((L >> 4) & 1) * 4 + ((L >> 5) & 1) * 2 + ((L >> 2) & 1);
+}
+
+template <int DK>
+__device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[DK / 64]) {
+    static_assert(DK % 64 == 0, "key-column scales need d_k = 64 or 128");
+    const int lane = threadIdx.x & 63;
+    const bool h0 = lane & 1, h1 = lane & 2, h2 = lane & 4, h3 = lane & 8;
+#pragma unroll
+    for (int t = 0; t < DK / 64; ++t) {
+        float g[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float *u = &U[64 * t + 16 * q];
+            float s[8], o[8], y[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                s[p] = h2 ? u[2 * p + 1] : u[2 * p];
+                o[p] = h2 ? u[2 * p] : u[2 * p + 1];
+            }
+            LORES_XMAX8(LORES_DPP_HALF_MIRROR);
+            float y2[4], y3[2];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[2 * p]),
+                                                                 __float_as_uint(y[2 * p + 1]),
+                                                                 false, false);
+                y2[p] = absmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(y2[2 * p]),
+                                                                 __float_as_uint(y2[2 * p + 1]),
+                                                                 false, false);
+                y3[p] = absmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            g[q] = xmax_pair<4>(y3[0], y3[1], h0);
+        }
+        cm[t] = xmax_pair<6>(xmax_pair<5>(g[0], g[1], h1), xmax_pair<5>(g[2], g[3], h1), h3);
+    }
+}
+#undef LORES_XMAX8
+#undef LORES_XMAX1
+
+// s_barrier after this wavefront's LDS writes have landed; later memory
+// accesses stay after it, loads already in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Column scales of a unit from its wavefronts' column maxima: wavefront wv
+// (row block rb of n_rb, the unit's blocks being wavefronts wv - rb ..
+// wv - rb + n_rb - 1 of the work-group) publishes its maxima in lds[wv][.],
+// then every wavefront of the unit reads all of them back as row vectors:
+// register i of snew / inv holds column 16 i + lane % 16.  snew = fl(m / r),
+// inv = the largest fp32 <= r / m (0 for a zero column).
+template <int DK>
+__device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *lds, int wv, int rb,
+                                           int n_rb, float R, float (&snew)[DK / 16],
+                                           float (&inv)[DK / 16]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < DK / 64; ++t) lds[wv * DK + key_col(t, lane)] = cm[t];
+    lds_barrier();
+    const float *base = lds + (wv - rb) * DK + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < DK / 16; ++i) {
+        float m = base[16 * i];
+        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DK + 16 * i]);
+        snew[i] = m / R;
+        inv[i] = rd_div(R, m);
+    }
+}
+
 template <bool BF16IN>
 __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx) {
     if constexpr (BF16IN) {
@@ -369,14 +546,19 @@ __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx)
 // store of the row's 16-byte chunks (chunk c at cp + c * dv_pad).  Shared by
 // the step and by the fp32 -> packed state entry.
 // ---------------------------------------------------------------------------
-template <int DK, int PREC>
+// KEY: key-column scales; invrow holds r / m_j as row vectors (register i,
+// column 16 i + lane % 16), m and scale_out are unused (the caller stores
+// the column scales).
+template <int DK, int PREC, bool KEY = false>
 __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, const StepMeta &meta,
                                                int b, int h, int row, bool active, u32x4 *cp,
-                                               long dv_pad, float *scale_out) {
+                                               long dv_pad, float *scale_out,
+                                               const float *invrow = nullptr) {
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = row_chunks<DK, PREC>();
+    static_assert(!KEY || has_scale<PREC>(), "key-column scales belong to scaled classes");
     float inv = 0.0f;
-    if constexpr (has_scale<PREC>()) {
+    if constexpr (has_scale<PREC>() && !KEY) {
         const float snew = m / Prec<PREC>::R;
         inv = rd_div(Prec<PREC>::R, m);
         if (active) *scale_out = snew;
@@ -409,6 +591,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
         constexpr Int6Stray<DK> stray;
         int j = 0;
         uint32_t carry = 0;                  // high bits of a field crossing into the next chunk
+        float zb[4];                         // key columns: sums of columns j & ~3 .. (j & ~3) + 3
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             uint32_t acc[4];
@@ -418,8 +601,21 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
             carry = 0;
 #pragma unroll
             for (; j < DK && 6 * j < 128 * (c + 1); ++j) {
-                const float z = __builtin_fmaf(U[j], inv, __uint_as_float(x));
-                x = step16(x, psi);
+                float z;
+                if constexpr (KEY) {
+                    if ((j & 3) == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            zb[e] = __uint_as_float(x);
+                            x = step16(x, psi);
+                        }
+                        fmac4_col(zb, invrow[j >> 4], &U[j], j & 15);
+                    }
+                    z = zb[j & 3];
+                } else {
+                    z = __builtin_fmaf(U[j], inv, __uint_as_float(x));
+                    x = step16(x, psi);
+                }
                 const uint32_t e = (uint32_t)z;
                 const int bit = 6 * j - 128 * c, w = bit >> 5, o = bit & 31;
                 acc[w] += e << o;
@@ -443,9 +639,11 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                     float z[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
+                        if constexpr (KEY) z[e] = __uint_as_float(x);
+                        else z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
                         x = step16(x, psi);
                     }
+                    if constexpr (KEY) fmac4_col(z, invrow[j >> 4], &U[j], j & 15);
                     const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
                     uint32_t word = (uint32_t)z0;           // 1 <= z < 256: bytes 1..3 are 0
                     cvt_u8_into<1>(word, z1);
@@ -459,12 +657,28 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 8;
                     float ze[4], zo[4];
+                    if constexpr (KEY) {
+                        float z[8];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
-                        x = step16(x, psi);
-                        zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
-                        x = step16(x, psi);
+                        for (int e = 0; e < 8; ++e) {
+                            z[e] = __uint_as_float(x);
+                            x = step16(x, psi);
+                        }
+                        fmac4_col(z, invrow[j >> 4], &U[j], j & 15);
+                        fmac4_col(z + 4, invrow[j >> 4], &U[j + 4], (j + 4) & 15);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            ze[p] = z[2 * p];
+                            zo[p] = z[2 * p + 1];
+                        }
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
+                            x = step16(x, psi);
+                            zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
+                            x = step16(x, psi);
+                        }
                     }
                     // z lies in [128, 256), where bits 16..22 of its fp32
                     // pattern are floor(z) - 128 = code + 8 (<= 15) and bit
@@ -482,9 +696,13 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 4;
                     uint32_t by[4];
+                    float yk[4];
+                    if constexpr (KEY) mul4_col(yk, invrow[j >> 4], &U[j], j & 15);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float y = U[j + e] * inv;
+                        float y;
+                        if constexpr (KEY) y = yk[e];
+                        else y = U[j + e] * inv;
                         const uint32_t t = __float_as_uint(y * 0x1p-120f) + (x << 4);
                         x = step16(x, psi);
                         const uint32_t u = t >> 20;
@@ -533,13 +751,18 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 // Per-task values loaded ahead of the task, besides its chunks: the row
 // scale and v of this lane's row, beta and a scalar alpha, and k, q and a
 // per-channel alpha as row vectors (NV registers each).
-template <int NV>
+// With key-column scales, sv holds the unit's column scales as a row vector.
+template <int NV, bool KEY = false>
 struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
     float kv[NV], qv[NV], av[NV];
+    float sv[KEY ? NV : 1];
 };
 
-template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
+// KEY: key-column scales (d_k per unit); the unit's row blocks are the
+// wavefronts wv - rb .. wv - rb + n_rb - 1 of one work-group, and `lds`
+// holds two buffers of kWavesPerGroup x DK column maxima.
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false>
 struct TaskStream {
     static constexpr int E = Prec<PREC>::E;
     static constexpr int NCH = row_chunks<DK, PREC>();
@@ -556,40 +779,49 @@ struct TaskStream {
     uint8_t *__restrict__ codes;
     float *__restrict__ scales;
     const StepMeta &meta;
-    int Hc, slot, h, row;
+    int Hc, slot, h, row, lrow, rb;
     long unit_bytes;
     bool active;
+    float *lds;
 
     __device__ __forceinline__ TaskStream(const void *q, const void *k, const void *v,
                                           const float *alpha, const float *beta, float *o,
                                           uint8_t *c, float *sc, const StepMeta &m,
-                                          const ClassDesc &cd, int task)
-        : qp(q), kp(k), vp(v), alphap(alpha), betap(beta), op(o), codes(c), scales(sc), meta(m) {
+                                          const ClassDesc &cd, int task, float *lds_ = nullptr)
+        : qp(q), kp(k), vp(v), alphap(alpha), betap(beta), op(o), codes(c), scales(sc), meta(m),
+          lds(lds_) {
         const int n_rb = m.n_rb;
         slot = n_rb == 1 ? task : n_rb == 2 ? task >> 1 : n_rb == 4 ? task >> 2 : task / 3;
-        const int rb = task - slot * n_rb;
+        rb = task - slot * n_rb;
         Hc = cd.Hc;
         unit_bytes = cd.unit_bytes;
         h = (int)m.heads[cd.head_off + slot];
         row = rb * 64 + (threadIdx.x & 63);
         active = row < m.dv;
+        // padding rows (row >= d_v) load row d_v - 1 and store nothing, so
+        // they repeat a real row (and leave column maxima unchanged)
+        lrow = active ? row : m.dv - 1;
     }
 
     static constexpr int NV = DK / 16;            // row-vector registers per vector
 
     // Loads of task b: chunks [C0, C1) and, with C0 = 0, the per-task values.
     template <int C0 = 0, int C1 = NCH>
-    __device__ __forceinline__ void issue(int b, u32x4 *cw, TaskSide<NV> &in) const {
+    __device__ __forceinline__ void issue(int b, u32x4 *cw, TaskSide<NV, KEY> &in) const {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;
-        // padding rows (row >= d_v) lie inside the unit and are read, never written
-        const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + row;
+        const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + lrow;
 #pragma unroll
         for (int c = C0; c < C1; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
         if constexpr (C0 != 0) return;
-        if constexpr (has_scale<PREC>()) in.s = scales[unit * dv_pad + row];
-        in.v = in_scalar<BF16IN>(vp, bh * meta.dv + (active ? row : meta.dv - 1));
+        if constexpr (KEY) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) in.sv[i] = scales[unit * DK + 16 * i + (threadIdx.x & 15)];
+        } else if constexpr (has_scale<PREC>()) {
+            in.s = scales[unit * dv_pad + lrow];
+        }
+        in.v = in_scalar<BF16IN>(vp, bh * meta.dv + lrow);
         in.beta = betap[bh];
         in.alpha = PC ? 1.0f : alphap[bh];
         // row vectors: register i holds element 16 i + lane % 16
@@ -603,8 +835,8 @@ struct TaskStream {
     }
 
     template <class Mid>
-    __device__ __forceinline__ void run(int b, const u32x4 *cw, const TaskSide<NV> &in,
-                                        Mid &&mid) const {
+    __device__ __forceinline__ void run(int b, const u32x4 *cw, const TaskSide<NV, KEY> &in,
+                                        Mid &&mid, int buf = 0) const {
         const float s = in.s, vi = in.v;
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
@@ -614,7 +846,12 @@ struct TaskStream {
         const float beta = in.beta;
         const float alpha_s = in.alpha;
         float a = 0.0f, na = 0.0f;
-        if constexpr (is_int<PREC>() && !PC) {
+        // key columns: sig_j = fl(s_j * alpha_j) as a row vector
+        float sig[KEY ? NV : 1];
+        if constexpr (KEY) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) sig[i] = in.sv[i] * (PC ? in.av[i] : alpha_s);
+        } else if constexpr (is_int<PREC>() && !PC) {
             a = s * alpha_s;
             na = a * -Prec<PREC>::OFF;
         } else if constexpr (PREC == LORES_FP8 && !PC) {
@@ -629,6 +866,7 @@ struct TaskStream {
         // then the group's share of r
         auto group_done = [&](int j) {
             if constexpr (PC && !has_scale<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
+            if constexpr (KEY) mul16(&U[j - 15], sig[j >> 4]);
             if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
             // without the projection nothing orders pass 1 before the
             // next task's loads; materialize the group here so the
@@ -638,11 +876,12 @@ struct TaskStream {
         if constexpr (PREC == LORES_INT6) {
 #pragma unroll
             for (int j = 0; j < DK; ++j) {
-                if constexpr (PC) {
+                if constexpr (PC && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
                 const float ub = (float)int6_field(cw, j);
-                if constexpr (PC) U[j] = (ub - Prec<PREC>::OFF) * aj[j & 15];
+                if constexpr (KEY) U[j] = ub - Prec<PREC>::OFF;     // times sig_j per group
+                else if constexpr (PC) U[j] = (ub - Prec<PREC>::OFF) * aj[j & 15];
                 else U[j] = __builtin_fmaf(ub, a, na);
                 if ((j & 15) == 15) group_done(j);
             }
@@ -653,14 +892,15 @@ struct TaskStream {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int j = c * E + e;
-                if constexpr (PC && has_scale<PREC>()) {
+                if constexpr (PC && has_scale<PREC>() && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
                 float sp;
                 if constexpr (PREC == LORES_FP8) {
                     // the E4M3 value (hardware decode of byte e & 3), times s * alpha
                     const float v = fp8_value(wd[e >> 2], e & 3);
-                    if constexpr (PC) sp = v * aj[j & 15];
+                    if constexpr (KEY) sp = v;                       // times sig_j per group
+                    else if constexpr (PC) sp = v * aj[j & 15];
                     else sp = v * a;
                 } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
@@ -673,7 +913,8 @@ struct TaskStream {
                                                      : and_opaque(w, 0x0F0F0F0Fu);
                         ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
                     }
-                    if constexpr (PC) sp = (ub - Prec<PREC>::OFF) * aj[j & 15];
+                    if constexpr (KEY) sp = ub - Prec<PREC>::OFF;   // times sig_j per group
+                    else if constexpr (PC) sp = (ub - Prec<PREC>::OFF) * aj[j & 15];
                     else sp = __builtin_fmaf(ub, a, na);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
@@ -699,14 +940,31 @@ struct TaskStream {
 #pragma unroll
         for (int gi = 0; gi < NV; ++gi) {
             upd16(&U[16 * gi], o, g, in.kv[gi], in.qv[gi]);
+            if constexpr (!KEY) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
+                for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
+            }
         }
         if (active) op[bh * meta.dv + row] = o;
 
         // ---- pass 3: requantize and store in place
-        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
-                                 has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+        if constexpr (KEY) {
+            // column maxima of the unit's rows, fresh column scales
+            float cm[DK / 64], snew[NV], inv[NV];
+            col_absmax<DK>(U, cm);
+            const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DK), wv, rb, meta.n_rb,
+                           Prec<PREC>::R, snew, inv);
+            if (rb == 0 && (threadIdx.x & 63) < 16) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i) scales[unit * DK + 16 * i + (threadIdx.x & 15)] = snew[i];
+            }
+            requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr,
+                                           inv);
+        } else {
+            requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+                                     has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+        }
     }
 };
 
@@ -716,30 +974,30 @@ struct TaskStream {
 // of a bf16 row (the rest are loaded as that task starts), none of an fp32
 // row.  The loop body holds two tasks, so the prefetched per-task values
 // alternate between two register sets instead of being copied.
-template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN>
-__device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN> &ts) {
-    using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN>;
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY>
+__device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY> &ts) {
+    using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY>;
     // fp32 rows (32 chunks at d_k = 128) leave no registers for a prefetch
     // beside U: only their per-task values are loaded ahead
     constexpr int P = TS::NCH <= kMaxPrefetchChunks ? TS::NCH
                     : PREC == LORES_BF16 ? kMaxPrefetchChunks : 0;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
-    TaskSide<TS::NV> in0, in1;
+    TaskSide<TS::NV, KEY> in0, in1;
     int b = blockIdx.y;
     ts.issue(b, cw, in0);
     while (true) {
         int bn = b + bstep;
         ts.run(b, cw, in0, [&] {
             if (bn < ts.meta.B) ts.template issue<0, P>(bn, cw, in1);
-        });
+        }, 0);
         if (bn >= ts.meta.B) break;
         b = bn;
         bn = b + bstep;
         if constexpr (P < TS::NCH) ts.template issue<P, TS::NCH>(b, cw, in1);
         ts.run(b, cw, in1, [&] {
             if (bn < ts.meta.B) ts.template issue<0, P>(bn, cw, in0);
-        });
+        }, 1);
         if (bn >= ts.meta.B) break;
         b = bn;
         if constexpr (P < TS::NCH) ts.template issue<P, TS::NCH>(b, cw, in0);
@@ -791,7 +1049,7 @@ constexpr bool pairable() {
     }
 }
 
-template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1>
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
@@ -801,7 +1059,22 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int gx = blockIdx.x;
     const int n_rb = meta.n_rb;
-    if constexpr (P1 < 0) {
+    if constexpr (KEY) {
+        // one class; the n_rb (1, 2 or 4) row blocks of a unit are
+        // consecutive tasks, so whole units share a work-group.  A wave past
+        // the last task still takes part in the work-group's barriers: one
+        // per sequence of its stride, as a working wave does.
+        static_assert(P1 < 0, "key-column scales run one class per launch");
+        __shared__ float cmax[2 * kWavesPerGroup * DK];
+        const int task = gx * kWavesPerGroup + wv;
+        if (task >= meta.cls[0].Hc * n_rb) {
+            for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
+            return;
+        }
+        run_single(TaskStream<DK, P0, PC, DELTA, BF16IN, true>(qp, kp, vp, alphap, betap, op,
+                                                               codes0, scales0, meta,
+                                                               meta.cls[0], task, cmax));
+    } else if constexpr (P1 < 0) {
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) return;
         run_single(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op, codes0,
@@ -858,9 +1131,9 @@ inline int device_cu_count() {
     return cached[dev];
 }
 
-template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1>
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false>
 hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
-    auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1>;
+    auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY>;
     static int per_cu = 0;                          // resident work-groups per CU
     if (!per_cu) {
         int n = 0;
@@ -888,19 +1161,19 @@ hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int DK, int P0, int P1>
+template <int DK, int P0, int P1, bool KEY = false>
 hipError_t launch_dk(bool pc, bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
                      hipStream_t s) {
     if (pc) {
-        if (delta) return bf16 ? launch_one<DK, true, true, true, P0, P1>(p, m, s)
-                               : launch_one<DK, true, true, false, P0, P1>(p, m, s);
-        return bf16 ? launch_one<DK, true, false, true, P0, P1>(p, m, s)
-                    : launch_one<DK, true, false, false, P0, P1>(p, m, s);
+        if (delta) return bf16 ? launch_one<DK, true, true, true, P0, P1, KEY>(p, m, s)
+                               : launch_one<DK, true, true, false, P0, P1, KEY>(p, m, s);
+        return bf16 ? launch_one<DK, true, false, true, P0, P1, KEY>(p, m, s)
+                    : launch_one<DK, true, false, false, P0, P1, KEY>(p, m, s);
     }
-    if (delta) return bf16 ? launch_one<DK, false, true, true, P0, P1>(p, m, s)
-                           : launch_one<DK, false, true, false, P0, P1>(p, m, s);
-    return bf16 ? launch_one<DK, false, false, true, P0, P1>(p, m, s)
-                : launch_one<DK, false, false, false, P0, P1>(p, m, s);
+    if (delta) return bf16 ? launch_one<DK, false, true, true, P0, P1, KEY>(p, m, s)
+                           : launch_one<DK, false, true, false, P0, P1, KEY>(p, m, s);
+    return bf16 ? launch_one<DK, false, false, true, P0, P1, KEY>(p, m, s)
+                : launch_one<DK, false, false, false, P0, P1, KEY>(p, m, s);
 }
 
 template <int P0, int P1>
@@ -911,6 +1184,17 @@ hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs
         case 64: return launch_dk<64, P0, P1>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, P1>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, P1>(pc, delta, bf16, p, m, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// key-column scales: one class per launch, d_k = 64 or 128
+template <int P0>
+hipError_t launch_classes_key(int dk, bool pc, bool delta, bool bf16, const StepPtrs &p,
+                              const StepMeta &m, hipStream_t s) {
+    switch (dk) {
+        case 64: return launch_dk<64, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 128: return launch_dk<128, P0, -1, true>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }

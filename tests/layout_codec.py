@@ -14,7 +14,7 @@ E = {0: 4, 1: 8, 2: 16, 3: 32}       # elements per 16-byte chunk (int6: a bit s
 OFFSET = {2: 128, 3: 8, 4: 32}       # offset-binary code offset
 QMAX = {2: 127, 3: 7, 4: 31}
 INT_CLASSES = (2, 3, 4)
-SCALED_CLASSES = (2, 3, 4, 5)        # classes with one fp32 scale per value row
+SCALED_CLASSES = (2, 3, 4, 5)        # classes with fp32 scales (per value row or key column)
 
 
 def n_chunks(c, dk):
@@ -48,25 +48,28 @@ def class_units(head_prec, B, c):
     return [(b, h) for b in range(B) for h in heads]
 
 
-def pack_unit(c, dk, dv, dv_pad, state_unit):
-    """One unit's state -> (code bytes [n_chunk*dv_pad*16] uint8, scales [dv_pad] fp32 | None).
+def pack_unit(c, dk, dv, dv_pad, state_unit, key=False):
+    """One unit's state -> (code bytes [n_chunk*dv_pad*16] uint8, scales | None).
 
     state_unit: {"codes": int [dv, dk], "scales": f32 [dv]} (int classes),
                 {"bits": uint16 [dv, dk]} (bf16) or {"X": f32 [dv, dk]} (fp32).
+    The stored scales are [dv_pad] (value rows) or, with key=True, the
+    unit's [dk] key-column scales.
     """
     n_chunk = n_chunks(c, dk)
     out = np.zeros((n_chunk, dv_pad, 16), np.uint8)
     sc = None
+    ns, nv = (dk, dk) if key else (dv_pad, dv)
     if c == 5:
-        sc = np.zeros(dv_pad, np.float32)
-        sc[:dv] = state_unit["scales"]
+        sc = np.zeros(ns, np.float32)
+        sc[:nv] = state_unit["scales"]
         by = np.asarray(state_unit["fp8"], np.uint8)
         out[:, :dv, :] = by.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
     elif c in INT_CLASSES:
         codes = np.asarray(state_unit["codes"], np.int64)
         assert codes.min() >= -QMAX[c] and codes.max() <= QMAX[c]
-        sc = np.zeros(dv_pad, np.float32)
-        sc[:dv] = state_unit["scales"]
+        sc = np.zeros(ns, np.float32)
+        sc[:nv] = state_unit["scales"]
         off = (codes + OFFSET[c]).astype(np.uint8)              # [dv, dk]
         if c == 2:
             out[:, :dv, :] = off.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
@@ -88,24 +91,25 @@ def pack_unit(c, dk, dv, dv_pad, state_unit):
     return out.reshape(-1), sc
 
 
-def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None):
+def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None, key=False):
     """Inverse of pack_unit."""
     n_chunk = n_chunks(c, dk)
+    nv = dk if key else dv
     raw = np.asarray(code_bytes, np.uint8).reshape(n_chunk, dv_pad, 16)[:, :dv, :]
     rows = np.ascontiguousarray(raw.transpose(1, 0, 2)).reshape(dv, n_chunk * 16)
     if c == 2:
         return {"codes": rows.astype(np.int32) - 128,
-                "scales": np.asarray(scales, np.float32)[:dv].copy()}
+                "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 5:
-        return {"fp8": rows.copy(), "scales": np.asarray(scales, np.float32)[:dv].copy()}
+        return {"fp8": rows.copy(), "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 4:
         return {"codes": _unpack6(rows, dk) - 32,
-                "scales": np.asarray(scales, np.float32)[:dv].copy()}
+                "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 3:
         lo = (rows & 0x0F).astype(np.int32)
         hi = (rows >> 4).astype(np.int32)
         codes = np.stack([lo, hi], axis=-1).reshape(dv, dk) - 8
-        return {"codes": codes, "scales": np.asarray(scales, np.float32)[:dv].copy()}
+        return {"codes": codes, "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 1:
         return {"bits": rows.view(np.uint16).reshape(dv, dk).copy()}
     return {"X": rows.view(np.float32).reshape(dv, dk).copy()}
@@ -116,8 +120,8 @@ def unit_ranges(layout, c, unit):
     ub = layout["unit_code_bytes"][c]
     cs = layout["codes_offset"][c] + unit * ub
     if c in SCALED_CLASSES:
-        dvp = layout["d_v_pad"]
-        return cs, ub, layout["scales_offset"][c] + unit * dvp * 4, dvp * 4
+        ns = layout["unit_scales"]
+        return cs, ub, layout["scales_offset"][c] + unit * ns * 4, ns * 4
     return cs, ub, None, 0
 
 
@@ -125,12 +129,14 @@ def read_unit(buf_host, layout, c, unit):
     """Decode unit `unit` of class c from a host copy (uint8 numpy) of the buffer."""
     cs, cl, ss, sl = unit_ranges(layout, c, unit)
     sc = buf_host[ss:ss + sl].view(np.float32) if ss is not None else None
-    return unpack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], buf_host[cs:cs + cl], sc)
+    return unpack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], buf_host[cs:cs + cl], sc,
+                       key=layout["scale_axis"] == 1)
 
 
 def write_unit(buf_host, layout, c, unit, state_unit):
     cs, cl, ss, sl = unit_ranges(layout, c, unit)
-    code_bytes, sc = pack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], state_unit)
+    code_bytes, sc = pack_unit(c, layout["d_k"], layout["d_v"], layout["d_v_pad"], state_unit,
+                               key=layout["scale_axis"] == 1)
     buf_host[cs:cs + cl] = code_bytes
     if ss is not None:
         buf_host[ss:ss + sl] = sc.view(np.uint8)

@@ -59,15 +59,16 @@ def head_precisions(w, inputs, calib_steps=32):
     return got
 
 
-def random_unit_state(c, dv, dk, g):
+def random_unit_state(c, dv, dk, g, axis="value"):
+    ns = dv if axis == "value" else dk
     if c == 5:
         by = g.integers(0, 256, (dv, dk)).astype(np.uint8)
         by[(by & 0x7F) == 0x7F] ^= 0x01                  # no NaN patterns
-        return {"fp8": by, "scales": np.exp(g.uniform(-7, -2, dv)).astype(F32)}
+        return {"fp8": by, "scales": np.exp(g.uniform(-7, -2, ns)).astype(F32)}
     if c in (2, 3, 4):
         r = {2: 127, 3: 7, 4: 31}[c]
         return {"codes": g.integers(-r, r + 1, (dv, dk)).astype(np.int32),
-                "scales": np.exp(g.uniform(-7, -2, dv)).astype(F32)}
+                "scales": np.exp(g.uniform(-7, -2, ns)).astype(F32)}
     X = (g.standard_normal((dv, dk)) * 0.05).astype(F32)
     if c == 1:
         return {"bits": (X.view(np.uint32) >> 16).astype(np.uint16)}
@@ -128,7 +129,7 @@ def _readout_scale(X):
 
 
 def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", inputs=None,
-               device="cuda", rounding="sr"):
+               device="cuda", rounding="sr", axis="value"):
     """Run T GPU steps with per-step resync to the oracle; returns Stats.
 
     units: list of (b, h) to compare (default: all).  init: "zero" (S_0 = 0),
@@ -136,13 +137,17 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
     function (prec, dv, dk, numpy Generator) -> one unit's state.
     rounding: "sr" (stochastic, the default) or "nearest" (the library's
     round-to-nearest mode, set on the state through the C ABI).
+    axis: "value" (value-row scales) or "key" (key-column scales, allocated
+    with LORES_SCALE_KEY).
     """
     B = w.B if B is None else B
     if inputs is None:
         inputs = make_inputs(w, seed, device, T=T, B=B)
     if head_prec is None:
         head_prec = head_precisions(w, inputs)
-    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device)
+    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device,
+                                 scale_axis=lores.LORES_SCALE_KEY if axis == "key"
+                                 else lores.LORES_SCALE_VALUE)
     if rounding == "nearest":
         lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
     lay = lores.lores_state_layout(st)
@@ -158,9 +163,9 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
         if callable(init):
             s = init(c, w.dv, w.dk, g)
         elif init == "zero":
-            s = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk).items()}
+            s = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk, axis=axis).items()}
         else:
-            s = random_unit_state(c, w.dv, w.dk, g)
+            s = random_unit_state(c, w.dv, w.dk, g, axis)
         ost[(b, h)] = s
     by_class = {}
     for (b, h) in units:
@@ -192,8 +197,8 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
             q, k, v = xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs]
             al, be = xin["alpha"][bs, hs], xin["beta"][bs, hs]
             new, o_ref = ostep.decode_step(c, prev, q, k, v, al, be, w.delta, seed, t, bs, hs,
-                                           rounding=rounding)
-            X_ref = ostep.dequant(c, new)
+                                           rounding=rounding, axis=axis)
+            X_ref = ostep.dequant(c, new, axis=axis)
             scale = _readout_scale(X_ref)
             o_err = (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()
             gpu = _stack([lc.read_unit(buf_host, lay, c, b * lay["n_class"][c] + hslot[h])
@@ -212,13 +217,14 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
                 # E4M3 has a value-relative grid like bf16: a differing value
                 # must lie within one E4M3 step of the oracle's value, plus the
                 # cancellation allowance of the bf16 rule
-                Xg = ostep.dequant(c, gpu).astype(np.float64)
+                Xg = ostep.dequant(c, gpu, axis=axis).astype(np.float64)
                 Xr = X_ref.astype(np.float64)
                 diff = gpu["fp8"] != new["fp8"]
                 stats.fp8 += diff.size
                 stats.fp8_diff += int(diff.sum())
                 if diff.any():
-                    rowmax = np.abs(Xr).max(axis=2, keepdims=True)
+                    # the maximum of the scale group (row, or key column)
+                    rowmax = np.abs(Xr).max(axis=2 if axis == "value" else 1, keepdims=True)
                     step = np.maximum(np.abs(Xr), np.abs(Xg)) / 8 + rowmax / 448 * 2.0 ** -9
                     excess = (np.abs(Xg - Xr) - step) / np.maximum(rowmax, 1e-300)
                     stats.fp8_excess = max(stats.fp8_excess, float(excess[diff].max()))

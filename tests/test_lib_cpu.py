@@ -40,10 +40,10 @@ def test_library_exports_every_declared_symbol(lores_lib):
 def test_spec_version(lores_lib):
     hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
     v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
-    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 3
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 4
 
 
-def _layout_bytes(B, H, dk, dv, head_prec):
+def _layout_bytes(B, H, dk, dv, head_prec, key=False):
     """Segment sizes as include/lores.h documents them."""
     bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}
     dvp = (dv + 63) // 64 * 64
@@ -54,9 +54,9 @@ def _layout_bytes(B, H, dk, dv, head_prec):
             continue
         off = (off + 255) // 256 * 256
         off += B * hc * -(-(dk * bits[c]) // 128) * 16 * dvp     # whole 16-byte chunks per row
-        if c in (2, 3, 4, 5):                      # one fp32 scale per value row
+        if c in (2, 3, 4, 5):                      # one fp32 scale per value row / key column
             off = (off + 255) // 256 * 256
-            off += B * hc * dvp * 4
+            off += B * hc * (dk if key else dvp) * 4
     return (off + 255) // 256 * 256
 
 
@@ -134,6 +134,31 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
     neg = (ctypes.c_float * 2)(0.5, -0.5)
     st = (ctypes.c_double * 2)()
     assert L.lores_decay_stat(neg, 1, 2, 1, st) == -1
+
+
+def test_key_axis_layout_and_limits(lores_lib):
+    """Key-column scales: d_k scales per unit of a scaled class, the shapes
+    that are not built return LORES_EUNSUPPORTED, an unknown axis EINVAL
+    (size queries only: no device work)."""
+    L = lores._lib.lib()
+    hp = (ctypes.c_uint8 * 3)(2, 3, 1)
+    n = ctypes.c_size_t(0)
+    assert L.lores_state_alloc_axis(4, 3, 128, 100, hp, 1, None, ctypes.byref(n), None, None) == 0
+    key_bytes = n.value
+    assert L.lores_state_alloc_axis(4, 3, 128, 100, hp, 0, None, ctypes.byref(n), None, None) == 0
+    val_bytes = n.value
+    want = _layout_bytes(4, 3, 128, 100, [2, 3, 1], key=True)
+    assert key_bytes == want, (key_bytes, want)
+    assert val_bytes == _layout_bytes(4, 3, 128, 100, [2, 3, 1])
+    for dk, dv in ((96, 64), (32, 64), (128, 150), (64, 192)):
+        assert L.lores_state_alloc_axis(2, 3, dk, dv, hp, 1, None, ctypes.byref(n), None,
+                                        None) == lores._lib.LORES_EUNSUPPORTED, (dk, dv)
+    for dv in (1, 64, 65, 128, 193, 256):
+        assert L.lores_state_alloc_axis(2, 3, 64, dv, hp, 1, None, ctypes.byref(n), None,
+                                        None) == 0, dv
+    assert L.lores_state_alloc_axis(2, 3, 64, 64, hp, 2, None, ctypes.byref(n), None,
+                                    None) == lores._lib.LORES_EINVAL
+    assert "scale_axis" in lores.lores_last_error()
 
 
 def test_error_message_is_thread_local_and_cleared(lores_lib):
