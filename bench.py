@@ -47,11 +47,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def unit_bytes(prec, dk, dv, in_bytes, per_channel):
+def unit_bytes(prec, dk, dv, in_bytes, per_channel, key=False):
     """Algorithmic bytes of one state update: the state read and written once,
-    plus q, k, v, alpha, beta read and o written."""
-    state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * dv, 3: dv * dk // 2 + 4 * dv,
-             4: 6 * dv * dk // 8 + 4 * dv, 5: dv * dk + 4 * dv}[prec]
+    plus q, k, v, alpha, beta read and o written.  The scales are one fp32 per
+    value row, or per key column with key=True."""
+    ns = dk if key else dv
+    state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * ns, 3: dv * dk // 2 + 4 * ns,
+             4: 6 * dv * dk // 8 + 4 * ns, 5: dv * dk + 4 * ns}[prec]
     io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
     return 2 * state + io
 
@@ -72,6 +74,9 @@ def parse(argv=None):
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="how the timed steps are issued")
+    ap.add_argument("--scale-axis", default="value", choices=["value", "key"],
+                    help="scale grouping of the int / fp8 heads: one scale per value row "
+                         "(the method's choice) or per key column")
     return ap.parse_args(argv)
 
 
@@ -97,7 +102,7 @@ def copy_mode(args, torch):
                       "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
 
 
-SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta)
+SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis])
     ("int8+int4 (C5)", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1),
     ("int8+int4 (C5), delta 0", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 0),
     ("int8", 2048, 32, 128, 128, [2] * 32, 1),
@@ -108,6 +113,11 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta)
     ("int4, delta 0", 2048, 32, 128, 128, [3] * 32, 0),
     ("bf16", 1024, 32, 128, 128, [1] * 32, 1),
     ("int8, d_v 64 (C3 shape), delta 0", 256, 128, 128, 64, [2] * 128, 0),
+    ("int8, key columns", 2048, 32, 128, 128, [2] * 32, 1, "key"),
+    ("int4, key columns", 2048, 32, 128, 128, [3] * 32, 1, "key"),
+    ("int6, key columns", 2048, 32, 128, 128, [4] * 32, 1, "key"),
+    ("fp8 (E4M3), key columns", 2048, 32, 128, 128, [5] * 32, 1, "key"),
+    ("int8, d_v 64 (C3 shape), key columns", 256, 128, 128, 64, [2] * 128, 0, "key"),
 ]
 
 
@@ -119,7 +129,8 @@ def sweep_mode(args, torch):
     import quantized_linear_recurrence_amd as lores
     dev = torch.device("cuda:0")
     rows = []
-    for label, B, H, dk, dv, prec, delta in SWEEP:
+    for label, B, H, dk, dv, prec, delta, *ax in SWEEP:
+        key = bool(ax) and ax[0] == "key"
         g = torch.Generator(device=dev)
         g.manual_seed(args.seed)
 
@@ -130,7 +141,8 @@ def sweep_mode(args, torch):
         v = torch.randn(B, H, dv, generator=g, device=dev)
         alpha = (0.7 + 0.3 * torch.rand(B, H, generator=g, device=dev)).contiguous()
         beta = (2 * torch.sigmoid(torch.randn(B, H, generator=g, device=dev))).contiguous()
-        st = lores.lores_state_alloc(B, H, dk, dv, prec, device=dev)
+        st = lores.lores_state_alloc(B, H, dk, dv, prec, device=dev,
+                                     scale_axis=lores.LORES_SCALE_KEY if key else 0)
         o = torch.empty(B, H, dv, device=dev)
         for t in range(1, 9):
             lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, t, o=o)
@@ -147,16 +159,17 @@ def sweep_mode(args, torch):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / steps * 1e3
-        nbytes = sum(B * prec.count(c) * unit_bytes(c, dk, dv, 4, False) for c in range(6))
+        nbytes = sum(B * prec.count(c) * unit_bytes(c, dk, dv, 4, False, key) for c in range(6))
         gbs = nbytes / us / 1e3
         rows.append({"state": label, "B": B, "H": H, "d_k": dk, "d_v": dv, "delta": delta,
+                     "scale_axis": "key" if key else "value",
                      "us_per_step": us, "GBps": gbs, "frac": gbs / HBM_PEAK_GBPS})
         print(f"[sweep] {label:34s} {us:8.1f} us/step {gbs:7.0f} GB/s  {gbs / HBM_PEAK_GBPS:.3f}",
               file=sys.stderr, flush=True)
     print(json.dumps({"mode": "sweep", "rows": rows}), flush=True)
 
 
-def cpu_baseline(w, inputs, head_prec, target_s, seed):
+def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value"):
     """Time the oracle (as it stands) on a bounded sample of the same workload:
     the first units of the batch, step after step, until target_s has passed."""
     import numpy as np
@@ -167,7 +180,7 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed):
     by_class = {}
     for b, h in units:
         by_class.setdefault(head_prec[h], []).append((b, h))
-    states = {c: ostep.zero_state(c, len(us), w.dv, w.dk) for c, us in by_class.items()}
+    states = {c: ostep.zero_state(c, len(us), w.dv, w.dk, axis=axis) for c, us in by_class.items()}
     T_in = inputs["k"].shape[0]
     host = {}
     for t in range(min(T_in, 64)):
@@ -181,7 +194,8 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed):
             hs = np.array([h for _, h in us])
             states[c], _ = ostep.decode_step(c, states[c], xin["q"][bs, hs], xin["k"][bs, hs],
                                              xin["v"][bs, hs], xin["alpha"][bs, hs],
-                                             xin["beta"][bs, hs], w.delta, seed, steps + 1, bs, hs)
+                                             xin["beta"][bs, hs], w.delta, seed, steps + 1, bs, hs,
+                                             axis=axis)
         steps += 1
         el = time.perf_counter() - t0
         if el >= target_s:
@@ -253,9 +267,12 @@ def main(argv=None):
                                                  [f for f, _ in w.tiers], [p for _, p in w.tiers])
 
     in_bytes = 2 if w.in_bf16 else 4
-    step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel)
+    key = args.scale_axis == "key"
+    axis_code = lores.LORES_SCALE_KEY if key else lores.LORES_SCALE_VALUE
+    step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel,
+                                                           key)
                      for c in range(6))
-    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev)
+    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev, scale_axis=axis_code)
     o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
 
     def step(t):
@@ -267,7 +284,8 @@ def main(argv=None):
 
     def reset_state():
         nonlocal st
-        st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf)
+        st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf,
+                                     scale_axis=axis_code)
 
     print(f"[bench] warmup {W} eager steps", file=sys.stderr, flush=True)
     for t in range(1, W + 1):
@@ -317,7 +335,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     achieved = step_bytes / n_launches_per_step / (avg_launch_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.key)
+    traffic = load_traffic(w.key) if not key else None
     result = {
         "metric": METRIC,
         "value": w.B * w.H * K / (ms_total * 1e-3),
@@ -337,7 +355,8 @@ def main(argv=None):
             "decay": w.decay, "inputs": "bf16" if w.in_bf16 else "fp32",
             "state": {name: head_prec.count(c) for c, name in
                       enumerate(["fp32", "bf16", "int8", "int4", "int6", "fp8"]) if head_prec.count(c)},
-            "rounding": "stochastic", "parallelism": "single GPU",
+            "rounding": "stochastic", "scale_axis": args.scale_axis,
+            "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,
         "launch": mode,
@@ -355,7 +374,8 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, inputs, head_prec, args.cpu_seconds, args.seed)
+        result["cpu_baseline"] = cpu_baseline(w, inputs, head_prec, args.cpu_seconds, args.seed,
+                                              args.scale_axis)
     print(json.dumps(result), flush=True)
 
 

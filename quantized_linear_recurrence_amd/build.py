@@ -29,6 +29,9 @@ COMMON = [
     # no implicit contraction: every fused multiply-add is an explicit fmaf
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # fully unroll the per-element loops (register-resident rows) even where
+    # the unrolled body is large
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     # no packed fp32 instructions in any GPU code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",

@@ -121,13 +121,14 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     }
     u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * cd.unit_bytes) + row;
     if constexpr (KEY) {
-        __shared__ float cmax[kWavesPerGroup * DK];
-        float cm[DK / 64], snew[DK / 16], inv[DK / 16];
+        __shared__ float cmax[2 * kWavesPerGroup * DK];     // maxima, staging
+        float cm[DK / 64], snew[DK / 64], inv[DK / 16];
         col_absmax<DK>(U, cm);
-        key_scales<DK>(cm, cmax, wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv);
-        if (rb == 0 && lane < 16) {
+        key_scales<DK>(cm, cmax, cmax + kWavesPerGroup * DK, wv, rb, meta.n_rb, Prec<PREC>::R,
+                       snew, inv);
+        if (rb == 0) {
 #pragma unroll
-            for (int i = 0; i < DK / 16; ++i) scales[unit * DK + 16 * i + lane] = snew[i];
+            for (int t = 0; t < DK / 64; ++t) scales[unit * DK + key_col(t, lane)] = snew[t];
         }
         requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr, inv);
     } else {

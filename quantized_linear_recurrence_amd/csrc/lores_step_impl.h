@@ -508,28 +508,36 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Column scales of a unit from its wavefronts' column maxima: wavefront wv
-// (row block rb of n_rb, the unit's blocks being wavefronts wv - rb ..
-// wv - rb + n_rb - 1 of the work-group) publishes its maxima in lds[wv][.],
-// then every wavefront of the unit reads all of them back as row vectors:
-// register i of snew / inv holds column 16 i + lane % 16.  snew = fl(m / r),
-// inv = the largest fp32 <= r / m (0 for a zero column).
+// Column scales of a unit from its wavefronts' column maxima.  Wavefront wv
+// (row block rb of n_rb; the unit's blocks are wavefronts wv - rb ..
+// wv - rb + n_rb - 1 of the work-group) publishes its maxima in part[wv][.]
+// and, after the barrier, combines the unit's: lane L then holds column
+// key_col(t, L) of snew = fl(m / r) and of inv = the largest fp32 <= r / m
+// (0 for a zero column).  inv goes through the wavefront's own slot of
+// `stage` to the row-vector form the requantization reads: register i of
+// invrow holds column 16 i + lane % 16.
 template <int DK>
-__device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *lds, int wv, int rb,
-                                           int n_rb, float R, float (&snew)[DK / 16],
-                                           float (&inv)[DK / 16]) {
+__device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *part, float *stage,
+                                           int wv, int rb, int n_rb, float R,
+                                           float (&snew)[DK / 64], float (&invrow)[DK / 16]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < DK / 64; ++t) lds[wv * DK + key_col(t, lane)] = cm[t];
+    for (int t = 0; t < DK / 64; ++t) part[wv * DK + 64 * t + lane] = cm[t];
     lds_barrier();
-    const float *base = lds + (wv - rb) * DK + (lane & 15);
+    const float *base = part + (wv - rb) * DK + lane;
+    float *mine = stage + wv * DK;
 #pragma unroll
-    for (int i = 0; i < DK / 16; ++i) {
-        float m = base[16 * i];
-        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DK + 16 * i]);
-        snew[i] = m / R;
-        inv[i] = rd_div(R, m);
+    for (int t = 0; t < DK / 64; ++t) {
+        float m = base[64 * t];
+        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DK + 64 * t]);
+        snew[t] = m / R;
+        mine[key_col(t, lane)] = rd_div(R, m);
     }
+    // this wavefront's own writes, read back by its other lanes: LDS keeps a
+    // wavefront's accesses in order, the compiler must not reorder them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < DK / 16; ++i) invrow[i] = mine[16 * i + (lane & 15)];
 }
 
 template <bool BF16IN>
@@ -730,9 +738,10 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                 for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
             }
             if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
-            // keep the next chunk's draws after this store: unpinned, the
-            // whole (cheap, input-independent) chain is computed up front
-            // and held in registers
+            // key-column rows: keep the next chunk's draws after this store
+            // (unpinned, the cheap, input-independent chain may be computed
+            // up front and held in registers)
+            if constexpr (KEY) asm volatile("" : "+v"(x));
         }
     }
 }
@@ -751,17 +760,21 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 // Per-task values loaded ahead of the task, besides its chunks: the row
 // scale and v of this lane's row, beta and a scalar alpha, and k, q and a
 // per-channel alpha as row vectors (NV registers each).
-// With key-column scales, sv holds the unit's column scales as a row vector.
+// With key-column scales, sl and al hold the unit's column scales and a
+// per-channel alpha in lane form (lane L: columns 64 t + L), two registers
+// each at d_k = 128; the row vectors of their product are built at the start
+// of the task.
 template <int NV, bool KEY = false>
 struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
-    float kv[NV], qv[NV], av[NV];
-    float sv[KEY ? NV : 1];
+    float kv[NV], qv[NV], av[KEY ? 1 : NV];
+    float sl[KEY ? NV / 4 : 1], al[KEY ? NV / 4 : 1];
 };
 
 // KEY: key-column scales (d_k per unit); the unit's row blocks are the
 // wavefronts wv - rb .. wv - rb + n_rb - 1 of one work-group, and `lds`
-// holds two buffers of kWavesPerGroup x DK column maxima.
+// holds two buffers of kWavesPerGroup x DK column maxima (tasks alternate
+// between them) and a kWavesPerGroup x DK staging area.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false>
 struct TaskStream {
     static constexpr int E = Prec<PREC>::E;
@@ -817,7 +830,10 @@ struct TaskStream {
         if constexpr (C0 != 0) return;
         if constexpr (KEY) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) in.sv[i] = scales[unit * DK + 16 * i + (threadIdx.x & 15)];
+            for (int t = 0; t < NV / 4; ++t) {
+                in.sl[t] = scales[unit * DK + 64 * t + (threadIdx.x & 63)];
+                if constexpr (PC) in.al[t] = alphap[bh * DK + 64 * t + (threadIdx.x & 63)];
+            }
         } else if constexpr (has_scale<PREC>()) {
             in.s = scales[unit * dv_pad + lrow];
         }
@@ -830,7 +846,7 @@ struct TaskStream {
         for (int i = 0; i < NV; ++i) {
             in.kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
             in.qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
-            if constexpr (PC) in.av[i] = alphap[kb + 16 * i];
+            if constexpr (PC && !KEY) in.av[i] = alphap[kb + 16 * i];
         }
     }
 
@@ -846,11 +862,18 @@ struct TaskStream {
         const float beta = in.beta;
         const float alpha_s = in.alpha;
         float a = 0.0f, na = 0.0f;
-        // key columns: sig_j = fl(s_j * alpha_j) as a row vector
+        // key columns: sig_j = fl(s_j * alpha_j), turned into row vectors
+        // through this wavefront's staging slot
         float sig[KEY ? NV : 1];
         if constexpr (KEY) {
+            const int lane = threadIdx.x & 63;
+            float *mine = lds + 2 * kWavesPerGroup * DK +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DK;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) sig[i] = in.sv[i] * (PC ? in.av[i] : alpha_s);
+            for (int t = 0; t < NV / 4; ++t) mine[64 * t + lane] = in.sl[t] * (PC ? in.al[t] : alpha_s);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < NV; ++i) sig[i] = mine[16 * i + (lane & 15)];
         } else if constexpr (is_int<PREC>() && !PC) {
             a = s * alpha_s;
             na = a * -Prec<PREC>::OFF;
@@ -950,14 +973,15 @@ struct TaskStream {
         // ---- pass 3: requantize and store in place
         if constexpr (KEY) {
             // column maxima of the unit's rows, fresh column scales
-            float cm[DK / 64], snew[NV], inv[NV];
+            float cm[DK / 64], snew[DK / 64], inv[NV];
             col_absmax<DK>(U, cm);
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DK), wv, rb, meta.n_rb,
-                           Prec<PREC>::R, snew, inv);
-            if (rb == 0 && (threadIdx.x & 63) < 16) {
+            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DK), lds + 2 * kWavesPerGroup * DK,
+                           wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv);
+            if (rb == 0) {
 #pragma unroll
-                for (int i = 0; i < NV; ++i) scales[unit * DK + 16 * i + (threadIdx.x & 15)] = snew[i];
+                for (int t = 0; t < DK / 64; ++t)
+                    scales[unit * DK + key_col(t, threadIdx.x & 63)] = snew[t];
             }
             requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr,
                                            inv);
@@ -1065,7 +1089,7 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         // the last task still takes part in the work-group's barriers: one
         // per sequence of its stride, as a working wave does.
         static_assert(P1 < 0, "key-column scales run one class per launch");
-        __shared__ float cmax[2 * kWavesPerGroup * DK];
+        __shared__ float cmax[3 * kWavesPerGroup * DK];    // two maxima buffers, staging
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) {
             for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
