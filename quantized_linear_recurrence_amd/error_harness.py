@@ -32,8 +32,9 @@ import math
 
 import numpy as np
 
-from . import (LORES_FP32, LORES_ROUND_NEAREST, LORES_ROUND_STOCHASTIC, lores_decode_step,
-               lores_dequant_state, lores_state_alloc, lores_state_set_rounding)
+from . import (LORES_FP32, LORES_ROUND_NEAREST, LORES_ROUND_STOCHASTIC, LORES_SCALE_KEY,
+               LORES_SCALE_VALUE, lores_decode_step, lores_dequant_state, lores_quant_state,
+               lores_state_alloc, lores_state_set_rounding)
 
 
 def sample_points(T, n=24):
@@ -44,9 +45,10 @@ def sample_points(T, n=24):
 
 def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_lo=0.9,
                      alpha_hi=0.999, beta=0.5, drift=0.05, rounding=LORES_ROUND_STOCHASTIC,
-                     seed=0, points=None, device="cuda"):
+                     seed=0, points=None, device="cuda", scale_axis=LORES_SCALE_VALUE):
     """Run T steps of a state with per-head precisions `head_prec` (a list,
-    or a function of the per-head decays giving one) and of its fp32 twin;
+    or a function of the per-head decays giving one; scales per value row or,
+    with scale_axis = LORES_SCALE_KEY, per key column) and of its fp32 twin;
     return {"t": [...], "rel_err": [H lists], "o_rel_err": [H lists],
     "alpha": [H], "head_prec": [H]} with errors averaged over the B
     sequences at each sampled t.
@@ -71,7 +73,7 @@ def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_l
 
     if callable(head_prec):
         head_prec = head_prec(alpha_h.cpu().numpy())
-    sq = lores_state_alloc(B, H, d_k, d_v, list(head_prec), device=dev)
+    sq = lores_state_alloc(B, H, d_k, d_v, list(head_prec), device=dev, scale_axis=scale_axis)
     lores_state_set_rounding(sq, rounding)
     sf = lores_state_alloc(B, H, d_k, d_v, [LORES_FP32] * H, device=dev)
     oq = torch.empty((B, H, d_v), dtype=f32, device=dev)
@@ -144,24 +146,76 @@ def decay_assigned(H, tiers):
     return f
 
 
+def grouping_readout_error(prec, B=64, H=8, d_k=128, d_v=128, row_spread=2.0, col_spread=2.0,
+                           seed=0, device="cuda"):
+    """Readout error of one quantization of synthetic states under value-row
+    and key-column scales, against Proposition 1 ("Intra-State Quantization
+    (Section 4)"): with round to nearest and a uniform rounding error,
+    E[e_i^2] = M_i^2 / 12 r^2 (value rows; M_i the row range, |q| = 1) and
+    sum_j q_j^2 C_j^2 / 12 r^2 (key columns; C_j the column range).  States
+    S_ij = g_ij exp(a_i) exp(b_j) with a_i ~ U(-row_spread, row_spread),
+    b_j ~ U(-col_spread, col_spread): the row spread favours value rows, the
+    column spread key columns.  Quantized by lores_quant_state (nearest mode)
+    and read back by lores_dequant_state; returns measured and predicted mean
+    e_i^2 per grouping."""
+    import torch
+
+    r = {2: 127, 3: 7, 4: 31}[prec]
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    f64 = torch.float64
+    a = (2 * torch.rand(B, H, d_v, 1, generator=g, device=dev) - 1) * row_spread
+    b = (2 * torch.rand(B, H, 1, d_k, generator=g, device=dev) - 1) * col_spread
+    X = (torch.randn(B, H, d_v, d_k, generator=g, device=dev) * a.exp() * b.exp()).float().contiguous()
+    q = torch.randn(B, H, d_k, generator=g, device=dev, dtype=f64)
+    q = q / q.norm(dim=-1, keepdim=True)
+    Xd = X.double()
+    M = Xd.abs().amax(dim=3)                                     # [B, H, d_v]
+    C = Xd.abs().amax(dim=2)                                     # [B, H, d_k]
+    pred = {"value": (M ** 2).mean().item() / (12 * r * r),
+            "key": ((q ** 2 * C ** 2).sum(-1, keepdim=True).expand(B, H, d_v)).mean().item()
+            / (12 * r * r)}
+    out = {"prec": prec, "row_spread": row_spread, "col_spread": col_spread}
+    for name, axis in (("value", LORES_SCALE_VALUE), ("key", LORES_SCALE_KEY)):
+        st = lores_state_alloc(B, H, d_k, d_v, [prec] * H, device=dev, scale_axis=axis)
+        lores_state_set_rounding(st, LORES_ROUND_NEAREST)
+        lores_quant_state(st, X, seed)
+        E = lores_dequant_state(st).double() - Xd
+        e = (E @ q.unsqueeze(-1)).squeeze(-1)                    # [B, H, d_v]
+        out[name] = {"mean_e2": (e ** 2).mean().item(), "prop1": pred[name]}
+    return out
+
+
 def run_suite(T=2048, B=32, H=12, d=128, seed=1, device="cuda"):
     """The harness's report: random writes (drift 100), scalar decay, delta
-    = 0, two decay regimes; int8, E4M3, int6 and int4 states and the decay-assigned
-    mixes that keep the slowest half of the heads at 8 or 6 bits (6.25 and
-    5.25 effective bits); stochastic and nearest rounding."""
+    = 0, two decay regimes; int8, E4M3, int6 and int4 states, int8 and int4
+    with key-column scales, and the decay-assigned mixes that keep the
+    slowest half of the heads at 8 or 6 bits (6.25 and 5.25 effective bits);
+    stochastic and nearest rounding.  Then Proposition 1's value-row versus
+    key-column readout error on states with row or column outliers."""
     names = {0: "stochastic", 1: "nearest"}
     rows = []
     for lo, hi in ((0.9, 1.0), (0.99, 1.0)):
-        for label, prec in (("int8", [2] * H), ("fp8 (E4M3)", [5] * H), ("int6", [4] * H),
-                            ("int4", [3] * H),
-                            ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)])),
-                            ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]))):
+        for label, prec, axis in (
+                ("int8", [2] * H, LORES_SCALE_VALUE), ("fp8 (E4M3)", [5] * H, LORES_SCALE_VALUE),
+                ("int6", [4] * H, LORES_SCALE_VALUE), ("int4", [3] * H, LORES_SCALE_VALUE),
+                ("int8, key columns", [2] * H, LORES_SCALE_KEY),
+                ("int4, key columns", [3] * H, LORES_SCALE_KEY),
+                ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)]),
+                 LORES_SCALE_VALUE),
+                ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]),
+                 LORES_SCALE_VALUE)):
             for rnd in (LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST):
                 res = error_trajectory(prec, B=B, d_k=d, d_v=d, T=T, delta=0, alpha_lo=lo,
                                        alpha_hi=hi, beta=0.5, drift=100.0, rounding=rnd, seed=seed,
-                                       device=device)
+                                       device=device, scale_axis=axis)
                 rows.append({"decay": [lo, hi], "state": label, "rounding": names[rnd],
                              "effective_bits": effective_bits(res["head_prec"], d),
                              "mean_rel_err_T": float(np.mean([e[-1] for e in res["rel_err"]])),
                              "by_decay_bin": summarize(res, bins=3)})
+    for prec in (2, 4):
+        for rs, cs in ((2.0, 0.0), (0.0, 2.0), (1.0, 1.0)):
+            rows.append({"grouping": grouping_readout_error(prec, row_spread=rs, col_spread=cs,
+                                                            seed=seed, device=device)})
     return rows

@@ -94,3 +94,22 @@ def test_int8_beats_e4m3_at_the_same_bits():
     ef = np.mean([e[-1] for e in _run(5, 0.9, 1.0, SR, T=512)["rel_err"]])
     log(f"int8 {e8:.4f} fp8 {ef:.4f}")
     assert e8 < ef
+
+
+@pytest.mark.parametrize("prec", [2, 4])
+def test_grouping_readout_error_follows_proposition1(prec):
+    """One quantization under value-row and key-column scales: the measured
+    readout error matches Proposition 1's formula for each grouping, and the
+    grouping that wins follows the outlier structure (value rows with row
+    outliers, key columns with column outliers)."""
+    log(f"case: Proposition 1 value rows vs key columns, prec={prec}")
+    rows = eh.grouping_readout_error(prec, row_spread=2.0, col_spread=0.0, seed=3)
+    cols = eh.grouping_readout_error(prec, row_spread=0.0, col_spread=2.0, seed=3)
+    for res in (rows, cols):
+        for name in ("value", "key"):
+            ratio = res[name]["mean_e2"] / res[name]["prop1"]
+            log(f"  spread rows={res['row_spread']} cols={res['col_spread']} {name}: "
+                f"measured/Prop1 = {ratio:.3f}")
+            assert 0.85 < ratio < 1.05, (res, name, ratio)
+    assert rows["value"]["mean_e2"] < 0.5 * rows["key"]["mean_e2"], rows
+    assert cols["key"]["mean_e2"] < 0.5 * cols["value"]["mean_e2"], cols
