@@ -15,6 +15,9 @@ Source pages, cited by title and section:
           Proposition 1, decay-based mixed precision, Proposition 2,
           rounding, Proposition 3) and the paper abstract (value-axis
           scale grouping, decay-based mixed precision, stochastic rounding).
+  [PACE]  "PACE: Periodic and Channel-Aligned Encoding of Four-Bit Recurrent
+          States", abstract (rounding once every few tokens with a buffer;
+          column scales); [LeapQuant] abstract (per-window quantization).
 
 Parity status per function (what pins it is listed in each module):
   exact.fma32 / exact.rd_div32 / exact.rn_div32 .... pinned (Fraction brute force)
@@ -25,6 +28,11 @@ Parity status per function (what pins it is listed in each module):
   step.decode_step (fp32 heads) .................... pinned (closed forms, bounds)
   step.decode_step (int8 / int4 / bf16 heads) ...... pinned (exhaustive SR, bounds,
        Propositions 1-3)
+  step.quantize_rows / decode_step, axis="key" ..... pinned (hand-worked codes,
+       rank-one structure, transpose identity, unbiasedness, variance)
   assign.decay_stat / assign.assign_precision ...... pinned (hand-worked cases)
+  window.window_step / replay ...................... pinned (W = 1 is the per-step
+       step; closed forms for delta = 0; the fp64 recurrence inside a window;
+       one rounding per window)
 """
-from . import exact, rng, step, assign  # noqa: F401
+from . import exact, rng, step, assign, window  # noqa: F401
