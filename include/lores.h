@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 4
+#define LORES_SPEC_VERSION 5
 
 /* Per-head state precision. */
 enum {
@@ -83,6 +83,7 @@ enum {
 #define LORES_MAX_HEADS 512 /* heads per state                                   */
 #define LORES_MAX_DV 256    /* value rows per head                               */
 #define LORES_ROW_BLOCK 64  /* value rows per stored row block (one wavefront)   */
+#define LORES_MAX_WINDOW 16 /* steps per requantization window                   */
 
 /* Opaque host handle: dimensions, per-head precision, layout and the bound
  * device buffer.  Created by lores_state_alloc, released by lores_state_free. */
@@ -97,6 +98,8 @@ typedef struct lores_state lores_state;
  *   codes  [B][H_c][n_chunk][d_v_pad][16 bytes]
  *   scales [B][H_c][d_v_pad] fp32                 (int8, int4, int6, fp8 classes)
  *          [B][H_c][d_k] fp32                     (the same, key-column scales)
+ *   window [B][H_c][unit_window_bytes]            (scaled classes of a windowed
+ *                                                  state, window W > 1)
  *
  * H_c = heads of class c, ordered by head index (head_slot below).
  * d_v_pad = d_v rounded up to LORES_ROW_BLOCK; padding rows are never read
@@ -117,6 +120,10 @@ typedef struct lores_state lores_state;
  * The value of an int element is scale[row] * code (scale[column] * code
  * with key-column scales).  A row of all-zero bytes with scale 0 also reads
  * as zero, so a zero-filled buffer is S = 0.
+ * A unit's window block holds W - 1 token slots: g [W-1][d_v_pad] fp32 (the
+ * write vector of the token), then k [W-1][d_k] fp32, then alpha [W-1] fp32,
+ * the whole block padded to 16 bytes.  Slot tau - 1 holds token tau of the
+ * current window (lores_state_alloc_window).
  */
 typedef struct {
     int32_t B, H, d_k, d_v, d_v_pad;
@@ -127,6 +134,10 @@ typedef struct {
     uint64_t total_bytes;      /* bytes the caller's buffer must hold           */
     int32_t scale_axis;        /* LORES_SCALE_VALUE or LORES_SCALE_KEY          */
     int32_t unit_scales;       /* fp32 scales per (sequence, head): d_v_pad or d_k */
+    int32_t window;            /* W: steps per requantization (1: every step)   */
+    int32_t window_fill;       /* tokens of the current window in the buffer    */
+    int64_t window_offset[LORES_NUM_PREC];    /* byte offset of class windows, -1 */
+    int64_t unit_window_bytes[LORES_NUM_PREC];/* window bytes per unit, 0       */
 } lores_layout;
 
 /*
@@ -164,6 +175,33 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
 int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                            const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
                            size_t *bytes, void *stream, lores_state **out);
+
+/*
+ * lores_state_alloc_window - lores_state_alloc for a state whose scaled heads
+ * (int8, int4, int6, fp8; value-row scales) are requantized once per window
+ * of W steps instead of every step, the window's tokens being kept at fp32
+ * in a per-unit buffer (the reading of the PACE and LeapQuant abstracts:
+ * rounding once every few tokens, with the tokens in between buffered, cuts
+ * the error that accumulates in the state).  Windows are the steps
+ * t = kW + 1 .. (k + 1) W.  Inside a window the stored state is the state at
+ * the window start, X_0, and is not written; step t at position
+ * p = (t - 1) mod W + 1 < W computes g, o from X_0 and the buffered tokens
+ * and appends (g, k, alpha) to the buffer; the step at p = W rebuilds the
+ * state by the fp32 recurrence (S'_1 = fl(c fl(s alpha_1)), then
+ * U_tau = fma(g_tau, k_tau, S'_tau), S'_tau = fl(U_{tau-1} alpha_tau)), steps
+ * it and requantizes it as lores_decode_step does.  W = 1 is
+ * lores_state_alloc.  fp32 and bf16 heads step every token as usual.
+ *   window      W, 1 <= W <= LORES_MAX_WINDOW
+ * Built for d_k in {64, 128} when W > 1 (LORES_EUNSUPPORTED otherwise).
+ * Steps on a windowed state must come in order (t = 1, 2, ... from the
+ * allocation or a lores_quant_state; the handle counts the buffered tokens
+ * and lores_decode_step returns LORES_EINVAL for a step t whose window
+ * position does not follow them), with a scalar alpha (alpha_per_channel = 0,
+ * else LORES_EUNSUPPORTED).  Each scaled class runs one launch per step.
+ */
+int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                             const uint8_t *head_prec, int32_t window, void *d_buf,
+                             size_t *bytes, void *stream, lores_state **out);
 
 void lores_state_free(lores_state *st);
 
@@ -260,7 +298,9 @@ int lores_step_launches(const lores_state *st, int32_t *n);
 /*
  * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32,
  * value = scale * code for int heads (the row's or the column's scale), the
- * stored value for bf16 / fp32 heads.
+ * stored value for bf16 / fp32 heads.  For a windowed state with buffered
+ * tokens: the current state, the stored state followed by the buffered
+ * tokens' fp32 recurrence (as lores_state_alloc_window describes).
  */
 int lores_dequant_state(const lores_state *st, float *out, void *stream);
 
@@ -278,7 +318,8 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream);
  *              lores_dequant_state writes), finite
  *   seed, seq_base, head_base   as for lores_decode_step
  * LORES_EINVAL on a NULL or misaligned X or out-of-range bases; nothing is
- * launched then.
+ * launched then.  On a windowed state it also empties the window buffer: the
+ * next step is a window's first (t = 1, W + 1, ...).
  */
 int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t seq_base,
                       int64_t head_base, void *stream);

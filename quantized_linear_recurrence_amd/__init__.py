@@ -15,13 +15,14 @@ import numpy as np
 
 from . import _lib
 from ._lib import (LORES_BF16, LORES_FP8, LORES_FP32, LORES_INT4, LORES_INT6, LORES_INT8,
-                   LORES_ROUND_NEAREST, LORES_ROUND_STOCHASTIC, LORES_SCALE_KEY,
+                   LORES_MAX_WINDOW, LORES_ROUND_NEAREST, LORES_ROUND_STOCHASTIC, LORES_SCALE_KEY,
                    LORES_SCALE_VALUE, LoresLayout, LoresLibraryMissing)
 
 __all__ = ["LORES_FP32", "LORES_BF16", "LORES_INT8", "LORES_INT4", "LORES_INT6", "LORES_FP8",
            "LORES_ROUND_STOCHASTIC", "LORES_ROUND_NEAREST", "LORES_SCALE_VALUE", "LORES_SCALE_KEY",
            "LoresError", "lores_state_set_rounding",
-           "LoresLibraryMissing", "LoresState", "lores_state_alloc", "lores_state_alloc_axis",
+           "LORES_MAX_WINDOW", "LoresLibraryMissing", "LoresState", "lores_state_alloc",
+           "lores_state_alloc_axis", "lores_state_alloc_window",
            "lores_state_layout",
            "lores_state_head_map", "lores_decay_stat", "lores_assign_precision",
            "lores_decode_step", "lores_step_launches", "lores_quant_state", "lores_dequant_state",
@@ -81,7 +82,8 @@ class LoresState:
     is freed when this object is garbage-collected.
     """
 
-    def __init__(self, handle, buf, B, H, d_k, d_v, head_prec, scale_axis=LORES_SCALE_VALUE):
+    def __init__(self, handle, buf, B, H, d_k, d_v, head_prec, scale_axis=LORES_SCALE_VALUE,
+                 window=1):
         self._h = handle
         self.buf = buf
         self.device = buf.device
@@ -89,6 +91,7 @@ class LoresState:
         self.head_prec = list(head_prec)
         self.rounding = LORES_ROUND_STOCHASTIC
         self.scale_axis = scale_axis
+        self.window = window
 
     @property
     def handle(self):
@@ -105,22 +108,32 @@ class LoresState:
 
 
 def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=None,
-                      scale_axis=LORES_SCALE_VALUE):
+                      scale_axis=LORES_SCALE_VALUE, window=1):
     """Plan the packed layout; size query if device and buf are both None.
 
     Returns the byte size (size query) or a LoresState whose buffer (a new
     torch uint8 tensor on `device`, or the given `buf`) is cleared to S_0 = 0
     on `stream`.  scale_axis: LORES_SCALE_VALUE (one scale per value row,
     lores_state_alloc) or LORES_SCALE_KEY (one per key column,
-    lores_state_alloc_axis).
+    lores_state_alloc_axis).  window > 1: requantize the scaled heads once per
+    window of that many steps (lores_state_alloc_window; value-row scales).
     """
     L = _lib.lib()
     hp, hp_ptr = _host_array(head_prec, np.uint8)
     if hp.size != H:
         raise ValueError(f"head_prec must have H = {H} entries")
+    window = int(window)
+    if window != 1 and int(scale_axis) != LORES_SCALE_VALUE:
+        raise ValueError("windowed states keep value-row scales")
+
+    def alloc(ptr, size, stream_ptr, out):
+        if window != 1:
+            return L.lores_state_alloc_window(B, H, d_k, d_v, hp_ptr, window, ptr, size,
+                                              stream_ptr, out)
+        return L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis), ptr, size,
+                                        stream_ptr, out)
     nbytes = ctypes.c_size_t(0)
-    _check(L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis), None,
-                                    ctypes.byref(nbytes), None, None))
+    _check(alloc(None, ctypes.byref(nbytes), None, None))
     if device is None and buf is None:
         return nbytes.value
     import torch
@@ -129,13 +142,13 @@ def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=N
     device = buf.device
     size = ctypes.c_size_t(buf.numel() * buf.element_size())
     out = ctypes.c_void_p()
-    _check(L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis),
-                                    ctypes.c_void_p(buf.data_ptr()), ctypes.byref(size),
-                                    _stream_ptr(stream, device), ctypes.byref(out)))
-    return LoresState(out.value, buf, B, H, d_k, d_v, hp.tolist(), int(scale_axis))
+    _check(alloc(ctypes.c_void_p(buf.data_ptr()), ctypes.byref(size), _stream_ptr(stream, device),
+                 ctypes.byref(out)))
+    return LoresState(out.value, buf, B, H, d_k, d_v, hp.tolist(), int(scale_axis), window)
 
 
 lores_state_alloc_axis = lores_state_alloc
+lores_state_alloc_window = lores_state_alloc
 
 
 def lores_state_layout(state):
@@ -145,7 +158,10 @@ def lores_state_layout(state):
             "n_class": list(lay.n_class), "codes_offset": list(lay.codes_offset),
             "scales_offset": list(lay.scales_offset),
             "unit_code_bytes": list(lay.unit_code_bytes), "total_bytes": lay.total_bytes,
-            "scale_axis": lay.scale_axis, "unit_scales": lay.unit_scales}
+            "scale_axis": lay.scale_axis, "unit_scales": lay.unit_scales,
+            "window": lay.window, "window_fill": lay.window_fill,
+            "window_offset": list(lay.window_offset),
+            "unit_window_bytes": list(lay.unit_window_bytes)}
 
 
 def lores_state_head_map(state):

@@ -8,17 +8,19 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblores.so")
 
-SPEC_VERSION = 4                     # LORES_SPEC_VERSION of include/lores.h
+SPEC_VERSION = 5                     # LORES_SPEC_VERSION of include/lores.h
 LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4, LORES_INT6, LORES_FP8 = 0, 1, 2, 3, 4, 5
 NUM_PREC = 6
 LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST = 0, 1
 LORES_SCALE_VALUE, LORES_SCALE_KEY = 0, 1
+LORES_MAX_WINDOW = 16
 LORES_OK, LORES_EINVAL, LORES_EUNSUPPORTED, LORES_ESIZE, LORES_EHIP, LORES_ENOMEM = 0, -1, -2, -3, -4, -5
 STATUS_NAMES = {0: "LORES_OK", -1: "LORES_EINVAL", -2: "LORES_EUNSUPPORTED", -3: "LORES_ESIZE",
                 -4: "LORES_EHIP", -5: "LORES_ENOMEM"}
 
 # every symbol include/lores.h declares
-EXPORTS = ("lores_state_alloc", "lores_state_alloc_axis", "lores_state_free", "lores_state_layout", "lores_state_head_map",
+EXPORTS = ("lores_state_alloc", "lores_state_alloc_axis", "lores_state_alloc_window",
+           "lores_state_free", "lores_state_layout", "lores_state_head_map",
            "lores_decay_stat", "lores_assign_precision", "lores_decode_step",
            "lores_step_launches", "lores_state_set_rounding", "lores_quant_state",
            "lores_dequant_state",
@@ -36,7 +38,10 @@ class LoresLayout(ctypes.Structure):
                 ("scales_offset", ctypes.c_int64 * NUM_PREC),
                 ("unit_code_bytes", ctypes.c_int64 * NUM_PREC),
                 ("total_bytes", ctypes.c_uint64),
-                ("scale_axis", ctypes.c_int32), ("unit_scales", ctypes.c_int32)]
+                ("scale_axis", ctypes.c_int32), ("unit_scales", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("window_fill", ctypes.c_int32),
+                ("window_offset", ctypes.c_int64 * NUM_PREC),
+                ("unit_window_bytes", ctypes.c_int64 * NUM_PREC)]
 
 
 _lib = None
@@ -58,6 +63,9 @@ def lib():
     L.lores_state_alloc_axis.argtypes = [i32, i32, i32, i32, vp, i32, vp,
                                          ctypes.POINTER(ctypes.c_size_t), vp, ctypes.POINTER(vp)]
     L.lores_state_alloc_axis.restype = ctypes.c_int
+    L.lores_state_alloc_window.argtypes = [i32, i32, i32, i32, vp, i32, vp,
+                                           ctypes.POINTER(ctypes.c_size_t), vp, ctypes.POINTER(vp)]
+    L.lores_state_alloc_window.restype = ctypes.c_int
     L.lores_state_free.argtypes = [vp]
     L.lores_state_free.restype = None
     L.lores_state_layout.argtypes = [vp, ctypes.POINTER(LoresLayout)]

@@ -25,6 +25,9 @@ struct lores_state {
     uint8_t *base;
     int32_t rounding;        // LORES_ROUND_*
     int32_t axis;            // LORES_SCALE_*
+    int32_t window;          // W: steps per requantization of the scaled classes
+    int32_t n_buf;           // tokens of the current window held in the buffer
+    int64_t win_off[LORES_NUM_PREC], unit_win[LORES_NUM_PREC];   // bytes
 };
 
 namespace {
@@ -94,7 +97,8 @@ int plan(lores_state *st, const uint8_t *head_prec) {
     st->n_rb = st->dv_pad / LORES_ROW_BLOCK;
     uint64_t off = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c) {
-        st->codes_off[c] = st->scales_off[c] = -1;
+        st->codes_off[c] = st->scales_off[c] = st->win_off[c] = -1;
+        st->unit_win[c] = 0;
         st->unit_bytes[c] = row_bytes(c, st->dk) * st->dv_pad;
         if (!st->n_class[c]) continue;
         const double units = (double)st->B * st->n_class[c];
@@ -106,6 +110,14 @@ int plan(lores_state *st, const uint8_t *head_prec) {
             off = align256(off);
             st->scales_off[c] = (int64_t)off;
             off += (uint64_t)st->B * st->n_class[c] * unit_scales(st) * sizeof(float);
+        }
+        st->win_off[c] = -1;
+        st->unit_win[c] = 0;
+        if (has_scales(c) && st->window > 1) {
+            st->unit_win[c] = lores::window_unit_floats(st->window, st->dv_pad, st->dk) * 4;
+            off = align256(off);
+            st->win_off[c] = (int64_t)off;
+            off += (uint64_t)st->B * st->n_class[c] * st->unit_win[c];
         }
         // launch grid: y = sequence (at most 65535), x = groups of row-block tasks
     }
@@ -196,9 +208,9 @@ const char *lores_last_error(void) { return g_err.c_str(); }
 
 int lores_spec_version(void) { return LORES_SPEC_VERSION; }
 
-int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
-                           const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
-                           size_t *bytes, void *stream, lores_state **out) {
+static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint8_t *head_prec,
+                      int32_t scale_axis, int32_t window, void *d_buf, size_t *bytes,
+                      void *stream, lores_state **out) {
     try {
         int rc = check_dims(B, H, d_k, d_v);
         if (rc) return rc;
@@ -224,6 +236,8 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
         tmp.base = nullptr;
         tmp.rounding = LORES_ROUND_STOCHASTIC;
         tmp.axis = scale_axis;
+        tmp.window = window;
+        tmp.n_buf = 0;
         rc = plan(&tmp, head_prec);
         if (rc) return rc;
         if (!d_buf) {
@@ -250,10 +264,27 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
     }
 }
 
+int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                           const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
+                           size_t *bytes, void *stream, lores_state **out) {
+    return alloc_impl(B, H, d_k, d_v, head_prec, scale_axis, 1, d_buf, bytes, stream, out);
+}
+
 int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint8_t *head_prec,
                       void *d_buf, size_t *bytes, void *stream, lores_state **out) {
-    return lores_state_alloc_axis(B, H, d_k, d_v, head_prec, LORES_SCALE_VALUE, d_buf, bytes,
-                                  stream, out);
+    return alloc_impl(B, H, d_k, d_v, head_prec, LORES_SCALE_VALUE, 1, d_buf, bytes, stream, out);
+}
+
+int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
+                             const uint8_t *head_prec, int32_t window, void *d_buf,
+                             size_t *bytes, void *stream, lores_state **out) {
+    if (window < 1 || window > LORES_MAX_WINDOW)
+        return fail(LORES_EINVAL, "window must be in [1, %d] (got %d)", LORES_MAX_WINDOW, window);
+    if (window > 1 && d_k != 64 && d_k != 128)
+        return fail(LORES_EUNSUPPORTED, "windowed states are built for d_k = 64 and 128 (got %d)",
+                    d_k);
+    return alloc_impl(B, H, d_k, d_v, head_prec, LORES_SCALE_VALUE, window, d_buf, bytes, stream,
+                      out);
 }
 
 void lores_state_free(lores_state *st) { delete st; }
@@ -274,6 +305,12 @@ int lores_state_layout(const lores_state *st, lores_layout *out) {
     out->total_bytes = st->total;
     out->scale_axis = st->axis;
     out->unit_scales = (int32_t)unit_scales(st);
+    out->window = st->window;
+    out->window_fill = st->n_buf;
+    for (int c = 0; c < LORES_NUM_PREC; ++c) {
+        out->window_offset[c] = st->win_off[c];
+        out->unit_window_bytes[c] = st->unit_win[c];
+    }
     return ok();
 }
 
@@ -363,7 +400,8 @@ static int plan_launches(const lores_state *st, int groups[LORES_NUM_PREC][2],
     int present[LORES_NUM_PREC], n = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c)
         if (st->n_class[c]) present[n++] = c;
-    if (n == 2 && st->axis == LORES_SCALE_VALUE && lores::fusable_pair(present[0], present[1])) {
+    if (n == 2 && st->axis == LORES_SCALE_VALUE && st->window == 1 &&
+        lores::fusable_pair(present[0], present[1])) {
         groups[0][0] = present[0];
         groups[0][1] = present[1];
         width[0] = 2;
@@ -407,6 +445,23 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         if (head_base < 0 || (uint64_t)head_base + (uint64_t)st->H > (1ull << 32))
             return fail(LORES_EINVAL, "head_base + H must lie in [0, 2^32]");
         const hipStream_t s = (hipStream_t)stream;
+        // windowed states: the step's position in its window must follow the
+        // tokens the buffer holds
+        const bool windowed = st->window > 1;
+        int wpos = 1;
+        if (windowed) {
+            bool scaled = false;
+            for (int c = 0; c < LORES_NUM_PREC; ++c) scaled |= st->n_class[c] && has_scales(c);
+            if (scaled && alpha_per_channel)
+                return fail(LORES_EUNSUPPORTED, "windowed states take a scalar alpha per head "
+                                                "(alpha_per_channel = 0)");
+            wpos = (int)((t - 1) % (uint64_t)st->window) + 1;
+            if (wpos != st->n_buf + 1)
+                return fail(LORES_EINVAL, "windowed state: the buffer holds %d tokens of the current "
+                                          "window, so the next step is at window position %d, but "
+                                          "t = %llu is at position %d (steps must come in order)",
+                            st->n_buf, st->n_buf + 1, (unsigned long long)t, wpos);
+        }
         int groups[LORES_NUM_PREC][2], width[LORES_NUM_PREC];
         const int n_launch = plan_launches(st, groups, width);
         for (int l = 0; l < n_launch; ++l) {
@@ -415,6 +470,8 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             m.t = t;
             m.seq_base = seq_base;
             m.head_base = head_base;
+            m.wpos = wpos;
+            m.window = st->window;
             lores::StepPtrs p;
             std::memset(&p, 0, sizeof p);
             p.q = q;
@@ -430,11 +487,18 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             }
             const int p1 = width[l] == 2 ? groups[l][1] : -1;
             const bool key = st->axis == LORES_SCALE_KEY && has_scales(groups[l][0]);
-            hipError_t e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16,
-                                              groups[l][0], p1, p, m, s, key);
+            hipError_t e;
+            if (windowed && has_scales(groups[l][0])) {
+                p.win[0] = (float *)(st->base + st->win_off[groups[l][0]]);
+                e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, p, m, s);
+            } else {
+                e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16, groups[l][0], p1, p,
+                                       m, s, key);
+            }
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "decode-step launch failed: %s", hipGetErrorString(e));
         }
+        if (windowed) st->n_buf = wpos == st->window ? 0 : wpos;
         return ok();
     } catch (...) {
         return fail(LORES_EINVAL, "internal error in lores_decode_step");
@@ -464,6 +528,7 @@ int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t se
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "quantize launch failed: %s", hipGetErrorString(e));
         }
+        st->n_buf = 0;
         return ok();
     } catch (...) {
         return fail(LORES_EINVAL, "internal error in lores_quant_state");
@@ -478,9 +543,18 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
             if (!st->n_class[c]) continue;
             lores::StepMeta m = make_meta(st, &c, 1);
             const float *sc = has_scales(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
-            hipError_t e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
-                                                 (hipStream_t)stream,
-                                                 st->axis == LORES_SCALE_KEY && has_scales(c));
+            hipError_t e;
+            if (st->window > 1 && st->n_buf > 0 && has_scales(c)) {
+                m.wpos = st->n_buf;
+                m.window = st->window;
+                e = lores::launch_window_dequant(c, st->dk, st->base + st->codes_off[c], sc,
+                                                 (const float *)(st->base + st->win_off[c]), out, m,
+                                                 (hipStream_t)stream);
+            } else {
+                e = lores::launch_dequant(c, st->dk, st->base + st->codes_off[c], sc, out, m,
+                                          (hipStream_t)stream,
+                                          st->axis == LORES_SCALE_KEY && has_scales(c));
+            }
             if (e != hipSuccess) return fail(LORES_EHIP, "dequant launch failed: %s", hipGetErrorString(e));
         }
         return ok();

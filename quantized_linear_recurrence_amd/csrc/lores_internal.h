@@ -26,6 +26,9 @@ struct ClassDesc {
 struct StepMeta {
     int32_t B, H, dv, dv_pad, n_rb, n_cls;
     int32_t rounding;                  // LORES_ROUND_*
+    int32_t wpos;                      // windowed states: position p of step t (1 .. window),
+                                       // or, for the dequantization, the buffered tokens
+    int32_t window;                    // W (1: requantize every step)
     int32_t pad_;
     uint64_t seed, t;
     int64_t seq_base, head_base;
@@ -40,7 +43,14 @@ struct StepPtrs {
     float *o;
     uint8_t *codes[2];
     float *scales[2];        // int classes, else nullptr
+    float *win[2];           // window buffers of a windowed state, else nullptr
 };
+
+// Floats of one unit's window block: W - 1 slots of g (d_v_pad), k (d_k) and
+// alpha (1), padded to 16 bytes.
+__host__ __device__ inline int64_t window_unit_floats(int window, int dv_pad, int dk) {
+    return ((int64_t)(window - 1) * (dv_pad + dk + 1) + 3) / 4 * 4;
+}
 
 // One launch covers one class or one of the fused pairs (int8, int4),
 // (int4, int6), (bf16, int8), (bf16, int4); `p1` is -1 for a single class.  Returns the
@@ -66,9 +76,19 @@ hipError_t launch_step_key_int4(int, bool, bool, bool, const StepPtrs &, const S
 hipError_t launch_step_key_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_key_fp8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 
+// Windowed states (value-row scales, scalar decay, d_k 64 or 128): the step
+// at window position m.wpos < m.window (read the stored state, buffer the
+// token) or = m.window (rebuild, step and requantize).  One class per launch.
+hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, const StepPtrs &p,
+                              const StepMeta &m, hipStream_t s);
+
 // Dequant uses the same StepMeta with one class; `key`: key-column scales.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
                           float *out, const StepMeta &m, hipStream_t s, bool key);
+// The current state of a windowed class: the stored state followed by the
+// first m.wpos (>= 1) buffered tokens.
+hipError_t launch_window_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
+                                 const float *win, float *out, const StepMeta &m, hipStream_t s);
 hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
                         const StepMeta &m, hipStream_t s, bool key);
 hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);

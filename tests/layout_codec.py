@@ -140,3 +140,38 @@ def write_unit(buf_host, layout, c, unit, state_unit):
     buf_host[cs:cs + cl] = code_bytes
     if ss is not None:
         buf_host[ss:ss + sl] = sc.view(np.uint8)
+
+
+def window_ranges(layout, c, unit):
+    """(start, length) of a unit's window block, or None."""
+    off = layout["window_offset"][c]
+    if off < 0:
+        return None
+    ub = layout["unit_window_bytes"][c]
+    return off + unit * ub, ub
+
+
+def read_window(buf_host, layout, c, unit):
+    """A unit's window buffer as {"g": [W-1, d_v], "k": [W-1, d_k], "alpha": [W-1]}:
+    slots of g [W-1][d_v_pad], then k [W-1][d_k], then alpha [W-1] (fp32)."""
+    W, dvp, dk, dv = layout["window"], layout["d_v_pad"], layout["d_k"], layout["d_v"]
+    s, n = window_ranges(layout, c, unit)
+    f = buf_host[s:s + n].view(np.float32)
+    ns = W - 1
+    g = f[:ns * dvp].reshape(ns, dvp)[:, :dv].copy()
+    k = f[ns * dvp:ns * (dvp + dk)].reshape(ns, dk).copy()
+    a = f[ns * (dvp + dk):ns * (dvp + dk + 1)].copy()
+    return {"g": g, "k": k, "alpha": a}
+
+
+def write_window(buf_host, layout, c, unit, win):
+    W, dvp, dk, dv = layout["window"], layout["d_v_pad"], layout["d_k"], layout["d_v"]
+    s, n = window_ranges(layout, c, unit)
+    f = np.zeros(n // 4, np.float32)
+    ns = W - 1
+    g = np.zeros((ns, dvp), np.float32)
+    g[:, :dv] = win["g"]
+    f[:ns * dvp] = g.reshape(-1)
+    f[ns * dvp:ns * (dvp + dk)] = np.asarray(win["k"], np.float32).reshape(-1)
+    f[ns * (dvp + dk):ns * (dvp + dk + 1)] = win["alpha"]
+    buf_host[s:s + n] = f.view(np.uint8)

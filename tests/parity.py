@@ -283,3 +283,113 @@ def run_free_fp32(w, T, B=None, seed=0, device="cuda"):
         err = np.abs(o.cpu().numpy().reshape(B * w.H, -1) - o_ref).max(axis=1) / scale
         worst = max(worst, float(err.max()))
     return worst
+
+
+def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="random", inputs=None,
+                      device="cuda", rounding="sr"):
+    """Windowed states (lores_state_alloc_window): T steps with per-step
+    resync of the stored state and of the window buffer to the oracle's
+    (oracle.window).  Checked per step: o (1e-3 of the readout scale of the
+    current state), the stored state unchanged inside a window and requantized
+    at window ends (the code rules of Stats), the buffered token (g within
+    1e-5 of |v_i| + the readout scale, times beta; k and alpha exact).
+    Returns Stats."""
+    from oracle import window as owin
+    B = w.B if B is None else B
+    if inputs is None:
+        inputs = make_inputs(w, seed, device, T=T, B=B)
+    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device, window=W)
+    if rounding == "nearest":
+        lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
+    lay = lores.lores_state_layout(st)
+    assert lay["window"] == W
+    _, hslot = lores.lores_state_head_map(st)
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(w.H)]
+    g = np.random.default_rng(4321 + seed)
+    ost, obuf = {}, {}
+    for (b, h) in units:
+        c = head_prec[h]
+        if init == "zero":
+            ost[(b, h)] = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk).items()}
+        else:
+            ost[(b, h)] = random_unit_state(c, w.dv, w.dk, g)
+        obuf[(b, h)] = {k: v[0] for k, v in owin.empty_buffer(1, W, w.dv, w.dk).items()}
+    by_class = {}
+    for (b, h) in units:
+        by_class.setdefault(head_prec[h], []).append((b, h))
+    buf_host = st.buf.cpu().numpy()
+    stats = Stats()
+    stats.g_err = 0.0
+    for t in range(1, T + 1):
+        p = owin.position(t, W)
+        assert lores.lores_state_layout(st)["window_fill"] == p - 1
+        for (b, h), s in ost.items():
+            c = head_prec[h]
+            unit = b * lay["n_class"][c] + hslot[h]
+            lc.write_unit(buf_host, lay, c, unit, s)
+            lc.write_window(buf_host, lay, c, unit, obuf[(b, h)])
+            for a, n in (lc.unit_ranges(lay, c, unit)[:2], lc.unit_ranges(lay, c, unit)[2:],
+                         lc.window_ranges(lay, c, unit)):
+                st.buf[a:a + n].copy_(torch.from_numpy(buf_host[a:a + n]))
+        x = {k: v[t - 1] for k, v in inputs.items()}
+        o = lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], w.delta,
+                                    seed, t)
+        torch.cuda.synchronize()
+        buf_host = st.buf.cpu().numpy()
+        o_host = o.cpu().numpy()
+        xin = {k: v.float().cpu().numpy() for k, v in x.items()}
+        for c, us in by_class.items():
+            bs = np.array([b for b, _ in us])
+            hs = np.array([h for _, h in us])
+            prev = _stack([ost[u] for u in us])
+            pbuf = _stack([obuf[u] for u in us])
+            new, nbuf, o_ref = owin.window_step(
+                c, prev, pbuf, xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs],
+                xin["alpha"][bs, hs], xin["beta"][bs, hs], w.delta, seed, t, bs, hs, W,
+                rounding=rounding)
+            Xcur = owin.replay(c, new, nbuf, 0 if p == W else p)
+            scale = _readout_scale(Xcur)
+            stats.o_err_q = max(stats.o_err_q, float(
+                (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()))
+            units_idx = [b * lay["n_class"][c] + hslot[h] for (b, h) in us]
+            gpu = _stack([lc.read_unit(buf_host, lay, c, u) for u in units_idx])
+            field = "fp8" if c == 5 else "codes"
+            if p < W:
+                # the stored state is not written inside a window
+                assert np.array_equal(gpu[field], prev[field]), (t, c)
+                assert np.array_equal(gpu["scales"].view(np.uint32), prev["scales"].view(np.uint32))
+                gw = _stack([lc.read_window(buf_host, lay, c, u) for u in units_idx])
+                assert np.array_equal(gw["k"][:, p - 1], nbuf["k"][:, p - 1]), (t, c)
+                assert np.array_equal(gw["alpha"][:, p - 1], nbuf["alpha"][:, p - 1]), (t, c)
+                bound = (np.abs(xin["v"][bs, hs]) + scale[:, None]) * np.abs(xin["beta"][bs, hs])[:, None]
+                ge = np.abs(gw["g"][:, p - 1].astype(np.float64) - nbuf["g"][:, p - 1]) / \
+                    np.maximum(bound, 1e-30)
+                stats.g_err = max(stats.g_err, float(ge.max()))
+            elif c == 5:
+                Xg = ostep.dequant(c, gpu).astype(np.float64)
+                Xr = ostep.dequant(c, new).astype(np.float64)
+                diff = gpu["fp8"] != new["fp8"]
+                stats.fp8 += diff.size
+                stats.fp8_diff += int(diff.sum())
+                if diff.any():
+                    rowmax = np.abs(Xr).max(axis=2, keepdims=True)
+                    step = np.maximum(np.abs(Xr), np.abs(Xg)) / 8 + rowmax / 448 * 2.0 ** -9
+                    excess = (np.abs(Xg - Xr) - step) / np.maximum(rowmax, 1e-300)
+                    stats.fp8_excess = max(stats.fp8_excess, float(excess[diff].max()))
+            else:
+                d = np.abs(gpu["codes"].astype(np.int64) - new["codes"])
+                stats.codes += d.size
+                stats.code_diff += int((d > 0).sum())
+                stats.max_dc = max(stats.max_dc, int(d.max()))
+            if p == W:
+                rel = np.abs(gpu["scales"].astype(np.float64) - new["scales"]) / \
+                    np.maximum(np.abs(new["scales"]).astype(np.float64), 1e-38)
+                rel[(new["scales"] == 0) & (gpu["scales"] == 0)] = 0
+                stats.scale_rel = max(stats.scale_rel, float(rel.max()))
+            for i, u in enumerate(us):
+                ost[u] = {kk: vv[i] for kk, vv in new.items()}
+                obuf[u] = {kk: vv[i] for kk, vv in nbuf.items()}
+        stats.steps += 1
+    assert stats.g_err <= 1e-5, stats.g_err
+    return stats

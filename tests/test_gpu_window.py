@@ -1,0 +1,147 @@
+"""GPU parity of windowed requantization (lores_state_alloc_window) against
+the oracle's oracle.window, through the C ABI, and the windowed state's
+contract: in-order steps, scalar decay, the buffer's dequantization, W = 1.
+
+Tolerances: tests/parity.py (run_window_parity).  Every case prints its
+name before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_linear_recurrence_amd as lores
+from oracle import step as ostep
+from oracle import window as owin
+from tests import layout_codec as lc
+from tests.parity import log, random_unit_state, run_window_parity
+from workloads import get_workload, make_inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+C1 = get_workload("C1")
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("prec", [2, 3, 4, 5])
+@pytest.mark.parametrize("W,dk,dv,delta", [(2, 64, 64, 1), (4, 128, 100, 1), (3, 128, 128, 0),
+                                           (5, 64, 200, 1)])
+def test_each_scaled_class(prec, W, dk, dv, delta):
+    w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, delta=delta)
+    log(f"case: window W={W} prec={prec} B=3 H=4 dk={dk} dv={dv} delta={delta}, "
+        f"{w.T} steps from a random state")
+    s = run_window_parity(w, T=w.T, W=W, head_prec=[prec] * w.H)
+    log(s.summary())
+    s.check()
+
+
+def test_mixed_heads_from_zero_nearest():
+    w = C1.scaled(B=2, H=4, dk=128, dv=128, T=9, delta=1)
+    log("case: window W=4, heads int8/int4/int6/fp8 from S_0 = 0, nearest rounding")
+    s = run_window_parity(w, T=w.T, W=4, head_prec=[2, 3, 4, 5], init="zero",
+                          rounding="nearest")
+    log(s.summary())
+    s.check()
+
+
+def test_unscaled_heads_step_every_token():
+    """fp32 and bf16 heads of a windowed state step every token, exactly as
+    in a plain state (their segments come first, so the bytes line up)."""
+    w = C1.scaled(B=2, H=3, dk=64, dv=64, T=5)
+    log("case: fp32 / bf16 heads of a windowed state match a plain state's")
+    x = make_inputs(w, 2, DEV, T=w.T)
+    a = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, [0, 1, 2], device=DEV)
+    b = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, [0, 1, 2], device=DEV, window=4)
+    for t in range(1, w.T + 1):
+        xs = {k: v[t - 1] for k, v in x.items()}
+        oa = lores.lores_decode_step(a, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 4, t)
+        ob = lores.lores_decode_step(b, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 4, t)
+        assert torch.equal(oa[:, :2], ob[:, :2])
+    la, lb = lores.lores_state_layout(a), lores.lores_state_layout(b)
+    for c in (0, 1):
+        assert la["codes_offset"][c] == lb["codes_offset"][c]
+        s0, n = la["codes_offset"][c], la["unit_code_bytes"][c] * w.B
+        assert torch.equal(a.buf[s0:s0 + n], b.buf[s0:s0 + n])
+
+
+def test_full_size_c2_window8():
+    w = get_workload("C2")
+    g = np.random.default_rng(3)
+    idx = g.choice(w.B * w.H, size=16, replace=False)
+    units = sorted((int(i // w.H), int(i % w.H)) for i in idx)
+    log("case: window W=8 on the full C2 batch (bf16 inputs), 16 sampled units, 9 steps")
+    s = run_window_parity(w, T=9, W=8, head_prec=[2] * w.H, units=units)
+    log(s.summary())
+    s.check()
+
+
+def test_window_one_is_the_plain_state():
+    w = C1.scaled(B=2, H=4, dk=128, dv=96, T=4)
+    log("case: lores_state_alloc_window(W = 1) steps like lores_state_alloc")
+    x = make_inputs(w, 0, DEV, T=w.T)
+    a = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, [2, 3, 4, 5], device=DEV)
+    b = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, [2, 3, 4, 5], device=DEV, window=1)
+    for t in range(1, w.T + 1):
+        xs = {k: v[t - 1] for k, v in x.items()}
+        oa = lores.lores_decode_step(a, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 4, t)
+        ob = lores.lores_decode_step(b, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 4, t)
+        assert torch.equal(oa, ob)
+    assert torch.equal(a.buf, b.buf)
+
+
+@pytest.mark.parametrize("prec", [2, 3, 4, 5])
+def test_dequant_replays_the_buffer(prec):
+    """Inside a window lores_dequant_state returns the current state: the
+    stored state followed by the buffered tokens' fp32 recurrence, bit for
+    bit against the oracle's replay of the same (oracle-written) buffer."""
+    W, B, H, dk, dv, n = 6, 2, 3, 128, 72, 3
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=n)
+    log(f"case: window dequant after {n} buffered tokens, prec={prec}")
+    st = lores.lores_state_alloc(B, H, dk, dv, [prec] * H, device=DEV, window=W)
+    x = make_inputs(w, 1, DEV, T=n)
+    for t in range(1, n + 1):           # the handle now counts n buffered tokens
+        xs = {k: v[t - 1] for k, v in x.items()}
+        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, t)
+    torch.cuda.synchronize()
+    lay = lores.lores_state_layout(st)
+    assert lay["window_fill"] == n
+    _, slot = lores.lores_state_head_map(st)
+    g = np.random.default_rng(prec)
+    host = st.buf.cpu().numpy()
+    want = np.zeros((B, H, dv, dk), np.float32)
+    for b in range(B):
+        for h in range(H):
+            s = random_unit_state(prec, dv, dk, g)
+            win = {"g": g.standard_normal((W - 1, dv)).astype(np.float32),
+                   "k": (g.standard_normal((W - 1, dk)) / np.sqrt(dk)).astype(np.float32),
+                   "alpha": g.uniform(0.8, 1.0, W - 1).astype(np.float32)}
+            u = b * lay["n_class"][prec] + slot[h]
+            lc.write_unit(host, lay, prec, u, s)
+            lc.write_window(host, lay, prec, u, win)
+            want[b, h] = owin.replay(prec, {k: v[None] for k, v in s.items()},
+                                     {k: v[None] for k, v in win.items()}, n)[0]
+    st.buf.copy_(torch.from_numpy(host))
+    got = lores.lores_dequant_state(st).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_windowed_state_contract():
+    log("case: windowed state errors: per-channel alpha, out-of-order t, quant_state resets")
+    w = C1.scaled(B=2, H=2, dk=64, dv=64, T=3)
+    x = make_inputs(w, 0, DEV, T=3)
+    st = lores.lores_state_alloc(2, 2, 64, 64, [2, 3], device=DEV, window=4)
+    xs = {k: v[0] for k, v in x.items()}
+    pc = torch.full((2, 2, 64), 0.9, device=DEV)
+    with pytest.raises(lores.LoresError, match="EUNSUPPORTED"):
+        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], pc, xs["beta"], 1, 0, 1)
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 2)
+    lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 1)
+    assert lores.lores_state_layout(st)["window_fill"] == 1
+    X = torch.zeros(2, 2, 64, 64, device=DEV)
+    lores.lores_quant_state(st, X, 0)
+    assert lores.lores_state_layout(st)["window_fill"] == 0
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 2)
+    lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 5)
+    torch.cuda.synchronize()

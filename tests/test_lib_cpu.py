@@ -40,10 +40,10 @@ def test_library_exports_every_declared_symbol(lores_lib):
 def test_spec_version(lores_lib):
     hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
     v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
-    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 4
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 5
 
 
-def _layout_bytes(B, H, dk, dv, head_prec, key=False):
+def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
     """Segment sizes as include/lores.h documents them."""
     bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}
     dvp = (dv + 63) // 64 * 64
@@ -57,6 +57,9 @@ def _layout_bytes(B, H, dk, dv, head_prec, key=False):
         if c in (2, 3, 4, 5):                      # one fp32 scale per value row / key column
             off = (off + 255) // 256 * 256
             off += B * hc * (dk if key else dvp) * 4
+            if window > 1:                         # W - 1 slots of g, k, alpha per unit
+                off = (off + 255) // 256 * 256
+                off += B * hc * (((window - 1) * (dvp + dk + 1) * 4 + 15) // 16 * 16)
     return (off + 255) // 256 * 256
 
 
@@ -159,6 +162,25 @@ def test_key_axis_layout_and_limits(lores_lib):
     assert L.lores_state_alloc_axis(2, 3, 64, 64, hp, 2, None, ctypes.byref(n), None,
                                     None) == lores._lib.LORES_EINVAL
     assert "scale_axis" in lores.lores_last_error()
+
+
+def test_window_layout_and_limits(lores_lib):
+    """Windowed states: the window segment per scaled class, W in [1, 16],
+    d_k 64 or 128 when W > 1 (size queries only)."""
+    L = lores._lib.lib()
+    hp = (ctypes.c_uint8 * 4)(2, 3, 1, 5)
+    n = ctypes.c_size_t(0)
+    for W in (1, 2, 8, 16):
+        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, W, None, ctypes.byref(n), None,
+                                          None) == 0
+        assert n.value == _layout_bytes(5, 4, 128, 100, [2, 3, 1, 5], window=W), W
+    for W in (0, 17, -1):
+        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, W, None, ctypes.byref(n), None,
+                                          None) == lores._lib.LORES_EINVAL
+    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 4, None, ctypes.byref(n), None,
+                                      None) == lores._lib.LORES_EUNSUPPORTED
+    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 1, None, ctypes.byref(n), None,
+                                      None) == 0
 
 
 def test_error_message_is_thread_local_and_cleared(lores_lib):
