@@ -47,14 +47,23 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def unit_bytes(prec, dk, dv, in_bytes, per_channel, key=False):
+def unit_bytes(prec, dk, dv, in_bytes, per_channel, key=False, window=1):
     """Algorithmic bytes of one state update: the state read and written once,
     plus q, k, v, alpha, beta read and o written.  The scales are one fp32 per
-    value row, or per key column with key=True."""
+    value row, or per key column with key=True.  A windowed state (window W >
+    1, scaled classes) is read every step and written once per window, and
+    per window its buffer is written once and read back by the later steps
+    of the window (token tau is read by the W - tau later steps): averaged
+    per step, state (1 + 1/W) + buffer ((W - 1) + W (W - 1) / 2) / W slots of
+    (d_v + d_k + 1) fp32."""
     ns = dk if key else dv
     state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * ns, 3: dv * dk // 2 + 4 * ns,
              4: 6 * dv * dk // 8 + 4 * ns, 5: dv * dk + 4 * ns}[prec]
     io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
+    if window > 1 and prec in (2, 3, 4, 5):
+        W = window
+        slot = 4 * (dv + dk + 1)
+        return state * (W + 1) / W + slot * ((W - 1) + W * (W - 1) / 2) / W + io
     return 2 * state + io
 
 
@@ -74,6 +83,9 @@ def parse(argv=None):
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="how the timed steps are issued")
+    ap.add_argument("--window", type=int, default=1,
+                    help="requantize the int / fp8 heads once per window of this many steps "
+                         "(windowed states; 1: every step)")
     ap.add_argument("--scale-axis", default="value", choices=["value", "key"],
                     help="scale grouping of the int / fp8 heads: one scale per value row "
                          "(the method's choice) or per key column")
@@ -102,7 +114,7 @@ def copy_mode(args, torch):
                       "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
 
 
-SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis])
+SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis or window])
     ("int8+int4 (C5)", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1),
     ("int8+int4 (C5), delta 0", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 0),
     ("int8", 2048, 32, 128, 128, [2] * 32, 1),
@@ -118,6 +130,10 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis])
     ("int6, key columns", 2048, 32, 128, 128, [4] * 32, 1, "key"),
     ("fp8 (E4M3), key columns", 2048, 32, 128, 128, [5] * 32, 1, "key"),
     ("int8, d_v 64 (C3 shape), key columns", 256, 128, 128, 64, [2] * 128, 0, "key"),
+    ("int8, window 4", 2048, 32, 128, 128, [2] * 32, 1, 4),
+    ("int8, window 8", 2048, 32, 128, 128, [2] * 32, 1, 8),
+    ("int4, window 8", 2048, 32, 128, 128, [3] * 32, 1, 8),
+    ("int8+int4 (C5), window 8", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, 8),
 ]
 
 
@@ -131,6 +147,7 @@ def sweep_mode(args, torch):
     rows = []
     for label, B, H, dk, dv, prec, delta, *ax in SWEEP:
         key = bool(ax) and ax[0] == "key"
+        window = ax[0] if ax and isinstance(ax[0], int) else 1
         g = torch.Generator(device=dev)
         g.manual_seed(args.seed)
 
@@ -142,15 +159,15 @@ def sweep_mode(args, torch):
         alpha = (0.7 + 0.3 * torch.rand(B, H, generator=g, device=dev)).contiguous()
         beta = (2 * torch.sigmoid(torch.randn(B, H, generator=g, device=dev))).contiguous()
         st = lores.lores_state_alloc(B, H, dk, dv, prec, device=dev,
-                                     scale_axis=lores.LORES_SCALE_KEY if key else 0)
+                                     scale_axis=lores.LORES_SCALE_KEY if key else 0, window=window)
         o = torch.empty(B, H, dv, device=dev)
         for t in range(1, 9):
             lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, t, o=o)
-        steps = 64
+        steps = 64                        # a whole number of windows: each replay starts one
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for t in range(1, steps + 1):
-                lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, 100 + t, o=o)
+            for t in range(9, 9 + steps):
+                lores.lores_decode_step(st, q, k, v, alpha, beta, delta, args.seed, t, o=o)
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -159,21 +176,25 @@ def sweep_mode(args, torch):
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / steps * 1e3
-        nbytes = sum(B * prec.count(c) * unit_bytes(c, dk, dv, 4, False, key) for c in range(6))
+        nbytes = sum(B * prec.count(c) * unit_bytes(c, dk, dv, 4, False, key, window)
+                     for c in range(6))
         gbs = nbytes / us / 1e3
         rows.append({"state": label, "B": B, "H": H, "d_k": dk, "d_v": dv, "delta": delta,
-                     "scale_axis": "key" if key else "value",
-                     "us_per_step": us, "GBps": gbs, "frac": gbs / HBM_PEAK_GBPS})
+                     "scale_axis": "key" if key else "value", "window": window,
+                     "us_per_step": us, "updates_per_s": B * H / (us * 1e-6), "GBps": gbs,
+                     "frac": gbs / HBM_PEAK_GBPS})
         print(f"[sweep] {label:34s} {us:8.1f} us/step {gbs:7.0f} GB/s  {gbs / HBM_PEAK_GBPS:.3f}",
               file=sys.stderr, flush=True)
     print(json.dumps({"mode": "sweep", "rows": rows}), flush=True)
 
 
-def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value"):
+def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value", window=1):
     """Time the oracle (as it stands) on a bounded sample of the same workload:
-    the first units of the batch, step after step, until target_s has passed."""
+    the first units of the batch, step after step, until target_s has passed.
+    Windowed states (window > 1) run the oracle's windowed step."""
     import numpy as np
     from oracle import step as ostep
+    from oracle import window as owin
 
     n_units = min(w.B * w.H, 64)
     units = [(u // w.H, u % w.H) for u in range(n_units)]
@@ -181,6 +202,7 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value"):
     for b, h in units:
         by_class.setdefault(head_prec[h], []).append((b, h))
     states = {c: ostep.zero_state(c, len(us), w.dv, w.dk, axis=axis) for c, us in by_class.items()}
+    bufs = {c: owin.empty_buffer(len(us), window, w.dv, w.dk) for c, us in by_class.items()}
     T_in = inputs["k"].shape[0]
     host = {}
     for t in range(min(T_in, 64)):
@@ -192,10 +214,14 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value"):
         for c, us in by_class.items():
             bs = np.array([b for b, _ in us])
             hs = np.array([h for _, h in us])
-            states[c], _ = ostep.decode_step(c, states[c], xin["q"][bs, hs], xin["k"][bs, hs],
-                                             xin["v"][bs, hs], xin["alpha"][bs, hs],
-                                             xin["beta"][bs, hs], w.delta, seed, steps + 1, bs, hs,
-                                             axis=axis)
+            a = (xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs], xin["alpha"][bs, hs],
+                 xin["beta"][bs, hs])
+            if window > 1 and c in ostep.SCALED:
+                states[c], bufs[c], _ = owin.window_step(c, states[c], bufs[c], *a, w.delta, seed,
+                                                         steps + 1, bs, hs, window)
+            else:
+                states[c], _ = ostep.decode_step(c, states[c], *a, w.delta, seed, steps + 1, bs,
+                                                 hs, axis=axis)
         steps += 1
         el = time.perf_counter() - t0
         if el >= target_s:
@@ -253,6 +279,11 @@ def main(argv=None):
     w = get_workload(args.workload)
     dev = torch.device("cuda:0")
     K, W = args.steps, args.warmup
+    win = args.window
+    if win > 1:
+        if args.scale_axis != "value" or w.per_channel:
+            sys.exit("bench.py: windowed states keep value-row scales and take a scalar decay")
+        K, W = -(-K // win) * win, -(-W // win) * win       # whole windows
     T_in = min(w.T, max(K, W, 1))
     print(f"[bench] generating {T_in} steps of {w.key} inputs on {dev}", file=sys.stderr, flush=True)
     inputs = make_inputs(w, args.seed, dev, T=T_in)
@@ -270,9 +301,10 @@ def main(argv=None):
     key = args.scale_axis == "key"
     axis_code = lores.LORES_SCALE_KEY if key else lores.LORES_SCALE_VALUE
     step_bytes = sum(w.B * head_prec.count(c) * unit_bytes(c, w.dk, w.dv, in_bytes, w.per_channel,
-                                                           key)
+                                                           key, win)
                      for c in range(6))
-    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev, scale_axis=axis_code)
+    st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, device=dev, scale_axis=axis_code,
+                                 window=win)
     o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device=dev)
 
     def step(t):
@@ -285,7 +317,7 @@ def main(argv=None):
     def reset_state():
         nonlocal st
         st = lores.lores_state_alloc(w.B, w.H, w.dk, w.dv, head_prec, buf=st.buf,
-                                     scale_axis=axis_code)
+                                     scale_axis=axis_code, window=win)
 
     print(f"[bench] warmup {W} eager steps", file=sys.stderr, flush=True)
     for t in range(1, W + 1):
@@ -335,7 +367,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     achieved = step_bytes / n_launches_per_step / (avg_launch_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.key) if not key else None
+    traffic = load_traffic(w.key) if not key and win == 1 else None
     result = {
         "metric": METRIC,
         "value": w.B * w.H * K / (ms_total * 1e-3),
@@ -355,7 +387,7 @@ def main(argv=None):
             "decay": w.decay, "inputs": "bf16" if w.in_bf16 else "fp32",
             "state": {name: head_prec.count(c) for c, name in
                       enumerate(["fp32", "bf16", "int8", "int4", "int6", "fp8"]) if head_prec.count(c)},
-            "rounding": "stochastic", "scale_axis": args.scale_axis,
+            "rounding": "stochastic", "scale_axis": args.scale_axis, "window": win,
             "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -375,7 +407,7 @@ def main(argv=None):
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inputs, head_prec, args.cpu_seconds, args.seed,
-                                              args.scale_axis)
+                                              args.scale_axis, win)
     print(json.dumps(result), flush=True)
 
 

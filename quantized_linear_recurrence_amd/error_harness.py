@@ -45,10 +45,11 @@ def sample_points(T, n=24):
 
 def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_lo=0.9,
                      alpha_hi=0.999, beta=0.5, drift=0.05, rounding=LORES_ROUND_STOCHASTIC,
-                     seed=0, points=None, device="cuda", scale_axis=LORES_SCALE_VALUE):
+                     seed=0, points=None, device="cuda", scale_axis=LORES_SCALE_VALUE, window=1):
     """Run T steps of a state with per-head precisions `head_prec` (a list,
     or a function of the per-head decays giving one; scales per value row or,
-    with scale_axis = LORES_SCALE_KEY, per key column) and of its fp32 twin;
+    with scale_axis = LORES_SCALE_KEY, per key column; requantized every step
+    or, with window = W > 1, once per window of W steps) and of its fp32 twin;
     return {"t": [...], "rel_err": [H lists], "o_rel_err": [H lists],
     "alpha": [H], "head_prec": [H]} with errors averaged over the B
     sequences at each sampled t.
@@ -73,7 +74,8 @@ def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_l
 
     if callable(head_prec):
         head_prec = head_prec(alpha_h.cpu().numpy())
-    sq = lores_state_alloc(B, H, d_k, d_v, list(head_prec), device=dev, scale_axis=scale_axis)
+    sq = lores_state_alloc(B, H, d_k, d_v, list(head_prec), device=dev, scale_axis=scale_axis,
+                           window=window)
     lores_state_set_rounding(sq, rounding)
     sf = lores_state_alloc(B, H, d_k, d_v, [LORES_FP32] * H, device=dev)
     oq = torch.empty((B, H, d_v), dtype=f32, device=dev)
@@ -190,27 +192,29 @@ def grouping_readout_error(prec, B=64, H=8, d_k=128, d_v=128, row_spread=2.0, co
 def run_suite(T=2048, B=32, H=12, d=128, seed=1, device="cuda"):
     """The harness's report: random writes (drift 100), scalar decay, delta
     = 0, two decay regimes; int8, E4M3, int6 and int4 states, int8 and int4
-    with key-column scales, and the decay-assigned mixes that keep the
-    slowest half of the heads at 8 or 6 bits (6.25 and 5.25 effective bits);
-    stochastic and nearest rounding.  Then Proposition 1's value-row versus
-    key-column readout error on states with row or column outliers."""
+    with key-column scales, int8 and int4 requantized once per window of 4 or
+    16 steps, and the decay-assigned mixes that keep the slowest half of the
+    heads at 8 or 6 bits (6.25 and 5.25 effective bits); stochastic and
+    nearest rounding.  Then Proposition 1's value-row versus key-column
+    readout error on states with row or column outliers."""
     names = {0: "stochastic", 1: "nearest"}
     rows = []
     for lo, hi in ((0.9, 1.0), (0.99, 1.0)):
-        for label, prec, axis in (
-                ("int8", [2] * H, LORES_SCALE_VALUE), ("fp8 (E4M3)", [5] * H, LORES_SCALE_VALUE),
-                ("int6", [4] * H, LORES_SCALE_VALUE), ("int4", [3] * H, LORES_SCALE_VALUE),
-                ("int8, key columns", [2] * H, LORES_SCALE_KEY),
-                ("int4, key columns", [3] * H, LORES_SCALE_KEY),
-                ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)]),
-                 LORES_SCALE_VALUE),
-                ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]),
-                 LORES_SCALE_VALUE)):
+        V = LORES_SCALE_VALUE
+        for label, prec, axis, win in (
+                ("int8", [2] * H, V, 1), ("fp8 (E4M3)", [5] * H, V, 1),
+                ("int6", [4] * H, V, 1), ("int4", [3] * H, V, 1),
+                ("int8, key columns", [2] * H, LORES_SCALE_KEY, 1),
+                ("int4, key columns", [3] * H, LORES_SCALE_KEY, 1),
+                ("int8, window 4", [2] * H, V, 4), ("int4, window 4", [3] * H, V, 4),
+                ("int4, window 16", [3] * H, V, 16),
+                ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)]), V, 1),
+                ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]), V, 1)):
             for rnd in (LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST):
                 res = error_trajectory(prec, B=B, d_k=d, d_v=d, T=T, delta=0, alpha_lo=lo,
                                        alpha_hi=hi, beta=0.5, drift=100.0, rounding=rnd, seed=seed,
-                                       device=device, scale_axis=axis)
-                rows.append({"decay": [lo, hi], "state": label, "rounding": names[rnd],
+                                       device=device, scale_axis=axis, window=win)
+                rows.append({"decay": [lo, hi], "state": label, "rounding": names[rnd], "window": win,
                              "effective_bits": effective_bits(res["head_prec"], d),
                              "mean_rel_err_T": float(np.mean([e[-1] for e in res["rel_err"]])),
                              "by_decay_bin": summarize(res, bins=3)})

@@ -113,3 +113,21 @@ def test_grouping_readout_error_follows_proposition1(prec):
             assert 0.85 < ratio < 1.05, (res, name, ratio)
     assert rows["value"]["mean_e2"] < 0.5 * rows["key"]["mean_e2"], rows
     assert cols["key"]["mean_e2"] < 0.5 * cols["value"]["mean_e2"], cols
+
+
+def test_windowed_requantization_accumulates_less_error():
+    """Rounding once per window of W steps (the buffer holding the window's
+    tokens at fp32) leaves the state with less accumulated error than
+    rounding every step, under stochastic and nearest rounding (the PACE
+    abstract's claim), and the error falls as W grows."""
+    log("case: windowed int4 vs per-step int4, slow decay, 1024 steps")
+    errs = {}
+    for rnd in (SR, NEAR):
+        for W in (1, 4, 16):
+            res = eh.error_trajectory([3] * 12, B=32, T=1024, delta=0, alpha_lo=0.99, alpha_hi=1.0,
+                                      beta=0.5, drift=100.0, rounding=rnd, seed=1, window=W)
+            errs[(rnd, W)] = float(np.mean([e[-1] for e in res["rel_err"]]))
+            log(f"  rounding={rnd} W={W}: rel err {errs[(rnd, W)]:.4f}")
+    for rnd in (SR, NEAR):
+        assert errs[(rnd, 4)] < 0.75 * errs[(rnd, 1)], errs
+        assert errs[(rnd, 16)] < errs[(rnd, 4)], errs
