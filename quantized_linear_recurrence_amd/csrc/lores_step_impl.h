@@ -540,6 +540,29 @@ __device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *pa
     for (int i = 0; i < DK / 16; ++i) invrow[i] = mine[16 * i + (lane & 15)];
 }
 
+// u[e] = fma(g, row element e of kv, u[e]) for e < 16
+__device__ __forceinline__ void axpy16(float *u, float g, float kv) {
+    asm("s_nop 1\n"
+        "v_fmac_f32_dpp %0, %17, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %1, %17, %16 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %2, %17, %16 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %3, %17, %16 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %4, %17, %16 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %5, %17, %16 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %6, %17, %16 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %7, %17, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %8, %17, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %9, %17, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %10, %17, %16 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %11, %17, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %12, %17, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %13, %17, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %14, %17, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_fmac_f32_dpp %15, %17, %16 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : LORES_PV16(u)
+        : "v"(g), "v"(kv));
+}
+
 template <bool BF16IN>
 __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx) {
     if constexpr (BF16IN) {
@@ -767,6 +790,7 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 template <int NV, bool KEY = false>
 struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
+    float alpha_t = 1.0f;              // window end: this step's decay (alpha is token 1's)
     float kv[NV], qv[NV], av[KEY ? 1 : NV];
     float sl[KEY ? NV / 4 : 1], al[KEY ? NV / 4 : 1];
 };
@@ -775,7 +799,10 @@ struct TaskSide {
 // wavefronts wv - rb .. wv - rb + n_rb - 1 of one work-group, and `lds`
 // holds two buffers of kWavesPerGroup x DK column maxima (tasks alternate
 // between them) and a kWavesPerGroup x DK staging area.
-template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false>
+// WEND: the last step of a window of a windowed state (value-row scales,
+// scalar decay): pass 1 dequantizes with the window's first decay, then the
+// window buffer's tokens are replayed on U before this step's token.
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false, bool WEND = false>
 struct TaskStream {
     static constexpr int E = Prec<PREC>::E;
     static constexpr int NCH = row_chunks<DK, PREC>();
@@ -796,13 +823,15 @@ struct TaskStream {
     long unit_bytes;
     bool active;
     float *lds;
+    const float *win;                  // window buffers of the class (WEND)
 
     __device__ __forceinline__ TaskStream(const void *q, const void *k, const void *v,
                                           const float *alpha, const float *beta, float *o,
                                           uint8_t *c, float *sc, const StepMeta &m,
-                                          const ClassDesc &cd, int task, float *lds_ = nullptr)
+                                          const ClassDesc &cd, int task, float *lds_ = nullptr,
+                                          const float *win_ = nullptr)
         : qp(q), kp(k), vp(v), alphap(alpha), betap(beta), op(o), codes(c), scales(sc), meta(m),
-          lds(lds_) {
+          lds(lds_), win(win_) {
         const int n_rb = m.n_rb;
         slot = n_rb == 1 ? task : n_rb == 2 ? task >> 1 : n_rb == 4 ? task >> 2 : task / 3;
         rb = task - slot * n_rb;
@@ -840,6 +869,12 @@ struct TaskStream {
         in.v = in_scalar<BF16IN>(vp, bh * meta.dv + lrow);
         in.beta = betap[bh];
         in.alpha = PC ? 1.0f : alphap[bh];
+        if constexpr (WEND) {
+            // pass 1 decays with the window's first token's alpha
+            in.alpha_t = in.alpha;
+            in.alpha = win[unit * window_unit_floats(meta.window, meta.dv_pad, DK) +
+                           (long)(meta.window - 1) * (meta.dv_pad + DK)];
+        }
         // row vectors: register i holds element 16 i + lane % 16
         const long kb = bh * DK + (threadIdx.x & 15);
 #pragma unroll
@@ -890,7 +925,7 @@ struct TaskStream {
         auto group_done = [&](int j) {
             if constexpr (PC && !has_scale<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
             if constexpr (KEY) mul16(&U[j - 15], sig[j >> 4]);
-            if constexpr (DELTA) dot16(r, &U[j - 15], in.kv[j >> 4]);
+            if constexpr (DELTA && !WEND) dot16(r, &U[j - 15], in.kv[j >> 4]);
             // without the projection nothing orders pass 1 before the
             // next task's loads; materialize the group here so the
             // chunk registers are free when `mid` reuses them
@@ -955,6 +990,39 @@ struct TaskStream {
 
         mid();                                           // the chunks are consumed
 
+        if constexpr (WEND) {
+            // the window's buffered tokens: U = fma(g_tau, k_tau, S'_tau), then
+            // the next token's S' = fl(U alpha); the slots of token tau + 1 load
+            // while token tau is applied
+            const int nslot = meta.window - 1;
+            const float *ub = win + unit * window_unit_floats(meta.window, meta.dv_pad, DK);
+            const float *gs = ub + lrow, *ks = ub + (long)nslot * dv_pad + (threadIdx.x & 15);
+            const float *as = ub + (long)nslot * (dv_pad + DK);
+            float gt = gs[0], kt[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) kt[i] = ks[16 * i];
+            for (int tau = 1; tau <= nslot; ++tau) {
+                float gn = 0.0f, kn[NV], an = in.alpha_t;
+                if (tau < nslot) {
+                    gn = gs[(long)tau * dv_pad];
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) kn[i] = ks[(long)tau * DK + 16 * i];
+                    an = as[tau];
+                }
+#pragma unroll
+                for (int gi = 0; gi < NV; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
+#pragma unroll
+                for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
+                gt = gn;
+#pragma unroll
+                for (int i = 0; i < NV; ++i) kt[i] = kn[i];
+            }
+            if constexpr (DELTA) {
+#pragma unroll
+                for (int gi = 0; gi < NV; ++gi) dot16(r, &U[16 * gi], in.kv[gi]);
+            }
+        }
+
         // ---- write gate
         const float g = DELTA ? beta * (vi - r) : beta * vi;
 
@@ -998,9 +1066,10 @@ struct TaskStream {
 // of a bf16 row (the rest are loaded as that task starts), none of an fp32
 // row.  The loop body holds two tasks, so the prefetched per-task values
 // alternate between two register sets instead of being copied.
-template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY>
-__device__ __forceinline__ void run_single(const TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY> &ts) {
-    using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY>;
+template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY, bool WEND>
+__device__ __forceinline__ void run_single(
+    const TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY, WEND> &ts) {
+    using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY, WEND>;
     // fp32 rows (32 chunks at d_k = 128) leave no registers for a prefetch
     // beside U: only their per-task values are loaded ahead
     constexpr int P = TS::NCH <= kMaxPrefetchChunks ? TS::NCH
@@ -1073,17 +1142,27 @@ constexpr bool pairable() {
     }
 }
 
-template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false>
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
+          bool WEND = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
                   uint8_t *__restrict__ codes0, float *__restrict__ scales0,
-                  uint8_t *__restrict__ codes1, float *__restrict__ scales1, const StepMeta meta) {
+                  uint8_t *__restrict__ codes1, float *__restrict__ scales1,
+                  const float *__restrict__ win0, const StepMeta meta) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int gx = blockIdx.x;
     const int n_rb = meta.n_rb;
-    if constexpr (KEY) {
+    if constexpr (WEND) {
+        // the last step of a window: one scaled class, scalar decay
+        static_assert(P1 < 0 && !PC && !KEY, "window ends run one class with a scalar decay");
+        const int task = gx * kWavesPerGroup + wv;
+        if (task >= meta.cls[0].Hc * n_rb) return;
+        run_single(TaskStream<DK, P0, false, DELTA, BF16IN, false, true>(
+            qp, kp, vp, alphap, betap, op, codes0, scales0, meta, meta.cls[0], task, nullptr,
+            win0));
+    } else if constexpr (KEY) {
         // one class; the n_rb (1, 2 or 4) row blocks of a unit are
         // consecutive tasks, so whole units share a work-group.  A wave past
         // the last task still takes part in the work-group's barriers: one
@@ -1155,9 +1234,10 @@ inline int device_cu_count() {
     return cached[dev];
 }
 
-template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false>
+template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
+          bool WEND = false>
 hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
-    auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY>;
+    auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY, WEND>;
     static int per_cu = 0;                          // resident work-groups per CU
     if (!per_cu) {
         int n = 0;
@@ -1181,7 +1261,7 @@ hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     if (gy > m.B) gy = m.B;
     hipLaunchKernelGGL(kern, dim3(gx, (unsigned)gy), dim3(64 * kWavesPerGroup), 0, s, p.q, p.k,
                        p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.codes[1],
-                       p.scales[1], m);
+                       p.scales[1], p.win[0], m);
     return hipGetLastError();
 }
 

@@ -24,29 +24,6 @@
 
 namespace lores {
 
-// u[e] = fma(g, row element e of kv, u[e]) for e < 16
-__device__ __forceinline__ void axpy16(float *u, float g, float kv) {
-    asm("s_nop 1\n"
-        "v_fmac_f32_dpp %0, %17, %16 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %1, %17, %16 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %2, %17, %16 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %3, %17, %16 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %4, %17, %16 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %5, %17, %16 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %6, %17, %16 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %7, %17, %16 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %8, %17, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %9, %17, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %10, %17, %16 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %11, %17, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %12, %17, %16 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %13, %17, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %14, %17, %16 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
-        "v_fmac_f32_dpp %15, %17, %16 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
-        : LORES_PV16(u)
-        : "v"(g), "v"(kv));
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -203,79 +180,6 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
 }
 
 // ---------------------------------------------------------------------------
-// the last step of a window (p = W): rebuild, step, requantize
-// ---------------------------------------------------------------------------
-template <int DK, int PREC, bool DELTA, bool BF16IN>
-__global__ void __launch_bounds__(64 * kWavesPerGroup)
-lores_window_end_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
-                        const void *__restrict__ vp, const float *__restrict__ alphap,
-                        const float *__restrict__ betap, float *__restrict__ op,
-                        uint8_t *__restrict__ codes, float *__restrict__ scales,
-                        const float *__restrict__ win, const StepMeta meta) {
-    constexpr int NCH = row_chunks<DK, PREC>(), NV = DK / 16;
-    WindowTask w;
-    if (!window_task(meta, w)) return;
-    const int lane = threadIdx.x & 63;
-    const int b = blockIdx.y;
-    const long dv_pad = meta.dv_pad;
-    u32x4 *cp = reinterpret_cast<u32x4 *>(codes + w.unit * meta.cls[0].unit_bytes) + w.row;
-    const u32x4 *lp = reinterpret_cast<const u32x4 *>(codes + w.unit * meta.cls[0].unit_bytes) + w.lrow;
-    u32x4 cw[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(lp + c * dv_pad);
-    const float s = scales[w.unit * dv_pad + w.lrow];
-    const float v = in_scalar<BF16IN>(vp, w.bh * meta.dv + w.lrow);
-    const float beta = betap[w.bh], alpha = alphap[w.bh];
-    float kv[NV], qv[NV];
-    const long kb = w.bh * DK + (lane & 15);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
-        qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
-    }
-    const int nslot = meta.window - 1;
-    const float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
-    const float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
-
-    // token 1: S'_1 = fl(c fl(s alpha_1))
-    float U[DK];
-    const float a1 = s * aslot[0];
-    float na1 = 0.0f;
-    if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
-#pragma unroll
-    for (int j = 0; j < DK; ++j) U[j] = scaled_code<PREC>(cw, j, a1, na1);
-    // tokens 1 .. W - 1: U = fma(g, k, S'), S' of the next token = fl(U alpha)
-    for (int tau = 1; tau <= nslot; ++tau) {
-        const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
-        float kt[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) kt[i] = kslot[(long)(tau - 1) * DK + 16 * i + (lane & 15)];
-#pragma unroll
-        for (int gi = 0; gi < NV; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
-        const float an = tau < nslot ? aslot[tau] : alpha;     // the next token's decay
-#pragma unroll
-        for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
-    }
-    // token W: r, g, the write, the readout, a fresh scale and the rounding
-    float r = 0.0f;
-    if constexpr (DELTA) {
-#pragma unroll
-        for (int gi = 0; gi < NV; ++gi) dot16(r, &U[16 * gi], kv[gi]);
-    }
-    const float g = DELTA ? beta * (v - r) : beta * v;
-    float o = 0.0f, m = 0.0f;
-#pragma unroll
-    for (int gi = 0; gi < NV; ++gi) {
-        upd16(&U[16 * gi], o, g, kv[gi], qv[gi]);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
-    }
-    if (w.active) op[w.bh * meta.dv + w.row] = o;
-    requantize_row<DK, PREC>(U, m, meta, b, w.h, w.row, w.active, cp, dv_pad,
-                             scales + w.unit * dv_pad + w.row);
-}
-
-// ---------------------------------------------------------------------------
 // the current state of a windowed unit: the stored state followed by the
 // first meta.wpos buffered tokens (lores_dequant_state)
 // ---------------------------------------------------------------------------
@@ -323,19 +227,23 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
     for (int j = 0; j < DK; j += 4) *reinterpret_cast<f32x4 *>(orow + j) = f32x4{U[j], U[j + 1], U[j + 2], U[j + 3]};
 }
 
+// Inside a window: one task per wavefront (a read-only pass, many waves per
+// SIMD).  The window's last step: the step kernel's persistent task stream
+// with the buffer replayed between pass 1 and the token's own update.
 template <int DK, int PREC>
 static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
                             hipStream_t s) {
+    if (m.wpos == m.window) {
+        if (delta) return bf16 ? launch_one<DK, false, true, true, PREC, -1, false, true>(p, m, s)
+                               : launch_one<DK, false, true, false, PREC, -1, false, true>(p, m, s);
+        return bf16 ? launch_one<DK, false, false, true, PREC, -1, false, true>(p, m, s)
+                    : launch_one<DK, false, false, false, PREC, -1, false, true>(p, m, s);
+    }
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
-    const bool end = m.wpos == m.window;
 #define LORES_WIN_LAUNCH(D, BF)                                                                 \
-    if (end)                                                                                    \
-        hipLaunchKernelGGL((lores_window_end_kernel<DK, PREC, D, BF>), grid, block, 0, s, p.q,  \
-                           p.k, p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m); \
-    else                                                                                        \
-        hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF>), grid, block, 0, s, p.q, \
-                           p.k, p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
+    hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF>), grid, block, 0, s, p.q, p.k,   \
+                       p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
     if (delta) {
         if (bf16) { LORES_WIN_LAUNCH(true, true) } else { LORES_WIN_LAUNCH(true, false) }
     } else {
