@@ -198,6 +198,8 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * and lores_decode_step returns LORES_EINVAL for a step t whose window
  * position does not follow them), with a scalar alpha (alpha_per_channel = 0,
  * else LORES_EUNSUPPORTED).  Each scaled class runs one launch per step.
+ * The count is kept on the host: a captured graph of steps on a windowed
+ * state replays correctly when it covers whole windows.
  */
 int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                              const uint8_t *head_prec, int32_t window, void *d_buf,
