@@ -35,6 +35,18 @@ def test_each_scaled_class(prec, W, dk, dv, delta):
     s.check()
 
 
+@pytest.mark.parametrize("prec,dk,dv", [(2, 128, 128), (3, 64, 1)])
+def test_longest_window(prec, dk, dv):
+    """W = LORES_MAX_WINDOW (15 buffered tokens replayed at the window end),
+    and a single value row."""
+    W = lores.LORES_MAX_WINDOW
+    w = C1.scaled(B=2, H=2, dk=dk, dv=dv, T=W + 2, delta=1)
+    log(f"case: window W={W} prec={prec} dk={dk} dv={dv}, {w.T} steps")
+    s = run_window_parity(w, T=w.T, W=W, head_prec=[prec] * w.H)
+    log(s.summary())
+    s.check()
+
+
 def test_mixed_heads_from_zero_nearest():
     w = C1.scaled(B=2, H=4, dk=128, dv=128, T=9, delta=1)
     log("case: window W=4, heads int8/int4/int6/fp8 from S_0 = 0, nearest rounding")
