@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,15 +36,24 @@ HBM_PEAK_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "quantized_linear_recurrence_amd", "csrc")
 
 
+def _code_only(text):
+    """C++ source without comments and blank space, so that a comment edit
+    leaves the hash alone."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
-    """Hash of the step kernel's sources (its header and every step
-    translation unit): a stored HBM byte count is used only while it matches."""
+    """Hash of the step kernel's code (its header and every step translation
+    unit, comments dropped): a stored HBM byte count is used only while it
+    matches."""
     h = hashlib.sha256()
     names = sorted(f for f in os.listdir(CSRC) if f.startswith("lores_step") or f == "lores_internal.h")
     for f in names:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

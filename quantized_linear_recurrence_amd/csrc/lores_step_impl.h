@@ -14,12 +14,16 @@
 //
 // Mapping: one wavefront per (sequence, head, block of 64 value rows); lane i
 // owns row i of the block for the whole step.  All lanes walk the key columns
-// in lock-step, so k_j, q_j and a per-channel alpha_j are wave-uniform and
-// are read with scalar loads into SGPRs; no LDS, no barriers, no cross-lane
-// reductions.  Codes are stored chunk-major (16-byte column chunks of 64
-// consecutive rows), so each chunk load or store of a wavefront is one
-// contiguous 1 KiB access.  The updated row U lives in d_k VGPRs between
-// the passes (dequant+r, update+readout+max, quantize+store).
+// in lock-step, so k_j, q_j and a per-channel alpha_j are wave-uniform: they
+// are held as 16-lane row vectors and broadcast by the DPP modifier of the
+// FMA that consumes them, so value-row states need no LDS, no barriers and no
+// cross-lane reductions (key-column states add one column reduction and an
+// LDS exchange per task).  Codes are stored chunk-major (16-byte column
+// chunks of 64 consecutive rows), so each chunk load or store of a wavefront
+// is one contiguous 1 KiB access.  The updated row U lives in d_k VGPRs
+// between the passes (dequant+r, update+readout+max, quantize+store).  A
+// persistent grid walks the sequences, loading the next task while the
+// current one computes.
 //
 // Arithmetic (must match the CPU oracle bit for bit where it decides codes):
 //   int heads   a = fl(s * alpha); S' = fl(c * a), computed as
@@ -31,10 +35,11 @@
 //   g           fl(beta * fl(v - r))            (contraction disabled)
 //   U           fma(g, k_j, S'_j)
 //   s'          fl(m / r) (IEEE division);  inv = the largest fp32 <= r / m
-//   code        e = floor(fma(U, inv, bias + n 2^-16)), bias + n 2^-16 built by
-//               one byte permute of the noise word into a constant's mantissa;
-//               e is the stored offset-binary byte (int8) or, mod 16, the
-//               offset-binary nibble (int4, bias 136 = 128 + 8)
+//   code        e = floor(fma(U, inv, bias + n 2^-16)): the addend register
+//               holds bias + n 2^-16 (n in its low 16 mantissa bits) and steps
+//               to the next column's draw with one packed 16-bit add; e is the
+//               stored offset-binary byte (int8) or, mod 16, the offset-binary
+//               nibble (int4, bias 136 = 128 + 8), or the 6-bit field (int6)
 //   bf16        bits of U plus the 16-bit draw, truncated to the high half
 #pragma once
 
