@@ -93,6 +93,11 @@ def parse(argv=None):
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="how the timed steps are issued")
+    ap.add_argument("--state", default="assigned",
+                    choices=["assigned", "fp32", "bf16", "int8", "int4", "int6", "fp8"],
+                    help="precision of every head: the workload's decay-based assignment "
+                         "(default), or one precision for all heads (fp32 / bf16: the "
+                         "unquantized-state comparison)")
     ap.add_argument("--window", type=int, default=1,
                     help="requantize the int / fp8 heads once per window of this many steps "
                          "(windowed states; 1: every step)")
@@ -299,7 +304,10 @@ def main(argv=None):
     inputs = make_inputs(w, args.seed, dev, T=T_in)
 
     # precision per head from the decay statistic of a calibration sample
-    if len(w.tiers) == 1:
+    if args.state != "assigned":
+        code = {"fp32": 0, "bf16": 1, "int8": 2, "int4": 3, "int6": 4, "fp8": 5}[args.state]
+        head_prec = [code] * w.H
+    elif len(w.tiers) == 1:
         head_prec = [w.tiers[0][1]] * w.H
     else:
         cal = inputs["alpha"][:min(T_in, 32)].float().cpu().numpy()
@@ -377,7 +385,7 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     achieved = step_bytes / n_launches_per_step / (avg_launch_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.key) if not key and win == 1 else None
+    traffic = load_traffic(w.key) if not key and win == 1 and args.state == "assigned" else None
     result = {
         "metric": METRIC,
         "value": w.B * w.H * K / (ms_total * 1e-3),
@@ -398,6 +406,7 @@ def main(argv=None):
             "state": {name: head_prec.count(c) for c, name in
                       enumerate(["fp32", "bf16", "int8", "int4", "int6", "fp8"]) if head_prec.count(c)},
             "rounding": "stochastic", "scale_axis": args.scale_axis, "window": win,
+            "state_override": args.state,
             "parallelism": "single GPU",
         },
         "hbm_GBps_timed_loop": step_bytes / (ms_step * 1e-3) / 1e9,
