@@ -222,6 +222,11 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value", window=1):
     host = {}
     for t in range(min(T_in, 64)):
         host[t] = {k: v[t].float().cpu().numpy() for k, v in inputs.items()}
+    try:                                   # one thread: BLAS pools stay at 1
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except ImportError:
+        limiter = None
     t0 = time.perf_counter()
     steps = 0
     while True:
@@ -241,8 +246,11 @@ def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value", window=1):
         el = time.perf_counter() - t0
         if el >= target_s:
             break
+    if limiter is not None:
+        limiter.unregister()
     return {"value": n_units * steps / el, "unit": "state-updates/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cores_available": len(os.sched_getaffinity(0)),
+            "blas_threads": 1,
             "sample": f"{n_units} (sequence, head) units x {steps} decode steps of {w.key} "
                       f"({el:.1f} s; NumPy oracle, single-threaded elementwise ops and "
                       f"einsum, fp32-exact rounding emulation)"}
