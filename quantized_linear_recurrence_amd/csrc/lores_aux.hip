@@ -94,7 +94,9 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     const ClassDesc &cd = meta.cls[0];
     const int task = blockIdx.x * kWavesPerGroup + wv;
     if (task >= cd.Hc * meta.n_rb) {
-        if constexpr (KEY) lds_barrier();          // the work-group's one barrier
+        if constexpr (KEY) {
+            if (meta.n_rb > 1) lds_barrier();      // the work-group's one barrier
+        }
         return;
     }
     const int slot = task / meta.n_rb;

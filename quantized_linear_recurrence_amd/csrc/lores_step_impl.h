@@ -528,7 +528,9 @@ __device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *pa
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int t = 0; t < DK / 64; ++t) part[wv * DK + 64 * t + lane] = cm[t];
-    lds_barrier();
+    // a unit of one row block reads back only its own maxima
+    if (n_rb > 1) lds_barrier();
+    else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const float *base = part + (wv - rb) * DK + lane;
     float *mine = stage + wv * DK;
 #pragma unroll
@@ -1171,12 +1173,14 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         // one class; the n_rb (1, 2 or 4) row blocks of a unit are
         // consecutive tasks, so whole units share a work-group.  A wave past
         // the last task still takes part in the work-group's barriers: one
-        // per sequence of its stride, as a working wave does.
+        // per sequence of its stride, as a working wave does (units of one
+        // row block take no barrier at all).
         static_assert(P1 < 0, "key-column scales run one class per launch");
         __shared__ float cmax[3 * kWavesPerGroup * DK];    // two maxima buffers, staging
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) {
-            for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
+            if (n_rb > 1)
+                for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
             return;
         }
         run_single(TaskStream<DK, P0, PC, DELTA, BF16IN, true>(qp, kp, vp, alphap, betap, op,
