@@ -129,7 +129,7 @@ def copy_mode(args, torch):
                       "ms_per_copy": ms, "copy_GBps": 2 * n / ms / 1e6}), flush=True)
 
 
-SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis or window])
+SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, "key"][, window])
     ("int8+int4 (C5)", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1),
     ("int8+int4 (C5), delta 0", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 0),
     ("int8", 2048, 32, 128, 128, [2] * 32, 1),
@@ -149,6 +149,7 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, scale axis or w
     ("int8, window 8", 2048, 32, 128, 128, [2] * 32, 1, 8),
     ("int4, window 8", 2048, 32, 128, 128, [3] * 32, 1, 8),
     ("int8+int4 (C5), window 8", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, 8),
+    ("int8+int4 (C5), key columns, window 4", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, "key", 4),
 ]
 
 
@@ -161,8 +162,8 @@ def sweep_mode(args, torch):
     dev = torch.device("cuda:0")
     rows = []
     for label, B, H, dk, dv, prec, delta, *ax in SWEEP:
-        key = bool(ax) and ax[0] == "key"
-        window = ax[0] if ax and isinstance(ax[0], int) else 1
+        key = "key" in ax
+        window = next((a for a in ax if isinstance(a, int)), 1)
         g = torch.Generator(device=dev)
         g.manual_seed(args.seed)
 
@@ -304,8 +305,8 @@ def main(argv=None):
     K, W = args.steps, args.warmup
     win = args.window
     if win > 1:
-        if args.scale_axis != "value" or w.per_channel:
-            sys.exit("bench.py: windowed states keep value-row scales and take a scalar decay")
+        if w.per_channel:
+            sys.exit("bench.py: windowed states take a scalar decay")
         K, W = -(-K // win) * win, -(-W // win) * win       # whole windows
     T_in = min(w.T, max(K, W, 1))
     print(f"[bench] generating {T_in} steps of {w.key} inputs on {dev}", file=sys.stderr, flush=True)

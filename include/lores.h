@@ -177,9 +177,9 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                            size_t *bytes, void *stream, lores_state **out);
 
 /*
- * lores_state_alloc_window - lores_state_alloc for a state whose scaled heads
- * (int8, int4, int6, fp8; value-row scales) are requantized once per window
- * of W steps instead of every step, the window's tokens being kept at fp32
+ * lores_state_alloc_window - lores_state_alloc_axis for a state whose scaled
+ * heads (int8, int4, int6, fp8) are requantized once per window of W steps
+ * instead of every step, the window's tokens being kept at fp32
  * in a per-unit buffer (the reading of the PACE and LeapQuant abstracts:
  * rounding once every few tokens, with the tokens in between buffered, cuts
  * the error that accumulates in the state).  Windows are the steps
@@ -190,7 +190,10 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * state by the fp32 recurrence (S'_1 = fl(c fl(s alpha_1)), then
  * U_tau = fma(g_tau, k_tau, S'_tau), S'_tau = fl(U_{tau-1} alpha_tau)), steps
  * it and requantizes it as lores_decode_step does.  W = 1 is
- * lores_state_alloc.  fp32 and bf16 heads step every token as usual.
+ * lores_state_alloc_axis.  fp32 and bf16 heads step every token as usual.
+ * With key-column scales (PACE shares scales within a column), s_i above is
+ * the column's s_j and the window's end takes the column maxima.
+ *   scale_axis  LORES_SCALE_VALUE or LORES_SCALE_KEY (as lores_state_alloc_axis)
  *   window      W, 1 <= W <= LORES_MAX_WINDOW
  * Built for d_k in {64, 128} when W > 1 (LORES_EUNSUPPORTED otherwise).
  * Steps on a windowed state must come in order (t = 1, 2, ... from the
@@ -202,8 +205,8 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * state replays correctly when it covers whole windows.
  */
 int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
-                             const uint8_t *head_prec, int32_t window, void *d_buf,
-                             size_t *bytes, void *stream, lores_state **out);
+                             const uint8_t *head_prec, int32_t scale_axis, int32_t window,
+                             void *d_buf, size_t *bytes, void *stream, lores_state **out);
 
 void lores_state_free(lores_state *st);
 

@@ -116,20 +116,18 @@ def lores_state_alloc(B, H, d_k, d_v, head_prec, device=None, stream=None, buf=N
     on `stream`.  scale_axis: LORES_SCALE_VALUE (one scale per value row,
     lores_state_alloc) or LORES_SCALE_KEY (one per key column,
     lores_state_alloc_axis).  window > 1: requantize the scaled heads once per
-    window of that many steps (lores_state_alloc_window; value-row scales).
+    window of that many steps (lores_state_alloc_window).
     """
     L = _lib.lib()
     hp, hp_ptr = _host_array(head_prec, np.uint8)
     if hp.size != H:
         raise ValueError(f"head_prec must have H = {H} entries")
     window = int(window)
-    if window != 1 and int(scale_axis) != LORES_SCALE_VALUE:
-        raise ValueError("windowed states keep value-row scales")
 
     def alloc(ptr, size, stream_ptr, out):
         if window != 1:
-            return L.lores_state_alloc_window(B, H, d_k, d_v, hp_ptr, window, ptr, size,
-                                              stream_ptr, out)
+            return L.lores_state_alloc_window(B, H, d_k, d_v, hp_ptr, int(scale_axis), window, ptr,
+                                              size, stream_ptr, out)
         return L.lores_state_alloc_axis(B, H, d_k, d_v, hp_ptr, int(scale_axis), ptr, size,
                                         stream_ptr, out)
     nbytes = ctypes.c_size_t(0)

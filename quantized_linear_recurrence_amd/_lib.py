@@ -63,7 +63,7 @@ def lib():
     L.lores_state_alloc_axis.argtypes = [i32, i32, i32, i32, vp, i32, vp,
                                          ctypes.POINTER(ctypes.c_size_t), vp, ctypes.POINTER(vp)]
     L.lores_state_alloc_axis.restype = ctypes.c_int
-    L.lores_state_alloc_window.argtypes = [i32, i32, i32, i32, vp, i32, vp,
+    L.lores_state_alloc_window.argtypes = [i32, i32, i32, i32, vp, i32, i32, vp,
                                            ctypes.POINTER(ctypes.c_size_t), vp, ctypes.POINTER(vp)]
     L.lores_state_alloc_window.restype = ctypes.c_int
     L.lores_state_free.argtypes = [vp]

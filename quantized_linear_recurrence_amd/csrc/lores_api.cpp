@@ -276,15 +276,14 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
 }
 
 int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
-                             const uint8_t *head_prec, int32_t window, void *d_buf,
-                             size_t *bytes, void *stream, lores_state **out) {
+                             const uint8_t *head_prec, int32_t scale_axis, int32_t window,
+                             void *d_buf, size_t *bytes, void *stream, lores_state **out) {
     if (window < 1 || window > LORES_MAX_WINDOW)
         return fail(LORES_EINVAL, "window must be in [1, %d] (got %d)", LORES_MAX_WINDOW, window);
     if (window > 1 && d_k != 64 && d_k != 128)
         return fail(LORES_EUNSUPPORTED, "windowed states are built for d_k = 64 and 128 (got %d)",
                     d_k);
-    return alloc_impl(B, H, d_k, d_v, head_prec, LORES_SCALE_VALUE, window, d_buf, bytes, stream,
-                      out);
+    return alloc_impl(B, H, d_k, d_v, head_prec, scale_axis, window, d_buf, bytes, stream, out);
 }
 
 void lores_state_free(lores_state *st) { delete st; }
@@ -490,7 +489,7 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             hipError_t e;
             if (windowed && has_scales(groups[l][0])) {
                 p.win[0] = (float *)(st->base + st->win_off[groups[l][0]]);
-                e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, p, m, s);
+                e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, key, p, m, s);
             } else {
                 e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16, groups[l][0], p1, p,
                                        m, s, key);
@@ -547,7 +546,8 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
             if (st->window > 1 && st->n_buf > 0 && has_scales(c)) {
                 m.wpos = st->n_buf;
                 m.window = st->window;
-                e = lores::launch_window_dequant(c, st->dk, st->base + st->codes_off[c], sc,
+                e = lores::launch_window_dequant(c, st->dk, st->axis == LORES_SCALE_KEY,
+                                                 st->base + st->codes_off[c], sc,
                                                  (const float *)(st->base + st->win_off[c]), out, m,
                                                  (hipStream_t)stream);
             } else {

@@ -76,19 +76,21 @@ hipError_t launch_step_key_int4(int, bool, bool, bool, const StepPtrs &, const S
 hipError_t launch_step_key_int6(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 hipError_t launch_step_key_fp8(int, bool, bool, bool, const StepPtrs &, const StepMeta &, hipStream_t);
 
-// Windowed states (value-row scales, scalar decay, d_k 64 or 128): the step
-// at window position m.wpos < m.window (read the stored state, buffer the
-// token) or = m.window (rebuild, step and requantize).  One class per launch.
-hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, const StepPtrs &p,
-                              const StepMeta &m, hipStream_t s);
+// Windowed states (scalar decay, d_k 64 or 128; `key`: key-column scales):
+// the step at window position m.wpos < m.window (read the stored state,
+// buffer the token) or = m.window (rebuild, step and requantize).  One class
+// per launch.
+hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key,
+                              const StepPtrs &p, const StepMeta &m, hipStream_t s);
 
 // Dequant uses the same StepMeta with one class; `key`: key-column scales.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
                           float *out, const StepMeta &m, hipStream_t s, bool key);
 // The current state of a windowed class: the stored state followed by the
 // first m.wpos (>= 1) buffered tokens.
-hipError_t launch_window_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                                 const float *win, float *out, const StepMeta &m, hipStream_t s);
+hipError_t launch_window_dequant(int prec, int dk, bool key, const uint8_t *codes,
+                                 const float *scales, const float *win, float *out,
+                                 const StepMeta &m, hipStream_t s);
 hipError_t launch_quant(int prec, int dk, const float *X, uint8_t *codes, float *scales,
                         const StepMeta &m, hipStream_t s, bool key);
 hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);

@@ -806,9 +806,9 @@ struct TaskSide {
 // wavefronts wv - rb .. wv - rb + n_rb - 1 of one work-group, and `lds`
 // holds two buffers of kWavesPerGroup x DK column maxima (tasks alternate
 // between them) and a kWavesPerGroup x DK staging area.
-// WEND: the last step of a window of a windowed state (value-row scales,
-// scalar decay): pass 1 dequantizes with the window's first decay, then the
-// window buffer's tokens are replayed on U before this step's token.
+// WEND: the last step of a window of a windowed state (scalar decay): pass 1
+// dequantizes with the window's first decay, then the window buffer's
+// tokens are replayed on U before this step's token.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false, bool WEND = false>
 struct TaskStream {
     static constexpr int E = Prec<PREC>::E;
@@ -1161,9 +1161,9 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int gx = blockIdx.x;
     const int n_rb = meta.n_rb;
-    if constexpr (WEND) {
+    static_assert(!WEND || (P1 < 0 && !PC), "window ends run one class with a scalar decay");
+    if constexpr (WEND && !KEY) {
         // the last step of a window: one scaled class, scalar decay
-        static_assert(P1 < 0 && !PC && !KEY, "window ends run one class with a scalar decay");
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) return;
         run_single(TaskStream<DK, P0, false, DELTA, BF16IN, false, true>(
@@ -1183,9 +1183,8 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                 for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
             return;
         }
-        run_single(TaskStream<DK, P0, PC, DELTA, BF16IN, true>(qp, kp, vp, alphap, betap, op,
-                                                               codes0, scales0, meta,
-                                                               meta.cls[0], task, cmax));
+        run_single(TaskStream<DK, P0, PC, DELTA, BF16IN, true, WEND>(
+            qp, kp, vp, alphap, betap, op, codes0, scales0, meta, meta.cls[0], task, cmax, win0));
     } else if constexpr (P1 < 0) {
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) return;

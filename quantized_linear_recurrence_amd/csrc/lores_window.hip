@@ -103,7 +103,9 @@ __device__ __forceinline__ bool window_task(const StepMeta &meta, WindowTask &w)
 // ---------------------------------------------------------------------------
 // a step inside a window (p < W): read X_0, buffer the token
 // ---------------------------------------------------------------------------
-template <int DK, int PREC, bool DELTA, bool BF16IN>
+// KEY: key-column scales: X_0 . k = sum_j c_ij (s_j k_j), so the dot products
+// take s o k and s o q and there is no row scale.
+template <int DK, int PREC, bool DELTA, bool BF16IN, bool KEY>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                          const void *__restrict__ vp, const float *__restrict__ alphap,
@@ -119,15 +121,23 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     u32x4 cw[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
-    const float s = scales[w.unit * dv_pad + w.lrow];
+    const float s = KEY ? 1.0f : scales[w.unit * dv_pad + w.lrow];
     const float v = in_scalar<BF16IN>(vp, w.bh * meta.dv + w.lrow);
     const float beta = betap[w.bh], alpha = alphap[w.bh];
-    float kv[NV], qv[NV];
+    float kv[NV], qv[NV], ks[NV], qs[NV];
     const long kb = w.bh * DK + (lane & 15);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
         qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
+        if constexpr (KEY) {
+            const float sc = scales[w.unit * DK + 16 * i + (lane & 15)];
+            ks[i] = sc * kv[i];
+            qs[i] = sc * qv[i];
+        } else {
+            ks[i] = kv[i];
+            qs[i] = qv[i];
+        }
     }
     const int p = meta.wpos, nslot = meta.window - 1;
     float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
@@ -140,8 +150,8 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
         float x[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = code_of<PREC>(cw, 16 * gi + e);
-        if constexpr (DELTA) dot16(A, x, kv[gi]);
-        dot16(Bq, x, qv[gi]);
+        if constexpr (DELTA) dot16(A, x, ks[gi]);
+        dot16(Bq, x, qs[gi]);
     }
 
     // the buffered tokens, latest first: d_tau = product of the later decays
@@ -183,7 +193,7 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
 // the current state of a windowed unit: the stored state followed by the
 // first meta.wpos buffered tokens (lores_dequant_state)
 // ---------------------------------------------------------------------------
-template <int DK, int PREC>
+template <int DK, int PREC, bool KEY>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                             const float *__restrict__ win, float *__restrict__ out,
@@ -197,16 +207,19 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
     u32x4 cw[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) cw[c] = lp[c * dv_pad];
-    const float s = scales[w.unit * dv_pad + w.lrow];
     const int nslot = meta.window - 1, n = meta.wpos;
     const float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     const float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
     float U[DK];
-    const float a1 = s * aslot[0];
-    float na1 = 0.0f;
-    if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
+    // token 1: fl(c fl(s alpha_1)), with the row's or column j's scale s
+    const float s = KEY ? 0.0f : scales[w.unit * dv_pad + w.lrow];
 #pragma unroll
-    for (int j = 0; j < DK; ++j) U[j] = scaled_code<PREC>(cw, j, a1, na1);
+    for (int j = 0; j < DK; ++j) {
+        const float a1 = (KEY ? scales[w.unit * DK + j] : s) * aslot[0];
+        float na1 = 0.0f;
+        if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
+        U[j] = scaled_code<PREC>(cw, j, a1, na1);
+    }
     for (int tau = 1; tau <= n; ++tau) {
         const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
         float kt[NV];
@@ -230,20 +243,20 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
 // Inside a window: one task per wavefront (a read-only pass, many waves per
 // SIMD).  The window's last step: the step kernel's persistent task stream
 // with the buffer replayed between pass 1 and the token's own update.
-template <int DK, int PREC>
+template <int DK, int PREC, bool KEY>
 static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
                             hipStream_t s) {
     if (m.wpos == m.window) {
-        if (delta) return bf16 ? launch_one<DK, false, true, true, PREC, -1, false, true>(p, m, s)
-                               : launch_one<DK, false, true, false, PREC, -1, false, true>(p, m, s);
-        return bf16 ? launch_one<DK, false, false, true, PREC, -1, false, true>(p, m, s)
-                    : launch_one<DK, false, false, false, PREC, -1, false, true>(p, m, s);
+        if (delta) return bf16 ? launch_one<DK, false, true, true, PREC, -1, KEY, true>(p, m, s)
+                               : launch_one<DK, false, true, false, PREC, -1, KEY, true>(p, m, s);
+        return bf16 ? launch_one<DK, false, false, true, PREC, -1, KEY, true>(p, m, s)
+                    : launch_one<DK, false, false, false, PREC, -1, KEY, true>(p, m, s);
     }
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
 #define LORES_WIN_LAUNCH(D, BF)                                                                 \
-    hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF>), grid, block, 0, s, p.q, p.k,   \
-                       p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
+    hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF, KEY>), grid, block, 0, s, p.q,   \
+                       p.k, p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
     if (delta) {
         if (bf16) { LORES_WIN_LAUNCH(true, true) } else { LORES_WIN_LAUNCH(true, false) }
     } else {
@@ -254,33 +267,43 @@ static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const Step
 }
 
 template <int PREC>
-static hipError_t window_prec(int dk, bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
-                              hipStream_t s) {
+static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, const StepPtrs &p,
+                              const StepMeta &m, hipStream_t s) {
     switch (dk) {
-        case 64: return window_dk<64, PREC>(delta, bf16, p, m, s);
-        case 128: return window_dk<128, PREC>(delta, bf16, p, m, s);
+        case 64: return key ? window_dk<64, PREC, true>(delta, bf16, p, m, s)
+                            : window_dk<64, PREC, false>(delta, bf16, p, m, s);
+        case 128: return key ? window_dk<128, PREC, true>(delta, bf16, p, m, s)
+                             : window_dk<128, PREC, false>(delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, const StepPtrs &p,
-                              const StepMeta &m, hipStream_t s) {
+hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key,
+                              const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     if (m.wpos < 1 || m.wpos > m.window || m.window < 2) return hipErrorInvalidValue;
     switch (prec) {
-        case LORES_INT8: return window_prec<LORES_INT8>(dk, delta, in_bf16, p, m, s);
-        case LORES_INT4: return window_prec<LORES_INT4>(dk, delta, in_bf16, p, m, s);
-        case LORES_INT6: return window_prec<LORES_INT6>(dk, delta, in_bf16, p, m, s);
-        case LORES_FP8: return window_prec<LORES_FP8>(dk, delta, in_bf16, p, m, s);
+        case LORES_INT8: return window_prec<LORES_INT8>(dk, delta, in_bf16, key, p, m, s);
+        case LORES_INT4: return window_prec<LORES_INT4>(dk, delta, in_bf16, key, p, m, s);
+        case LORES_INT6: return window_prec<LORES_INT6>(dk, delta, in_bf16, key, p, m, s);
+        case LORES_FP8: return window_prec<LORES_FP8>(dk, delta, in_bf16, key, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_window_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
-                                 const float *win, float *out, const StepMeta &m, hipStream_t s) {
+hipError_t launch_window_dequant(int prec, int dk, bool key, const uint8_t *codes,
+                                 const float *scales, const float *win, float *out,
+                                 const StepMeta &m, hipStream_t s) {
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
-#define LORES_WD(DK, P) hipLaunchKernelGGL((lores_window_dequant_kernel<DK, P>), grid, block, 0, s, \
-                                           codes, scales, win, out, m)
+#define LORES_WD(DK, P)                                                                         \
+    do {                                                                                        \
+        if (key)                                                                                \
+            hipLaunchKernelGGL((lores_window_dequant_kernel<DK, P, true>), grid, block, 0, s,   \
+                               codes, scales, win, out, m);                                     \
+        else                                                                                    \
+            hipLaunchKernelGGL((lores_window_dequant_kernel<DK, P, false>), grid, block, 0, s,  \
+                               codes, scales, win, out, m);                                     \
+    } while (0)
     if (dk == 64) {
         switch (prec) {
             case LORES_INT8: LORES_WD(64, LORES_INT8); break;

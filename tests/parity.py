@@ -286,7 +286,7 @@ def run_free_fp32(w, T, B=None, seed=0, device="cuda"):
 
 
 def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="random", inputs=None,
-                      device="cuda", rounding="sr"):
+                      device="cuda", rounding="sr", axis="value"):
     """Windowed states (lores_state_alloc_window): T steps with per-step
     resync of the stored state and of the window buffer to the oracle's
     (oracle.window).  Checked per step: o (1e-3 of the readout scale of the
@@ -298,7 +298,9 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
     B = w.B if B is None else B
     if inputs is None:
         inputs = make_inputs(w, seed, device, T=T, B=B)
-    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device, window=W)
+    st = lores.lores_state_alloc(B, w.H, w.dk, w.dv, head_prec, device=device, window=W,
+                                 scale_axis=lores.LORES_SCALE_KEY if axis == "key"
+                                 else lores.LORES_SCALE_VALUE)
     if rounding == "nearest":
         lores.lores_state_set_rounding(st, lores.LORES_ROUND_NEAREST)
     lay = lores.lores_state_layout(st)
@@ -311,9 +313,9 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
     for (b, h) in units:
         c = head_prec[h]
         if init == "zero":
-            ost[(b, h)] = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk).items()}
+            ost[(b, h)] = {k: v[0] for k, v in ostep.zero_state(c, 1, w.dv, w.dk, axis=axis).items()}
         else:
-            ost[(b, h)] = random_unit_state(c, w.dv, w.dk, g)
+            ost[(b, h)] = random_unit_state(c, w.dv, w.dk, g, axis)
         obuf[(b, h)] = {k: v[0] for k, v in owin.empty_buffer(1, W, w.dv, w.dk).items()}
     by_class = {}
     for (b, h) in units:
@@ -347,8 +349,8 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
             new, nbuf, o_ref = owin.window_step(
                 c, prev, pbuf, xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs],
                 xin["alpha"][bs, hs], xin["beta"][bs, hs], w.delta, seed, t, bs, hs, W,
-                rounding=rounding)
-            Xcur = owin.replay(c, new, nbuf, 0 if p == W else p)
+                rounding=rounding, axis=axis)
+            Xcur = owin.replay(c, new, nbuf, 0 if p == W else p, axis)
             scale = _readout_scale(Xcur)
             stats.o_err_q = max(stats.o_err_q, float(
                 (np.abs(o_host[bs, hs] - o_ref).max(axis=1) / scale).max()))
@@ -367,13 +369,13 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
                     np.maximum(bound, 1e-30)
                 stats.g_err = max(stats.g_err, float(ge.max()))
             elif c == 5:
-                Xg = ostep.dequant(c, gpu).astype(np.float64)
-                Xr = ostep.dequant(c, new).astype(np.float64)
+                Xg = ostep.dequant(c, gpu, axis=axis).astype(np.float64)
+                Xr = ostep.dequant(c, new, axis=axis).astype(np.float64)
                 diff = gpu["fp8"] != new["fp8"]
                 stats.fp8 += diff.size
                 stats.fp8_diff += int(diff.sum())
                 if diff.any():
-                    rowmax = np.abs(Xr).max(axis=2, keepdims=True)
+                    rowmax = np.abs(Xr).max(axis=2 if axis == "value" else 1, keepdims=True)
                     step = np.maximum(np.abs(Xr), np.abs(Xg)) / 8 + rowmax / 448 * 2.0 ** -9
                     excess = (np.abs(Xg - Xr) - step) / np.maximum(rowmax, 1e-300)
                     stats.fp8_excess = max(stats.fp8_excess, float(excess[diff].max()))

@@ -47,6 +47,18 @@ def test_longest_window(prec, dk, dv):
     s.check()
 
 
+@pytest.mark.parametrize("prec", [2, 3, 4, 5])
+@pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256)])
+def test_key_column_windows(prec, W, dk, dv):
+    """Windows over key-column scales (the PACE combination): the window end
+    takes the column maxima of the replayed state."""
+    w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, delta=1)
+    log(f"case: key-column window W={W} prec={prec} dk={dk} dv={dv}, {w.T} steps")
+    s = run_window_parity(w, T=w.T, W=W, head_prec=[prec] * w.H, axis="key")
+    log(s.summary())
+    s.check()
+
+
 def test_mixed_heads_from_zero_nearest():
     w = C1.scaled(B=2, H=4, dk=128, dv=128, T=9, delta=1)
     log("case: window W=4, heads int8/int4/int6/fp8 from S_0 = 0, nearest rounding")
@@ -102,14 +114,16 @@ def test_window_one_is_the_plain_state():
 
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
-def test_dequant_replays_the_buffer(prec):
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_dequant_replays_the_buffer(prec, axis):
     """Inside a window lores_dequant_state returns the current state: the
     stored state followed by the buffered tokens' fp32 recurrence, bit for
     bit against the oracle's replay of the same (oracle-written) buffer."""
     W, B, H, dk, dv, n = 6, 2, 3, 128, 72, 3
     w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=n)
-    log(f"case: window dequant after {n} buffered tokens, prec={prec}")
-    st = lores.lores_state_alloc(B, H, dk, dv, [prec] * H, device=DEV, window=W)
+    log(f"case: window dequant after {n} buffered tokens, prec={prec} axis={axis}")
+    st = lores.lores_state_alloc(B, H, dk, dv, [prec] * H, device=DEV, window=W,
+                                 scale_axis=lores.LORES_SCALE_KEY if axis == "key" else 0)
     x = make_inputs(w, 1, DEV, T=n)
     for t in range(1, n + 1):           # the handle now counts n buffered tokens
         xs = {k: v[t - 1] for k, v in x.items()}
@@ -123,7 +137,7 @@ def test_dequant_replays_the_buffer(prec):
     want = np.zeros((B, H, dv, dk), np.float32)
     for b in range(B):
         for h in range(H):
-            s = random_unit_state(prec, dv, dk, g)
+            s = random_unit_state(prec, dv, dk, g, axis)
             win = {"g": g.standard_normal((W - 1, dv)).astype(np.float32),
                    "k": (g.standard_normal((W - 1, dk)) / np.sqrt(dk)).astype(np.float32),
                    "alpha": g.uniform(0.8, 1.0, W - 1).astype(np.float32)}
@@ -131,7 +145,7 @@ def test_dequant_replays_the_buffer(prec):
             lc.write_unit(host, lay, prec, u, s)
             lc.write_window(host, lay, prec, u, win)
             want[b, h] = owin.replay(prec, {k: v[None] for k, v in s.items()},
-                                     {k: v[None] for k, v in win.items()}, n)[0]
+                                     {k: v[None] for k, v in win.items()}, n, axis)[0]
     st.buf.copy_(torch.from_numpy(host))
     got = lores.lores_dequant_state(st).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -171,16 +171,22 @@ def test_window_layout_and_limits(lores_lib):
     hp = (ctypes.c_uint8 * 4)(2, 3, 1, 5)
     n = ctypes.c_size_t(0)
     for W in (1, 2, 8, 16):
-        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, W, None, ctypes.byref(n), None,
+        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, 0, W, None, ctypes.byref(n), None,
                                           None) == 0
         assert n.value == _layout_bytes(5, 4, 128, 100, [2, 3, 1, 5], window=W), W
     for W in (0, 17, -1):
-        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, W, None, ctypes.byref(n), None,
+        assert L.lores_state_alloc_window(5, 4, 128, 100, hp, 0, W, None, ctypes.byref(n), None,
                                           None) == lores._lib.LORES_EINVAL
-    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 4, None, ctypes.byref(n), None,
+    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 0, 4, None, ctypes.byref(n), None,
                                       None) == lores._lib.LORES_EUNSUPPORTED
-    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 1, None, ctypes.byref(n), None,
+    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 0, 1, None, ctypes.byref(n), None,
                                       None) == 0
+    # key-column windows: d_k scales per unit plus the window block
+    assert L.lores_state_alloc_window(5, 4, 128, 100, hp, 1, 4, None, ctypes.byref(n), None,
+                                      None) == 0
+    assert n.value == _layout_bytes(5, 4, 128, 100, [2, 3, 1, 5], key=True, window=4)
+    assert L.lores_state_alloc_window(5, 4, 128, 150, hp, 1, 4, None, ctypes.byref(n), None,
+                                      None) == lores._lib.LORES_EUNSUPPORTED
 
 
 def test_error_message_is_thread_local_and_cleared(lores_lib):

@@ -37,14 +37,15 @@ def _inputs(g, T, N, dv, dk, delta):
             "beta": (g.uniform(0.2, 1.5, (T, N)) if delta else g.uniform(0.1, 2.0, (T, N))).astype(F32)}
 
 
-def _random_state(prec, N, dv, dk, g):
+def _random_state(prec, N, dv, dk, g, axis="value"):
+    ns = dv if axis == "value" else dk
     if prec == step.PREC_FP8:
         by = g.integers(0, 256, (N, dv, dk)).astype(np.uint8)
         by[(by & 0x7F) == 0x7F] ^= 1
-        return {"fp8": by, "scales": np.exp(g.uniform(-5, -2, (N, dv))).astype(F32)}
+        return {"fp8": by, "scales": np.exp(g.uniform(-5, -2, (N, ns))).astype(F32)}
     r = step.QMAX[prec]
     return {"codes": g.integers(-r, r + 1, (N, dv, dk)).astype(np.int32),
-            "scales": np.exp(g.uniform(-5, -2, (N, dv))).astype(F32)}
+            "scales": np.exp(g.uniform(-5, -2, (N, ns))).astype(F32)}
 
 
 def test_hand_worked_window():
@@ -73,18 +74,19 @@ def test_hand_worked_window():
 
 @pytest.mark.parametrize("prec", SCALED)
 @pytest.mark.parametrize("delta", [0, 1])
-def test_window_one_is_the_per_step_method(prec, delta):
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_window_one_is_the_per_step_method(prec, delta, axis):
     g = np.random.default_rng(100 + prec + 10 * delta)
     N, dv, dk, T = 4, 24, 32, 5
     x = _inputs(g, T, N, dv, dk, delta)
-    st = _random_state(prec, N, dv, dk, g)
+    st = _random_state(prec, N, dv, dk, g, axis)
     ref = {k: v.copy() for k, v in st.items()}
     buf = window.empty_buffer(N, 1, dv, dk)
     b, h = np.arange(N), np.full(N, 3)
     for t in range(1, T + 1):
         a = [x[k][t - 1] for k in ("q", "k", "v", "alpha", "beta")]
-        st, buf, o = window.window_step(prec, st, buf, *a, delta, 9, t, b, h, W=1)
-        ref, o_ref = step.decode_step(prec, ref, *a, delta, 9, t, b, h)
+        st, buf, o = window.window_step(prec, st, buf, *a, delta, 9, t, b, h, W=1, axis=axis)
+        ref, o_ref = step.decode_step(prec, ref, *a, delta, 9, t, b, h, axis=axis)
         for key in ref:
             assert np.array_equal(st[key], ref[key]), (t, key)
         assert np.array_equal(o, o_ref)
@@ -137,32 +139,37 @@ def test_readouts_follow_the_fp64_recurrence(delta):
 
 
 @pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
-def test_one_rounding_per_window(prec):
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_one_rounding_per_window(prec, axis):
     """alpha = 1, delta = 0: the window-end state is the quantization of the
     stored state plus every write of the window (nearest mode), and the
-    codes move only at window ends."""
+    codes move only at window ends; with key-column scales the scale of a
+    column is its maximum over the rows."""
     g = np.random.default_rng(400 + prec)
     N, dv, dk, W, T = 3, 16, 32, 4, 12
     x = _inputs(g, T, N, dv, dk, 0)
     x["alpha"][:] = 1.0
-    st = _random_state(prec, N, dv, dk, g)
+    st = _random_state(prec, N, dv, dk, g, axis)
+    gax = 2 if axis == "value" else 1
     buf = window.empty_buffer(N, W, dv, dk)
     b, h = np.arange(N), np.zeros(N, np.int64)
     r = step.QMAX[prec]
     for t in range(1, T + 1):
         a = [x[kk][t - 1] for kk in ("q", "k", "v", "alpha", "beta")]
         if (t - 1) % W == 0:
-            X0 = step.dequant(prec, st).astype(np.float64)
+            X0 = step.dequant(prec, st, axis=axis).astype(np.float64)
             acc = X0.copy()
         acc += a[4][:, None, None].astype(np.float64) * a[2][:, :, None] * a[1][:, None, :]
         prev = st["codes"].copy()
-        st, buf, _ = window.window_step(prec, st, buf, *a, 0, 2, t, b, h, W=W, rounding="nearest")
+        st, buf, _ = window.window_step(prec, st, buf, *a, 0, 2, t, b, h, W=W, rounding="nearest",
+                                        axis=axis)
         if t % W:
             assert np.array_equal(st["codes"], prev)
         else:
-            X = step.dequant(prec, st).astype(np.float64)
-            s = st["scales"].astype(np.float64)[:, :, None]
+            X = step.dequant(prec, st, axis=axis).astype(np.float64)
+            sc = st["scales"].astype(np.float64)
+            s = sc[:, :, None] if axis == "value" else sc[:, None, :]
             # nearest rounding of the exact window sum, up to fp32 rounding
             assert np.all(np.abs(X - acc) <= s * (0.5 + 1e-3)), t
-            m = np.abs(acc).max(axis=2)
+            m = np.abs(acc).max(axis=gax)
             assert np.allclose(st["scales"], m / r, rtol=1e-5)
