@@ -193,7 +193,7 @@ def run_suite(T=2048, B=32, H=12, d=128, seed=1, device="cuda"):
     """The harness's report: random writes (drift 100), scalar decay, delta
     = 0, two decay regimes; int8, E4M3, int6 and int4 states, int8 and int4
     with key-column scales, int8 and int4 requantized once per window of 4 or
-    16 steps, and the decay-assigned mixes that keep the slowest half of the
+    16 steps (int4 also over key columns), and the decay-assigned mixes that keep the slowest half of the
     heads at 8 or 6 bits (6.25 and 5.25 effective bits); stochastic and
     nearest rounding.  Then Proposition 1's value-row versus key-column
     readout error on states with row or column outliers."""
@@ -208,6 +208,7 @@ def run_suite(T=2048, B=32, H=12, d=128, seed=1, device="cuda"):
                 ("int4, key columns", [3] * H, LORES_SCALE_KEY, 1),
                 ("int8, window 4", [2] * H, V, 4), ("int4, window 4", [3] * H, V, 4),
                 ("int4, window 16", [3] * H, V, 16),
+                ("int4, key columns, window 4", [3] * H, LORES_SCALE_KEY, 4),
                 ("int8 slowest half + int4", decay_assigned(H, [(0.5, 2), (0.5, 3)]), V, 1),
                 ("int6 slowest half + int4", decay_assigned(H, [(0.5, 4), (0.5, 3)]), V, 1)):
             for rnd in (LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST):
