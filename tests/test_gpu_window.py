@@ -171,3 +171,33 @@ def test_windowed_state_contract():
         lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 2)
     lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 5)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_shard_invariance_of_windowed_states(axis):
+    """Sequence and head shards of a windowed state (seq_base / head_base key
+    the rounding at window ends) reproduce the whole batch bit for bit: the
+    readouts of every step and the current state after two windows and a
+    half."""
+    B, head_prec, dk, dv, W = 10, [2, 3, 4, 5], 128, 96, 4
+    H = len(head_prec)
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=2 * W + 2)
+    log(f"case: windowed shard invariance axis={axis} B={B} H={H} W={W}")
+    sa = lores.LORES_SCALE_KEY if axis == "key" else lores.LORES_SCALE_VALUE
+    inp = make_inputs(w, 5, DEV)
+    full = lores.lores_state_alloc(B, H, dk, dv, head_prec, device=DEV, window=W, scale_axis=sa)
+    cuts = [(0, 4, 0, 2), (0, 4, 2, 4), (4, 10, 0, 4)]
+    shards = [(b0, b1, h0, h1, lores.lores_state_alloc(b1 - b0, h1 - h0, dk, dv, head_prec[h0:h1],
+                                                       device=DEV, window=W, scale_axis=sa))
+              for b0, b1, h0, h1 in cuts]
+    for t in range(1, w.T + 1):
+        x = {k: v[t - 1] for k, v in inp.items()}
+        o_full = lores.lores_decode_step(full, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, 8, t)
+        for b0, b1, h0, h1, st in shards:
+            xs = {k: v[b0:b1, h0:h1].contiguous() for k, v in x.items()}
+            o_s = lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1,
+                                          8, t, seq_base=b0, head_base=h0)
+            assert torch.equal(o_s, o_full[b0:b1, h0:h1]), (t, b0, h0)
+    X = lores.lores_dequant_state(full)
+    for b0, b1, h0, h1, st in shards:
+        assert torch.equal(lores.lores_dequant_state(st), X[b0:b1, h0:h1])
