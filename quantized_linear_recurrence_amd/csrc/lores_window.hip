@@ -62,13 +62,6 @@ __device__ __forceinline__ float stored(const u32x4 *cw, int j) {
     }
 }
 
-// c_ij (int rows) or the E4M3 value (fp8 rows), unscaled
-template <int PREC>
-__device__ __forceinline__ float code_of(const u32x4 *cw, int j) {
-    if constexpr (PREC == LORES_FP8) return stored<PREC>(cw, j);
-    else return stored<PREC>(cw, j) - Prec<PREC>::OFF;
-}
-
 // fl(code * a): int rows as fma(code + off, a, -off a), exact since off * a is
 // a power-of-two multiple of a
 template <int PREC>
@@ -143,15 +136,24 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
 
-    // sum_j c_ij k_j and sum_j c_ij q_j over the stored row (codes unscaled)
+    // sum_j c_ij k_j and sum_j c_ij q_j over the stored row (codes unscaled):
+    // int rows take the stored offset-binary integers c + off and subtract
+    // off * sum_j k_j once (a different rounding of the same sum)
     float A = 0.0f, Bq = 0.0f;
 #pragma unroll
     for (int gi = 0; gi < NV; ++gi) {
         float x[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = code_of<PREC>(cw, 16 * gi + e);
+        for (int e = 0; e < 16; ++e) x[e] = stored<PREC>(cw, 16 * gi + e);
         if constexpr (DELTA) dot16(A, x, ks[gi]);
         dot16(Bq, x, qs[gi]);
+    }
+    if constexpr (PREC != LORES_FP8) {
+        float ones[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) ones[i] = 1.0f;
+        if constexpr (DELTA) A = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(ks, ones), A);
+        Bq = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(qs, ones), Bq);
     }
 
     // the buffered tokens, latest first: d_tau = product of the later decays
