@@ -201,3 +201,47 @@ def test_shard_invariance_of_windowed_states(axis):
     X = lores.lores_dequant_state(full)
     for b0, b1, h0, h1, st in shards:
         assert torch.equal(lores.lores_dequant_state(st), X[b0:b1, h0:h1])
+
+
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_windowed_graph_replays_match_eager(axis):
+    """A captured graph of two whole windows replays the eager steps' bytes
+    and readouts exactly, three times over, with eager work between."""
+    B, head_prec, W = 48, [2, 3] * 4, 4
+    w = C1.scaled(B=B, H=8, dk=128, dv=128, T=2 * W)
+    log(f"case: windowed graph replays axis={axis} B={B} H=8 W={W}")
+    sa = lores.LORES_SCALE_KEY if axis == "key" else lores.LORES_SCALE_VALUE
+    inp = make_inputs(w, 6, DEV)
+    st = lores.lores_state_alloc(B, 8, 128, 128, head_prec, device=DEV, window=W, scale_axis=sa)
+    warm = {k: v[0] for k, v in inp.items()}
+    for t in range(1, W + 1):           # a first window, so the stored state is not zero
+        lores.lores_decode_step(st, warm["q"], warm["k"], warm["v"], warm["alpha"], warm["beta"],
+                                1, 2, t)
+    torch.cuda.synchronize()
+    init = st.buf.clone()
+    outs = [torch.empty((B, 8, 128), dtype=torch.float32, device=DEV) for _ in range(w.T)]
+
+    def steps():
+        for t in range(1, w.T + 1):
+            x = {k: v[t - 1] for k, v in inp.items()}
+            lores.lores_decode_step(st, x["q"], x["k"], x["v"], x["alpha"], x["beta"], 1, 3,
+                                    W + t, o=outs[t - 1])
+
+    steps()
+    torch.cuda.synchronize()
+    ref_buf, ref_o = st.buf.clone(), [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    st.buf.copy_(init)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        steps()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st.buf.copy_(init)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.buf, ref_buf), rep
+        assert all(torch.equal(a, b) for a, b in zip(outs, ref_o)), rep
