@@ -107,6 +107,36 @@ def parse(argv=None):
     return ap.parse_args(argv)
 
 
+def effective_bits(head_prec, dk, dv, key=False):
+    """Mean stored bits per state element: codes plus the fp32 scales."""
+    per = []
+    for p in head_prec:
+        bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}[p]
+        if p in (2, 3, 4, 5):
+            bits += 32.0 * (dk if key else dv) / (dk * dv)
+        per.append(bits)
+    return sum(per) / len(per)
+
+
+def copy_reference(torch, nbytes):
+    """Event time of a plain device-to-device copy that reads and writes
+    nbytes / 2 each (the state's read + write traffic), after a warm copy."""
+    n = max(int(nbytes) // 2, 1)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    return {"bytes": 2 * n, "us": us, "GBps": 2 * n / us / 1e3}
+
+
 def copy_mode(args, torch):
     """Plain device-to-device copy of --copy-mib MiB, 10 times: the calibration
     kernel for FETCH_SIZE / WRITE_SIZE counters and a measured copy bandwidth."""
@@ -430,6 +460,8 @@ def main(argv=None):
             "launches_per_step": n_launches_per_step,
         },
         "kernel_source_hash": kernel_source_hash(),
+        "effective_bits": effective_bits(head_prec, w.dk, w.dv, key),
+        "copy_reference": copy_reference(torch, step_bytes),
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
