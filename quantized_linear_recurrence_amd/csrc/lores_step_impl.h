@@ -1170,8 +1170,9 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
             qp, kp, vp, alphap, betap, op, codes0, scales0, meta, meta.cls[0], task, nullptr,
             win0));
     } else if constexpr (KEY) {
-        // one class; the n_rb (1, 2 or 4) row blocks of a unit are
-        // consecutive tasks, so whole units share a work-group.  A wave past
+        // one class (a step, or with WEND a window's end); the n_rb (1, 2
+        // or 4) row blocks of a unit are consecutive tasks, so whole units
+        // share a work-group.  A wave past
         // the last task still takes part in the work-group's barriers: one
         // per sequence of its stride, as a working wave does (units of one
         // row block take no barrier at all).
