@@ -579,6 +579,23 @@ __device__ __forceinline__ float in_scalar(const void *__restrict__ p, long idx)
     }
 }
 
+// Prefetched inputs: a bf16 element is held as its 16 bits (zero-extended)
+// until the task that uses it widens it, so nothing waits for the load
+// where it is issued.
+template <bool BF16IN>
+__device__ __forceinline__ float in_raw(const void *__restrict__ p, long idx) {
+    if constexpr (BF16IN) {
+        return __uint_as_float((uint32_t)((const uint16_t *)p)[idx]);
+    } else {
+        return ((const float *)p)[idx];
+    }
+}
+template <bool BF16IN>
+__device__ __forceinline__ float from_raw(float x) {
+    if constexpr (BF16IN) return __uint_as_float(__float_as_uint(x) << 16);
+    else return x;
+}
+
 // ---------------------------------------------------------------------------
 // requantization of one row (one lane): fresh scale, rounding, packing and
 // store of the row's 16-byte chunks (chunk c at cp + c * dv_pad).  Shared by
@@ -873,7 +890,7 @@ struct TaskStream {
         } else if constexpr (has_scale<PREC>()) {
             in.s = scales[unit * dv_pad + lrow];
         }
-        in.v = in_scalar<BF16IN>(vp, bh * meta.dv + lrow);
+        in.v = in_raw<BF16IN>(vp, bh * meta.dv + lrow);
         in.beta = betap[bh];
         in.alpha = PC ? 1.0f : alphap[bh];
         if constexpr (WEND) {
@@ -886,8 +903,8 @@ struct TaskStream {
         const long kb = bh * DK + (threadIdx.x & 15);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            in.kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
-            in.qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
+            in.kv[i] = in_raw<BF16IN>(kp, kb + 16 * i);
+            in.qv[i] = in_raw<BF16IN>(qp, kb + 16 * i);
             if constexpr (PC && !KEY) in.av[i] = alphap[kb + 16 * i];
         }
     }
@@ -895,7 +912,13 @@ struct TaskStream {
     template <class Mid>
     __device__ __forceinline__ void run(int b, const u32x4 *cw, const TaskSide<NV, KEY> &in,
                                         Mid &&mid, int buf = 0) const {
-        const float s = in.s, vi = in.v;
+        const float s = in.s, vi = from_raw<BF16IN>(in.v);
+        float kv[NV], qv[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            kv[i] = from_raw<BF16IN>(in.kv[i]);
+            qv[i] = from_raw<BF16IN>(in.qv[i]);
+        }
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;           // index into [B][H] inputs
@@ -932,7 +955,7 @@ struct TaskStream {
         auto group_done = [&](int j) {
             if constexpr (PC && !has_scale<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
             if constexpr (KEY) mul16(&U[j - 15], sig[j >> 4]);
-            if constexpr (DELTA && !WEND) dot16(r, &U[j - 15], in.kv[j >> 4]);
+            if constexpr (DELTA && !WEND) dot16(r, &U[j - 15], kv[j >> 4]);
             // without the projection nothing orders pass 1 before the
             // next task's loads; materialize the group here so the
             // chunk registers are free when `mid` reuses them
@@ -1026,7 +1049,7 @@ struct TaskStream {
             }
             if constexpr (DELTA) {
 #pragma unroll
-                for (int gi = 0; gi < NV; ++gi) dot16(r, &U[16 * gi], in.kv[gi]);
+                for (int gi = 0; gi < NV; ++gi) dot16(r, &U[16 * gi], kv[gi]);
             }
         }
 
@@ -1037,7 +1060,7 @@ struct TaskStream {
         float o = 0.0f, m = 0.0f;
 #pragma unroll
         for (int gi = 0; gi < NV; ++gi) {
-            upd16(&U[16 * gi], o, g, in.kv[gi], in.qv[gi]);
+            upd16(&U[16 * gi], o, g, kv[gi], qv[gi]);
             if constexpr (!KEY) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
