@@ -193,6 +193,31 @@ __device__ __forceinline__ uint32_t and_opaque(uint32_t x, uint32_t m) {
     return r;
 }
 
+// (float)(int8_t) of byte k of w, in one SDWA conversion with sign extension.
+// With w = stored bytes ^ 0x80808080 this is the int8 code (byte - 128).
+__device__ __forceinline__ float cvt_sbyte(uint32_t w, int k) {
+    float r;
+    switch (k) {
+        case 0:
+            asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0"
+                : "=v"(r) : "v"(w));
+            break;
+        case 1:
+            asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1"
+                : "=v"(r) : "v"(w));
+            break;
+        case 2:
+            asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2"
+                : "=v"(r) : "v"(w));
+            break;
+        default:
+            asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+                : "=v"(r) : "v"(w));
+            break;
+    }
+    return r;
+}
+
 // Byte 2 of the fp32 patterns of z[0..3] into bytes 0..3 (three v_perm_b32).
 __device__ __forceinline__ uint32_t gather_byte2(const float *z) {
     // selector bytes: 0-3 pick the second operand's bytes, 4-7 the first's,
@@ -992,7 +1017,11 @@ struct TaskStream {
                     else sp = v * a;
                 } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
-                    if constexpr (PREC == LORES_INT8) {
+                    if constexpr (PREC == LORES_INT8 && (KEY || PC)) {
+                        // the code itself (byte - 128), for a product with a
+                        // per-column factor
+                        ub = cvt_sbyte(wd[e >> 2] ^ 0x80808080u, e & 3);
+                    } else if constexpr (PREC == LORES_INT8) {
                         ub = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
                     } else {
                         // low nibbles (even elements) and high nibbles (odd) as bytes
@@ -1001,8 +1030,9 @@ struct TaskStream {
                                                      : and_opaque(w, 0x0F0F0F0Fu);
                         ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
                     }
-                    if constexpr (KEY) sp = ub - Prec<PREC>::OFF;   // times sig_j per group
-                    else if constexpr (PC) sp = (ub - Prec<PREC>::OFF) * aj[j & 15];
+                    constexpr float OFF = PREC == LORES_INT8 && (KEY || PC) ? 0.0f : Prec<PREC>::OFF;
+                    if constexpr (KEY) sp = ub - OFF;               // times sig_j per group
+                    else if constexpr (PC) sp = (ub - OFF) * aj[j & 15];
                     else sp = __builtin_fmaf(ub, a, na);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
