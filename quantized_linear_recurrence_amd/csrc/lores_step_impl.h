@@ -831,7 +831,8 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 
 // Per-task values loaded ahead of the task, besides its chunks: the row
 // scale and v of this lane's row, beta and a scalar alpha, and k, q and a
-// per-channel alpha as row vectors (NV registers each).
+// per-channel alpha as row vectors (NV registers each).  With bf16 inputs, v,
+// k and q hold the raw 16 bits (from in_raw) until `run` widens them.
 // With key-column scales, sl and al hold the unit's column scales and a
 // per-channel alpha in lane form (lane L: columns 64 t + L), two registers
 // each at d_k = 128; the row vectors of their product are built at the start
