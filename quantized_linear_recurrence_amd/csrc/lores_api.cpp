@@ -149,13 +149,14 @@ lores::StepMeta make_meta(const lores_state *st, const int *cls, int n_cls) {
         off += d.Hc;
     }
     // a launch of the two int classes pairs task p of one with task p of the
-    // other in one wavefront; `groups` then counts only the unpaired rest
+    // other in one wavefront; `groups` then counts only the unpaired rest, in
+    // the kPairWavesPerGroup-wavefront groups of such launches
     if (n_cls == 2 && is_int_prec(cls[0]) && is_int_prec(cls[1])) {
         const int n0 = m.cls[0].Hc * st->n_rb, n1 = m.cls[1].Hc * st->n_rb;
         const int paired = n0 < n1 ? n0 : n1;
         for (int i = 0; i < 2; ++i) {
             const int rest = (i ? n1 : n0) - paired;
-            m.cls[i].groups = (rest + lores::kWavesPerGroup - 1) / lores::kWavesPerGroup;
+            m.cls[i].groups = (rest + lores::kPairWavesPerGroup - 1) / lores::kPairWavesPerGroup;
         }
     }
     return m;

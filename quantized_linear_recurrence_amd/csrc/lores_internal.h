@@ -13,7 +13,7 @@ namespace lores {
 struct ClassDesc {
     int32_t prec;          // LORES_* code
     int32_t Hc;            // heads of the class
-    int32_t groups;        // work-groups along grid x: ceil(Hc * n_rb / kWavesPerGroup)
+    int32_t groups;        // work-groups along grid x: ceil(tasks / wavefronts per group)
     int32_t head_off;      // first entry of the class's head list in StepMeta::heads
     int64_t unit_bytes;    // code bytes per (sequence, head) unit
 };
@@ -97,5 +97,8 @@ hipError_t launch_fill_zero(void *buf, uint64_t bytes, hipStream_t s);
 
 // Tasks (one wavefront each) per 256-thread work-group.
 constexpr int kWavesPerGroup = 4;
+// Wavefronts per work-group of a fused int-pair launch (512 threads: one
+// group per CU at two wavefronts per SIMD, sharing a work queue).
+constexpr int kPairWavesPerGroup = 8;
 
 }  // namespace lores

@@ -1158,30 +1158,109 @@ __device__ __forceinline__ void run_single(
     }
 }
 
-// Two streams of different int classes in one wavefront, alternating task by
-// task: every wavefront (so every SIMD) carries the same mix of the
-// VALU-heavier and the HBM-heavier class, and each task's pass 1 is followed
-// by the loads of the other stream's next task.
-template <int DK, int P0, int P1, bool PC, bool DELTA, bool BF16IN>
-__device__ __forceinline__ void run_paired(const TaskStream<DK, P0, PC, DELTA, BF16IN> &t0,
-                                           const TaskStream<DK, P1, PC, DELTA, BF16IN> &t1) {
-    static_assert(TaskStream<DK, P0, PC, DELTA, BF16IN>::NCH <= kMaxPrefetchChunks &&
-                      TaskStream<DK, P1, PC, DELTA, BF16IN>::NCH <= kMaxPrefetchChunks,
-                  "paired streams need prefetchable rows");
-    const int bstep = gridDim.y;
-    u32x4 cw[kMaxPrefetchChunks];
-    TaskSide<TaskStream<DK, P0, PC, DELTA, BF16IN>::NV> in0;
-    TaskSide<TaskStream<DK, P1, PC, DELTA, BF16IN>::NV> in1;
-    int b = blockIdx.y;
-    t0.issue(b, cw, in0);
+// ---------------------------------------------------------------------------
+// Work queue of a work-group (launches of a fused int pair).  Wavefronts do
+// not progress at the same rate: of two wavefronts sharing a SIMD the older
+// one is issued first, so with a fixed share of tasks per wavefront one of
+// them finishes long before the other.  A fused-pair launch runs one
+// kPairWavesPerGroup-wavefront group per CU whose items are handed out by an
+// LDS counter: item n is task slot task_base + n % kPairWavesPerGroup and
+// sequence blockIdx.y + (n / kPairWavesPerGroup) gridDim.y, and a wavefront
+// takes its next item as it starts a task (slots past the class's last task
+// are skipped).
+// ---------------------------------------------------------------------------
+struct WorkQueue {
+    int *counter;                      // LDS, zeroed before the group's first take
+    int task_base, n_tasks, total;
+
+    __device__ __forceinline__ WorkQueue(int *c, int base, int n, int B)
+        : counter(c), task_base(base), n_tasks(n) {
+        const int nb = (B - (int)blockIdx.y + (int)gridDim.y - 1) / (int)gridDim.y;
+        total = kPairWavesPerGroup * (nb > 0 ? nb : 0);
+    }
+    // the next valid item, or -1 when the group's items are used up
+    __device__ __forceinline__ int take() const {
+        while (true) {
+            int n = 0;
+            if ((threadIdx.x & 63) == 0)
+                n = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            n = __builtin_amdgcn_readfirstlane(n);
+            if (n >= total) return -1;
+            if (task_base + n % kPairWavesPerGroup < n_tasks) return n;
+        }
+    }
+    __device__ __forceinline__ int task(int n) const { return task_base + n % kPairWavesPerGroup; }
+    __device__ __forceinline__ int seq(int n) const {
+        return (int)blockIdx.y + (n / kPairWavesPerGroup) * (int)gridDim.y;
+    }
+};
+
+// One class through the work queue; `make(task)` builds the task's stream.
+// Loads are prefetched as in run_single: the next item's per-task values and
+// chunks right after pass 1 of the current one.
+template <class Make>
+__device__ __forceinline__ void run_queue(const WorkQueue &wq, Make &&make) {
+    using TS = decltype(make(0));
+    constexpr int P = TS::NCH;                   // whole rows are prefetched
+    static_assert(P <= kMaxPrefetchChunks, "queued streams hold prefetchable rows");
+    u32x4 cw[TS::NCH];
+    TaskSide<TS::NV> in0, in1;
+    int n = wq.take();
+    if (n < 0) return;
+    make(wq.task(n)).issue(wq.seq(n), cw, in0);
     while (true) {
-        const int bn = b + bstep;
-        t0.run(b, cw, in0, [&] { t1.issue(b, cw, in1); });
-        t1.run(b, cw, in1, [&] {
-            if (bn < t0.meta.B) t0.issue(bn, cw, in0);
+        int nn = wq.take();
+        {
+            const TS cur = make(wq.task(n));
+            const TS nxt = make(wq.task(nn >= 0 ? nn : n));
+            cur.run(wq.seq(n), cw, in0, [&] {
+                if (nn >= 0) nxt.template issue<0, P>(wq.seq(nn), cw, in1);
+            }, 0);
+            if (nn < 0) break;
+        }
+        n = nn;
+        nn = wq.take();
+        {
+            const TS cur = make(wq.task(n));
+            const TS nxt = make(wq.task(nn >= 0 ? nn : n));
+            cur.run(wq.seq(n), cw, in1, [&] {
+                if (nn >= 0) nxt.template issue<0, P>(wq.seq(nn), cw, in0);
+            }, 1);
+            if (nn < 0) break;
+        }
+        n = nn;
+    }
+}
+
+// A fused pair of int classes through the work queue: an item is task p of
+// class 0 then task p of class 1 for one sequence, alternating in one
+// wavefront, so every SIMD carries the same mix of the VALU-heavier and the
+// HBM-heavier class; each task's pass 1 is followed by the loads of the other
+// stream's next task.
+template <class Make0, class Make1>
+__device__ __forceinline__ void run_queue_paired(const WorkQueue &wq, Make0 &&make0, Make1 &&make1) {
+    using T0 = decltype(make0(0));
+    using T1 = decltype(make1(0));
+    static_assert(T0::NCH <= kMaxPrefetchChunks && T1::NCH <= kMaxPrefetchChunks,
+                  "paired streams need prefetchable rows");
+    u32x4 cw[kMaxPrefetchChunks];
+    TaskSide<T0::NV> in0;
+    TaskSide<T1::NV> in1;
+    int n = wq.take();
+    if (n < 0) return;
+    make0(wq.task(n)).issue(wq.seq(n), cw, in0);
+    while (true) {
+        const int nn = wq.take();
+        const int b = wq.seq(n);
+        const T0 a = make0(wq.task(n));
+        const T1 c = make1(wq.task(n));
+        a.run(b, cw, in0, [&] { c.issue(b, cw, in1); });
+        const T0 an = make0(wq.task(nn >= 0 ? nn : n));
+        c.run(b, cw, in1, [&] {
+            if (nn >= 0) an.issue(wq.seq(nn), cw, in0);
         });
-        if (bn >= t0.meta.B) break;
-        b = bn;
+        if (nn < 0) break;
+        n = nn;
     }
 }
 
@@ -1203,9 +1282,16 @@ constexpr bool pairable() {
     }
 }
 
+// Wavefronts per work-group of a launch: fused int pairs run one queued
+// group per CU.
+template <int P0, int P1, int DK>
+constexpr int group_waves() {
+    return pairable<P0, P1, DK>() ? kPairWavesPerGroup : kWavesPerGroup;
+}
+
 template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
           bool WEND = false>
-__global__ void __launch_bounds__(64 * kWavesPerGroup)
+__global__ void __launch_bounds__((64 * group_waves<P0, P1, DK>()))
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
@@ -1245,25 +1331,38 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         if (task >= meta.cls[0].Hc * n_rb) return;
         run_single(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op, codes0,
                                                          scales0, meta, meta.cls[0], task));
-    } else {
+    } else if constexpr (pairable<P0, P1, DK>()) {
+        // fused int pair: the paired tasks, then the rest of either class,
+        // each group through its work queue
+        __shared__ int counter;
+        if (threadIdx.x == 0) counter = 0;
+        __syncthreads();
+        auto make0 = [&](int task) {
+            return TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op, codes0,
+                                                         scales0, meta, meta.cls[0], task);
+        };
+        auto make1 = [&](int task) {
+            return TaskStream<DK, P1, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op, codes1,
+                                                         scales1, meta, meta.cls[1], task);
+        };
         const int n0 = meta.cls[0].Hc * n_rb, n1 = meta.cls[1].Hc * n_rb;
-        int paired = 0;
-        if constexpr (pairable<P0, P1, DK>()) {
-            paired = n0 < n1 ? n0 : n1;
-            const int pg = (paired + kWavesPerGroup - 1) / kWavesPerGroup;
-            if (gx < pg) {
-                const int task = gx * kWavesPerGroup + wv;
-                if (task >= paired) return;
-                run_paired(TaskStream<DK, P0, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
-                                                                 codes0, scales0, meta,
-                                                                 meta.cls[0], task),
-                           TaskStream<DK, P1, PC, DELTA, BF16IN>(qp, kp, vp, alphap, betap, op,
-                                                                 codes1, scales1, meta,
-                                                                 meta.cls[1], task));
-                return;
-            }
-            gx -= pg;
-        }
+        const int paired = n0 < n1 ? n0 : n1;
+        const int pg = (paired + kPairWavesPerGroup - 1) / kPairWavesPerGroup;
+        if (gx < pg)
+            run_queue_paired(WorkQueue(&counter, gx * kPairWavesPerGroup, paired, meta.B), make0,
+                             make1);
+        else if (gx - pg < meta.cls[0].groups)
+            run_queue(WorkQueue(&counter, paired + (gx - pg) * kPairWavesPerGroup, n0, meta.B),
+                      make0);
+        else
+            run_queue(WorkQueue(&counter,
+                                paired + (gx - pg - meta.cls[0].groups) * kPairWavesPerGroup, n1,
+                                meta.B),
+                      make1);
+    } else {
+        // two classes side by side (bf16 with an int class): groups of class 0, then of class 1
+        const int n0 = meta.cls[0].Hc * n_rb, n1 = meta.cls[1].Hc * n_rb;
+        const int paired = 0;
         if (gx < meta.cls[0].groups) {
             const int task = paired + gx * kWavesPerGroup + wv;
             if (task >= n0) return;
@@ -1301,11 +1400,12 @@ template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = f
           bool WEND = false>
 hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY, WEND>;
+    constexpr int W = group_waves<P0, P1, DK>();
     static int per_cu = 0;                          // resident work-groups per CU
     if (!per_cu) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern),
-                                                         64 * kWavesPerGroup, 0) != hipSuccess ||
+                                                         64 * W, 0) != hipSuccess ||
             n <= 0)
             n = 1;
         per_cu = n;
@@ -1314,15 +1414,13 @@ hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     if constexpr (pairable<P0, P1, DK>()) {
         const int n0 = m.cls[0].Hc * m.n_rb, n1 = m.cls[1].Hc * m.n_rb;
         const int paired = n0 < n1 ? n0 : n1;
-        gx = (paired + kWavesPerGroup - 1) / kWavesPerGroup +
-             (n0 - paired + kWavesPerGroup - 1) / kWavesPerGroup +
-             (n1 - paired + kWavesPerGroup - 1) / kWavesPerGroup;
+        gx = (paired + W - 1) / W + (n0 - paired + W - 1) / W + (n1 - paired + W - 1) / W;
     }
     long resident = (long)per_cu * device_cu_count();
     long gy = resident / gx;
     if (gy < 1) gy = 1;
     if (gy > m.B) gy = m.B;
-    hipLaunchKernelGGL(kern, dim3(gx, (unsigned)gy), dim3(64 * kWavesPerGroup), 0, s, p.q, p.k,
+    hipLaunchKernelGGL(kern, dim3(gx, (unsigned)gy), dim3(64 * W), 0, s, p.q, p.k,
                        p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.codes[1],
                        p.scales[1], p.win[0], m);
     return hipGetLastError();

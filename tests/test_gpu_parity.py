@@ -70,6 +70,31 @@ def test_nearest_rounding_fused_pair_full_size():
     s.check()
 
 
+@pytest.mark.parametrize("B,n8,n4,dv", [
+    (300, 7, 4, 128),     # paired tasks plus an int8 remainder; several sequence strides per group
+    (300, 3, 9, 100),     # an int4 remainder, ragged row blocks
+    (5, 5, 5, 64),        # pairs only, one sequence per group
+])
+def test_fused_pair_work_queue(B, n8, n4, dv):
+    # heads interleaved, so each class's head list is not contiguous
+    prec = ([2, 3] * max(n8, n4))
+    head_prec, c8, c4 = [], 0, 0
+    for p in prec:
+        if (p == 2 and c8 < n8) or (p == 3 and c4 < n4):
+            head_prec.append(p)
+            c8 += p == 2
+            c4 += p == 3
+    w = C1.scaled(B=B, H=n8 + n4, dk=128, dv=dv, T=3)
+    log(f"case: fused int8 + int4 work queue B={B} int8 heads {n8} int4 heads {n4} d_v={dv}")
+    units = None
+    if B * w.H > 200:
+        units = _sample_units(B, w.H, 64, seed=B + n8)
+        units = sorted(set(units + [(0, 0), (B - 1, w.H - 1), (B - 1, 0), (0, w.H - 1)]))
+    s = run_parity(w, T=w.T, units=units, head_prec=head_prec, init="random")
+    log(s.summary())
+    s.check()
+
+
 def test_bf16_inputs_small():
     w = C1.scaled(B=2, H=4, T=8, in_bf16=True)
     log("case: bf16 q/k/v inputs, mixed precisions")
