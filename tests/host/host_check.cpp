@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "../../include/lores.h"
+#include "../../quantized_linear_recurrence_amd/csrc/lores_internal.h"
 #include "launch_log.h"
 
 static int g_fail = 0;
@@ -118,6 +119,45 @@ int main() {
                     }
 
     Args x;
+    // work-groups of each step launch cover its tasks: a fused int pair counts
+    // only the unpaired rest of either class, in groups of kPairWavesPerGroup
+    // wavefronts; other launches count all tasks of a class in groups of
+    // kWavesPerGroup
+    {
+        const std::vector<std::vector<uint8_t>> mixes = {
+            {2, 3}, {2, 2, 2, 3}, {3, 3, 3, 3, 3, 2}, {3, 4, 4}, {1, 2, 2}, {1, 3, 3, 3},
+            {2, 3, 4}, {0, 1, 2, 3, 4, 5}, {2, 2, 2, 2, 2, 2, 2, 2, 2, 3}};
+        for (auto &prec : mixes)
+            for (int dv : {1, 64, 100, 128, 256}) {
+                const int B = 2, H = (int)prec.size();
+                size_t n = size_of(B, H, 128, dv, prec);
+                Buf buf(n);
+                lores_state *st = nullptr;
+                CHECK(lores_state_alloc(B, H, 128, dv, prec.data(), buf.p, &n, nullptr, &st) ==
+                      LORES_OK);
+                g_launches.clear();
+                CHECK(step(st, x, 1) == LORES_OK);
+                int heads = 0;
+                for (auto &l : g_launches.v) {
+                    const bool pair = l.p1 == LORES_INT4 || l.p1 == LORES_INT6;
+                    const bool pair_ints = pair && l.p0 != LORES_BF16;
+                    const int n0 = l.Hc[0] * l.n_rb, n1 = l.p1 >= 0 ? l.Hc[1] * l.n_rb : 0;
+                    CHECK(l.n_rb == (dv + 63) / 64);
+                    heads += l.Hc[0] + (l.p1 >= 0 ? l.Hc[1] : 0);
+                    if (pair_ints) {
+                        const int paired = n0 < n1 ? n0 : n1, w = lores::kPairWavesPerGroup;
+                        CHECK(l.groups[0] == (n0 - paired + w - 1) / w);
+                        CHECK(l.groups[1] == (n1 - paired + w - 1) / w);
+                    } else {
+                        const int w = lores::kWavesPerGroup;
+                        CHECK(l.groups[0] == (n0 + w - 1) / w);
+                        if (l.p1 >= 0) CHECK(l.groups[1] == (n1 + w - 1) / w);
+                    }
+                }
+                CHECK(heads == H);
+                lores_state_free(st);
+            }
+    }
     // launch grouping: a fused pair for value rows, one launch per class for key columns
     {
         std::vector<uint8_t> prec = {2, 3, 2, 3};

@@ -13,7 +13,9 @@ extern "C" const char *hipGetErrorString(hipError_t) { return "stub"; }
 namespace lores {
 
 static hipError_t rec(const char *kind, int p0, int p1, const StepMeta &m) {
-    g_launches.add(kind, p0, p1, m.wpos, m.window, m.n_cls);
+    const int Hc[2] = {m.cls[0].Hc, m.cls[1].Hc};
+    const int groups[2] = {m.cls[0].groups, m.cls[1].groups};
+    g_launches.add(kind, p0, p1, m.wpos, m.window, m.n_cls, m.n_rb, Hc, groups);
     return hipSuccess;
 }
 
