@@ -21,8 +21,9 @@ struct ClassDesc {
 // Description of one launch, passed by value as a kernel argument (about
 // 2.2 KiB), so no device allocation is needed.  Grid: x runs over the
 // work-groups of class 0 then class 1 (kWavesPerGroup (head slot, row block)
-// tasks each); y strides over sequences: a wavefront handles sequences
-// blockIdx.y, blockIdx.y + gridDim.y, ...
+// tasks each; a fused int pair first pairs the two classes' tasks, in groups
+// of kPairWavesPerGroup); y strides over sequences blockIdx.y,
+// blockIdx.y + gridDim.y, ...
 struct StepMeta {
     int32_t B, H, dv, dv_pad, n_rb, n_cls;
     int32_t rounding;                  // LORES_ROUND_*

@@ -1267,12 +1267,14 @@ __device__ __forceinline__ void run_queue_paired(const WorkQueue &wq, Make0 &&ma
 // ---------------------------------------------------------------------------
 // the step kernel: one class (P1 < 0) or a fused pair of classes
 // ---------------------------------------------------------------------------
-// Grid x, single class: groups of kWavesPerGroup tasks of class 0.  Fused
-// pair: first the paired groups (task p of class 0 with task p of class 1,
-// when both classes are prefetchable int classes), then the remaining tasks
-// of class 0, then those of class 1.  meta.cls[i].groups counts the groups
-// of the unpaired remainder of class i; the paired groups number
-// ceil(min(n0, n1) / kWavesPerGroup) when pairing applies, else 0.
+// Grid x, single class: groups of kWavesPerGroup tasks of class 0.  Two
+// classes side by side (bf16 with an int class): the groups of class 0, then
+// those of class 1.  Fused int pair (both classes prefetchable int classes),
+// in groups of kPairWavesPerGroup: first the paired groups (task p of class 0
+// with task p of class 1), then the remaining tasks of class 0, then those of
+// class 1; meta.cls[i].groups then counts the groups of the unpaired
+// remainder of class i and the paired groups number
+// ceil(min(n0, n1) / kPairWavesPerGroup).
 template <int P0, int P1, int DK>
 constexpr bool pairable() {
     if constexpr (P1 < 0 || !is_int<P0>() || !is_int<P1>()) {
