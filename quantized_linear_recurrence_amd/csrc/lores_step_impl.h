@@ -1383,8 +1383,14 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
 
 // ---------------------------------------------------------------------------
 // launcher: the grid holds every (class, head slot, row block) group along x
-// and as many sequence strides along y as fit on the device at once
+// and along y as many sequence strides as fit on the device at once, or, for
+// launches without a work queue, enough that no wavefront gets more than
+// kSeqPerWave sequences
 // ---------------------------------------------------------------------------
+// Sequences per wavefront of the launches without a work queue (the first
+// prefetched behind the second).
+constexpr long kSeqPerWave = 2;
+
 inline int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
@@ -1421,6 +1427,15 @@ hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     long resident = (long)per_cu * device_cu_count();
     long gy = resident / gx;
     if (gy < 1) gy = 1;
+    if constexpr (!pairable<P0, P1, DK>()) {
+        // at most kSeqPerWave sequences per wavefront: the grid's further
+        // rows are started by the dispatcher as earlier work-groups finish,
+        // which balances the CUs better than long fixed streams (a fused
+        // pair balances through its work queue instead)
+        const long gmin = (m.B + kSeqPerWave - 1) / kSeqPerWave;
+        if (gy < gmin) gy = gmin;
+    }
+    if (gy > 65535) gy = 65535;                     // grid y limit
     if (gy > m.B) gy = m.B;
     hipLaunchKernelGGL(kern, dim3(gx, (unsigned)gy), dim3(64 * W), 0, s, p.q, p.k,
                        p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.codes[1],
