@@ -22,8 +22,8 @@
 // chunks of 64 consecutive rows), so each chunk load or store of a wavefront
 // is one contiguous 1 KiB access.  The updated row U lives in d_k VGPRs
 // between the passes (dequant+r, update+readout+max, quantize+store).  A
-// persistent grid walks the sequences, loading the next task while the
-// current one computes.
+// wavefront walks two sequences (a fused int pair: a work queue of them),
+// loading the next task while the current one computes.
 //
 // Arithmetic (must match the CPU oracle bit for bit where it decides codes):
 //   int heads   a = fl(s * alpha); S' = fl(c * a), computed as

@@ -243,7 +243,7 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
 }
 
 // Inside a window: one task per wavefront (a read-only pass, many waves per
-// SIMD).  The window's last step: the step kernel's persistent task stream
+// SIMD).  The window's last step: the step kernel's task stream
 // with the buffer replayed between pass 1 and the token's own update.
 template <int DK, int PREC, bool KEY>
 static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
