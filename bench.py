@@ -91,6 +91,9 @@ def parse(argv=None):
     ap.add_argument("--error-steps", type=int, default=2048,
                     help="horizon of the error-accumulation harness (--mode error)")
     ap.add_argument("--copy-mib", type=int, default=2048)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="repetitions of the K timed steps after the timed region, from a fresh "
+                         "state each, reported as their median, min and max")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="how the timed steps are issued")
     ap.add_argument("--state", default="assigned",
@@ -425,6 +428,16 @@ def main(argv=None):
 
     achieved = step_bytes / n_launches_per_step / (avg_launch_ms * 1e-3) / 1e9
     traffic = load_traffic(w.key) if not key and win == 1 and args.state == "assigned" else None
+
+    # after the timed region: the same K steps repeated from a fresh state,
+    # for the spread of the measurement (the reported value is the timed
+    # region's alone)
+    reps = []
+    for _ in range(args.repeats):
+        reset_state()
+        reps.append(timed(graph.replay if mode == "graph" else
+                          (lambda: [step(t) for t in range(1, K + 1)])) / K)
+    reps.sort()
     result = {
         "metric": METRIC,
         "value": w.B * w.H * K / (ms_total * 1e-3),
@@ -462,6 +475,9 @@ def main(argv=None):
         "kernel_source_hash": kernel_source_hash(),
         "effective_bits": effective_bits(head_prec, w.dk, w.dv, key),
         "copy_reference": copy_reference(torch, step_bytes),
+        "repeats": {"n": len(reps), "ms_per_step_median": reps[len(reps) // 2] if reps else None,
+                    "ms_per_step_min": reps[0] if reps else None,
+                    "ms_per_step_max": reps[-1] if reps else None},
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
