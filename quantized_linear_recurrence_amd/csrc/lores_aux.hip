@@ -121,7 +121,7 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
         U[c + 2] = v.z;
         U[c + 3] = v.w;
     }
-    u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * cd.unit_bytes) + row;
+    const CodeRows io(codes + unit * cd.unit_bytes, cd.unit_bytes, row, dv_pad);
     if constexpr (KEY) {
         __shared__ float cmax[2 * kWavesPerGroup * DK];     // maxima, staging
         float cm[DK / 64], snew[DK / 64], inv[DK / 16];
@@ -132,11 +132,11 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
 #pragma unroll
             for (int t = 0; t < DK / 64; ++t) scales[unit * DK + key_col(t, lane)] = snew[t];
         }
-        requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr, inv);
+        requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr, inv);
     } else {
 #pragma unroll
         for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
-        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, io,
                                  has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
     }
 }

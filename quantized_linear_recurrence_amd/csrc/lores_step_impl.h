@@ -622,8 +622,37 @@ __device__ __forceinline__ float from_raw(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// A unit's code rows through a buffer resource: chunk c of a lane's row is at
+// byte voff + c * cstride of the unit's codes (voff = 16 row, cstride =
+// 16 d_v_pad), so a load or store takes the lane's offset from one VGPR and
+// the chunk's from an SGPR, with no per-access address arithmetic in the
+// vector ALU.  The resource's size is the unit's code bytes: an access
+// outside it reads zeros and writes nothing.
+// ---------------------------------------------------------------------------
+struct CodeRows {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int voff, cstride;
+
+    // raw (untyped) 32-bit data format, the buffer-resource word 3 of gfx9 parts
+    static constexpr int kRawFormat = 0x00020000;
+    static constexpr int kNT = 2;                  // nontemporal
+
+    __device__ __forceinline__ CodeRows(const uint8_t *unit_codes, long unit_bytes, int row,
+                                        long dv_pad)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(unit_codes), 0,
+                                                 (int)unit_bytes, kRawFormat)),
+          voff(row * 16), cstride((int)dv_pad * 16) {}
+    __device__ __forceinline__ u32x4 load(int c) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, c * cstride, kNT);
+    }
+    __device__ __forceinline__ void store(int c, u32x4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff, c * cstride, kNT);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // requantization of one row (one lane): fresh scale, rounding, packing and
-// store of the row's 16-byte chunks (chunk c at cp + c * dv_pad).  Shared by
+// store of the row's 16-byte chunks (chunk c through `io`).  Shared by
 // the step and by the fp32 -> packed state entry.
 // ---------------------------------------------------------------------------
 // KEY: key-column scales; invrow holds r / m_j as row vectors (register i,
@@ -631,8 +660,8 @@ __device__ __forceinline__ float from_raw(float x) {
 // the column scales).
 template <int DK, int PREC, bool KEY = false>
 __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, const StepMeta &meta,
-                                               int b, int h, int row, bool active, u32x4 *cp,
-                                               long dv_pad, float *scale_out,
+                                               int b, int h, int row, bool active,
+                                               const CodeRows &io, float *scale_out,
                                                const float *invrow = nullptr) {
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = row_chunks<DK, PREC>();
@@ -705,7 +734,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                 }
             }
             if (active)
-                __builtin_nontemporal_store(u32x4{acc[0], acc[1], acc[2], acc[3]}, cp + c * dv_pad);
+                io.store(c, u32x4{acc[0], acc[1], acc[2], acc[3]});
             asm volatile("" : "+v"(x));
         }
     } else {
@@ -809,7 +838,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) ow[q4] = __float_as_uint(U[c * E + q4]);
             }
-            if (active) __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, cp + c * dv_pad);
+            if (active) io.store(c, u32x4{ow[0], ow[1], ow[2], ow[3]});
             // key-column rows: keep the next chunk's draws after this store
             // (unpinned, the cheap, input-independent chain may be computed
             // up front and held in registers)
@@ -903,9 +932,9 @@ struct TaskStream {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;
-        const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * unit_bytes) + lrow;
+        const CodeRows io(codes + unit * unit_bytes, unit_bytes, lrow, dv_pad);
 #pragma unroll
-        for (int c = C0; c < C1; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
+        for (int c = C0; c < C1; ++c) cw[c] = io.load(c);
         if constexpr (C0 != 0) return;
         if constexpr (KEY) {
 #pragma unroll
@@ -948,7 +977,7 @@ struct TaskStream {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;           // index into [B][H] inputs
-        u32x4 *cp = reinterpret_cast<u32x4 *>(codes + unit * unit_bytes) + row;
+        const CodeRows io(codes + unit * unit_bytes, unit_bytes, row, dv_pad);
 
         const float beta = in.beta;
         const float alpha_s = in.alpha;
@@ -1112,10 +1141,10 @@ struct TaskStream {
                 for (int t = 0; t < DK / 64; ++t)
                     scales[unit * DK + key_col(t, threadIdx.x & 63)] = snew[t];
             }
-            requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, cp, dv_pad, nullptr,
+            requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr,
                                            inv);
         } else {
-            requantize_row<DK, PREC>(U, m, meta, b, h, row, active, cp, dv_pad,
+            requantize_row<DK, PREC>(U, m, meta, b, h, row, active, io,
                                      has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
         }
     }
