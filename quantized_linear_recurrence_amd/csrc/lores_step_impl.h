@@ -1150,7 +1150,8 @@ struct TaskStream {
     }
 };
 
-// One stream over all its sequences.  Right after pass 1 of a task (when
+// One stream over its sequences (at most kSeqPerWave of them unless the
+// batch exceeds the grid's y limit).  Right after pass 1 of a task (when
 // the chunk registers are free) the next sequence's per-task values and
 // first chunks are loaded: all of an int row, the first kMaxPrefetchChunks
 // of a bf16 row (the rest are loaded as that task starts), none of an fp32
@@ -1416,8 +1417,8 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
 // launches without a work queue, enough that no wavefront gets more than
 // kSeqPerWave sequences
 // ---------------------------------------------------------------------------
-// Sequences per wavefront of the launches without a work queue (the first
-// prefetched behind the second).
+// Sequences per wavefront of the launches without a work queue (the second
+// prefetched behind the first).
 constexpr long kSeqPerWave = 2;
 
 inline int device_cu_count() {
