@@ -624,10 +624,10 @@ __device__ __forceinline__ float from_raw(float x) {
 // ---------------------------------------------------------------------------
 // A unit's code rows through a buffer resource: chunk c of a lane's row is at
 // byte voff + c * cstride of the unit's codes (voff = 16 row, cstride =
-// 16 d_v_pad), so a load or store takes the lane's offset from one VGPR and
-// the chunk's from an SGPR, with no per-access address arithmetic in the
-// vector ALU.  The resource's size is the unit's code bytes: an access
-// outside it reads zeros and writes nothing.
+// 16 d_v_pad), so a load takes the lane's offset from one VGPR and the
+// chunk's from an SGPR, with no per-access address arithmetic in the vector
+// ALU (a store adds the two in a VGPR, below).  The resource's size is the
+// unit's code bytes: an access outside it reads zeros and writes nothing.
 // ---------------------------------------------------------------------------
 struct CodeRows {
     __amdgpu_buffer_rsrc_t rsrc;
@@ -645,8 +645,14 @@ struct CodeRows {
     __device__ __forceinline__ u32x4 load(int c) const {
         return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, c * cstride, kNT);
     }
+    // A store of more than 64 bits needs one wait state before a VALU
+    // instruction rewrites its data registers; the compiler inserts it for a
+    // buffer store only when the store's SGPR offset field holds no register.
+    // With the chunk's offset there, the next chunk's first packed word has
+    // been seen to overwrite dword 0 of a store in flight (in lanes 12..15
+    // of each row), so a store takes its whole offset from the VGPR.
     __device__ __forceinline__ void store(int c, u32x4 v) const {
-        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff, c * cstride, kNT);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, voff + c * cstride, 0, kNT);
     }
 };
 

@@ -94,6 +94,7 @@ class Stats:
         self.fp8_excess = 0.0           # worst excess over one E4M3 step / row max
         self.bf16_far = 0               # differing by more than one ulp
         self.bf16_far_rel = 0.0         # their worst excess over one ulp / row max
+        self.far_at = []                # (step, b, h, row, col) of the first far elements
         self.o_err_q = 0.0
         self.o_err_f = 0.0
         self.x_err_f = 0.0
@@ -105,7 +106,8 @@ class Stats:
                 f"max|dbits|={self.max_dbits} far={self.bf16_far} "
                 f"far_rel={self.bf16_far_rel:.2e} fp8_flip={self.fp8_diff}/{self.fp8} "
                 f"fp8_excess={self.fp8_excess:.2e} o_err_q={self.o_err_q:.2e} "
-                f"o_err_f32={self.o_err_f:.2e} x_err_f32={self.x_err_f:.2e}")
+                f"o_err_f32={self.o_err_f:.2e} x_err_f32={self.x_err_f:.2e}"
+                + (f" far_at(t,b,h,row,col)={self.far_at}" if self.far_at else ""))
 
     def check(self):
         assert self.max_dc <= 1, self.summary()
@@ -247,6 +249,8 @@ def run_parity(w, T, B=None, units=None, seed=0, head_prec=None, init="zero", in
                     rowmax = np.abs(xr).max(axis=2, keepdims=True)
                     excess = (np.abs(xg - xr) - ulp) / np.maximum(rowmax, 1e-300)
                     stats.bf16_far += int(far.sum())
+                    for (i, r, col) in np.argwhere(far)[:8 - len(stats.far_at)]:
+                        stats.far_at.append((t, us[i][0], us[i][1], int(r), int(col)))
                     stats.bf16_far_rel = max(stats.bf16_far_rel, float(excess[far].max()))
                 stats.o_err_q = max(stats.o_err_q, float(o_err))
             else:
