@@ -218,6 +218,39 @@ __device__ __forceinline__ float cvt_sbyte(uint32_t w, int k) {
     return r;
 }
 
+// fl(x * A + B) where x is the f16 number held in the low (hi = 0) or high
+// (hi = 1) half of h, in one rounding (v_fma_mix_f32: the f16 operand is
+// widened exactly).  A half whose pattern P is below 2048 is the number
+// P 2^-24 exactly (an f16 subnormal below 1024; exponent field 1 above), so
+// with P an offset-binary code, A = a 2^24 and B = -off a the result is
+// fl((P - off) a): code and dequantization in one instruction.
+__device__ __forceinline__ float mix_f16(uint32_t h, int hi, float A, float B) {
+    float r;
+    if (hi)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(h), "v"(A), "v"(B));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(h), "v"(A), "v"(B));
+    return r;
+}
+
+// Bytes 1 and 3 of w into the low bytes of its two halves, the high bytes 0.
+__device__ __forceinline__ uint32_t odd_bytes(uint32_t w) {
+    return __builtin_amdgcn_perm(w, w, 0x0c030c01u);
+}
+
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+// Uses of v and of the k and q row vectors: every load of them has completed
+// here (forces the compiler's wait for them at this point).
+template <int NV>
+__device__ __forceinline__ void pin_inputs(float v, const float (&kv)[NV], const float (&qv)[NV]) {
+    asm volatile("" ::"v"(v));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) asm volatile("" ::"v"(kv[i]), "v"(qv[i]));
+}
+
 // Byte 2 of the fp32 patterns of z[0..3] into bytes 0..3 (three v_perm_b32).
 __device__ __forceinline__ uint32_t gather_byte2(const float *z) {
     // selector bytes: 0-3 pick the second operand's bytes, 4-7 the first's,
@@ -1022,6 +1055,15 @@ struct TaskStream {
             // chunk registers are free when `mid` reuses them
             else pin16(&U[j - 15]);
         };
+        // Value-row int8 and int4 codes under a scalar decay take the code
+        // and the dequantization in one v_fma_mix_f32 (MIX): the code's bits as an
+        // f16 half times a 2^24, plus -off a.  a 2^24 must be finite, so a
+        // wavefront with a row scale near the top of the fp32 range takes the
+        // conversion and fma instead (the same values).
+        constexpr bool kMixable = (PREC == LORES_INT8 || PREC == LORES_INT4) && !KEY && !PC;
+        const float A0 = a * 0x1p24f, A1 = a * 0x1p20f;
+        auto pass1 = [&](auto mix_flag) {
+        constexpr bool MIX = decltype(mix_flag)::value;
         if constexpr (PREC == LORES_INT6) {
 #pragma unroll
             for (int j = 0; j < DK; ++j) {
@@ -1038,6 +1080,28 @@ struct TaskStream {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const uint32_t wd[4] = {cw[c].x, cw[c].y, cw[c].z, cw[c].w};
+            // MIX: the codes of each dword spread over f16 halves, each half
+            // holding one code in its low bits.  int8: bytes 0, 2 and bytes
+            // 1, 3.  int4 (nibble k = element 8 d + k): nibbles 0, 4 and
+            // 1, 5 (the latter times 16, so read with a 2^20), then the same
+            // of bytes 1 and 3.
+            uint32_t hv[4][4] = {};
+            if constexpr (MIX && PREC == LORES_INT8) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    hv[d][0] = wd[d] & 0x00FF00FFu;
+                    hv[d][1] = odd_bytes(wd[d]);
+                }
+            } else if constexpr (MIX && PREC == LORES_INT4) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t t = odd_bytes(wd[d]);
+                    hv[d][0] = wd[d] & 0x000F000Fu;
+                    hv[d][1] = wd[d] & 0x00F000F0u;
+                    hv[d][2] = t & 0x000F000Fu;
+                    hv[d][3] = t & 0x00F000F0u;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int j = c * E + e;
@@ -1051,6 +1115,10 @@ struct TaskStream {
                     if constexpr (KEY) sp = v;                       // times sig_j per group
                     else if constexpr (PC) sp = v * aj[j & 15];
                     else sp = v * a;
+                } else if constexpr (MIX && PREC == LORES_INT8) {
+                    sp = mix_f16(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na);
+                } else if constexpr (MIX && PREC == LORES_INT4) {
+                    sp = mix_f16(hv[e >> 3][e & 3], (e >> 2) & 1, (e & 1) ? A1 : A0, na);
                 } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
                     if constexpr (PREC == LORES_INT8 && (KEY || PC)) {
@@ -1082,6 +1150,18 @@ struct TaskStream {
                 if ((j & 15) == 15) group_done(j);
             }
         }
+        }
+        };
+        if constexpr (kMixable) {
+            if (__builtin_amdgcn_ballot_w64(!(a < 0x1p100f)) == 0) pass1(Flag<true>{});
+            else pass1(Flag<false>{});
+            // Both branches have waited for this task's loads, but the
+            // structurized branch leaves a path around them in the compiler's
+            // graph: without these uses the next task's loads would be
+            // followed by waits for themselves in pass 2.
+            pin_inputs<NV>(vi, kv, qv);
+        } else {
+            pass1(Flag<false>{});
         }
 
         mid();                                           // the chunks are consumed
