@@ -5,13 +5,15 @@ A step is one decode step of the whole batch: every (sequence, head) state is
 dequantized, updated, read out and requantized in place.  Inputs for all
 timed steps are generated on the device before timing.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C5]
 
 Workloads (synthetic, shapes of the decode layers the method targets):
-  C2 (default) Gated-DeltaNet decode, B=64 H=32 d_k=d_v=128, bf16 q/k/v, int8 state
+  C5 (default) large batch, B=2048 H=32 d=128, 16 int8 + 16 int4 heads (the
+     largest workload: its 839 MB state exceeds the 256 MB last-level cache,
+     so its bytes are HBM bytes)
+  C2 Gated-DeltaNet decode, B=64 H=32 d_k=d_v=128, bf16 q/k/v, int8 state
   C3 Mamba-2 / SSD decode, B=256 H=128 d_v=64 d_k=128, no delta correction, int8
   C4 KDA per-channel decay, B=128 H=32 d=128, 8 bf16 + 24 int8 heads
-  C5 large batch, B=2048 H=32 d=128, 16 int8 + 16 int4 heads
   C5i6 the same shape with the slowest half of the heads in int6 (5.25 bits)
   C1 is the tiny parity case (launch-bound; not a throughput workload).
 --mode copy times a plain device copy (the HBM calibration used for the
@@ -82,10 +84,12 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", default="C2", choices=["C1", "C2", "C3", "C4", "C5", "C5i6"])
+    ap.add_argument("--workload", default="C5", choices=["C1", "C2", "C3", "C4", "C5", "C5i6"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
+                    help="target time of the oracle baseline sample (per worker process)")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="worker processes of the oracle baseline (at most the host's cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "error", "sweep"])
     ap.add_argument("--error-steps", type=int, default=2048,
@@ -237,57 +241,89 @@ def sweep_mode(args, torch):
     print(json.dumps({"mode": "sweep", "rows": rows}), flush=True)
 
 
-def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value", window=1):
-    """Time the oracle (as it stands) on a bounded sample of the same workload:
-    the first units of the batch, step after step, until target_s has passed.
-    Windowed states (window > 1) run the oracle's windowed step."""
+def _oracle_worker(job):
+    """One CPU worker of the baseline (a child process): the oracle, as it
+    stands, stepping its own (sequence, head) units from the common start time
+    until target_s has passed.  Returns (updates, start, end) wall times."""
     import numpy as np
     from oracle import step as ostep
     from oracle import window as owin
-
-    n_units = min(w.B * w.H, 64)
-    units = [(u // w.H, u % w.H) for u in range(n_units)]
-    by_class = {}
-    for b, h in units:
-        by_class.setdefault(head_prec[h], []).append((b, h))
-    states = {c: ostep.zero_state(c, len(us), w.dv, w.dk, axis=axis) for c, us in by_class.items()}
-    bufs = {c: owin.empty_buffer(len(us), window, w.dv, w.dk) for c, us in by_class.items()}
-    T_in = inputs["k"].shape[0]
-    host = {}
-    for t in range(min(T_in, 64)):
-        host[t] = {k: v[t].float().cpu().numpy() for k, v in inputs.items()}
-    try:                                   # one thread: BLAS pools stay at 1
+    try:                                   # one thread per worker: BLAS pools stay at 1
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
+        threadpool_limits(1)
     except ImportError:
-        limiter = None
-    t0 = time.perf_counter()
+        pass
+    units, host, head_prec, dims, target_s, seed, axis, window, t_start = job
+    dk, dv, delta = dims
+    by_class = {}
+    for i, (b, h) in enumerate(units):
+        by_class.setdefault(head_prec[h], []).append((i, b, h))
+    states = {c: ostep.zero_state(c, len(us), dv, dk, axis=axis) for c, us in by_class.items()}
+    bufs = {c: owin.empty_buffer(len(us), window, dv, dk) for c, us in by_class.items()}
+    while time.time() < t_start:
+        time.sleep(0.001)
+    t0 = time.time()
     steps = 0
     while True:
         xin = host[steps % len(host)]
         for c, us in by_class.items():
-            bs = np.array([b for b, _ in us])
-            hs = np.array([h for _, h in us])
-            a = (xin["q"][bs, hs], xin["k"][bs, hs], xin["v"][bs, hs], xin["alpha"][bs, hs],
-                 xin["beta"][bs, hs])
+            rows = np.array([i for i, _, _ in us])
+            bs = np.array([b for _, b, _ in us])
+            hs = np.array([h for _, _, h in us])
+            a = tuple(xin[k][rows] for k in ("q", "k", "v", "alpha", "beta"))
             if window > 1 and c in ostep.SCALED:
-                states[c], bufs[c], _ = owin.window_step(c, states[c], bufs[c], *a, w.delta, seed,
+                states[c], bufs[c], _ = owin.window_step(c, states[c], bufs[c], *a, delta, seed,
                                                          steps + 1, bs, hs, window)
             else:
-                states[c], _ = ostep.decode_step(c, states[c], *a, w.delta, seed, steps + 1, bs,
+                states[c], _ = ostep.decode_step(c, states[c], *a, delta, seed, steps + 1, bs,
                                                  hs, axis=axis)
         steps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s:
+        if time.time() - t0 >= target_s:
             break
-    if limiter is not None:
-        limiter.unregister()
-    return {"value": n_units * steps / el, "unit": "state-updates/s", "cores": 1,
-            "kind": "oracle", "host_cores_available": len(os.sched_getaffinity(0)),
-            "blas_threads": 1,
-            "sample": f"{n_units} (sequence, head) units x {steps} decode steps of {w.key} "
-                      f"({el:.1f} s; NumPy oracle, single-threaded elementwise ops and "
-                      f"einsum, fp32-exact rounding emulation)"}
+    return len(units) * steps, t0, time.time(), steps
+
+
+def cpu_baseline(w, inputs, head_prec, target_s, seed, axis="value", window=1, workers=None):
+    """Time the oracle (as it stands) on a bounded sample of the same workload,
+    on the host's cores: independent worker processes, each stepping its own
+    64 (sequence, head) units of the batch (the first units in order), all
+    from one common start time for about target_s seconds.  The rate is the
+    total state updates over the span from that start to the last worker's
+    end.  Windowed states (window > 1) run the oracle's windowed step."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    avail = len(os.sched_getaffinity(0))
+    n_workers = max(1, min(workers or 16, avail))
+    per = 64
+    n_units = min(w.B * w.H, per * n_workers)
+    n_workers = -(-n_units // per)
+    units = [(u // w.H, u % w.H) for u in range(n_units)]
+    T_in = min(inputs["k"].shape[0], 64)
+    b_hi = max(b for b, _ in units) + 1
+    # the sampled sequences' inputs on the host, [T][unit] per tensor
+    host_all = {k: v[:T_in, :b_hi].float().cpu().numpy() for k, v in inputs.items()}
+    jobs = []
+    t_start = time.time() + 10.0            # the workers' interpreters start meanwhile
+    for j in range(n_workers):
+        us = units[j * per:(j + 1) * per]
+        bs = [b for b, _ in us]
+        hs = [h for _, h in us]
+        host = [{k: v[t][bs, hs] for k, v in host_all.items()} for t in range(T_in)]
+        jobs.append((us, host, list(head_prec), (w.dk, w.dv, w.delta), target_s, seed, axis,
+                     window, t_start))
+    # fresh interpreters (spawn): the workers never touch the GPU runtime of
+    # this process; a worker that fails raises here instead of being restarted
+    with ProcessPoolExecutor(n_workers, mp_context=mp.get_context("spawn")) as pool:
+        res = list(pool.map(_oracle_worker, jobs))
+    updates = sum(r[0] for r in res)
+    span = max(r[2] for r in res) - min(r[1] for r in res)
+    steps = min(r[3] for r in res)
+    return {"value": updates / span, "unit": "state-updates/s", "cores": n_workers,
+            "kind": "oracle", "host_cores_available": avail, "blas_threads": 1,
+            "sample": f"{n_units} (sequence, head) units of {w.key} ({w.name}), in {n_workers} "
+                      f"worker processes of {per} units, >= {steps} decode steps each over "
+                      f"{span:.1f} s (NumPy oracle, one thread per process, fp32-exact rounding "
+                      f"emulation)"}
 
 
 def load_traffic(workload):
@@ -301,6 +337,35 @@ def load_traffic(workload):
     if d.get("source_hash") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+# VALU peak in lane-instructions per second: 256 CUs, each issuing one
+# 64-lane VALU instruction per cycle (four SIMD16 units, four cycles per
+# wave64 instruction), at 2.4 GHz
+VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
+
+
+def load_valu(workload):
+    """VALU wave-instructions per launch (SQ_INSTS_VALU) from the committed
+    rocprofv3 --pmc summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"valu_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("valu_insts_per_launch")
+
+
+def limiter(frac_hbm, frac_valu):
+    """Which roof the launch sits closer to: "hbm", "valu", or both when the two
+    fractions are within 0.05 of each other."""
+    if frac_valu is None:
+        return "hbm (VALU not profiled on these kernel sources)"
+    if abs(frac_hbm - frac_valu) < 0.05:
+        return "hbm and valu"
+    return "hbm" if frac_hbm > frac_valu else "valu"
 
 
 def main(argv=None):
@@ -427,7 +492,15 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     achieved = step_bytes / n_launches_per_step / (avg_launch_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.key) if not key and win == 1 and args.state == "assigned" else None
+    profiled = not key and win == 1 and args.state == "assigned"
+    traffic = load_traffic(w.key) if profiled else None
+    valu_insts = load_valu(w.key) if profiled else None
+    valu = None
+    if valu_insts is not None:
+        lane_ops = valu_insts * 64 / (avg_launch_ms * 1e-3)
+        valu = {"achieved": lane_ops, "peak": VALU_PEAK_LANE_OPS,
+                "unit": "VALU lane-instructions/s", "frac": lane_ops / VALU_PEAK_LANE_OPS,
+                "insts_per_launch": valu_insts}
 
     # after the timed region: the same K steps repeated from a fresh state,
     # for the spread of the measurement (the reported value is the timed
@@ -471,6 +544,8 @@ def main(argv=None):
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
             "kernel": "lores_step_kernel (fused dequant-update-readout-requant)",
             "launches_per_step": n_launches_per_step,
+            "valu": valu,
+            "limiter": limiter(achieved / HBM_PEAK_GBPS, valu["frac"] if valu else None),
         },
         "kernel_source_hash": kernel_source_hash(),
         "effective_bits": effective_bits(head_prec, w.dk, w.dv, key),
@@ -483,7 +558,7 @@ def main(argv=None):
         print(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
               flush=True)
         result["cpu_baseline"] = cpu_baseline(w, inputs, head_prec, args.cpu_seconds, args.seed,
-                                              args.scale_axis, win)
+                                              args.scale_axis, win, args.cpu_workers)
     print(json.dumps(result), flush=True)
 
 

@@ -279,6 +279,20 @@ __device__ __forceinline__ void cvt_u8_into(uint32_t &word, float z) {
     }
 }
 
+// m / R correctly rounded, for an int class's R (7, 31 or 127) and every
+// finite m >= 0: Markstein's correction step with the rounded reciprocal,
+// one product and two fused multiply-adds in place of an IEEE division
+// (checked against the IEEE quotient for every finite non-negative fp32 m on
+// the host).  A non-finite m gives NaN rather than inf.
+template <int PREC>
+__device__ __forceinline__ float div_by_r(float m) {
+    static_assert(is_int<PREC>(), "checked for the int classes' R only");
+    constexpr float R = Prec<PREC>::R;
+    constexpr float z = 1.0f / R;
+    const float y = m * z;
+    return __builtin_fmaf(__builtin_fmaf(-y, R, m), z, y);
+}
+
 // Largest fp32 not above r / m (0 for m = 0).
 __device__ __forceinline__ float rd_div(float r, float m) {
     float q = r / m;                               // IEEE, correctly rounded
@@ -707,7 +721,9 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
     static_assert(!KEY || has_scale<PREC>(), "key-column scales belong to scaled classes");
     float inv = 0.0f;
     if constexpr (has_scale<PREC>() && !KEY) {
-        const float snew = m / Prec<PREC>::R;
+        float snew;
+        if constexpr (is_int<PREC>()) snew = div_by_r<PREC>(m);
+        else snew = m / Prec<PREC>::R;
         inv = rd_div(Prec<PREC>::R, m);
         if (active) *scale_out = snew;
     }
