@@ -203,6 +203,13 @@ hipError_t launch_step(int dk, bool pc, bool delta, bool bf16, int p0, int p1, c
 
 }  // namespace lores
 
+// Every launcher enqueues its kernels and returns the thread's last HIP
+// error.  That error is sticky: one left by earlier work on this thread (the
+// caller's, or a failed query) would be reported as the launch's own.  So it
+// is consumed right before each launcher call, and a returned error is then
+// the launch's.
+static void consume_stale_hip_error() { (void)hipGetLastError(); }
+
 extern "C" {
 
 const char *lores_last_error(void) { return g_err.c_str(); }
@@ -253,6 +260,7 @@ static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         lores_state *st = new (std::nothrow) lores_state(tmp);
         if (!st) return fail(LORES_ENOMEM, "host allocation of the state handle failed");
         st->base = (uint8_t *)d_buf;
+        consume_stale_hip_error();
         hipError_t e = lores::launch_fill_zero(d_buf, tmp.total, (hipStream_t)stream);
         if (e != hipSuccess) {
             delete st;
@@ -488,6 +496,7 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             const int p1 = width[l] == 2 ? groups[l][1] : -1;
             const bool key = st->axis == LORES_SCALE_KEY && has_scales(groups[l][0]);
             hipError_t e;
+            consume_stale_hip_error();
             if (windowed && has_scales(groups[l][0])) {
                 p.win[0] = (float *)(st->base + st->win_off[groups[l][0]]);
                 e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, key, p, m, s);
@@ -522,6 +531,7 @@ int lores_quant_state(lores_state *st, const float *X, uint64_t seed, int64_t se
             m.seq_base = seq_base;
             m.head_base = head_base;
             float *sc = has_scales(c) ? (float *)(st->base + st->scales_off[c]) : nullptr;
+            consume_stale_hip_error();
             hipError_t e = lores::launch_quant(c, st->dk, X, st->base + st->codes_off[c], sc, m,
                                                (hipStream_t)stream,
                                                st->axis == LORES_SCALE_KEY && has_scales(c));
@@ -544,6 +554,7 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
             lores::StepMeta m = make_meta(st, &c, 1);
             const float *sc = has_scales(c) ? (const float *)(st->base + st->scales_off[c]) : nullptr;
             hipError_t e;
+            consume_stale_hip_error();
             if (st->window > 1 && st->n_buf > 0 && has_scales(c)) {
                 m.wpos = st->n_buf;
                 m.window = st->window;

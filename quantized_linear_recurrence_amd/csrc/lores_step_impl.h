@@ -1523,14 +1523,21 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
 // prefetched behind the first).
 constexpr long kSeqPerWave = 2;
 
+// A failed query here falls back to a default and must not leave its error
+// behind for the launch's own check: it is consumed.
 inline int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
     if (!cached[dev]) {
         int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
             n = 256;
+        }
         cached[dev] = n;
     }
     return cached[dev];
@@ -1546,8 +1553,10 @@ hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern),
                                                          64 * W, 0) != hipSuccess ||
-            n <= 0)
+            n <= 0) {
+            (void)hipGetLastError();                // not the launch's error
             n = 1;
+        }
         per_cu = n;
     }
     int gx = m.cls[0].groups + (P1 < 0 ? 0 : m.cls[1].groups);

@@ -45,14 +45,18 @@ def sample_points(T, n=24):
 
 def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_lo=0.9,
                      alpha_hi=0.999, beta=0.5, drift=0.05, rounding=LORES_ROUND_STOCHASTIC,
-                     seed=0, points=None, device="cuda", scale_axis=LORES_SCALE_VALUE, window=1):
+                     seed=0, points=None, device="cuda", scale_axis=LORES_SCALE_VALUE, window=1,
+                     record=None):
     """Run T steps of a state with per-head precisions `head_prec` (a list,
     or a function of the per-head decays giving one; scales per value row or,
     with scale_axis = LORES_SCALE_KEY, per key column; requantized every step
     or, with window = W > 1, once per window of W steps) and of its fp32 twin;
     return {"t": [...], "rel_err": [H lists], "o_rel_err": [H lists],
     "alpha": [H], "head_prec": [H]} with errors averaged over the B
-    sequences at each sampled t.
+    sequences at each sampled t.  A dict passed as `record` receives the
+    inputs of every step on the host ("q", "k", "v": lists of [B, H, d]
+    arrays; "alpha", "beta": [B, H]), for recomputing the statistics
+    elsewhere.
     """
     import torch
 
@@ -74,6 +78,9 @@ def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_l
 
     if callable(head_prec):
         head_prec = head_prec(alpha_h.cpu().numpy())
+    if record is not None:
+        record["alpha"] = alpha.cpu().numpy()
+        record["beta"] = beta_t.cpu().numpy()
     sq = lores_state_alloc(B, H, d_k, d_v, list(head_prec), device=dev, scale_axis=scale_axis,
                            window=window)
     lores_state_set_rounding(sq, rounding)
@@ -89,6 +96,9 @@ def error_trajectory(head_prec, B=32, d_k=128, d_v=128, T=1024, delta=0, alpha_l
         v = v0 + drift * torch.randn(B, H, d_v, generator=g, device=dev, dtype=f32)
         lores_decode_step(sq, q, k, v, alpha, beta_t, delta, seed, t, o=oq)
         lores_decode_step(sf, q, k, v, alpha, beta_t, delta, seed, t, o=of)
+        if record is not None:
+            for name, x in (("q", q), ("k", k), ("v", v)):
+                record.setdefault(name, []).append(x.cpu().numpy())
         if t in pts:
             Xq = lores_dequant_state(sq).double()
             Xf = lores_dequant_state(sf).double()

@@ -245,6 +245,45 @@ int main() {
         CHECK(step(st, x, 13) == LORES_OK);
         lores_state_free(st);
     }
+    // launch errors: an error left on the thread by earlier work is not the
+    // call's own; a launch that fails is reported, and a windowed state then
+    // keeps its position, so the same step can be issued again
+    {
+        std::vector<uint8_t> prec = {2, 3};
+        const int W = 4;
+        size_t n = size_of(2, 2, 64, 64, prec, 0, W);
+        Buf buf(n);
+        lores_state *st = nullptr;
+        lores_layout lay;
+        g_sticky_error = hipErrorInvalidValue;
+        CHECK(lores_state_alloc_window(2, 2, 64, 64, prec.data(), 0, W, buf.p, &n, nullptr, &st) ==
+              LORES_OK);
+        g_sticky_error = hipErrorInvalidValue;
+        CHECK(step(st, x, 1) == LORES_OK);
+        CHECK(lores_state_layout(st, &lay) == LORES_OK && lay.window_fill == 1);
+        g_fail_next_launch = true;
+        CHECK(step(st, x, 2) == LORES_EHIP);
+        CHECK(std::strstr(lores_last_error(), "launch failed") != nullptr);
+        CHECK(lores_state_layout(st, &lay) == LORES_OK && lay.window_fill == 1);
+        CHECK(step(st, x, 2) == LORES_OK);
+        CHECK(lores_state_layout(st, &lay) == LORES_OK && lay.window_fill == 2);
+        Buf out(1 << 20);
+        g_sticky_error = hipErrorInvalidValue;
+        CHECK(lores_dequant_state(st, (float *)out.p, nullptr) == LORES_OK);
+        g_sticky_error = hipErrorInvalidValue;
+        CHECK(lores_quant_state(st, (const float *)out.p, 0, 0, 0, nullptr) == LORES_OK);
+        g_fail_next_launch = true;
+        CHECK(lores_dequant_state(st, (float *)out.p, nullptr) == LORES_EHIP);
+        g_fail_next_launch = true;
+        CHECK(lores_quant_state(st, (const float *)out.p, 0, 0, 0, nullptr) == LORES_EHIP);
+        CHECK(g_sticky_error == hipSuccess && !g_fail_next_launch);
+        lores_state_free(st);
+        std::vector<uint8_t> one = {2};
+        n = size_of(1, 1, 64, 64, one);
+        Buf b1(n);
+        g_fail_next_launch = true;
+        CHECK(lores_state_alloc(1, 1, 64, 64, one.data(), b1.p, &n, nullptr, &st) == LORES_EHIP);
+    }
     // decay statistic and precision assignment
     {
         const int H = 6;

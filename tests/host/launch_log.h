@@ -3,6 +3,8 @@
 #include <string>
 #include <vector>
 
+#include <hip/hip_runtime_api.h>
+
 struct Launch {
     std::string kind;
     int p0, p1, wpos, window, n_cls;
@@ -24,3 +26,8 @@ struct LaunchLog {
 };
 
 extern LaunchLog g_launches;
+
+// The stand-in sticky HIP error (launch_stubs.cpp): an error left by earlier
+// work on the thread, and a switch that makes the next stand-in launch fail.
+extern hipError_t g_sticky_error;
+extern bool g_fail_next_launch;

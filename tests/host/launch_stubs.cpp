@@ -10,13 +10,29 @@ LaunchLog g_launches;
 
 extern "C" const char *hipGetErrorString(hipError_t) { return "stub"; }
 
+// The thread's sticky last error, as HIP keeps it: hipGetLastError returns
+// and clears it.  Tests plant one (an earlier caller's failure) or make the
+// next stand-in launch fail.
+hipError_t g_sticky_error = hipSuccess;
+bool g_fail_next_launch = false;
+extern "C" hipError_t hipGetLastError(void) {
+    const hipError_t e = g_sticky_error;
+    g_sticky_error = hipSuccess;
+    return e;
+}
+
 namespace lores {
 
+// Like the real launchers: enqueue, then return the thread's last error.
 static hipError_t rec(const char *kind, int p0, int p1, const StepMeta &m) {
     const int Hc[2] = {m.cls[0].Hc, m.cls[1].Hc};
     const int groups[2] = {m.cls[0].groups, m.cls[1].groups};
     g_launches.add(kind, p0, p1, m.wpos, m.window, m.n_cls, m.n_rb, Hc, groups);
-    return hipSuccess;
+    if (g_fail_next_launch) {
+        g_fail_next_launch = false;
+        g_sticky_error = hipErrorLaunchFailure;
+    }
+    return hipGetLastError();
 }
 
 #define LORES_STUB(name, p0, p1)                                                               \

@@ -131,3 +131,98 @@ def test_windowed_requantization_accumulates_less_error():
     for rnd in (SR, NEAR):
         assert errs[(rnd, 4)] < 0.75 * errs[(rnd, 1)], errs
         assert errs[(rnd, 16)] < errs[(rnd, 4)], errs
+
+
+def _oracle_series(rec, head_prec, T, dk, dv, delta, seed, rounding, axis, window):
+    """The harness's two statistics recomputed by the oracle from the inputs
+    the harness recorded: per head and step, the mean over sequences of
+    ||S_q - S_f||_F / ||S_f||_F and of |o_q - o_f| / |o_f|, with S_q the
+    quantized state (its current value: inside a window the stored state
+    plus the buffered tokens) and S_f the fp32 state."""
+    from oracle import step as ostep
+    from oracle import window as owin
+    B, H = rec["alpha"].shape
+    rnd = "sr" if rounding == SR else "nearest"
+    rel = np.zeros((H, T))
+    orel = np.zeros((H, T))
+    for h in range(H):
+        c = head_prec[h]
+        bs, hs = np.arange(B), np.full(B, h)
+        sq = ostep.zero_state(c, B, dv, dk, axis=axis)
+        sf = ostep.zero_state(0, B, dv, dk)
+        buf = owin.empty_buffer(B, window, dv, dk)
+        al, be = rec["alpha"][:, h], rec["beta"][:, h]
+        for t in range(1, T + 1):
+            q, k, v = (rec[n][t - 1][:, h] for n in ("q", "k", "v"))
+            if window > 1 and c in ostep.SCALED:
+                sq, buf, oq = owin.window_step(c, sq, buf, q, k, v, al, be, delta, seed, t, bs, hs,
+                                               window, rounding=rnd, axis=axis)
+                p = owin.position(t, window)
+                Xq = owin.replay(c, sq, buf, 0 if p == window else p, axis)
+            else:
+                sq, oq = ostep.decode_step(c, sq, q, k, v, al, be, delta, seed, t, bs, hs,
+                                           rounding=rnd, axis=axis)
+                Xq = ostep.dequant(c, sq, axis=axis)
+            sf, of = ostep.decode_step(0, sf, q, k, v, al, be, delta, seed, t, bs, hs)
+            Xf = sf["X"].astype(np.float64)
+            num = ((Xq.astype(np.float64) - Xf) ** 2).sum(axis=(1, 2))
+            rel[h, t - 1] = np.sqrt(num / np.maximum((Xf ** 2).sum(axis=(1, 2)), 1e-300)).mean()
+            of64 = of.astype(np.float64)
+            orel[h, t - 1] = (np.linalg.norm(oq.astype(np.float64) - of64, axis=-1)
+                              / np.maximum(np.linalg.norm(of64, axis=-1), 1e-300)).mean()
+    return rel, orel
+
+
+@pytest.mark.parametrize("axis,window", [("value", 1), ("key", 1), ("value", 4), ("key", 4)])
+@pytest.mark.parametrize("rounding", [SR, NEAR])
+def test_harness_statistics_equal_the_oracle(axis, window, rounding):
+    """The harness's reported statistics against the oracle on the same
+    inputs: with delta = 0 (the harness's setting) no dot product enters the
+    state, so the GPU's quantized and fp32 trajectories are the oracle's bit
+    for bit in either rounding mode, and the relative state errors agree to
+    the rounding of the fp64 reductions; the readout errors differ only by the
+    summation order of o."""
+    head_prec = [2, 3, 4, 5]                   # int8, int4, int6, E4M3
+    T, d = 64, 64
+    log(f"case: harness vs oracle, B=2 H=4 d=64 T={T}, {axis} scales, window {window}, "
+        f"rounding {rounding}")
+    rec = {}
+    res = eh.error_trajectory(head_prec, B=2, d_k=d, d_v=d, T=T, delta=0, alpha_lo=0.9,
+                              alpha_hi=1.0, beta=0.5, drift=100.0, rounding=rounding, seed=3,
+                              points=list(range(1, T + 1)), scale_axis=lores.LORES_SCALE_KEY
+                              if axis == "key" else lores.LORES_SCALE_VALUE, window=window,
+                              record=rec)
+    rel, orel = _oracle_series(rec, head_prec, T, d, d, 0, 3, rounding, axis, window)
+    got_rel = np.array(res["rel_err"])
+    got_orel = np.array(res["o_rel_err"])
+    # inside the first window from S_0 = 0 nothing has been rounded yet: both
+    # sides report a zero state error there
+    nz = rel > 0
+    log(f"  final rel err per head: harness {np.round(got_rel[:, -1], 5).tolist()} "
+        f"oracle {np.round(rel[:, -1], 5).tolist()}; worst relative difference "
+        f"{np.max(np.abs(got_rel - rel)[nz] / rel[nz]):.2e} (state), worst readout difference "
+        f"{np.max(np.abs(got_orel - orel)):.2e}")
+    assert np.all(rel[:, -1] > 0)
+    assert np.array_equal(got_rel[~nz], rel[~nz])
+    np.testing.assert_allclose(got_rel, rel, rtol=1e-9, atol=0)
+    np.testing.assert_allclose(got_orel, orel, rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("rounding", [SR, NEAR])
+def test_harness_statistics_track_the_oracle_with_the_delta_rule(rounding):
+    """With delta = 1 the projection r = S k is summed in a different order on
+    the two sides, so a rare code decides differently and the trajectories
+    part; the statistics still agree closely (free-running, 64 steps)."""
+    head_prec = [2, 3, 4, 5]
+    T, d = 64, 64
+    log(f"case: harness vs oracle, delta rule, B=2 H=4 d=64 T={T}, rounding {rounding}")
+    rec = {}
+    res = eh.error_trajectory(head_prec, B=2, d_k=d, d_v=d, T=T, delta=1, alpha_lo=0.9,
+                              alpha_hi=1.0, beta=0.5, drift=100.0, rounding=rounding, seed=4,
+                              points=list(range(1, T + 1)), record=rec)
+    rel, orel = _oracle_series(rec, head_prec, T, d, d, 1, 4, rounding, "value", 1)
+    got_rel = np.array(res["rel_err"])
+    worst = float(np.max(np.abs(got_rel - rel) / rel))
+    log(f"  final rel err per head: harness {np.round(got_rel[:, -1], 5).tolist()} "
+        f"oracle {np.round(rel[:, -1], 5).tolist()}; worst relative difference {worst:.2e}")
+    assert worst < 0.05

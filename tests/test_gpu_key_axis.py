@@ -72,8 +72,8 @@ def test_c1_all_steps_int8_key():
 @pytest.mark.parametrize("name", ["C2", "C5"])
 def test_full_size_sampled(name):
     w = get_workload(name)
-    log(f"case: key columns, {name} full batch B={w.B} H={w.H}, 24 sampled units, 2 steps")
-    s = run_parity(w, T=2, units=_sample_units(w.B, w.H, 24, seed=11), init="random", axis="key")
+    log(f"case: key columns, {name} full batch B={w.B} H={w.H}, 64 sampled units, 8 steps")
+    s = run_parity(w, T=8, units=_sample_units(w.B, w.H, 64, seed=11), init="random", axis="key")
     log(s.summary())
     s.check()
 

@@ -13,7 +13,7 @@ import quantized_linear_recurrence_amd as lores
 from oracle import step as ostep
 from oracle import window as owin
 from tests import layout_codec as lc
-from tests.parity import log, random_unit_state, run_window_parity
+from tests.parity import head_precisions, log, random_unit_state, run_window_parity
 from workloads import get_workload, make_inputs
 
 pytestmark = [pytest.mark.gpu,
@@ -95,6 +95,23 @@ def test_full_size_c2_window8():
     units = sorted((int(i // w.H), int(i % w.H)) for i in idx)
     log("case: window W=8 on the full C2 batch (bf16 inputs), 16 sampled units, 9 steps")
     s = run_window_parity(w, T=9, W=8, head_prec=[2] * w.H, units=units)
+    log(s.summary())
+    s.check()
+
+
+@pytest.mark.parametrize("axis", ["value", "key"])
+def test_full_size_c5_window4(axis):
+    # the benchmarked windowed launch shape: the C5 batch, decay-assigned
+    # int8 + int4 heads, three whole windows
+    w = get_workload("C5")
+    inputs = make_inputs(w, 0, DEV, T=12)
+    head_prec = head_precisions(w, inputs)
+    g = np.random.default_rng(5)
+    idx = g.choice(w.B * w.H, size=64, replace=False)
+    units = sorted((int(i // w.H), int(i % w.H)) for i in idx)
+    log(f"case: window W=4 on the full C5 batch, {axis} scales, 64 sampled units, 12 steps")
+    s = run_window_parity(w, T=12, W=4, head_prec=head_prec, units=units, inputs=inputs,
+                          axis=axis)
     log(s.summary())
     s.check()
 

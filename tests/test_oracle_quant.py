@@ -168,6 +168,52 @@ def test_weyl_noise_matches_independent_noise_readout_error(prec):
     assert abs(errs["weyl"] / errs["iid"] - 1) < 0.10, errs
 
 
+def _rank_one_states(g, N, dv, dk):
+    """The state after one write from S_0 = 0: v k^T with a unit key."""
+    k = g.standard_normal((N, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    return np.einsum("ni,nj->nij", g.standard_normal((N, dv)), k).astype(F32)
+
+
+def _delta_rule_states(g, N, dv, dk, T):
+    """States after T steps of the gated delta rule (scalar decay in [0.7, 1),
+    beta = 2 sigmoid(N(0, 1)), unit keys, v ~ N(0, 1)) from S_0 = 0, in fp64:
+    the low-rank rows the decode path carries."""
+    S = np.zeros((N, dv, dk))
+    for _ in range(T):
+        k = g.standard_normal((N, dk))
+        k /= np.linalg.norm(k, axis=1, keepdims=True)
+        v = g.standard_normal((N, dv))
+        beta = 2.0 / (1.0 + np.exp(-g.standard_normal((N, 1))))
+        S = S * g.uniform(0.7, 1.0, (N, 1, 1))
+        r = np.einsum("nij,nj->ni", S, k)
+        S = S + np.einsum("ni,nj->nij", beta * (v - r), k)
+    return S.astype(F32)
+
+
+@pytest.mark.parametrize("shape", ["rank_one", "delta_rule_4", "delta_rule_16"])
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
+def test_weyl_noise_readout_error_on_recurrent_states(shape, prec):
+    """The same gate on the structured rows of the recurrence (every row of a
+    rank-one state is a multiple of the key, so its rounding fractions repeat
+    from row to row), averaged over eight step keys."""
+    g = np.random.default_rng(22)
+    N, dv, dk = 300, 32, 128
+    U = _rank_one_states(g, N, dv, dk) if shape == "rank_one" else \
+        _delta_rule_states(g, N, dv, dk, int(shape.rsplit("_", 1)[1]))
+    q = g.standard_normal((N, dk))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    errs = {}
+    for name, fn in (("weyl", rng.noise16), ("iid", rng.noise16_iid)):
+        tot = []
+        for t in range(8):
+            X = step.dequant(prec, step.quantize_rows(U, prec, fn(rng.unit_key(9, t + 1, np.arange(N), 2), dv, dk)))
+            e = np.einsum("nij,nj->ni", (X - U).astype(np.float64), q)
+            tot.append(np.mean(e ** 2))
+        errs[name] = float(np.mean(tot))
+    assert abs(errs["weyl"] / errs["iid"] - 1) < 0.10, errs
+
+
 @pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
 def test_nearest_mode_is_round_to_nearest(prec):
     """rounding="nearest" (the draw fixed at 2^15) rounds y = U * inv to the
