@@ -142,7 +142,9 @@ lores::StepMeta make_meta(const lores_state *st, const int *cls, int n_cls) {
         lores::ClassDesc &d = m.cls[i];
         d.prec = c;
         d.Hc = st->n_class[c];
-        d.groups = (d.Hc * st->n_rb + lores::kWavesPerGroup - 1) / lores::kWavesPerGroup;
+        const int gw = st->axis == LORES_SCALE_KEY && has_scales(c)
+                           ? lores::key_group_waves(st->n_rb) : lores::kWavesPerGroup;
+        d.groups = (d.Hc * st->n_rb + gw - 1) / gw;
         d.head_off = off;
         d.unit_bytes = st->unit_bytes[c];
         for (int k = 0; k < d.Hc; ++k) m.heads[off + k] = st->heads[c][k];
@@ -231,10 +233,6 @@ static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
             if (d_k != 64 && d_k != 128)
                 return fail(LORES_EUNSUPPORTED, "key-column scales are built for d_k = 64 and "
                                                 "128 (got %d)", d_k);
-            if (d_v > 128 && d_v <= 192)
-                return fail(LORES_EUNSUPPORTED, "key-column scales need d_v <= 128 or d_v > 192 "
-                                                "(three row blocks do not fill a work-group; got %d)",
-                            d_v);
         }
         lores_state tmp;
         tmp.B = B;

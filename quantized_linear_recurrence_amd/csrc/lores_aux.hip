@@ -92,7 +92,7 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ClassDesc &cd = meta.cls[0];
-    const int task = blockIdx.x * kWavesPerGroup + wv;
+    const int task = blockIdx.x * (KEY ? key_group_waves(meta.n_rb) : kWavesPerGroup) + wv;
     if (task >= cd.Hc * meta.n_rb) {
         if constexpr (KEY) {
             if (meta.n_rb > 1) lds_barrier();      // the work-group's one barrier
@@ -148,9 +148,11 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
     const dim3 block(64 * kWavesPerGroup);
     if constexpr (has_scale<PREC>()) {
         if (key) {
+            const int gw = key_group_waves(m.n_rb);
+            const dim3 kgrid((m.cls[0].Hc * m.n_rb + gw - 1) / gw, m.B), kblock(64 * gw);
             switch (dk) {
-                case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), grid, block, 0, s, X, codes, scales, m); break;
-                case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), grid, block, 0, s, X, codes, scales, m); break;
+                case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 default: return hipErrorInvalidValue;
             }
             return hipGetLastError();

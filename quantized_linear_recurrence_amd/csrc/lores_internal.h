@@ -102,4 +102,12 @@ constexpr int kWavesPerGroup = 4;
 // group per CU at two wavefronts per SIMD, sharing a work queue).
 constexpr int kPairWavesPerGroup = 8;
 
+// Wavefronts per work-group of the launches whose wavefronts exchange
+// key-column maxima (key-column steps and quantization): a unit's n_rb row
+// blocks must share one work-group, so units of three row blocks run in
+// three-wavefront groups and all others in kWavesPerGroup.
+__host__ __device__ constexpr int key_group_waves(int n_rb) {
+    return n_rb == 3 ? 3 : kWavesPerGroup;
+}
+
 }  // namespace lores

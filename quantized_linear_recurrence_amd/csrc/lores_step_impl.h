@@ -1452,7 +1452,7 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         // row block take no barrier at all).
         static_assert(P1 < 0, "key-column scales run one class per launch");
         __shared__ float cmax[3 * kWavesPerGroup * DK];    // two maxima buffers, staging
-        const int task = gx * kWavesPerGroup + wv;
+        const int task = gx * key_group_waves(n_rb) + wv;
         if (task >= meta.cls[0].Hc * n_rb) {
             if (n_rb > 1)
                 for (int b = blockIdx.y; b < meta.B; b += gridDim.y) lds_barrier();
@@ -1547,8 +1547,9 @@ template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = f
           bool WEND = false>
 hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY, WEND>;
-    constexpr int W = group_waves<P0, P1, DK>();
-    static int per_cu = 0;                          // resident work-groups per CU
+    const int W = KEY ? key_group_waves(m.n_rb) : group_waves<P0, P1, DK>();
+    static int per_cu_of[kWavesPerGroup + 1] = {0};      // resident work-groups per CU, by W
+    int &per_cu = per_cu_of[W <= kWavesPerGroup ? W : 0];
     if (!per_cu) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern),

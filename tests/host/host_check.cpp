@@ -63,7 +63,7 @@ int main() {
 
     // plans over many shapes: segments in bounds, disjoint, 256-aligned
     const int dks[] = {32, 64, 96, 128};
-    const int dvs[] = {1, 64, 65, 128, 200, 256};
+    const int dvs[] = {1, 64, 65, 128, 150, 200, 256};
     std::vector<std::vector<uint8_t>> mixes = {{2}, {3, 2}, {0, 1, 2, 3, 4, 5}, {5, 5, 4}, {1, 3}};
     for (int dk : dks)
         for (int dv : dvs)
@@ -75,8 +75,7 @@ int main() {
                         int rc = lores_state_alloc_window(B, H, dk, dv, mix.data(), axis, W, nullptr,
                                                           &n, nullptr, nullptr);
                         const bool key_ok = dk == 64 || dk == 128;
-                        const bool dv_ok = dv <= 128 || dv > 192;
-                        if (axis == 1 && !(key_ok && dv_ok)) {
+                        if (axis == 1 && !key_ok) {
                             CHECK(rc == LORES_EUNSUPPORTED);
                             continue;
                         }
@@ -198,6 +197,16 @@ int main() {
         CHECK(step(st, x, 1) == LORES_OK);
         CHECK(g_launches.v.size() == 2 && g_launches.v[0].kind == "launch_step_key_int8" &&
               g_launches.v[1].kind == "launch_step_key_int4");
+        lores_state_free(st);
+        // key columns over three row blocks: one unit per three-wavefront group
+        n = size_of(4, 4, 128, 150, prec, LORES_SCALE_KEY);
+        Buf k3(n);
+        CHECK(lores_state_alloc_axis(4, 4, 128, 150, prec.data(), LORES_SCALE_KEY, k3.p, &n, nullptr,
+                                     &st) == LORES_OK);
+        g_launches.clear();
+        CHECK(step(st, x, 1) == LORES_OK);
+        CHECK(g_launches.v.size() == 2);
+        for (auto &l : g_launches.v) CHECK(l.n_rb == 3 && l.groups[0] == l.Hc[0]);
         lores_state_free(st);
     }
     // windowed states: positions follow t, steps must come in order

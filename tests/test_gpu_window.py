@@ -48,7 +48,7 @@ def test_longest_window(prec, dk, dv):
 
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
-@pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256)])
+@pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256), (3, 128, 180)])
 def test_key_column_windows(prec, W, dk, dv):
     """Windows over key-column scales (the PACE combination): the window end
     takes the column maxima of the replayed state."""

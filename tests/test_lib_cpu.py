@@ -153,10 +153,10 @@ def test_key_axis_layout_and_limits(lores_lib):
     want = _layout_bytes(4, 3, 128, 100, [2, 3, 1], key=True)
     assert key_bytes == want, (key_bytes, want)
     assert val_bytes == _layout_bytes(4, 3, 128, 100, [2, 3, 1])
-    for dk, dv in ((96, 64), (32, 64), (128, 150), (64, 192)):
+    for dk, dv in ((96, 64), (32, 64)):
         assert L.lores_state_alloc_axis(2, 3, dk, dv, hp, 1, None, ctypes.byref(n), None,
                                         None) == lores._lib.LORES_EUNSUPPORTED, (dk, dv)
-    for dv in (1, 64, 65, 128, 193, 256):
+    for dv in (1, 64, 65, 128, 150, 192, 193, 256):
         assert L.lores_state_alloc_axis(2, 3, 64, dv, hp, 1, None, ctypes.byref(n), None,
                                         None) == 0, dv
     assert L.lores_state_alloc_axis(2, 3, 64, 64, hp, 2, None, ctypes.byref(n), None,
@@ -186,7 +186,8 @@ def test_window_layout_and_limits(lores_lib):
                                       None) == 0
     assert n.value == _layout_bytes(5, 4, 128, 100, [2, 3, 1, 5], key=True, window=4)
     assert L.lores_state_alloc_window(5, 4, 128, 150, hp, 1, 4, None, ctypes.byref(n), None,
-                                      None) == lores._lib.LORES_EUNSUPPORTED
+                                      None) == 0
+    assert n.value == _layout_bytes(5, 4, 128, 150, [2, 3, 1, 5], key=True, window=4)
 
 
 def test_error_message_is_thread_local_and_cleared(lores_lib):
