@@ -28,12 +28,12 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden", "window_case.json")
 SCALED = [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6, step.PREC_FP8]
 
 
-def _inputs(g, T, N, dv, dk, delta):
+def _inputs(g, T, N, dv, dk, delta, per_channel=False):
     def unit(x):
         return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(F32)
     return {"q": unit(g.standard_normal((T, N, dk))), "k": unit(g.standard_normal((T, N, dk))),
             "v": g.standard_normal((T, N, dv)).astype(F32),
-            "alpha": g.uniform(0.8, 1.0, (T, N)).astype(F32),
+            "alpha": g.uniform(0.8, 1.0, (T, N, dk) if per_channel else (T, N)).astype(F32),
             "beta": (g.uniform(0.2, 1.5, (T, N)) if delta else g.uniform(0.1, 2.0, (T, N))).astype(F32)}
 
 
@@ -75,10 +75,11 @@ def test_hand_worked_window():
 @pytest.mark.parametrize("prec", SCALED)
 @pytest.mark.parametrize("delta", [0, 1])
 @pytest.mark.parametrize("axis", ["value", "key"])
-def test_window_one_is_the_per_step_method(prec, delta, axis):
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_window_one_is_the_per_step_method(prec, delta, axis, per_channel):
     g = np.random.default_rng(100 + prec + 10 * delta)
     N, dv, dk, T = 4, 24, 32, 5
-    x = _inputs(g, T, N, dv, dk, delta)
+    x = _inputs(g, T, N, dv, dk, delta, per_channel)
     st = _random_state(prec, N, dv, dk, g, axis)
     ref = {k: v.copy() for k, v in st.items()}
     buf = window.empty_buffer(N, 1, dv, dk)
@@ -110,32 +111,75 @@ def test_inside_a_window_the_state_is_kept_and_the_buffer_fills(prec):
             want = (x["beta"][t - 1][:, None] * x["v"][t - 1]).astype(F32)
             assert np.array_equal(buf["g"][:, t - 1], want)
             assert np.array_equal(buf["k"][:, t - 1], x["k"][t - 1])
-            assert np.array_equal(buf["alpha"][:, t - 1], x["alpha"][t - 1])
+            assert np.array_equal(buf["alpha"][:, t - 1, 0], x["alpha"][t - 1])
         else:
             assert not np.array_equal(st["codes"], st0["codes"])
             assert np.all(buf["g"] == 0)
 
 
 @pytest.mark.parametrize("delta", [0, 1])
-def test_readouts_follow_the_fp64_recurrence(delta):
+@pytest.mark.parametrize("axis,per_channel", [("value", False), ("value", True), ("key", True)])
+def test_readouts_follow_the_fp64_recurrence(delta, axis, per_channel):
     g = np.random.default_rng(300 + delta)
     N, dv, dk, W = 4, 16, 32, 6
-    x = _inputs(g, W, N, dv, dk, delta)
+    x = _inputs(g, W, N, dv, dk, delta, per_channel)
     prec = step.PREC_INT8
-    st = _random_state(prec, N, dv, dk, g)
-    S = step.dequant(prec, st).astype(np.float64)
+    st = _random_state(prec, N, dv, dk, g, axis)
+    S = step.dequant(prec, st, axis=axis).astype(np.float64)
     buf = window.empty_buffer(N, W, dv, dk)
     b, h = np.arange(N), np.zeros(N, np.int64)
     for t in range(1, W):                      # the readouts before the window's rounding
         a = [x[kk][t - 1] for kk in ("q", "k", "v", "alpha", "beta")]
-        st, buf, o = window.window_step(prec, st, buf, *a, delta, 5, t, b, h, W=W)
+        st, buf, o = window.window_step(prec, st, buf, *a, delta, 5, t, b, h, W=W, axis=axis)
         for n in range(N):
             S[n], o_ref = step.reference_step64(S[n], a[0][n], a[1][n], a[2][n], a[3][n],
                                                 a[4][n], delta)
             scale = np.linalg.norm(S[n], axis=1).max()
             assert np.abs(o[n] - o_ref).max() <= 1e-5 * scale, (t, n)
-        X = window.replay(prec, st, buf, t)
+        X = window.replay(prec, st, buf, t, axis, per_channel)
         assert np.abs(X - S).max() <= 1e-5 * np.abs(S).max()
+        if per_channel:
+            assert np.array_equal(buf["alpha"][:, t - 1], a[3])
+
+
+def test_channel_decay_window_closed_form():
+    """delta = 0, one decay per key channel: the state a window rebuilds is
+    X_0 diag(prod alpha) + sum_tau beta_tau v_tau k_tau^T diag(prod of the
+    later alphas), to fp32 accuracy; and a window whose decays are all equal
+    per unit is the scalar-decay window, value for value."""
+    g = np.random.default_rng(77)
+    N, dv, dk, W = 3, 8, 32, 5
+    x = _inputs(g, W, N, dv, dk, 0, per_channel=True)
+    prec = step.PREC_INT4
+    st = _random_state(prec, N, dv, dk, g)
+    X0 = step.dequant(prec, st).astype(np.float64)
+    buf = window.empty_buffer(N, W, dv, dk)
+    b, h = np.arange(N), np.zeros(N, np.int64)
+    for t in range(1, W):
+        a = [x[kk][t - 1] for kk in ("q", "k", "v", "alpha", "beta")]
+        st, buf, _ = window.window_step(prec, st, buf, *a, 0, 5, t, b, h, W=W)
+    al = x["alpha"][:W - 1].astype(np.float64)                  # [tau, N, dk]
+    want = X0 * np.prod(al, axis=0)[:, None, :]
+    for tau in range(W - 1):
+        later = np.prod(al[tau + 1:], axis=0) if tau + 1 < W - 1 else np.ones((N, dk))
+        want += (x["beta"][tau][:, None, None] * x["v"][tau][:, :, None]
+                 * x["k"][tau][:, None, :] * later[:, None, :])
+    got = window.replay(prec, st, buf, W - 1, "value", True)
+    assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max()
+    # equal decays per unit: the channel form reduces to the scalar one
+    xs = _inputs(np.random.default_rng(78), W, N, dv, dk, 1)
+    xc = dict(xs, alpha=np.repeat(xs["alpha"][:, :, None], dk, axis=2))
+    s1 = s2 = _random_state(prec, N, dv, dk, np.random.default_rng(79))
+    b1 = window.empty_buffer(N, W, dv, dk)
+    b2 = window.empty_buffer(N, W, dv, dk)
+    for t in range(1, W + 1):
+        a1 = [xs[kk][t - 1] for kk in ("q", "k", "v", "alpha", "beta")]
+        a2 = [xc[kk][t - 1] for kk in ("q", "k", "v", "alpha", "beta")]
+        s1, b1, o1 = window.window_step(prec, s1, b1, *a1, 1, 5, t, b, h, W=W)
+        s2, b2, o2 = window.window_step(prec, s2, b2, *a2, 1, 5, t, b, h, W=W)
+        assert np.array_equal(o1, o2), t
+        for kk in s1:
+            assert np.array_equal(s1[kk], s2[kk]), (t, kk)
 
 
 @pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
