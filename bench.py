@@ -67,14 +67,14 @@ def unit_bytes(prec, dk, dv, in_bytes, per_channel, key=False, window=1):
     per window its buffer is written once and read back by the later steps
     of the window (token tau is read by the W - tau later steps): averaged
     per step, state (1 + 1/W) + buffer ((W - 1) + W (W - 1) / 2) / W slots of
-    (d_v + d_k + 1) fp32."""
+    (d_v + d_k + 1) fp32 (d_v + 2 d_k with a decay per key channel)."""
     ns = dk if key else dv
     state = {0: 4 * dv * dk, 1: 2 * dv * dk, 2: dv * dk + 4 * ns, 3: dv * dk // 2 + 4 * ns,
              4: 6 * dv * dk // 8 + 4 * ns, 5: dv * dk + 4 * ns}[prec]
     io = 2 * dk * in_bytes + dv * in_bytes + (4 * dk if per_channel else 4) + 4 + 4 * dv
     if window > 1 and prec in (2, 3, 4, 5):
         W = window
-        slot = 4 * (dv + dk + 1)
+        slot = 4 * (dv + dk + (dk if per_channel else 1))
         return state * (W + 1) / W + slot * ((W - 1) + W * (W - 1) / 2) / W + io
     return 2 * state + io
 
@@ -403,8 +403,6 @@ def main(argv=None):
     K, W = args.steps, args.warmup
     win = args.window
     if win > 1:
-        if w.per_channel:
-            sys.exit("bench.py: windowed states take a scalar decay")
         K, W = -(-K // win) * win, -(-W // win) * win       # whole windows
     T_in = min(w.T, max(K, W, 1))
     print(f"[bench] generating {T_in} steps of {w.key} inputs on {dev}", file=sys.stderr, flush=True)

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 5
+#define LORES_SPEC_VERSION 6
 
 /* Per-head state precision. */
 enum {

@@ -27,6 +27,7 @@ struct lores_state {
     int32_t axis;            // LORES_SCALE_*
     int32_t window;          // W: steps per requantization of the scaled classes
     int32_t n_buf;           // tokens of the current window held in the buffer
+    int32_t win_pc;          // those tokens carry one decay per key channel
     int64_t win_off[LORES_NUM_PREC], unit_win[LORES_NUM_PREC];   // bytes
 };
 
@@ -244,6 +245,7 @@ static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         tmp.axis = scale_axis;
         tmp.window = window;
         tmp.n_buf = 0;
+        tmp.win_pc = 0;
         rc = plan(&tmp, head_prec);
         if (rc) return rc;
         if (!d_buf) {
@@ -456,17 +458,19 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
         const bool windowed = st->window > 1;
         int wpos = 1;
         if (windowed) {
-            bool scaled = false;
-            for (int c = 0; c < LORES_NUM_PREC; ++c) scaled |= st->n_class[c] && has_scales(c);
-            if (scaled && alpha_per_channel)
-                return fail(LORES_EUNSUPPORTED, "windowed states take a scalar alpha per head "
-                                                "(alpha_per_channel = 0)");
             wpos = (int)((t - 1) % (uint64_t)st->window) + 1;
             if (wpos != st->n_buf + 1)
                 return fail(LORES_EINVAL, "windowed state: the buffer holds %d tokens of the current "
                                           "window, so the next step is at window position %d, but "
                                           "t = %llu is at position %d (steps must come in order)",
                             st->n_buf, st->n_buf + 1, (unsigned long long)t, wpos);
+            // the buffered tokens and this one share one kind of decay
+            if (wpos > 1 && alpha_per_channel != st->win_pc)
+                return fail(LORES_EINVAL, "windowed state: the window's buffered tokens carry %s "
+                                          "decay, this step %s (alpha_per_channel may change only "
+                                          "at a window's first step)",
+                            st->win_pc ? "a per-channel" : "a scalar",
+                            alpha_per_channel ? "a per-channel one" : "a scalar one");
         }
         int groups[LORES_NUM_PREC][2], width[LORES_NUM_PREC];
         const int n_launch = plan_launches(st, groups, width);
@@ -497,7 +501,9 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             consume_stale_hip_error();
             if (windowed && has_scales(groups[l][0])) {
                 p.win[0] = (float *)(st->base + st->win_off[groups[l][0]]);
-                e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, key, p, m, s);
+                m.win_pc = alpha_per_channel;
+                e = lores::launch_window_step(groups[l][0], st->dk, delta, in_bf16, key,
+                                              alpha_per_channel != 0, p, m, s);
             } else {
                 e = lores::launch_step(st->dk, alpha_per_channel, delta, in_bf16, groups[l][0], p1, p,
                                        m, s, key);
@@ -505,7 +511,10 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
             if (e != hipSuccess)
                 return fail(LORES_EHIP, "decode-step launch failed: %s", hipGetErrorString(e));
         }
-        if (windowed) st->n_buf = wpos == st->window ? 0 : wpos;
+        if (windowed) {
+            st->n_buf = wpos == st->window ? 0 : wpos;
+            st->win_pc = alpha_per_channel;
+        }
         return ok();
     } catch (...) {
         return fail(LORES_EINVAL, "internal error in lores_decode_step");
@@ -555,6 +564,7 @@ int lores_dequant_state(const lores_state *st, float *out, void *stream) {
             consume_stale_hip_error();
             if (st->window > 1 && st->n_buf > 0 && has_scales(c)) {
                 m.wpos = st->n_buf;
+                m.win_pc = st->win_pc;
                 m.window = st->window;
                 e = lores::launch_window_dequant(c, st->dk, st->axis == LORES_SCALE_KEY,
                                                  st->base + st->codes_off[c], sc,

@@ -30,7 +30,8 @@ struct StepMeta {
     int32_t wpos;                      // windowed states: position p of step t (1 .. window),
                                        // or, for the dequantization, the buffered tokens
     int32_t window;                    // W (1: requantize every step)
-    int32_t pad_;
+    int32_t win_pc;                    // windowed states: the window's tokens carry one
+                                       // decay per key channel (else a scalar per unit)
     uint64_t seed, t;
     int64_t seq_base, head_base;
     ClassDesc cls[2];
@@ -47,10 +48,11 @@ struct StepPtrs {
     float *win[2];           // window buffers of a windowed state, else nullptr
 };
 
-// Floats of one unit's window block: W - 1 slots of g (d_v_pad), k (d_k) and
-// alpha (1), padded to 16 bytes.
+// Floats of one unit's window block: W - 1 slots of g (d_v_pad), then W - 1
+// of k (d_k), then W - 1 of alpha (d_k: one decay per key channel, or a
+// scalar decay in element 0), padded to 16 bytes.
 __host__ __device__ inline int64_t window_unit_floats(int window, int dv_pad, int dk) {
-    return ((int64_t)(window - 1) * (dv_pad + dk + 1) + 3) / 4 * 4;
+    return ((int64_t)(window - 1) * (dv_pad + 2 * dk) + 3) / 4 * 4;
 }
 
 // One launch covers one class or one of the fused pairs (int8, int4),
@@ -81,7 +83,7 @@ hipError_t launch_step_key_fp8(int, bool, bool, bool, const StepPtrs &, const St
 // the step at window position m.wpos < m.window (read the stored state,
 // buffer the token) or = m.window (rebuild, step and requantize).  One class
 // per launch.
-hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key,
+hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key, bool pc,
                               const StepPtrs &p, const StepMeta &m, hipStream_t s);
 
 // Dequant uses the same StepMeta with one class; `key`: key-column scales.

@@ -921,19 +921,23 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 // per-channel alpha in lane form (lane L: columns 64 t + L), two registers
 // each at d_k = 128; the row vectors of their product are built at the start
 // of the task.
-template <int NV, bool KEY = false>
+// WPC: the end of a window whose tokens carry one decay per key channel:
+// av (al with key-column scales) holds the window's first token's decays and
+// avt this step's, as row vectors.
+template <int NV, bool KEY = false, bool WPC = false>
 struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
     float alpha_t = 1.0f;              // window end: this step's decay (alpha is token 1's)
     float kv[NV], qv[NV], av[KEY ? 1 : NV];
     float sl[KEY ? NV / 4 : 1], al[KEY ? NV / 4 : 1];
+    float avt[WPC ? NV : 1];
 };
 
 // KEY: key-column scales (d_k per unit); the unit's row blocks are the
 // wavefronts wv - rb .. wv - rb + n_rb - 1 of one work-group, and `lds`
 // holds two buffers of kWavesPerGroup x DK column maxima (tasks alternate
 // between them) and a kWavesPerGroup x DK staging area.
-// WEND: the last step of a window of a windowed state (scalar decay): pass 1
+// WEND: the last step of a window of a windowed state: pass 1
 // dequantizes with the window's first decay, then the window buffer's
 // tokens are replayed on U before this step's token.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false, bool WEND = false>
@@ -980,10 +984,11 @@ struct TaskStream {
     }
 
     static constexpr int NV = DK / 16;            // row-vector registers per vector
+    using Side = TaskSide<NV, KEY, WEND && PC>;
 
     // Loads of task b: chunks [C0, C1) and, with C0 = 0, the per-task values.
     template <int C0 = 0, int C1 = NCH>
-    __device__ __forceinline__ void issue(int b, u32x4 *cw, TaskSide<NV, KEY> &in) const {
+    __device__ __forceinline__ void issue(int b, u32x4 *cw, Side &in) const {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;
@@ -991,11 +996,18 @@ struct TaskStream {
 #pragma unroll
         for (int c = C0; c < C1; ++c) cw[c] = io.load(c);
         if constexpr (C0 != 0) return;
+        // window end with channel decays: pass 1 decays with the window's
+        // first token's, held in slot 0 of the unit's window buffer
+        const float *wa1 = nullptr;
+        if constexpr (WEND && PC)
+            wa1 = win + unit * window_unit_floats(meta.window, meta.dv_pad, DK) +
+                  (long)(meta.window - 1) * (meta.dv_pad + DK);
         if constexpr (KEY) {
 #pragma unroll
             for (int t = 0; t < NV / 4; ++t) {
                 in.sl[t] = scales[unit * DK + 64 * t + (threadIdx.x & 63)];
-                if constexpr (PC) in.al[t] = alphap[bh * DK + 64 * t + (threadIdx.x & 63)];
+                if constexpr (PC && WEND) in.al[t] = wa1[64 * t + (threadIdx.x & 63)];
+                else if constexpr (PC) in.al[t] = alphap[bh * DK + 64 * t + (threadIdx.x & 63)];
             }
         } else if constexpr (has_scale<PREC>()) {
             in.s = scales[unit * dv_pad + lrow];
@@ -1003,7 +1015,7 @@ struct TaskStream {
         in.v = in_raw<BF16IN>(vp, bh * meta.dv + lrow);
         in.beta = betap[bh];
         in.alpha = PC ? 1.0f : alphap[bh];
-        if constexpr (WEND) {
+        if constexpr (WEND && !PC) {
             // pass 1 decays with the window's first token's alpha
             in.alpha_t = in.alpha;
             in.alpha = win[unit * window_unit_floats(meta.window, meta.dv_pad, DK) +
@@ -1015,12 +1027,17 @@ struct TaskStream {
         for (int i = 0; i < NV; ++i) {
             in.kv[i] = in_raw<BF16IN>(kp, kb + 16 * i);
             in.qv[i] = in_raw<BF16IN>(qp, kb + 16 * i);
-            if constexpr (PC && !KEY) in.av[i] = alphap[kb + 16 * i];
+            if constexpr (PC && WEND) {
+                in.avt[i] = alphap[kb + 16 * i];
+                if constexpr (!KEY) in.av[i] = wa1[16 * i + (threadIdx.x & 15)];
+            } else if constexpr (PC && !KEY) {
+                in.av[i] = alphap[kb + 16 * i];
+            }
         }
     }
 
     template <class Mid>
-    __device__ __forceinline__ void run(int b, const u32x4 *cw, const TaskSide<NV, KEY> &in,
+    __device__ __forceinline__ void run(int b, const u32x4 *cw, const Side &in,
                                         Mid &&mid, int buf = 0) const {
         const float s = in.s, vi = from_raw<BF16IN>(in.v);
         float kv[NV], qv[NV];
@@ -1194,17 +1211,32 @@ struct TaskStream {
 #pragma unroll
             for (int i = 0; i < NV; ++i) kt[i] = ks[16 * i];
             for (int tau = 1; tau <= nslot; ++tau) {
-                float gn = 0.0f, kn[NV], an = in.alpha_t;
+                // the next token's decay: from slot tau, or this step's own
+                float gn = 0.0f, kn[NV], an = in.alpha_t, anv[PC ? NV : 1];
+                if constexpr (PC) {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) anv[i] = in.avt[i];
+                }
                 if (tau < nslot) {
                     gn = gs[(long)tau * dv_pad];
 #pragma unroll
                     for (int i = 0; i < NV; ++i) kn[i] = ks[(long)tau * DK + 16 * i];
-                    an = as[tau];
+                    if constexpr (PC) {
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) anv[i] = as[(long)tau * DK + 16 * i + (threadIdx.x & 15)];
+                    } else {
+                        an = as[(long)tau * DK];
+                    }
                 }
 #pragma unroll
                 for (int gi = 0; gi < NV; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
+                if constexpr (PC) {
 #pragma unroll
-                for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
+                    for (int gi = 0; gi < NV; ++gi) mul16(&U[16 * gi], anv[gi]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
+                }
                 gt = gn;
 #pragma unroll
                 for (int i = 0; i < NV; ++i) kt[i] = kn[i];
@@ -1269,7 +1301,7 @@ __device__ __forceinline__ void run_single(
                     : PREC == LORES_BF16 ? kMaxPrefetchChunks : 0;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
-    TaskSide<TS::NV, KEY> in0, in1;
+    typename TS::Side in0, in1;
     int b = blockIdx.y;
     ts.issue(b, cw, in0);
     while (true) {
@@ -1435,12 +1467,12 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int gx = blockIdx.x;
     const int n_rb = meta.n_rb;
-    static_assert(!WEND || (P1 < 0 && !PC), "window ends run one class with a scalar decay");
+    static_assert(!WEND || P1 < 0, "window ends run one class per launch");
     if constexpr (WEND && !KEY) {
-        // the last step of a window: one scaled class, scalar decay
+        // the last step of a window: one scaled class
         const int task = gx * kWavesPerGroup + wv;
         if (task >= meta.cls[0].Hc * n_rb) return;
-        run_single(TaskStream<DK, P0, false, DELTA, BF16IN, false, true>(
+        run_single(TaskStream<DK, P0, PC, DELTA, BF16IN, false, true>(
             qp, kp, vp, alphap, betap, op, codes0, scales0, meta, meta.cls[0], task, nullptr,
             win0));
     } else if constexpr (KEY) {

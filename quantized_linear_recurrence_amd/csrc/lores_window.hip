@@ -18,6 +18,13 @@
 // q (per unit):
 //   r_i = alpha_p (c s_i sum_j c_ij k_j + sum_tau d_tau g_tau,i (k_tau . k)),
 //   o_i = alpha_p (c s_i sum_j c_ij q_j + sum_tau d_tau g_tau,i (k_tau . q)) + g_i (k . q).
+// With one decay per key channel the products are per column: with
+// C_j = prod_{sigma < p} alpha_sigma,j and D_tau,j = prod_{tau < sigma < p}
+// alpha_sigma,j the decayed state S'_p = S_{p-1} diag(alpha_p) reads
+//   r_i = s_i sum_j c_ij (C alpha_p k)_j + sum_tau g_tau,i ((D_tau alpha_p k_tau) . k),
+//   o_i = s_i sum_j c_ij (C alpha_p q)_j + sum_tau g_tau,i ((D_tau alpha_p k_tau) . q)
+//         + g_i (k . q),
+// the same dot products with per-column weights (row vectors).
 // The last step of a window replays the buffer in the exact order above, so
 // its requantized state is the fp32 recurrence's, and steps as usual.
 #include "lores_step_impl.h"
@@ -97,8 +104,9 @@ __device__ __forceinline__ bool window_task(const StepMeta &meta, WindowTask &w)
 // a step inside a window (p < W): read X_0, buffer the token
 // ---------------------------------------------------------------------------
 // KEY: key-column scales: X_0 . k = sum_j c_ij (s_j k_j), so the dot products
-// take s o k and s o q and there is no row scale.
-template <int DK, int PREC, bool DELTA, bool BF16IN, bool KEY>
+// take s o k and s o q and there is no row scale.  PC: one decay per key
+// channel (alpha [B][H][d_k]; every token of the window has one).
+template <int DK, int PREC, bool DELTA, bool BF16IN, bool KEY, bool PC>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                          const void *__restrict__ vp, const float *__restrict__ alphap,
@@ -116,68 +124,90 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     for (int c = 0; c < NCH; ++c) cw[c] = __builtin_nontemporal_load(cp + c * dv_pad);
     const float s = KEY ? 1.0f : scales[w.unit * dv_pad + w.lrow];
     const float v = in_scalar<BF16IN>(vp, w.bh * meta.dv + w.lrow);
-    const float beta = betap[w.bh], alpha = alphap[w.bh];
-    float kv[NV], qv[NV], ks[NV], qs[NV];
+    const float beta = betap[w.bh], alpha = PC ? 1.0f : alphap[w.bh];
+    float kv[NV], qv[NV], sc[NV], av[NV];
     const long kb = w.bh * DK + (lane & 15);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         kv[i] = in_scalar<BF16IN>(kp, kb + 16 * i);
         qv[i] = in_scalar<BF16IN>(qp, kb + 16 * i);
-        if constexpr (KEY) {
-            const float sc = scales[w.unit * DK + 16 * i + (lane & 15)];
-            ks[i] = sc * kv[i];
-            qs[i] = sc * qv[i];
-        } else {
-            ks[i] = kv[i];
-            qs[i] = qv[i];
-        }
+        sc[i] = KEY ? scales[w.unit * DK + 16 * i + (lane & 15)] : 1.0f;
+        av[i] = PC ? alphap[kb + 16 * i] : 1.0f;
     }
     const int p = meta.wpos, nslot = meta.window - 1;
     float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
 
-    // sum_j c_ij k_j and sum_j c_ij q_j over the stored row (codes unscaled):
-    // int rows take the stored offset-binary integers c + off and subtract
-    // off * sum_j k_j once (a different rounding of the same sum)
+    // the buffered tokens, latest first.  Scalar decay: d = the product of
+    // the later decays, then (after the loop) c_{p-1}.  Per channel: E = the
+    // later decays times alpha_p, column by column, then C alpha_p.
+    float rs = 0.0f, os = 0.0f, d = 1.0f, E[PC ? NV : 1];
+    if constexpr (PC) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) E[i] = av[i];
+    }
+    for (int tau = p - 1; tau >= 1; --tau) {
+        const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
+        float kt[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) kt[i] = kslot[(long)(tau - 1) * DK + 16 * i + (lane & 15)];
+        if constexpr (PC) {
+            float ek[NV];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) ek[i] = E[i] * kt[i];
+            if constexpr (DELTA) rs = __builtin_fmaf(gt, rowdot<NV>(ek, kv), rs);
+            os = __builtin_fmaf(gt, rowdot<NV>(ek, qv), os);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) E[i] = E[i] * aslot[(long)(tau - 1) * DK + 16 * i + (lane & 15)];
+        } else {
+            const float dg = d * gt;
+            if constexpr (DELTA) rs = __builtin_fmaf(dg, rowdot<NV>(kt, kv), rs);
+            os = __builtin_fmaf(dg, rowdot<NV>(kt, qv), os);
+            d = d * aslot[(long)(tau - 1) * DK];
+        }
+    }
+
+    // sum_j c_ij w_j over the stored row (codes unscaled) with the weights
+    // w = s o k and s o q (scalar decay; s = 1 for value rows) or s o C alpha_p
+    // o k and ... o q (per channel): int rows take the stored offset-binary
+    // integers c + off and subtract off * sum_j w_j once (a different
+    // rounding of the same sum)
+    float wk[NV], wq[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        float f = sc[i];
+        if constexpr (PC) f = f * E[i];
+        wk[i] = f * kv[i];
+        wq[i] = f * qv[i];
+    }
     float A = 0.0f, Bq = 0.0f;
 #pragma unroll
     for (int gi = 0; gi < NV; ++gi) {
         float x[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = stored<PREC>(cw, 16 * gi + e);
-        if constexpr (DELTA) dot16(A, x, ks[gi]);
-        dot16(Bq, x, qs[gi]);
+        if constexpr (DELTA) dot16(A, x, wk[gi]);
+        dot16(Bq, x, wq[gi]);
     }
     if constexpr (PREC != LORES_FP8) {
         float ones[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) ones[i] = 1.0f;
-        if constexpr (DELTA) A = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(ks, ones), A);
-        Bq = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(qs, ones), Bq);
+        if constexpr (DELTA) A = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(wk, ones), A);
+        Bq = __builtin_fmaf(-Prec<PREC>::OFF, rowdot<NV>(wq, ones), Bq);
     }
 
-    // the buffered tokens, latest first: d_tau = product of the later decays
-    float rs = 0.0f, os = 0.0f, d = 1.0f;
-    for (int tau = p - 1; tau >= 1; --tau) {
-        const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
-        float kt[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) kt[i] = kslot[(long)(tau - 1) * DK + 16 * i + (lane & 15)];
-        const float dg = d * gt;
-        if constexpr (DELTA) rs = __builtin_fmaf(dg, rowdot<NV>(kt, kv), rs);
-        os = __builtin_fmaf(dg, rowdot<NV>(kt, qv), os);
-        d = d * aslot[tau - 1];
-    }
-    // d is now c_{p-1}, the product of the window's earlier decays
-    const float cs = d * s;
+    // scalar decay: d is now c_{p-1}, the product of the window's earlier decays
+    const float cs = PC ? s : d * s;
+    const float da = PC ? 1.0f : alpha;
     float g;
     if constexpr (DELTA) {
-        const float r = alpha * __builtin_fmaf(cs, A, rs);
+        const float r = da * __builtin_fmaf(cs, A, rs);
         g = beta * (v - r);
     } else {
         g = beta * v;
     }
-    const float o = __builtin_fmaf(g, rowdot<NV>(kv, qv), alpha * __builtin_fmaf(cs, Bq, os));
+    const float o = __builtin_fmaf(g, rowdot<NV>(kv, qv), da * __builtin_fmaf(cs, Bq, os));
     if (w.active) {
         op[w.bh * meta.dv + w.row] = o;
         gslot[(long)(p - 1) * dv_pad + w.row] = g;
@@ -185,9 +215,14 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     if (w.rb == 0) {
         if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) kslot[(long)(p - 1) * DK + 16 * i + lane] = kv[i];
+            for (int i = 0; i < NV; ++i) {
+                kslot[(long)(p - 1) * DK + 16 * i + lane] = kv[i];
+                if constexpr (PC) aslot[(long)(p - 1) * DK + 16 * i + lane] = av[i];
+            }
         }
-        if (lane == 0) aslot[p - 1] = alpha;
+        if constexpr (!PC) {
+            if (lane == 0) aslot[(long)(p - 1) * DK] = alpha;
+        }
     }
 }
 
@@ -213,11 +248,13 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
     const float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     const float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
     float U[DK];
-    // token 1: fl(c fl(s alpha_1)), with the row's or column j's scale s
+    // token 1: fl(c fl(s alpha_1,j)), with the row's or column j's scale s and
+    // the token's decay of column j (a scalar decay: every column alike)
+    const bool pc = meta.win_pc != 0;
     const float s = KEY ? 0.0f : scales[w.unit * dv_pad + w.lrow];
 #pragma unroll
     for (int j = 0; j < DK; ++j) {
-        const float a1 = (KEY ? scales[w.unit * DK + j] : s) * aslot[0];
+        const float a1 = (KEY ? scales[w.unit * DK + j] : s) * aslot[pc ? j : 0];
         float na1 = 0.0f;
         if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
         U[j] = scaled_code<PREC>(cw, j, a1, na1);
@@ -230,9 +267,9 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
 #pragma unroll
         for (int gi = 0; gi < NV; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
         if (tau < n) {
-            const float an = aslot[tau];
+            const float *an = aslot + (long)tau * DK;
 #pragma unroll
-            for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
+            for (int j = 0; j < DK; ++j) U[j] = U[j] * an[pc ? j : 0];
         }
     }
     if (!w.active) return;
@@ -245,20 +282,20 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
 // Inside a window: one task per wavefront (a read-only pass, many waves per
 // SIMD).  The window's last step: the step kernel's task stream
 // with the buffer replayed between pass 1 and the token's own update.
-template <int DK, int PREC, bool KEY>
+template <int DK, int PREC, bool KEY, bool PC>
 static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const StepMeta &m,
                             hipStream_t s) {
     if (m.wpos == m.window) {
-        if (delta) return bf16 ? launch_one<DK, false, true, true, PREC, -1, KEY, true>(p, m, s)
-                               : launch_one<DK, false, true, false, PREC, -1, KEY, true>(p, m, s);
-        return bf16 ? launch_one<DK, false, false, true, PREC, -1, KEY, true>(p, m, s)
-                    : launch_one<DK, false, false, false, PREC, -1, KEY, true>(p, m, s);
+        if (delta) return bf16 ? launch_one<DK, PC, true, true, PREC, -1, KEY, true>(p, m, s)
+                               : launch_one<DK, PC, true, false, PREC, -1, KEY, true>(p, m, s);
+        return bf16 ? launch_one<DK, PC, false, true, PREC, -1, KEY, true>(p, m, s)
+                    : launch_one<DK, PC, false, false, PREC, -1, KEY, true>(p, m, s);
     }
     const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
 #define LORES_WIN_LAUNCH(D, BF)                                                                 \
-    hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF, KEY>), grid, block, 0, s, p.q,   \
-                       p.k, p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
+    hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF, KEY, PC>), grid, block, 0, s,    \
+                       p.q, p.k, p.v, p.alpha, p.beta, p.o, p.codes[0], p.scales[0], p.win[0], m);
     if (delta) {
         if (bf16) { LORES_WIN_LAUNCH(true, true) } else { LORES_WIN_LAUNCH(true, false) }
     } else {
@@ -269,25 +306,29 @@ static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const Step
 }
 
 template <int PREC>
-static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, const StepPtrs &p,
-                              const StepMeta &m, hipStream_t s) {
+static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, bool pc,
+                              const StepPtrs &p, const StepMeta &m, hipStream_t s) {
+#define LORES_WIN_KEY_PC(DK)                                                                    \
+    (key ? (pc ? window_dk<DK, PREC, true, true>(delta, bf16, p, m, s)                          \
+               : window_dk<DK, PREC, true, false>(delta, bf16, p, m, s))                        \
+         : (pc ? window_dk<DK, PREC, false, true>(delta, bf16, p, m, s)                         \
+               : window_dk<DK, PREC, false, false>(delta, bf16, p, m, s)))
     switch (dk) {
-        case 64: return key ? window_dk<64, PREC, true>(delta, bf16, p, m, s)
-                            : window_dk<64, PREC, false>(delta, bf16, p, m, s);
-        case 128: return key ? window_dk<128, PREC, true>(delta, bf16, p, m, s)
-                             : window_dk<128, PREC, false>(delta, bf16, p, m, s);
+        case 64: return LORES_WIN_KEY_PC(64);
+        case 128: return LORES_WIN_KEY_PC(128);
         default: return hipErrorInvalidValue;
     }
+#undef LORES_WIN_KEY_PC
 }
 
-hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key,
+hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key, bool pc,
                               const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     if (m.wpos < 1 || m.wpos > m.window || m.window < 2) return hipErrorInvalidValue;
     switch (prec) {
-        case LORES_INT8: return window_prec<LORES_INT8>(dk, delta, in_bf16, key, p, m, s);
-        case LORES_INT4: return window_prec<LORES_INT4>(dk, delta, in_bf16, key, p, m, s);
-        case LORES_INT6: return window_prec<LORES_INT6>(dk, delta, in_bf16, key, p, m, s);
-        case LORES_FP8: return window_prec<LORES_FP8>(dk, delta, in_bf16, key, p, m, s);
+        case LORES_INT8: return window_prec<LORES_INT8>(dk, delta, in_bf16, key, pc, p, m, s);
+        case LORES_INT4: return window_prec<LORES_INT4>(dk, delta, in_bf16, key, pc, p, m, s);
+        case LORES_INT6: return window_prec<LORES_INT6>(dk, delta, in_bf16, key, pc, p, m, s);
+        case LORES_FP8: return window_prec<LORES_FP8>(dk, delta, in_bf16, key, pc, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }

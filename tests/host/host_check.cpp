@@ -58,7 +58,7 @@ int main() {
     CHECK(size_of(1, 1, 64, 64, {LORES_FP32}) == 16384);
     CHECK(size_of(1, 1, 64, 64, {LORES_INT8}, LORES_SCALE_KEY) == 4096 + 256);
     CHECK(size_of(1, 1, 128, 64, {LORES_INT8}, LORES_SCALE_KEY) == 8192 + 512);
-    CHECK(size_of(1, 1, 64, 64, {LORES_INT8}, 0, 3) == 4096 + 256 + 1280);   // 2*(64+64+1)*4 = 1032 -> 1280
+    CHECK(size_of(1, 1, 64, 64, {LORES_INT8}, 0, 3) == 4096 + 256 + 1536);   // 2*(64+2*64)*4 = 1536
     CHECK(size_of(1, 1, 64, 1, {LORES_INT6}) == 48 * 64 + 256);             // 3 chunks of 16 B per row
 
     // plans over many shapes: segments in bounds, disjoint, 256-aligned
@@ -235,7 +235,7 @@ int main() {
         }
         g_launches.clear();
         CHECK(step(st, x, 12) == LORES_EINVAL);              // the buffer holds token 9's window
-        CHECK(step(st, x, 10, 1) == LORES_EUNSUPPORTED);     // per-channel decay
+        CHECK(step(st, x, 10, 1) == LORES_EINVAL);           // the window's tokens are scalar-decay
         CHECK(g_launches.v.empty());
         Buf out(1 << 20);
         g_launches.clear();
@@ -252,6 +252,36 @@ int main() {
         CHECK(lores_state_layout(st, &lay) == LORES_OK && lay.window_fill == 0);
         CHECK(step(st, x, 10) == LORES_EINVAL);
         CHECK(step(st, x, 13) == LORES_OK);
+        lores_state_free(st);
+    }
+    // windows whose tokens carry one decay per key channel: one kind of decay
+    // per window, passed to the window's launches and to its dequantization
+    {
+        std::vector<uint8_t> prec = {2, 3};
+        const int W = 3;
+        size_t n = size_of(2, 2, 64, 64, prec, 0, W);
+        Buf buf(n);
+        lores_state *st = nullptr;
+        CHECK(lores_state_alloc_window(2, 2, 64, 64, prec.data(), 0, W, buf.p, &n, nullptr, &st) ==
+              LORES_OK);
+        g_launches.clear();
+        CHECK(step(st, x, 1, 1) == LORES_OK);
+        CHECK(g_launches.v.size() == 2);
+        for (auto &l : g_launches.v) CHECK(l.kind == "window_pc" && l.win_pc == 1 && l.wpos == 1);
+        g_launches.clear();
+        CHECK(step(st, x, 2, 0) == LORES_EINVAL);
+        CHECK(g_launches.v.empty());
+        Buf out(1 << 20);
+        CHECK(lores_dequant_state(st, (float *)out.p, nullptr) == LORES_OK);
+        CHECK(g_launches.v.size() == 2);
+        for (auto &l : g_launches.v) CHECK(l.kind == "window_dequant" && l.win_pc == 1);
+        CHECK(step(st, x, 2, 1) == LORES_OK);
+        CHECK(step(st, x, 3, 1) == LORES_OK);
+        lores_layout lay;
+        CHECK(lores_state_layout(st, &lay) == LORES_OK && lay.window_fill == 0);
+        g_launches.clear();
+        CHECK(step(st, x, 4, 0) == LORES_OK);              // a new window: a scalar decay again
+        for (auto &l : g_launches.v) CHECK(l.kind == "window" && l.win_pc == 0);
         lores_state_free(st);
     }
     // launch errors: an error left on the thread by earlier work is not the

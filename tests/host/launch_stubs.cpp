@@ -27,7 +27,7 @@ namespace lores {
 static hipError_t rec(const char *kind, int p0, int p1, const StepMeta &m) {
     const int Hc[2] = {m.cls[0].Hc, m.cls[1].Hc};
     const int groups[2] = {m.cls[0].groups, m.cls[1].groups};
-    g_launches.add(kind, p0, p1, m.wpos, m.window, m.n_cls, m.n_rb, Hc, groups);
+    g_launches.add(kind, p0, p1, m.wpos, m.window, m.n_cls, m.n_rb, Hc, groups, m.win_pc);
     if (g_fail_next_launch) {
         g_fail_next_launch = false;
         g_sticky_error = hipErrorLaunchFailure;
@@ -55,9 +55,10 @@ LORES_STUB(launch_step_key_int6, LORES_INT6, -2)
 LORES_STUB(launch_step_key_fp8, LORES_FP8, -2)
 #undef LORES_STUB
 
-hipError_t launch_window_step(int prec, int, bool, bool, bool key, const StepPtrs &,
+hipError_t launch_window_step(int prec, int, bool, bool, bool key, bool pc, const StepPtrs &,
                               const StepMeta &m, hipStream_t) {
-    return rec(key ? "window_key" : "window", prec, -1, m);
+    return rec(key ? (pc ? "window_key_pc" : "window_key") : (pc ? "window_pc" : "window"), prec,
+               -1, m);
 }
 hipError_t launch_dequant(int prec, int, const uint8_t *, const float *, float *,
                           const StepMeta &m, hipStream_t, bool) {

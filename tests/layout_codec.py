@@ -152,15 +152,16 @@ def window_ranges(layout, c, unit):
 
 
 def read_window(buf_host, layout, c, unit):
-    """A unit's window buffer as {"g": [W-1, d_v], "k": [W-1, d_k], "alpha": [W-1]}:
-    slots of g [W-1][d_v_pad], then k [W-1][d_k], then alpha [W-1] (fp32)."""
+    """A unit's window buffer as {"g": [W-1, d_v], "k": [W-1, d_k], "alpha": [W-1, d_k]}:
+    slots of g [W-1][d_v_pad], then k [W-1][d_k], then alpha [W-1][d_k] (fp32;
+    a scalar decay in element 0)."""
     W, dvp, dk, dv = layout["window"], layout["d_v_pad"], layout["d_k"], layout["d_v"]
     s, n = window_ranges(layout, c, unit)
     f = buf_host[s:s + n].view(np.float32)
     ns = W - 1
     g = f[:ns * dvp].reshape(ns, dvp)[:, :dv].copy()
     k = f[ns * dvp:ns * (dvp + dk)].reshape(ns, dk).copy()
-    a = f[ns * (dvp + dk):ns * (dvp + dk + 1)].copy()
+    a = f[ns * (dvp + dk):ns * (dvp + 2 * dk)].reshape(ns, dk).copy()
     return {"g": g, "k": k, "alpha": a}
 
 
@@ -173,5 +174,5 @@ def write_window(buf_host, layout, c, unit, win):
     g[:, :dv] = win["g"]
     f[:ns * dvp] = g.reshape(-1)
     f[ns * dvp:ns * (dvp + dk)] = np.asarray(win["k"], np.float32).reshape(-1)
-    f[ns * (dvp + dk):ns * (dvp + dk + 1)] = win["alpha"]
+    f[ns * (dvp + dk):ns * (dvp + 2 * dk)] = np.asarray(win["alpha"], np.float32).reshape(-1)
     buf_host[s:s + n] = f.view(np.uint8)

@@ -416,7 +416,7 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
                 c, prev, pbuf, xsel["q"][rows], xsel["k"][rows], xsel["v"][rows],
                 xsel["alpha"][rows], xsel["beta"][rows], w.delta, seed, t, bs, hs, W,
                 rounding=rounding, axis=axis)
-            Xcur = owin.replay(c, new, nbuf, 0 if p == W else p, axis)
+            Xcur = owin.replay(c, new, nbuf, 0 if p == W else p, axis, xsel["alpha"].ndim == 2)
             scale = _readout_scale(Xcur)
             o_rel, o_sc = o_errors(o_sel[rows], o_ref, Xcur)
             stats.o_err_q = max(stats.o_err_q, float(o_rel.max()))
@@ -430,7 +430,10 @@ def run_window_parity(w, T, W, head_prec, B=None, units=None, seed=0, init="rand
                 assert np.array_equal(gpu["scales"].view(np.uint32), prev["scales"].view(np.uint32))
                 gw = _stack([lc.read_window(buf_host, lay, c, u) for u in units_idx])
                 assert np.array_equal(gw["k"][:, p - 1], nbuf["k"][:, p - 1]), (t, c)
-                assert np.array_equal(gw["alpha"][:, p - 1], nbuf["alpha"][:, p - 1]), (t, c)
+                # a scalar decay is kept in element 0 of the slot's d_k values
+                na = xsel["alpha"].ndim == 1
+                assert np.array_equal(gw["alpha"][:, p - 1, :1] if na else gw["alpha"][:, p - 1],
+                                      nbuf["alpha"][:, p - 1, :1] if na else nbuf["alpha"][:, p - 1]), (t, c)
                 bound = (np.abs(xsel["v"][rows]) + scale[:, None]) * np.abs(xsel["beta"][rows])[:, None]
                 ge = np.abs(gw["g"][:, p - 1].astype(np.float64) - nbuf["g"][:, p - 1]) / \
                     np.maximum(bound, 1e-30)

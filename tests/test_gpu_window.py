@@ -116,6 +116,39 @@ def test_full_size_c5_window4(axis):
     s.check()
 
 
+@pytest.mark.parametrize("prec", [2, 3, 4, 5])
+@pytest.mark.parametrize("W,dk,dv,delta,axis", [(3, 64, 64, 1, "value"), (4, 128, 100, 1, "value"),
+                                               (4, 128, 128, 0, "value"), (3, 128, 100, 1, "key"),
+                                               (5, 64, 200, 1, "key")])
+def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
+    """Windows whose tokens carry one decay per key channel (the diagonal
+    decay of the recurrence): the in-window readouts from the stored state
+    and the buffer, the buffered (g, k, alpha), and the window end's replay
+    and requantization."""
+    w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, delta=delta, decay="kda_channel")
+    log(f"case: channel-decay window W={W} prec={prec} dk={dk} dv={dv} delta={delta} "
+        f"{axis} scales, {w.T} steps")
+    s = run_window_parity(w, T=w.T, W=W, head_prec=[prec] * w.H, axis=axis)
+    log(s.summary())
+    s.check()
+
+
+def test_full_size_c4_window4():
+    # the KDA-style workload (per-channel decay, 8 bf16 + 24 int8 heads): its
+    # int8 heads windowed, its bf16 heads stepping every token
+    w = get_workload("C4")
+    inputs = make_inputs(w, 0, DEV, T=8)
+    head_prec = head_precisions(w, inputs)
+    g = np.random.default_rng(6)
+    scaled = [h for h in range(w.H) if head_prec[h] == 2]   # the windowed heads
+    units = sorted({(int(g.integers(w.B)), int(g.choice(scaled))) for _ in range(64)})
+    log(f"case: window W=4 on the full C4 batch (per-channel decay), {len(units)} sampled "
+        "int8 units, 8 steps")
+    s = run_window_parity(w, T=8, W=4, head_prec=head_prec, units=units, inputs=inputs)
+    log(s.summary())
+    s.check()
+
+
 def test_window_one_is_the_plain_state():
     w = C1.scaled(B=2, H=4, dk=128, dv=96, T=4)
     log("case: lores_state_alloc_window(W = 1) steps like lores_state_alloc")
@@ -131,14 +164,17 @@ def test_window_one_is_the_plain_state():
 
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
-@pytest.mark.parametrize("axis", ["value", "key"])
-def test_dequant_replays_the_buffer(prec, axis):
+@pytest.mark.parametrize("axis,decay", [("value", "softplus_step"), ("key", "softplus_step"),
+                                        ("value", "kda_channel"), ("key", "kda_channel")])
+def test_dequant_replays_the_buffer(prec, axis, decay):
     """Inside a window lores_dequant_state returns the current state: the
     stored state followed by the buffered tokens' fp32 recurrence, bit for
-    bit against the oracle's replay of the same (oracle-written) buffer."""
+    bit against the oracle's replay of the same (oracle-written) buffer, for
+    scalar and per-channel decays."""
     W, B, H, dk, dv, n = 6, 2, 3, 128, 72, 3
-    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=n)
-    log(f"case: window dequant after {n} buffered tokens, prec={prec} axis={axis}")
+    pc = decay == "kda_channel"
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=n, decay=decay)
+    log(f"case: window dequant after {n} buffered tokens, prec={prec} axis={axis} decay={decay}")
     st = lores.lores_state_alloc(B, H, dk, dv, [prec] * H, device=DEV, window=W,
                                  scale_axis=lores.LORES_SCALE_KEY if axis == "key" else 0)
     x = make_inputs(w, 1, DEV, T=n)
@@ -157,29 +193,32 @@ def test_dequant_replays_the_buffer(prec, axis):
             s = random_unit_state(prec, dv, dk, g, axis)
             win = {"g": g.standard_normal((W - 1, dv)).astype(np.float32),
                    "k": (g.standard_normal((W - 1, dk)) / np.sqrt(dk)).astype(np.float32),
-                   "alpha": g.uniform(0.8, 1.0, W - 1).astype(np.float32)}
+                   "alpha": g.uniform(0.8, 1.0, (W - 1, dk)).astype(np.float32)}
             u = b * lay["n_class"][prec] + slot[h]
             lc.write_unit(host, lay, prec, u, s)
             lc.write_window(host, lay, prec, u, win)
             want[b, h] = owin.replay(prec, {k: v[None] for k, v in s.items()},
-                                     {k: v[None] for k, v in win.items()}, n, axis)[0]
+                                     {k: v[None] for k, v in win.items()}, n, axis, pc)[0]
     st.buf.copy_(torch.from_numpy(host))
     got = lores.lores_dequant_state(st).cpu().numpy()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
 def test_windowed_state_contract():
-    log("case: windowed state errors: per-channel alpha, out-of-order t, quant_state resets")
+    log("case: windowed state errors: the decay kind inside a window, out-of-order t, "
+        "quant_state resets")
     w = C1.scaled(B=2, H=2, dk=64, dv=64, T=3)
     x = make_inputs(w, 0, DEV, T=3)
     st = lores.lores_state_alloc(2, 2, 64, 64, [2, 3], device=DEV, window=4)
     xs = {k: v[0] for k, v in x.items()}
     pc = torch.full((2, 2, 64), 0.9, device=DEV)
-    with pytest.raises(lores.LoresError, match="EUNSUPPORTED"):
-        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], pc, xs["beta"], 1, 0, 1)
     with pytest.raises(lores.LoresError, match="EINVAL"):
         lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 2)
     lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], xs["alpha"], xs["beta"], 1, 0, 1)
+    assert lores.lores_state_layout(st)["window_fill"] == 1
+    # the window's tokens share one kind of decay
+    with pytest.raises(lores.LoresError, match="EINVAL"):
+        lores.lores_decode_step(st, xs["q"], xs["k"], xs["v"], pc, xs["beta"], 1, 0, 2)
     assert lores.lores_state_layout(st)["window_fill"] == 1
     X = torch.zeros(2, 2, 64, 64, device=DEV)
     lores.lores_quant_state(st, X, 0)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lores_lib):
 def test_spec_version(lores_lib):
     hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
     v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
-    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 5
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 6
 
 
 def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
@@ -59,7 +59,7 @@ def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
             off += B * hc * (dk if key else dvp) * 4
             if window > 1:                         # W - 1 slots of g, k, alpha per unit
                 off = (off + 255) // 256 * 256
-                off += B * hc * (((window - 1) * (dvp + dk + 1) * 4 + 15) // 16 * 16)
+                off += B * hc * (((window - 1) * (dvp + 2 * dk) * 4 + 15) // 16 * 16)
     return (off + 255) // 256 * 256
 
 
