@@ -22,7 +22,9 @@ SOURCES = ["lores_api.cpp", "lores_aux.hip", "lores_step_int8.hip", "lores_step_
            "lores_step_int6.hip", "lores_step_fp8.hip", "lores_step_bf16.hip", "lores_step_fp32.hip",
            "lores_step_int8_int4.hip", "lores_step_int4_int6.hip", "lores_step_bf16_int8.hip",
            "lores_step_bf16_int4.hip", "lores_step_key_int8.hip", "lores_step_key_int4.hip",
-           "lores_step_key_int6.hip", "lores_step_key_fp8.hip", "lores_window.hip"]
+           "lores_step_key_int6.hip", "lores_step_key_fp8.hip", "lores_window.hip",
+           "lores_window_int8.hip", "lores_window_int4.hip", "lores_window_int6.hip",
+           "lores_window_fp8.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

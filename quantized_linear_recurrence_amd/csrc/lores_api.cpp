@@ -289,9 +289,6 @@ int lores_state_alloc_window(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                              void *d_buf, size_t *bytes, void *stream, lores_state **out) {
     if (window < 1 || window > LORES_MAX_WINDOW)
         return fail(LORES_EINVAL, "window must be in [1, %d] (got %d)", LORES_MAX_WINDOW, window);
-    if (window > 1 && d_k != 64 && d_k != 128)
-        return fail(LORES_EUNSUPPORTED, "windowed states are built for d_k = 64 and 128 (got %d)",
-                    d_k);
     return alloc_impl(B, H, d_k, d_v, head_prec, scale_axis, window, d_buf, bytes, stream, out);
 }
 

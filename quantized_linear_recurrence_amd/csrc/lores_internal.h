@@ -86,6 +86,20 @@ hipError_t launch_step_key_fp8(int, bool, bool, bool, const StepPtrs &, const St
 hipError_t launch_window_step(int prec, int dk, bool delta, bool in_bf16, bool key, bool pc,
                               const StepPtrs &p, const StepMeta &m, hipStream_t s);
 
+// The per-precision window launchers behind the two above
+// (lores_window_<prec>.hip).
+#define LORES_WINDOW_PREC(N)                                                                   \
+    hipError_t launch_window_step_##N(int dk, bool delta, bool in_bf16, bool key, bool pc,     \
+                                      const StepPtrs &p, const StepMeta &m, hipStream_t s);    \
+    hipError_t launch_window_dequant_##N(int dk, bool key, const uint8_t *codes,              \
+                                         const float *scales, const float *win, float *out,    \
+                                         const StepMeta &m, hipStream_t s);
+LORES_WINDOW_PREC(int8)
+LORES_WINDOW_PREC(int4)
+LORES_WINDOW_PREC(int6)
+LORES_WINDOW_PREC(fp8)
+#undef LORES_WINDOW_PREC
+
 // Dequant uses the same StepMeta with one class; `key`: key-column scales.
 hipError_t launch_dequant(int prec, int dk, const uint8_t *codes, const float *scales,
                           float *out, const StepMeta &m, hipStream_t s, bool key);

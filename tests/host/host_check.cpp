@@ -79,10 +79,6 @@ int main() {
                             CHECK(rc == LORES_EUNSUPPORTED);
                             continue;
                         }
-                        if (W > 1 && !key_ok) {
-                            CHECK(rc == LORES_EUNSUPPORTED);
-                            continue;
-                        }
                         CHECK(rc == LORES_OK);
                         Buf buf(n);
                         lores_state *st = nullptr;

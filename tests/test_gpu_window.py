@@ -25,7 +25,7 @@ DEV = "cuda"
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("W,dk,dv,delta", [(2, 64, 64, 1), (4, 128, 100, 1), (3, 128, 128, 0),
-                                           (5, 64, 200, 1)])
+                                           (5, 64, 200, 1), (3, 32, 70, 1), (4, 96, 128, 1)])
 def test_each_scaled_class(prec, W, dk, dv, delta):
     w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, delta=delta)
     log(f"case: window W={W} prec={prec} B=3 H=4 dk={dk} dv={dv} delta={delta}, "
@@ -119,7 +119,8 @@ def test_full_size_c5_window4(axis):
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("W,dk,dv,delta,axis", [(3, 64, 64, 1, "value"), (4, 128, 100, 1, "value"),
                                                (4, 128, 128, 0, "value"), (3, 128, 100, 1, "key"),
-                                               (5, 64, 200, 1, "key")])
+                                               (5, 64, 200, 1, "key"), (3, 96, 64, 1, "value"),
+                                               (4, 32, 128, 1, "value")])
 def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
     """Windows whose tokens carry one decay per key channel (the diagonal
     decay of the recurrence): the in-window readouts from the stored state

@@ -165,8 +165,8 @@ def test_key_axis_layout_and_limits(lores_lib):
 
 
 def test_window_layout_and_limits(lores_lib):
-    """Windowed states: the window segment per scaled class, W in [1, 16],
-    d_k 64 or 128 when W > 1 (size queries only)."""
+    """Windowed states: the window segment per scaled class, W in [1, 16];
+    key-column windows at d_k 64 or 128 (size queries only)."""
     L = lores._lib.lib()
     hp = (ctypes.c_uint8 * 4)(2, 3, 1, 5)
     n = ctypes.c_size_t(0)
@@ -177,7 +177,11 @@ def test_window_layout_and_limits(lores_lib):
     for W in (0, 17, -1):
         assert L.lores_state_alloc_window(5, 4, 128, 100, hp, 0, W, None, ctypes.byref(n), None,
                                           None) == lores._lib.LORES_EINVAL
-    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 0, 4, None, ctypes.byref(n), None,
+    for dk in (32, 96):
+        assert L.lores_state_alloc_window(5, 4, dk, 100, hp, 0, 4, None, ctypes.byref(n), None,
+                                          None) == 0
+        assert n.value == _layout_bytes(5, 4, dk, 100, [2, 3, 1, 5], window=4)
+    assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 1, 4, None, ctypes.byref(n), None,
                                       None) == lores._lib.LORES_EUNSUPPORTED
     assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 0, 1, None, ctypes.byref(n), None,
                                       None) == 0
