@@ -29,6 +29,10 @@
  *     Device work is enqueued asynchronously on it; inputs must stay alive
  *     and unmodified until that work has run.
  *   - Calls on one lores_state handle are not re-entrant across streams.
+ *   - LORES_EHIP reports that a launch of this call failed.  Before each of
+ *     its launches the library consumes any HIP error left on the calling
+ *     thread by earlier work, so such an error is never reported as this
+ *     call's (and is no longer visible to the caller afterwards).
  */
 #ifndef LORES_H
 #define LORES_H
@@ -121,9 +125,10 @@ typedef struct lores_state lores_state;
  * with key-column scales).  A row of all-zero bytes with scale 0 also reads
  * as zero, so a zero-filled buffer is S = 0.
  * A unit's window block holds W - 1 token slots: g [W-1][d_v_pad] fp32 (the
- * write vector of the token), then k [W-1][d_k] fp32, then alpha [W-1] fp32,
- * the whole block padded to 16 bytes.  Slot tau - 1 holds token tau of the
- * current window (lores_state_alloc_window).
+ * write vector of the token), then k [W-1][d_k] fp32, then alpha [W-1][d_k]
+ * fp32 (the token's decay per key channel; a scalar decay in element 0, the
+ * others unused), the whole block padded to 16 bytes.  Slot tau - 1 holds
+ * token tau of the current window (lores_state_alloc_window).
  */
 typedef struct {
     int32_t B, H, d_k, d_v, d_v_pad;
@@ -142,8 +147,15 @@ typedef struct {
 
 /*
  * lores_state_alloc - plan the packed layout and bind a caller-owned buffer.
+ * The state of every (sequence, head) unit is S in R^{d_v x d_k} of the
+ * general recurrence ("Introduction and Theoretical Foundation"), held in
+ * the precision head_prec assigns to its head (decay-based mixed precision,
+ * "Intra-State Quantization (Section 4)") with one scale per value row (the
+ * same section, scale grouping), starting from S_0 = 0.
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
- *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128},
+ *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128} (a multiple
+ *               of 32 above 128 returns LORES_EUNSUPPORTED: the step keeps a
+ *               row of d_k fp32 values in one lane's registers),
  *               1 <= d_v <= LORES_MAX_DV
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
@@ -166,11 +178,10 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * and the same codes, rounding and draws otherwise (the comparison grouping
  * of "Intra-State Quantization (Section 4)", Scale Grouping and Proposition
  * 1).  A step then dequantizes S'_ij = fl(c_ij * fl(s_j * alpha_j)).
- * LORES_SCALE_KEY is built for d_k in {64, 128} and d_v in [1, 128] or
- * [193, 256] (a unit's row blocks must share one work-group of four
- * wavefronts); other shapes return LORES_EUNSUPPORTED.  A key-column state
- * runs one launch per precision class (no fused pairs).  LORES_EINVAL for
- * any other scale_axis.
+ * LORES_SCALE_KEY is built for d_k in {64, 128} and every d_v (the column
+ * maxima run over 64-column groups); d_k 32 or 96 return
+ * LORES_EUNSUPPORTED.  A key-column state runs one launch per precision
+ * class (no fused pairs).  LORES_EINVAL for any other scale_axis.
  */
 int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                            const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
@@ -188,19 +199,24 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * p = (t - 1) mod W + 1 < W computes g, o from X_0 and the buffered tokens
  * and appends (g, k, alpha) to the buffer; the step at p = W rebuilds the
  * state by the fp32 recurrence (S'_1 = fl(c fl(s alpha_1)), then
- * U_tau = fma(g_tau, k_tau, S'_tau), S'_tau = fl(U_{tau-1} alpha_tau)), steps
- * it and requantizes it as lores_decode_step does.  W = 1 is
+ * U_tau = fma(g_tau, k_tau, S'_tau), S'_tau = fl(U_{tau-1} alpha_tau), with a
+ * decay per key channel taken column by column), steps it and requantizes
+ * it as lores_decode_step does.  W = 1 is
  * lores_state_alloc_axis.  fp32 and bf16 heads step every token as usual.
  * With key-column scales (PACE shares scales within a column), s_i above is
  * the column's s_j and the window's end takes the column maxima.
  *   scale_axis  LORES_SCALE_VALUE or LORES_SCALE_KEY (as lores_state_alloc_axis)
  *   window      W, 1 <= W <= LORES_MAX_WINDOW
- * Built for d_k in {64, 128} when W > 1 (LORES_EUNSUPPORTED otherwise).
+ * Built for every d_k with value-row scales and for d_k in {64, 128} with
+ * key-column scales (LORES_EUNSUPPORTED otherwise).
  * Steps on a windowed state must come in order (t = 1, 2, ... from the
  * allocation or a lores_quant_state; the handle counts the buffered tokens
  * and lores_decode_step returns LORES_EINVAL for a step t whose window
- * position does not follow them), with a scalar alpha (alpha_per_channel = 0,
- * else LORES_EUNSUPPORTED).  Each scaled class runs one launch per step.
+ * position does not follow them).  The decay may be a scalar per head or
+ * one value per key channel (alpha_per_channel), the same kind for every
+ * token of a window: a step inside a window whose kind differs from the
+ * buffered tokens' returns LORES_EINVAL.  Each scaled class runs one launch
+ * per step.
  * The count is kept on the host: a captured graph of steps on a windowed
  * state replays correctly when it covers whole windows.
  */
@@ -259,7 +275,14 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
                            const uint8_t *tier_prec, int32_t n_tiers, uint8_t *head_prec);
 
 /*
- * lores_decode_step - one decode step t for all B x H units, in place.
+ * lores_decode_step - one decode step t for all B x H units, in place: the
+ * general recurrence S_t = S_{t-1} diag(alpha_t)(I - delta beta_t k_t k_t^T)
+ * + beta_t v_t k_t^T and the readout o_t = S_t q_t ("Introduction and
+ * Theoretical Foundation"), on a state that is dequantized, updated and
+ * requantized each step ("Intra-State Quantization Approach", property 3)
+ * with a fresh scale per value row and stochastic rounding ("Intra-State
+ * Quantization (Section 4)": scale grouping, Proposition 1, Rounding,
+ * Proposition 3).
  *   q, k        device [B][H][d_k]; fp32, or bfloat16 if in_bf16 != 0
  *   v           device [B][H][d_v]; same dtype as q and k
  *   alpha       device fp32 decay: [B][H] (scalar per head) or, if
@@ -301,7 +324,10 @@ int lores_decode_step(lores_state *st, const void *q, const void *k, const void 
 int lores_step_launches(const lores_state *st, int32_t *n);
 
 /*
- * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32,
+ * lores_dequant_state - packed state -> device out [B][H][d_v][d_k] fp32: the
+ * dequantization step of "Intra-State Quantization Approach" (the state read
+ * back at full precision between steps; for inspection, checkpoints and the
+ * error measurements of "Intra-State Quantization (Section 4)"),
  * value = scale * code for int heads (the row's or the column's scale), the
  * stored value for bf16 / fp32 heads.  For a windowed state with buffered
  * tokens: the current state, the stored state followed by the buffered
