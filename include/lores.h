@@ -178,10 +178,9 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * and the same codes, rounding and draws otherwise (the comparison grouping
  * of "Intra-State Quantization (Section 4)", Scale Grouping and Proposition
  * 1).  A step then dequantizes S'_ij = fl(c_ij * fl(s_j * alpha_j)).
- * LORES_SCALE_KEY is built for d_k in {64, 128} and every d_v (the column
- * maxima run over 64-column groups); d_k 32 or 96 return
- * LORES_EUNSUPPORTED.  A key-column state runs one launch per precision
- * class (no fused pairs).  LORES_EINVAL for any other scale_axis.
+ * LORES_SCALE_KEY is built for every d_k and d_v that lores_state_alloc
+ * accepts.  A key-column state runs one launch per precision class (no
+ * fused pairs).  LORES_EINVAL for any other scale_axis.
  */
 int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
                            const uint8_t *head_prec, int32_t scale_axis, void *d_buf,
@@ -207,8 +206,8 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * the column's s_j and the window's end takes the column maxima.
  *   scale_axis  LORES_SCALE_VALUE or LORES_SCALE_KEY (as lores_state_alloc_axis)
  *   window      W, 1 <= W <= LORES_MAX_WINDOW
- * Built for every d_k with value-row scales and for d_k in {64, 128} with
- * key-column scales (LORES_EUNSUPPORTED otherwise).
+ * Built for every d_k and d_v that lores_state_alloc accepts, on either
+ * scale axis.
  * Steps on a windowed state must come in order (t = 1, 2, ... from the
  * allocation or a lores_quant_state; the handle counts the buffered tokens
  * and lores_decode_step returns LORES_EINVAL for a step t whose window

@@ -123,14 +123,18 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     }
     const CodeRows io(codes + unit * cd.unit_bytes, cd.unit_bytes, row, dv_pad);
     if constexpr (KEY) {
-        __shared__ float cmax[2 * kWavesPerGroup * DK];     // maxima, staging
-        float cm[DK / 64], snew[DK / 64], inv[DK / 16];
+        constexpr int DKP = 64 * key_groups<DK>();          // padded to whole 64-column groups
+        __shared__ float cmax[2 * kWavesPerGroup * DKP];    // maxima, staging
+        float cm[key_groups<DK>()], snew[key_groups<DK>()], inv[DK / 16];
         col_absmax<DK>(U, cm);
-        key_scales<DK>(cm, cmax, cmax + kWavesPerGroup * DK, wv, rb, meta.n_rb, Prec<PREC>::R,
+        key_scales<DK>(cm, cmax, cmax + kWavesPerGroup * DKP, wv, rb, meta.n_rb, Prec<PREC>::R,
                        snew, inv);
         if (rb == 0) {
 #pragma unroll
-            for (int t = 0; t < DK / 64; ++t) scales[unit * DK + key_col(t, lane)] = snew[t];
+            for (int t = 0; t < key_groups<DK>(); ++t) {
+                const int col = key_col(t, lane);
+                if (col < DK) scales[unit * DK + col] = snew[t];
+            }
         }
         requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr, inv);
     } else {
@@ -151,7 +155,9 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
             const int gw = key_group_waves(m.n_rb);
             const dim3 kgrid((m.cls[0].Hc * m.n_rb + gw - 1) / gw, m.B), kblock(64 * gw);
             switch (dk) {
+                case 32: hipLaunchKernelGGL((lores_quant_kernel<32, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 default: return hipErrorInvalidValue;
             }
@@ -189,7 +195,9 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
     if constexpr (has_scale<PREC>()) {
         if (key) {
             switch (dk) {
+                case 32: hipLaunchKernelGGL((lores_dequant_kernel<32, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 default: return hipErrorInvalidValue;
             }

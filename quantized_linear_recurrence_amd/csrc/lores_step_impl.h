@@ -533,22 +533,27 @@ __device__ __forceinline__ float xmax_pair(float a, float b, bool hi) {
 // v_permlane16 swaps; bits 5, 4), lane ^ 1, lane ^ 2, lane ^ 8 (bits 0, 1, 3).
 // Depth first, 16 columns at a time, so only a few partial results are live.
 // Register t of lane L then holds the maximum of column key_col(t, L).
+template <int DK> constexpr int key_groups() { return (DK + 63) / 64; }
+
 __device__ __forceinline__ int key_col(int t, int L) {
     return 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + (L & 1) * 8 +
            ((L >> 4) & 1) * 4 + ((L >> 5) & 1) * 2 + ((L >> 2) & 1);
 }
 
+// With d_k = 32 or 96 the last group holds 32 columns; its other 32 read as
+// zeros, which leaves every real column's maximum as it is.
 template <int DK>
-__device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[DK / 64]) {
-    static_assert(DK % 64 == 0, "key-column scales need d_k = 64 or 128");
+__device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[key_groups<DK>()]) {
+    static_assert(DK % 32 == 0, "key-column scales need d_k a multiple of 32");
     const int lane = threadIdx.x & 63;
     const bool h0 = lane & 1, h1 = lane & 2, h2 = lane & 4, h3 = lane & 8;
+    const float zeros[16] = {};
 #pragma unroll
-    for (int t = 0; t < DK / 64; ++t) {
+    for (int t = 0; t < key_groups<DK>(); ++t) {
         float g[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float *u = &U[64 * t + 16 * q];
+            const float *u = 64 * t + 16 * q < DK ? &U[64 * t + 16 * q] : zeros;
             float s[8], o[8], y[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -593,22 +598,26 @@ __device__ __forceinline__ void lds_barrier() {
 // (0 for a zero column).  inv goes through the wavefront's own slot of
 // `stage` to the row-vector form the requantization reads: register i of
 // invrow holds column 16 i + lane % 16.
+// `part` and `stage` hold 64 key_groups<DK>() columns per wavefront (the
+// padding columns of d_k = 32, 96 read as zero columns).
 template <int DK>
-__device__ __forceinline__ void key_scales(const float (&cm)[DK / 64], float *part, float *stage,
-                                           int wv, int rb, int n_rb, float R,
-                                           float (&snew)[DK / 64], float (&invrow)[DK / 16]) {
+__device__ __forceinline__ void key_scales(const float (&cm)[key_groups<DK>()], float *part,
+                                           float *stage, int wv, int rb, int n_rb, float R,
+                                           float (&snew)[key_groups<DK>()],
+                                           float (&invrow)[DK / 16]) {
+    constexpr int DKP = 64 * key_groups<DK>();
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < DK / 64; ++t) part[wv * DK + 64 * t + lane] = cm[t];
+    for (int t = 0; t < key_groups<DK>(); ++t) part[wv * DKP + 64 * t + lane] = cm[t];
     // a unit of one row block reads back only its own maxima
     if (n_rb > 1) lds_barrier();
     else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const float *base = part + (wv - rb) * DK + lane;
-    float *mine = stage + wv * DK;
+    const float *base = part + (wv - rb) * DKP + lane;
+    float *mine = stage + wv * DKP;
 #pragma unroll
-    for (int t = 0; t < DK / 64; ++t) {
+    for (int t = 0; t < key_groups<DK>(); ++t) {
         float m = base[64 * t];
-        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DK + 64 * t]);
+        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DKP + 64 * t]);
         snew[t] = m / R;
         mine[key_col(t, lane)] = rd_div(R, m);
     }
@@ -919,8 +928,9 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 // k and q hold the raw 16 bits (from in_raw) until `run` widens them.
 // With key-column scales, sl and al hold the unit's column scales and a
 // per-channel alpha in lane form (lane L: columns 64 t + L), two registers
-// each at d_k = 128; the row vectors of their product are built at the start
-// of the task.
+// each at d_k = 128 (one per 64 columns, the last one padded with zeros at
+// d_k = 32, 96); the row vectors of their product are built at the start of
+// the task.
 // WPC: the end of a window whose tokens carry one decay per key channel:
 // av (al with key-column scales) holds the window's first token's decays and
 // avt this step's, as row vectors.
@@ -929,7 +939,7 @@ struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
     float alpha_t = 1.0f;              // window end: this step's decay (alpha is token 1's)
     float kv[NV], qv[NV], av[KEY ? 1 : NV];
-    float sl[KEY ? NV / 4 : 1], al[KEY ? NV / 4 : 1];
+    float sl[KEY ? (NV + 3) / 4 : 1], al[KEY ? (NV + 3) / 4 : 1];
     float avt[WPC ? NV : 1];
 };
 
@@ -1004,10 +1014,15 @@ struct TaskStream {
                   (long)(meta.window - 1) * (meta.dv_pad + DK);
         if constexpr (KEY) {
 #pragma unroll
-            for (int t = 0; t < NV / 4; ++t) {
-                in.sl[t] = scales[unit * DK + 64 * t + (threadIdx.x & 63)];
-                if constexpr (PC && WEND) in.al[t] = wa1[64 * t + (threadIdx.x & 63)];
-                else if constexpr (PC) in.al[t] = alphap[bh * DK + 64 * t + (threadIdx.x & 63)];
+            for (int t = 0; t < key_groups<DK>(); ++t) {
+                const int col = 64 * t + (threadIdx.x & 63);
+                in.sl[t] = 0.0f;
+                in.al[t] = 1.0f;
+                if (64 * t + 64 <= DK || col < DK) {
+                    in.sl[t] = scales[unit * DK + col];
+                    if constexpr (PC && WEND) in.al[t] = wa1[col];
+                    else if constexpr (PC) in.al[t] = alphap[bh * DK + col];
+                }
             }
         } else if constexpr (has_scale<PREC>()) {
             in.s = scales[unit * dv_pad + lrow];
@@ -1059,10 +1074,12 @@ struct TaskStream {
         float sig[KEY ? NV : 1];
         if constexpr (KEY) {
             const int lane = threadIdx.x & 63;
-            float *mine = lds + 2 * kWavesPerGroup * DK +
-                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DK;
+            constexpr int DKP = 64 * key_groups<DK>();
+            float *mine = lds + 2 * kWavesPerGroup * DKP +
+                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DKP;
 #pragma unroll
-            for (int t = 0; t < NV / 4; ++t) mine[64 * t + lane] = in.sl[t] * (PC ? in.al[t] : alpha_s);
+            for (int t = 0; t < key_groups<DK>(); ++t)
+                mine[64 * t + lane] = in.sl[t] * (PC ? in.al[t] : alpha_s);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
             for (int i = 0; i < NV; ++i) sig[i] = mine[16 * i + (lane & 15)];
@@ -1265,15 +1282,18 @@ struct TaskStream {
         // ---- pass 3: requantize and store in place
         if constexpr (KEY) {
             // column maxima of the unit's rows, fresh column scales
-            float cm[DK / 64], snew[DK / 64], inv[NV];
+            constexpr int DKP = 64 * key_groups<DK>();
+            float cm[key_groups<DK>()], snew[key_groups<DK>()], inv[NV];
             col_absmax<DK>(U, cm);
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DK), lds + 2 * kWavesPerGroup * DK,
+            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DKP), lds + 2 * kWavesPerGroup * DKP,
                            wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv);
             if (rb == 0) {
 #pragma unroll
-                for (int t = 0; t < DK / 64; ++t)
-                    scales[unit * DK + key_col(t, threadIdx.x & 63)] = snew[t];
+                for (int t = 0; t < key_groups<DK>(); ++t) {
+                    const int col = key_col(t, threadIdx.x & 63);
+                    if (col < DK) scales[unit * DK + col] = snew[t];
+                }
             }
             requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr,
                                            inv);
@@ -1483,7 +1503,7 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
         // per sequence of its stride, as a working wave does (units of one
         // row block take no barrier at all).
         static_assert(P1 < 0, "key-column scales run one class per launch");
-        __shared__ float cmax[3 * kWavesPerGroup * DK];    // two maxima buffers, staging
+        __shared__ float cmax[3 * kWavesPerGroup * 64 * key_groups<DK>()];  // two maxima buffers, staging
         const int task = gx * key_group_waves(n_rb) + wv;
         if (task >= meta.cls[0].Hc * n_rb) {
             if (n_rb > 1)
@@ -1644,12 +1664,14 @@ hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs
     }
 }
 
-// key-column scales: one class per launch, d_k = 64 or 128
+// key-column scales: one class per launch
 template <int P0>
 hipError_t launch_classes_key(int dk, bool pc, bool delta, bool bf16, const StepPtrs &p,
                               const StepMeta &m, hipStream_t s) {
     switch (dk) {
+        case 32: return launch_dk<32, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 64: return launch_dk<64, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 96: return launch_dk<96, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, -1, true>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }

@@ -317,21 +317,14 @@ static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, bool pc,
                : window_dk<DK, PREC, true, false>(delta, bf16, p, m, s))                        \
          : (pc ? window_dk<DK, PREC, false, true>(delta, bf16, p, m, s)                         \
                : window_dk<DK, PREC, false, false>(delta, bf16, p, m, s)))
-#define LORES_WIN_PC(DK)                                                                        \
-    (key ? hipErrorInvalidValue                                                                 \
-         : (pc ? window_dk<DK, PREC, false, true>(delta, bf16, p, m, s)                         \
-               : window_dk<DK, PREC, false, false>(delta, bf16, p, m, s)))
-    // key-column scales are built for d_k = 64 and 128 (their column maxima
-    // run over 64-column groups)
     switch (dk) {
-        case 32: return LORES_WIN_PC(32);
+        case 32: return LORES_WIN_KEY_PC(32);
         case 64: return LORES_WIN_KEY_PC(64);
-        case 96: return LORES_WIN_PC(96);
+        case 96: return LORES_WIN_KEY_PC(96);
         case 128: return LORES_WIN_KEY_PC(128);
         default: return hipErrorInvalidValue;
     }
 #undef LORES_WIN_KEY_PC
-#undef LORES_WIN_PC
 }
 
 // The current state of one windowed class (lores_dequant_state): the stored
@@ -346,9 +339,9 @@ static hipError_t window_dequant_prec(int dk, bool key, const uint8_t *codes, co
     hipLaunchKernelGGL((lores_window_dequant_kernel<DK, PREC, KEY>), grid, block, 0, s, codes,   \
                        scales, win, out, m)
     switch (dk) {
-        case 32: if (key) return hipErrorInvalidValue; LORES_WD(32, false); break;
+        case 32: if (key) LORES_WD(32, true); else LORES_WD(32, false); break;
         case 64: if (key) LORES_WD(64, true); else LORES_WD(64, false); break;
-        case 96: if (key) return hipErrorInvalidValue; LORES_WD(96, false); break;
+        case 96: if (key) LORES_WD(96, true); else LORES_WD(96, false); break;
         case 128: if (key) LORES_WD(128, true); else LORES_WD(128, false); break;
         default: return hipErrorInvalidValue;
     }

@@ -34,7 +34,7 @@ def _sample_units(B, H, n, seed=0):
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 100), (64, 256), (128, 200), (128, 150),
-                                   (64, 192)])
+                                   (64, 192), (32, 64), (96, 100), (32, 200), (96, 150)])
 def test_each_scaled_class(prec, dk, dv):
     w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=4, delta=1)
     log(f"case: key columns prec={prec} B=3 H=4 dk={dk} dv={dv} delta=1, random initial state")
@@ -79,7 +79,8 @@ def test_full_size_sampled(name):
     s.check()
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 200), (64, 1), (128, 160)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 200), (64, 1), (128, 160), (32, 70),
+                                   (96, 256)])
 def test_quant_and_dequant_match_oracle(dk, dv):
     """lores_quant_state with key columns equals the oracle bit for bit (the
     column maxima span every row block of a unit), and lores_dequant_state

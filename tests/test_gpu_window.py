@@ -48,7 +48,8 @@ def test_longest_window(prec, dk, dv):
 
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
-@pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256), (3, 128, 180)])
+@pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256), (3, 128, 180),
+                                    (4, 32, 100), (3, 96, 200)])
 def test_key_column_windows(prec, W, dk, dv):
     """Windows over key-column scales (the PACE combination): the window end
     takes the column maxima of the replayed state."""
@@ -120,7 +121,8 @@ def test_full_size_c5_window4(axis):
 @pytest.mark.parametrize("W,dk,dv,delta,axis", [(3, 64, 64, 1, "value"), (4, 128, 100, 1, "value"),
                                                (4, 128, 128, 0, "value"), (3, 128, 100, 1, "key"),
                                                (5, 64, 200, 1, "key"), (3, 96, 64, 1, "value"),
-                                               (4, 32, 128, 1, "value")])
+                                               (4, 32, 128, 1, "value"), (3, 96, 100, 1, "key"),
+                                               (4, 32, 64, 0, "key")])
 def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
     """Windows whose tokens carry one decay per key channel (the diagonal
     decay of the recurrence): the in-window readouts from the stored state
@@ -167,15 +169,17 @@ def test_window_one_is_the_plain_state():
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("axis,decay", [("value", "softplus_step"), ("key", "softplus_step"),
                                         ("value", "kda_channel"), ("key", "kda_channel")])
-def test_dequant_replays_the_buffer(prec, axis, decay):
+@pytest.mark.parametrize("dk", [128, 96])
+def test_dequant_replays_the_buffer(prec, axis, decay, dk):
     """Inside a window lores_dequant_state returns the current state: the
     stored state followed by the buffered tokens' fp32 recurrence, bit for
     bit against the oracle's replay of the same (oracle-written) buffer, for
     scalar and per-channel decays."""
-    W, B, H, dk, dv, n = 6, 2, 3, 128, 72, 3
+    W, B, H, dv, n = 6, 2, 3, 72, 3
     pc = decay == "kda_channel"
     w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=n, decay=decay)
-    log(f"case: window dequant after {n} buffered tokens, prec={prec} axis={axis} decay={decay}")
+    log(f"case: window dequant after {n} buffered tokens, prec={prec} axis={axis} decay={decay} "
+        f"dk={dk}")
     st = lores.lores_state_alloc(B, H, dk, dv, [prec] * H, device=DEV, window=W,
                                  scale_axis=lores.LORES_SCALE_KEY if axis == "key" else 0)
     x = make_inputs(w, 1, DEV, T=n)

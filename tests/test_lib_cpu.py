@@ -140,9 +140,9 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
 
 
 def test_key_axis_layout_and_limits(lores_lib):
-    """Key-column scales: d_k scales per unit of a scaled class, the shapes
-    that are not built return LORES_EUNSUPPORTED, an unknown axis EINVAL
-    (size queries only: no device work)."""
+    """Key-column scales: d_k scales per unit of a scaled class at every
+    built d_k and d_v, an unknown axis EINVAL (size queries only: no device
+    work)."""
     L = lores._lib.lib()
     hp = (ctypes.c_uint8 * 3)(2, 3, 1)
     n = ctypes.c_size_t(0)
@@ -153,9 +153,10 @@ def test_key_axis_layout_and_limits(lores_lib):
     want = _layout_bytes(4, 3, 128, 100, [2, 3, 1], key=True)
     assert key_bytes == want, (key_bytes, want)
     assert val_bytes == _layout_bytes(4, 3, 128, 100, [2, 3, 1])
-    for dk, dv in ((96, 64), (32, 64)):
+    for dk, dv in ((96, 64), (32, 64), (96, 200), (32, 1)):
         assert L.lores_state_alloc_axis(2, 3, dk, dv, hp, 1, None, ctypes.byref(n), None,
-                                        None) == lores._lib.LORES_EUNSUPPORTED, (dk, dv)
+                                        None) == 0, (dk, dv)
+        assert n.value == _layout_bytes(2, 3, dk, dv, [2, 3, 1], key=True), (dk, dv)
     for dv in (1, 64, 65, 128, 150, 192, 193, 256):
         assert L.lores_state_alloc_axis(2, 3, 64, dv, hp, 1, None, ctypes.byref(n), None,
                                         None) == 0, dv
@@ -165,8 +166,9 @@ def test_key_axis_layout_and_limits(lores_lib):
 
 
 def test_window_layout_and_limits(lores_lib):
-    """Windowed states: the window segment per scaled class, W in [1, 16];
-    key-column windows at d_k 64 or 128 (size queries only)."""
+    """Windowed states: the window segment per scaled class, W in [1, 16],
+    with value-row or key-column scales at every built d_k (size queries
+    only)."""
     L = lores._lib.lib()
     hp = (ctypes.c_uint8 * 4)(2, 3, 1, 5)
     n = ctypes.c_size_t(0)
@@ -182,7 +184,8 @@ def test_window_layout_and_limits(lores_lib):
                                           None) == 0
         assert n.value == _layout_bytes(5, 4, dk, 100, [2, 3, 1, 5], window=4)
     assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 1, 4, None, ctypes.byref(n), None,
-                                      None) == lores._lib.LORES_EUNSUPPORTED
+                                      None) == 0
+    assert n.value == _layout_bytes(5, 4, 96, 100, [2, 3, 1, 5], key=True, window=4)
     assert L.lores_state_alloc_window(5, 4, 96, 100, hp, 0, 1, None, ctypes.byref(n), None,
                                       None) == 0
     # key-column windows: d_k scales per unit plus the window block
