@@ -187,6 +187,9 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, "key"][, window
     ("int4, window 8", 2048, 32, 128, 128, [3] * 32, 1, 8),
     ("int8+int4 (C5), window 8", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, 8),
     ("int8+int4 (C5), key columns, window 4", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, "key", 4),
+    ("int8, d_k 256 (split rows)", 1024, 32, 256, 128, [2] * 32, 1),
+    ("int4, d_k 256 (split rows)", 1024, 32, 256, 128, [3] * 32, 1),
+    ("int8+int4, d_k 256 (one launch per class)", 1024, 32, 256, 128, [2] * 16 + [3] * 16, 1),
 ]
 
 

@@ -153,10 +153,12 @@ typedef struct {
  * "Intra-State Quantization (Section 4)") with one scale per value row (the
  * same section, scale grouping), starting from S_0 = 0.
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
- *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128} (a multiple
- *               of 32 above 128 returns LORES_EUNSUPPORTED: the step keeps a
- *               row of d_k fp32 values in one lane's registers),
- *               1 <= d_v <= LORES_MAX_DV
+ *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128, 256}
+ *               (160, 192 and 224 return LORES_EUNSUPPORTED, other values
+ *               LORES_EINVAL), 1 <= d_v <= LORES_MAX_DV.  At d_k = 256 a
+ *               state steps every token with value-row scales (no key-column
+ *               scales, no windows: LORES_EUNSUPPORTED) and its classes run
+ *               one launch each.
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
@@ -178,8 +180,8 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * and the same codes, rounding and draws otherwise (the comparison grouping
  * of "Intra-State Quantization (Section 4)", Scale Grouping and Proposition
  * 1).  A step then dequantizes S'_ij = fl(c_ij * fl(s_j * alpha_j)).
- * LORES_SCALE_KEY is built for every d_k and d_v that lores_state_alloc
- * accepts.  A key-column state runs one launch per precision class (no
+ * LORES_SCALE_KEY is built for d_k <= 128 and every d_v that
+ * lores_state_alloc accepts.  A key-column state runs one launch per precision class (no
  * fused pairs).  LORES_EINVAL for any other scale_axis.
  */
 int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
@@ -206,8 +208,7 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * the column's s_j and the window's end takes the column maxima.
  *   scale_axis  LORES_SCALE_VALUE or LORES_SCALE_KEY (as lores_state_alloc_axis)
  *   window      W, 1 <= W <= LORES_MAX_WINDOW
- * Built for every d_k and d_v that lores_state_alloc accepts, on either
- * scale axis.
+ * W > 1 is built for d_k <= 128 and every d_v, on either scale axis.
  * Steps on a windowed state must come in order (t = 1, 2, ... from the
  * allocation or a lores_quant_state; the handle counts the buffered tokens
  * and lores_decode_step returns LORES_EINVAL for a step t whose window

@@ -72,7 +72,9 @@ int check_dims(int32_t B, int32_t H, int32_t dk, int32_t dv) {
         return fail(LORES_EINVAL, "H must be in [1, %d] (got %d)", LORES_MAX_HEADS, H);
     if (dk < 32 || dk % 32 != 0)
         return fail(LORES_EINVAL, "d_k must be a positive multiple of 32 (got %d)", dk);
-    if (dk > 128) return fail(LORES_EUNSUPPORTED, "d_k > 128 is not built (got %d)", dk);
+    if (dk > 256) return fail(LORES_EINVAL, "d_k must be at most 256 (got %d)", dk);
+    if (dk > 128 && dk != 256)
+        return fail(LORES_EUNSUPPORTED, "d_k in (128, 256) is not built (got %d)", dk);
     if (dv < 1 || dv > LORES_MAX_DV)
         return fail(LORES_EINVAL, "d_v must be in [1, %d] (got %d)", LORES_MAX_DV, dv);
     return LORES_OK;
@@ -95,7 +97,8 @@ int plan(lores_state *st, const uint8_t *head_prec) {
         st->heads[p][st->n_class[p]++] = (uint16_t)h;
     }
     st->dv_pad = (st->dv + LORES_ROW_BLOCK - 1) / LORES_ROW_BLOCK * LORES_ROW_BLOCK;
-    st->n_rb = st->dv_pad / LORES_ROW_BLOCK;
+    // tasks of 64 rows, or of 32 rows split across lane pairs at d_k = 256
+    st->n_rb = st->dk > 128 ? (st->dv + 31) / 32 : st->dv_pad / LORES_ROW_BLOCK;
     uint64_t off = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c) {
         st->codes_off[c] = st->scales_off[c] = st->win_off[c] = -1;
@@ -230,6 +233,13 @@ static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         if (scale_axis != LORES_SCALE_VALUE && scale_axis != LORES_SCALE_KEY)
             return fail(LORES_EINVAL, "scale_axis must be LORES_SCALE_VALUE (0) or "
                                       "LORES_SCALE_KEY (1), got %d", scale_axis);
+        // rows split across lane pairs (d_k = 256) carry value-row scales and
+        // step every token
+        if (d_k > 128 && scale_axis == LORES_SCALE_KEY)
+            return fail(LORES_EUNSUPPORTED, "key-column scales are built for d_k <= 128 (got %d)",
+                        d_k);
+        if (d_k > 128 && window > 1)
+            return fail(LORES_EUNSUPPORTED, "windows are built for d_k <= 128 (got %d)", d_k);
         lores_state tmp;
         tmp.B = B;
         tmp.H = H;
@@ -400,7 +410,7 @@ static int plan_launches(const lores_state *st, int groups[LORES_NUM_PREC][2],
     int present[LORES_NUM_PREC], n = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c)
         if (st->n_class[c]) present[n++] = c;
-    if (n == 2 && st->axis == LORES_SCALE_VALUE && st->window == 1 &&
+    if (n == 2 && st->axis == LORES_SCALE_VALUE && st->window == 1 && st->dk <= 128 &&
         lores::fusable_pair(present[0], present[1])) {
         groups[0][0] = present[0];
         groups[0][1] = present[1];

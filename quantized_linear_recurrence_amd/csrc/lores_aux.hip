@@ -7,15 +7,21 @@
 namespace lores {
 
 // value = scale * code for int heads (fl of the product), the stored value
-// for bf16 / fp32 heads.  Same wavefront-per-64-rows mapping as the step.
+// for bf16 / fp32 heads.  Same row mapping as the step: a wavefront per 64
+// rows, or per 32 rows split across lane pairs at d_k = 256 (lane L + 32
+// takes the second half of the columns).
 // KEY: the scale of element j is the unit's key-column scale s_j.
 template <int DK, int PREC, bool KEY = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                      float *__restrict__ out, const StepMeta meta) {
+    constexpr bool SPLIT = DK > 128;
+    static_assert(!SPLIT || !KEY, "split rows carry value-row scales");
+    constexpr int CPL = SPLIT ? DK / 2 : DK, RPW = SPLIT ? 32 : 64;
     constexpr int E = Prec<PREC>::E;
-    constexpr int NCH = row_chunks<DK, PREC>();
+    constexpr int NCH = row_chunks<CPL, PREC>();     // chunks of the lane's columns
     const int lane = threadIdx.x & 63;
+    const int half = SPLIT ? lane >> 5 : 0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ClassDesc &cd = meta.cls[0];
     const int task = blockIdx.x * kWavesPerGroup + wv;
@@ -26,10 +32,11 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     const long unit = (long)b * cd.Hc + slot;
     const int h = (int)meta.heads[cd.head_off + slot];
     const long bh = (long)b * meta.H + h;
-    const int row = rb * 64 + lane;
+    const int row = rb * RPW + (lane & (RPW - 1));
     if (row >= meta.dv) return;
     const long dv_pad = meta.dv_pad;
-    const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * cd.unit_bytes) + row;
+    const u32x4 *cp = reinterpret_cast<const u32x4 *>(codes + unit * cd.unit_bytes) + row +
+                      half * NCH * dv_pad;
     float s = 0.0f;
     if constexpr (has_scale<PREC>() && !KEY) s = scales[unit * dv_pad + row];
     // the scale of element j (wave-uniform loads for key columns)
@@ -37,14 +44,14 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
         if constexpr (KEY) return scales[unit * DK + j];
         else return s;
     };
-    float *orow = out + (bh * meta.dv + row) * DK;
+    float *orow = out + (bh * meta.dv + row) * DK + half * CPL;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     if constexpr (PREC == LORES_INT6) {
         u32x4 cw[NCH];
 #pragma unroll
         for (int c = 0; c < NCH; ++c) cw[c] = cp[c * dv_pad];
 #pragma unroll
-        for (int j = 0; j < DK; j += 4) {
+        for (int j = 0; j < CPL; j += 4) {
             float x[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = sc(j + e) * ((float)int6_field(cw, j + e) - 32.0f);
@@ -82,14 +89,19 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 }
 
 // fp32 rows -> packed rows of one class with the step's own requantization
-// (requantize_row), keyed at meta.t.  Same wavefront-per-64-rows mapping.
+// (requantize_row), keyed at meta.t.  Same row mapping as the step (split
+// rows at d_k = 256: the row maximum combined across the lane pair).
 // KEY: key-column scales from the column maxima of the unit's rows (the
 // unit's row blocks are consecutive wavefronts of one work-group).
 template <int DK, int PREC, bool KEY = false>
 __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
                    float *__restrict__ scales, const StepMeta meta) {
+    constexpr bool SPLIT = DK > 128;
+    static_assert(!SPLIT || !KEY, "split rows carry value-row scales");
+    constexpr int CPL = SPLIT ? DK / 2 : DK, RPW = SPLIT ? 32 : 64;
     const int lane = threadIdx.x & 63;
+    const int half = SPLIT ? lane >> 5 : 0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const ClassDesc &cd = meta.cls[0];
     const int task = blockIdx.x * (KEY ? key_group_waves(meta.n_rb) : kWavesPerGroup) + wv;
@@ -105,23 +117,24 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     const long unit = (long)b * cd.Hc + slot;
     const int h = (int)meta.heads[cd.head_off + slot];
     const long bh = (long)b * meta.H + h;
-    const int row = rb * 64 + lane;
+    const int row = rb * RPW + (lane & (RPW - 1));
     const bool active = row < meta.dv;
     const long dv_pad = meta.dv_pad;
     // padding lanes read the last real row and store nothing
-    const float *xrow = X + (bh * meta.dv + (active ? row : meta.dv - 1)) * DK;
+    const float *xrow = X + (bh * meta.dv + (active ? row : meta.dv - 1)) * DK + half * CPL;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    float U[DK];
+    float U[CPL];
     float m = 0.0f;
 #pragma unroll
-    for (int c = 0; c < DK; c += 4) {
+    for (int c = 0; c < CPL; c += 4) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(xrow + c);
         U[c] = v.x;
         U[c + 1] = v.y;
         U[c + 2] = v.z;
         U[c + 3] = v.w;
     }
-    const CodeRows io(codes + unit * cd.unit_bytes, cd.unit_bytes, row, dv_pad);
+    const CodeRows io(codes + unit * cd.unit_bytes, cd.unit_bytes, row, dv_pad,
+                      half * row_chunks<CPL, PREC>());
     if constexpr (KEY) {
         constexpr int DKP = 64 * key_groups<DK>();          // padded to whole 64-column groups
         __shared__ float cmax[2 * kWavesPerGroup * DKP];    // maxima, staging
@@ -139,9 +152,11 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
         requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr, inv);
     } else {
 #pragma unroll
-        for (int j = 0; j < DK; ++j) m = fmaxf(m, fabsf(U[j]));
-        requantize_row<DK, PREC>(U, m, meta, b, h, row, active, io,
-                                 has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+        for (int j = 0; j < CPL; ++j) m = fmaxf(m, fabsf(U[j]));
+        if constexpr (SPLIT) m = pair_max(m);
+        requantize_row<CPL, PREC>(U, m, meta, b, h, row, active, io,
+                                  has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr,
+                                  nullptr, half * CPL);
     }
 }
 
@@ -169,6 +184,7 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
         case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 256: hipLaunchKernelGGL((lores_quant_kernel<256, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -209,6 +225,7 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
         case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 256: hipLaunchKernelGGL((lores_dequant_kernel<256, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -584,6 +584,20 @@ __device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[key
 #undef LORES_XMAX8
 #undef LORES_XMAX1
 
+// x of lane L combined with x of lane L ^ 32 (v_permlane32_swap gives each
+// lane both halves' values; the operations commute, so both lanes of a pair
+// hold the same result).
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 // s_barrier after this wavefront's LDS writes have landed; later memory
 // accesses stay after it, loads already in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() {
@@ -693,11 +707,13 @@ struct CodeRows {
     static constexpr int kRawFormat = 0x00020000;
     static constexpr int kNT = 2;                  // nontemporal
 
+    // c0: the lane's first chunk of the row (a lane holding the second half
+    // of a split row starts there)
     __device__ __forceinline__ CodeRows(const uint8_t *unit_codes, long unit_bytes, int row,
-                                        long dv_pad)
+                                        long dv_pad, int c0 = 0)
         : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(unit_codes), 0,
                                                  (int)unit_bytes, kRawFormat)),
-          voff(row * 16), cstride((int)dv_pad * 16) {}
+          voff(row * 16 + c0 * (int)dv_pad * 16), cstride((int)dv_pad * 16) {}
     __device__ __forceinline__ u32x4 load(int c) const {
         return __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, c * cstride, kNT);
     }
@@ -719,12 +735,13 @@ struct CodeRows {
 // ---------------------------------------------------------------------------
 // KEY: key-column scales; invrow holds r / m_j as row vectors (register i,
 // column 16 i + lane % 16), m and scale_out are unused (the caller stores
-// the column scales).
+// the column scales).  col0: the row's column of U[0] (a split row's second
+// lane: its draws continue the row's, and the other lane stores the scale).
 template <int DK, int PREC, bool KEY = false>
 __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, const StepMeta &meta,
                                                int b, int h, int row, bool active,
                                                const CodeRows &io, float *scale_out,
-                                               const float *invrow = nullptr) {
+                                               const float *invrow = nullptr, int col0 = 0) {
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = row_chunks<DK, PREC>();
     static_assert(!KEY || has_scale<PREC>(), "key-column scales belong to scaled classes");
@@ -734,7 +751,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
         if constexpr (is_int<PREC>()) snew = div_by_r<PREC>(m);
         else snew = m / Prec<PREC>::R;
         inv = rd_div(Prec<PREC>::R, m);
-        if (active) *scale_out = snew;
+        if (active && col0 == 0) *scale_out = snew;
     }
     // int: x holds the fma addend bias + n_ij * 2^-16 of the current
     // column (in [128, 256), where one fp32 ulp is 2^-16: the draw is the
@@ -746,7 +763,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
         const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
                                     (uint64_t)(meta.head_base + h));
         uint32_t n0 = fmix32(K ^ (uint32_t)row) & 0xFFFFu;
-        if (nearest) n0 = 0x8000u;
+        n0 = nearest ? 0x8000u : (n0 + (uint32_t)col0 * kPsi16) & 0xFFFFu;
         const uint32_t n1 = nearest ? n0 : (n0 + kPsi16) & 0xFFFFu;
         if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
         else if constexpr (PREC == LORES_BF16) x = n0 | (n1 << 16);
@@ -950,13 +967,24 @@ struct TaskSide {
 // WEND: the last step of a window of a windowed state: pass 1
 // dequantizes with the window's first decay, then the window buffer's
 // tokens are replayed on U before this step's token.
+// SPLIT (d_k > 128): a row of d_k fp32 values does not fit one lane's
+// registers beside the rest, so two lanes share it: lane L < 32 holds
+// columns [0, d_k / 2) of row 32 rb + L and lane L + 32 the other half
+// (each half whole 16-byte chunks of every class at d_k = 256).  Each lane
+// runs the per-lane code on its CPL = d_k / 2 columns; r, o and the row
+// maximum are combined across the pair with one v_permlane32_swap each (in
+// the same order in both lanes, so both hold the same values), and the
+// second lane's draws start at column CPL.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false, bool WEND = false>
 struct TaskStream {
+    static constexpr bool SPLIT = DK > 128;
+    static constexpr int CPL = SPLIT ? DK / 2 : DK;   // columns per lane
+    static constexpr int RPW = SPLIT ? 32 : 64;       // rows per wavefront task
+    static_assert(!SPLIT || (DK == 256 && !KEY && !WEND),
+                  "split rows: d_k = 256, value-row scales, no windows");
     static constexpr int E = Prec<PREC>::E;
-    static constexpr int NCH = row_chunks<DK, PREC>();
-    static_assert(PREC == LORES_INT6 || DK % E == 0, "d_k must be a whole number of 16-byte chunks");
-    static constexpr int kInB = BF16IN ? 2 : 4;
-    static constexpr int kVecBytes = DK * kInB;      // bytes of k (and of q)
+    static constexpr int NCH = row_chunks<CPL, PREC>();   // chunks of the lane's columns
+    static_assert(PREC == LORES_INT6 || CPL % E == 0, "d_k must be a whole number of 16-byte chunks");
 
     const void *__restrict__ qp;
     const void *__restrict__ kp;
@@ -967,7 +995,7 @@ struct TaskStream {
     uint8_t *__restrict__ codes;
     float *__restrict__ scales;
     const StepMeta &meta;
-    int Hc, slot, h, row, lrow, rb;
+    int Hc, slot, h, row, lrow, rb, half;
     long unit_bytes;
     bool active;
     float *lds;
@@ -981,19 +1009,20 @@ struct TaskStream {
         : qp(q), kp(k), vp(v), alphap(alpha), betap(beta), op(o), codes(c), scales(sc), meta(m),
           lds(lds_), win(win_) {
         const int n_rb = m.n_rb;
-        slot = n_rb == 1 ? task : n_rb == 2 ? task >> 1 : n_rb == 4 ? task >> 2 : task / 3;
+        slot = n_rb == 1 ? task : n_rb == 2 ? task >> 1 : n_rb == 4 ? task >> 2 : task / n_rb;
         rb = task - slot * n_rb;
         Hc = cd.Hc;
         unit_bytes = cd.unit_bytes;
         h = (int)m.heads[cd.head_off + slot];
-        row = rb * 64 + (threadIdx.x & 63);
+        half = SPLIT ? (int)(threadIdx.x & 63) >> 5 : 0;
+        row = rb * RPW + (threadIdx.x & (RPW - 1));
         active = row < m.dv;
         // padding rows (row >= d_v) load row d_v - 1 and store nothing, so
         // they repeat a real row (and leave column maxima unchanged)
         lrow = active ? row : m.dv - 1;
     }
 
-    static constexpr int NV = DK / 16;            // row-vector registers per vector
+    static constexpr int NV = CPL / 16;           // row-vector registers per vector
     using Side = TaskSide<NV, KEY, WEND && PC>;
 
     // Loads of task b: chunks [C0, C1) and, with C0 = 0, the per-task values.
@@ -1002,7 +1031,7 @@ struct TaskStream {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;
-        const CodeRows io(codes + unit * unit_bytes, unit_bytes, lrow, dv_pad);
+        const CodeRows io(codes + unit * unit_bytes, unit_bytes, lrow, dv_pad, half * NCH);
 #pragma unroll
         for (int c = C0; c < C1; ++c) cw[c] = io.load(c);
         if constexpr (C0 != 0) return;
@@ -1036,8 +1065,9 @@ struct TaskStream {
             in.alpha = win[unit * window_unit_floats(meta.window, meta.dv_pad, DK) +
                            (long)(meta.window - 1) * (meta.dv_pad + DK)];
         }
-        // row vectors: register i holds element 16 i + lane % 16
-        const long kb = bh * DK + (threadIdx.x & 15);
+        // row vectors: register i holds element 16 i + lane % 16 (of the
+        // lane's half of the columns with SPLIT)
+        const long kb = bh * DK + half * CPL + (threadIdx.x & 15);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             in.kv[i] = in_raw<BF16IN>(kp, kb + 16 * i);
@@ -1064,7 +1094,7 @@ struct TaskStream {
         const long dv_pad = meta.dv_pad;
         const long unit = (long)b * Hc + slot;
         const long bh = (long)b * meta.H + h;           // index into [B][H] inputs
-        const CodeRows io(codes + unit * unit_bytes, unit_bytes, row, dv_pad);
+        const CodeRows io(codes + unit * unit_bytes, unit_bytes, row, dv_pad, half * NCH);
 
         const float beta = in.beta;
         const float alpha_s = in.alpha;
@@ -1091,7 +1121,7 @@ struct TaskStream {
         }
 
         // ---- pass 1: dequantize, decay, delta projection r = S'_i . k
-        float U[DK];
+        float U[CPL];
         float r = 0.0f;
         float aj[16];                                    // s * alpha_j of one group (int, per channel)
         // after each group of 16 columns: per-channel decay of float heads,
@@ -1116,7 +1146,7 @@ struct TaskStream {
         constexpr bool MIX = decltype(mix_flag)::value;
         if constexpr (PREC == LORES_INT6) {
 #pragma unroll
-            for (int j = 0; j < DK; ++j) {
+            for (int j = 0; j < CPL; ++j) {
                 if constexpr (PC && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
@@ -1264,6 +1294,8 @@ struct TaskStream {
             }
         }
 
+        if constexpr (SPLIT && DELTA) r = pair_sum(r);
+
         // ---- write gate
         const float g = DELTA ? beta * (vi - r) : beta * vi;
 
@@ -1277,7 +1309,11 @@ struct TaskStream {
                 for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(U[16 * gi + e]));
             }
         }
-        if (active) op[bh * meta.dv + row] = o;
+        if constexpr (SPLIT) {
+            o = pair_sum(o);
+            m = pair_max(m);
+        }
+        if (active && half == 0) op[bh * meta.dv + row] = o;
 
         // ---- pass 3: requantize and store in place
         if constexpr (KEY) {
@@ -1298,8 +1334,9 @@ struct TaskStream {
             requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr,
                                            inv);
         } else {
-            requantize_row<DK, PREC>(U, m, meta, b, h, row, active, io,
-                                     has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr);
+            requantize_row<CPL, PREC>(U, m, meta, b, h, row, active, io,
+                                      has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr,
+                                      nullptr, half * CPL);
         }
     }
 };
@@ -1660,6 +1697,10 @@ hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs
         case 64: return launch_dk<64, P0, P1>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, P1>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, P1>(pc, delta, bf16, p, m, s);
+        case 256:
+            // split rows run one class per launch
+            if constexpr (P1 < 0) return launch_dk<256, P0, P1>(pc, delta, bf16, p, m, s);
+            else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

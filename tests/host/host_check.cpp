@@ -62,7 +62,7 @@ int main() {
     CHECK(size_of(1, 1, 64, 1, {LORES_INT6}) == 48 * 64 + 256);             // 3 chunks of 16 B per row
 
     // plans over many shapes: segments in bounds, disjoint, 256-aligned
-    const int dks[] = {32, 64, 96, 128};
+    const int dks[] = {32, 64, 96, 128, 256};
     const int dvs[] = {1, 64, 65, 128, 150, 200, 256};
     std::vector<std::vector<uint8_t>> mixes = {{2}, {3, 2}, {0, 1, 2, 3, 4, 5}, {5, 5, 4}, {1, 3}};
     for (int dk : dks)
@@ -74,6 +74,10 @@ int main() {
                         size_t n = 0;
                         int rc = lores_state_alloc_window(B, H, dk, dv, mix.data(), axis, W, nullptr,
                                                           &n, nullptr, nullptr);
+                        if (dk > 128 && (axis == 1 || W > 1)) {    // split rows: value rows, no windows
+                            CHECK(rc == LORES_EUNSUPPORTED);
+                            continue;
+                        }
                         CHECK(rc == LORES_OK);
                         Buf buf(n);
                         lores_state *st = nullptr;
@@ -109,6 +113,26 @@ int main() {
                     }
 
     Args x;
+    // d_k = 256: rows split across lane pairs, 32 rows per task, one launch
+    // per class (no fused pairs)
+    for (int dv : {1, 32, 33, 100, 256}) {
+        const std::vector<uint8_t> prec = {2, 3, 1, 3};
+        const int B = 2, H = (int)prec.size();
+        size_t n = size_of(B, H, 256, dv, prec);
+        Buf buf(n);
+        lores_state *st = nullptr;
+        CHECK(lores_state_alloc(B, H, 256, dv, prec.data(), buf.p, &n, nullptr, &st) == LORES_OK);
+        g_launches.clear();
+        CHECK(step(st, x, 1) == LORES_OK);
+        CHECK(g_launches.v.size() == 3);
+        for (auto &l : g_launches.v) {
+            CHECK(l.p1 < 0);
+            CHECK(l.n_rb == (dv + 31) / 32);
+            CHECK(l.groups[0] == (l.Hc[0] * l.n_rb + lores::kWavesPerGroup - 1) /
+                                     lores::kWavesPerGroup);
+        }
+        lores_state_free(st);
+    }
     // work-groups of each step launch cover its tasks: a fused int pair counts
     // only the unpaired rest of either class, in groups of kPairWavesPerGroup
     // wavefronts; other launches count all tasks of a class in groups of

@@ -40,13 +40,37 @@ def test_small_each_precision(prec, delta):
     s.check()
 
 
-@pytest.mark.parametrize("dk,dv", [(96, 100), (32, 1), (128, 65), (64, 128)])
+@pytest.mark.parametrize("dk,dv", [(96, 100), (32, 1), (128, 65), (64, 128), (256, 100),
+                                   (256, 33)])
 @pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
 def test_ragged_mixed_precisions(dk, dv, decay):
     w = C1.scaled(B=3, H=6, dk=dk, dv=dv, T=5, decay=decay)
     log(f"case: ragged mixed B=3 H=6 dk={dk} dv={dv} decay={decay} "
         "heads fp32/bf16/int8/int4/int6/fp8")
     s = run_parity(w, T=w.T, head_prec=[0, 1, 2, 3, 4, 5], init="random")
+    log(s.summary())
+    s.check()
+
+
+@pytest.mark.parametrize("prec", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("delta", [0, 1])
+def test_split_rows_each_precision(prec, delta):
+    """d_k = 256: each row split across a lane pair (r, o and the row maximum
+    combined across the pair, the second lane's draws from column 128)."""
+    w = C1.scaled(B=2, H=3, dk=256, dv=70, T=8, delta=delta)
+    log(f"case: split rows B=2 H=3 d_k=256 d_v=70 prec={prec} delta={delta}, random initial state")
+    s = run_parity(w, T=w.T, head_prec=[prec] * w.H, init="random")
+    log(s.summary())
+    s.check()
+
+
+def test_split_rows_sampled_batch():
+    """d_k = 256 at a large batch (one launch per class), sampled units."""
+    w = get_workload("C5").scaled(B=256, dk=256, T=8)
+    units = _sample_units(w.B, w.H, 48, seed=256)
+    log(f"case: split rows B={w.B} H={w.H} d_k=256 d_v=128 int8 + int4, {len(units)} units, "
+        f"{w.T} steps")
+    s = run_parity(w, T=w.T, units=units)
     log(s.summary())
     s.check()
 
@@ -124,23 +148,24 @@ def test_c5_seed_sweep(seed):
     s.check()
 
 
-@pytest.mark.parametrize("delta,decay", [(1, "softplus_step"), (0, "softplus_step"),
-                                         (1, "kda_channel")])
-def test_fp32_path_free_running(delta, decay):
-    w = C1.scaled(B=2, H=2, T=128, delta=delta, decay=decay)
-    log(f"case: fp32 heads free-running 128 steps delta={delta} decay={decay}")
+@pytest.mark.parametrize("delta,decay,dk", [(1, "softplus_step", 64), (0, "softplus_step", 64),
+                                            (1, "kda_channel", 64), (1, "kda_channel", 256)])
+def test_fp32_path_free_running(delta, decay, dk):
+    w = C1.scaled(B=2, H=2, dk=dk, T=128, delta=delta, decay=decay)
+    log(f"case: fp32 heads free-running 128 steps delta={delta} decay={decay} d_k={dk}")
     worst, worst_scale = run_free_fp32(w, T=w.T)
     log(f"worst o error / largest readout = {worst:.2e} (over the readout scale {worst_scale:.2e})")
     assert worst <= 1e-5
 
 
-@pytest.mark.parametrize("B,H,dv,prec", [
-    (65535, 1, 64, [2]),                                  # the largest batch (grid y limit)
-    (3, 512, 256, [0, 1, 2, 3, 4] * 102 + [2, 3]),        # the most heads, the tallest state
+@pytest.mark.parametrize("B,H,dk,dv,prec", [
+    (65535, 1, 128, 64, [2]),                                  # the largest batch (grid y limit)
+    (3, 512, 128, 256, [0, 1, 2, 3, 4] * 102 + [2, 3]),        # the most heads, the tallest state
+    (3, 512, 256, 256, [0, 1, 2, 3, 4, 5] * 85 + [2, 3]),      # and the widest
 ])
-def test_maximum_sizes(B, H, dv, prec):
-    w = C1.scaled(B=B, H=H, dk=128, dv=dv, T=2)
-    log(f"case: maximum sizes B={B} H={H} d_v={dv} d_k=128, sampled units")
+def test_maximum_sizes(B, H, dk, dv, prec):
+    w = C1.scaled(B=B, H=H, dk=dk, dv=dv, T=2)
+    log(f"case: maximum sizes B={B} H={H} d_v={dv} d_k={dk}, sampled units")
     units = _sample_units(B, H, 40, seed=B + H)
     units += [(B - 1, H - 1), (0, 0), (B - 1, 0), (0, H - 1)]
     s = run_parity(w, T=w.T, units=sorted(set(units)), head_prec=prec, init="random")

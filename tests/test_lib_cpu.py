@@ -67,7 +67,8 @@ def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
     (1, 2, 64, 64, [2, 2]), (64, 32, 128, 128, [2] * 32), (256, 128, 128, 64, [2] * 128),
     (128, 32, 128, 128, [1] * 8 + [2] * 24), (2048, 32, 128, 128, [2] * 16 + [3] * 16),
     (3, 4, 96, 100, [0, 1, 2, 3]), (1, 1, 32, 1, [3]), (2048, 32, 128, 128, [4] * 16 + [3] * 16),
-    (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4]), (4, 6, 64, 100, [5, 4, 3, 2, 1, 0])])
+    (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4]), (4, 6, 64, 100, [5, 4, 3, 2, 1, 0]),
+    (3, 6, 256, 100, [5, 4, 3, 2, 1, 0]), (2, 2, 256, 1, [2, 3])])
 def test_size_query_matches_documented_layout(lores_lib, B, H, dk, dv, prec):
     assert lores.lores_state_alloc(B, H, dk, dv, prec) == _layout_bytes(B, H, dk, dv, prec)
 
@@ -107,7 +108,20 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
     for B, H, dk, dv in bad_dims:
         assert L.lores_state_alloc(B, H, dk, dv, hp, None, ctypes.byref(nb), None, None) == -1
         assert lores.lores_last_error()
-    assert L.lores_state_alloc(1, 4, 256, 64, hp, None, ctypes.byref(nb), None, None) == -2
+    # d_k in (128, 256) is not built; d_k = 256 (split rows) takes value-row
+    # scales and steps every token
+    for dk in (160, 192, 224):
+        assert L.lores_state_alloc(1, 4, dk, 64, hp, None, ctypes.byref(nb), None, None) == -2
+    assert L.lores_state_alloc(1, 4, 288, 64, hp, None, ctypes.byref(nb), None, None) == -1
+    assert L.lores_state_alloc(1, 4, 256, 64, hp, None, ctypes.byref(nb), None, None) == 0
+    assert L.lores_state_alloc_axis(1, 4, 256, 64, hp, 1, None, ctypes.byref(nb), None,
+                                    None) == -2
+    assert "key-column" in lores.lores_last_error()
+    assert L.lores_state_alloc_window(1, 4, 256, 64, hp, 0, 4, None, ctypes.byref(nb), None,
+                                      None) == -2
+    assert "windows" in lores.lores_last_error()
+    assert L.lores_state_alloc_window(1, 4, 256, 64, hp, 0, 1, None, ctypes.byref(nb), None,
+                                      None) == 0
     bad = (ctypes.c_uint8 * 4)(2, 2, 9, 2)
     assert L.lores_state_alloc(1, 4, 64, 64, bad, None, ctypes.byref(nb), None, None) == -1
     assert L.lores_state_alloc(1, 4, 64, 64, None, None, ctypes.byref(nb), None, None) == -1
