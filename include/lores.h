@@ -156,9 +156,8 @@ typedef struct {
  *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128, 256}
  *               (160, 192 and 224 return LORES_EUNSUPPORTED, other values
  *               LORES_EINVAL), 1 <= d_v <= LORES_MAX_DV.  At d_k = 256 a
- *               state steps every token with value-row scales (no key-column
- *               scales, no windows: LORES_EUNSUPPORTED) and its classes run
- *               one launch each.
+ *               state has value-row scales (key-column scales return
+ *               LORES_EUNSUPPORTED) and its classes run one launch each.
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
@@ -208,7 +207,7 @@ int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * the column's s_j and the window's end takes the column maxima.
  *   scale_axis  LORES_SCALE_VALUE or LORES_SCALE_KEY (as lores_state_alloc_axis)
  *   window      W, 1 <= W <= LORES_MAX_WINDOW
- * W > 1 is built for d_k <= 128 and every d_v, on either scale axis.
+ * Built for every d_k and d_v that lores_state_alloc_axis accepts.
  * Steps on a windowed state must come in order (t = 1, 2, ... from the
  * allocation or a lores_quant_state; the handle counts the buffered tokens
  * and lores_decode_step returns LORES_EINVAL for a step t whose window

@@ -980,8 +980,7 @@ struct TaskStream {
     static constexpr bool SPLIT = DK > 128;
     static constexpr int CPL = SPLIT ? DK / 2 : DK;   // columns per lane
     static constexpr int RPW = SPLIT ? 32 : 64;       // rows per wavefront task
-    static_assert(!SPLIT || (DK == 256 && !KEY && !WEND),
-                  "split rows: d_k = 256, value-row scales, no windows");
+    static_assert(!SPLIT || (DK == 256 && !KEY), "split rows: d_k = 256, value-row scales");
     static constexpr int E = Prec<PREC>::E;
     static constexpr int NCH = row_chunks<CPL, PREC>();   // chunks of the lane's columns
     static_assert(PREC == LORES_INT6 || CPL % E == 0, "d_k must be a whole number of 16-byte chunks");
@@ -1074,7 +1073,7 @@ struct TaskStream {
             in.qv[i] = in_raw<BF16IN>(qp, kb + 16 * i);
             if constexpr (PC && WEND) {
                 in.avt[i] = alphap[kb + 16 * i];
-                if constexpr (!KEY) in.av[i] = wa1[16 * i + (threadIdx.x & 15)];
+                if constexpr (!KEY) in.av[i] = wa1[half * CPL + 16 * i + (threadIdx.x & 15)];
             } else if constexpr (PC && !KEY) {
                 in.av[i] = alphap[kb + 16 * i];
             }
@@ -1252,7 +1251,8 @@ struct TaskStream {
             // while token tau is applied
             const int nslot = meta.window - 1;
             const float *ub = win + unit * window_unit_floats(meta.window, meta.dv_pad, DK);
-            const float *gs = ub + lrow, *ks = ub + (long)nslot * dv_pad + (threadIdx.x & 15);
+            const float *gs = ub + lrow,
+                        *ks = ub + (long)nslot * dv_pad + half * CPL + (threadIdx.x & 15);
             const float *as = ub + (long)nslot * (dv_pad + DK);
             float gt = gs[0], kt[NV];
 #pragma unroll
@@ -1270,7 +1270,8 @@ struct TaskStream {
                     for (int i = 0; i < NV; ++i) kn[i] = ks[(long)tau * DK + 16 * i];
                     if constexpr (PC) {
 #pragma unroll
-                        for (int i = 0; i < NV; ++i) anv[i] = as[(long)tau * DK + 16 * i + (threadIdx.x & 15)];
+                        for (int i = 0; i < NV; ++i)
+                            anv[i] = as[(long)tau * DK + half * CPL + 16 * i + (threadIdx.x & 15)];
                     } else {
                         an = as[(long)tau * DK];
                     }
@@ -1282,7 +1283,7 @@ struct TaskStream {
                     for (int gi = 0; gi < NV; ++gi) mul16(&U[16 * gi], anv[gi]);
                 } else {
 #pragma unroll
-                    for (int j = 0; j < DK; ++j) U[j] = U[j] * an;
+                    for (int j = 0; j < CPL; ++j) U[j] = U[j] * an;
                 }
                 gt = gn;
 #pragma unroll

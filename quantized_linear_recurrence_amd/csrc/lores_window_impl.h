@@ -90,10 +90,13 @@ struct WindowTask {
 __device__ __forceinline__ bool window_task(const StepMeta &meta, WindowTask &w) {
     const ClassDesc &cd = meta.cls[0];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // tasks of 64 rows (the split rows of the step at d_k = 256 do not apply
+    // here: these kernels hold no fp32 row beside the codes)
+    const int nrb = (int)(meta.dv_pad / 64);
     const int task = blockIdx.x * kWavesPerGroup + wv;
-    if (task >= cd.Hc * meta.n_rb) return false;
-    w.slot = task / meta.n_rb;
-    w.rb = task - w.slot * meta.n_rb;
+    if (task >= cd.Hc * nrb) return false;
+    w.slot = task / nrb;
+    w.rb = task - w.slot * nrb;
     const int b = blockIdx.y;
     w.unit = (long)b * cd.Hc + w.slot;
     w.h = (int)meta.heads[cd.head_off + w.slot];
@@ -239,7 +242,7 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                             const float *__restrict__ win, float *__restrict__ out,
                             const StepMeta meta) {
-    constexpr int NCH = row_chunks<DK, PREC>(), NV = DK / 16;
+    constexpr int NCH = row_chunks<DK, PREC>();
     WindowTask w;
     if (!window_task(meta, w)) return;
     const int lane = threadIdx.x & 63;
@@ -251,36 +254,44 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
     const int nslot = meta.window - 1, n = meta.wpos;
     const float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     const float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
-    float U[DK];
-    // token 1: fl(c fl(s alpha_1,j)), with the row's or column j's scale s and
-    // the token's decay of column j (a scalar decay: every column alike)
+    // columns are independent in the replay: blocks of at most 128 of them
+    constexpr int CB = DK < 128 ? DK : 128, NVB = CB / 16;
     const bool pc = meta.win_pc != 0;
     const float s = KEY ? 0.0f : scales[w.unit * dv_pad + w.lrow];
-#pragma unroll
-    for (int j = 0; j < DK; ++j) {
-        const float a1 = (KEY ? scales[w.unit * DK + j] : s) * aslot[pc ? j : 0];
-        float na1 = 0.0f;
-        if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
-        U[j] = scaled_code<PREC>(cw, j, a1, na1);
-    }
-    for (int tau = 1; tau <= n; ++tau) {
-        const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
-        float kt[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) kt[i] = kslot[(long)(tau - 1) * DK + 16 * i + (lane & 15)];
-#pragma unroll
-        for (int gi = 0; gi < NV; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
-        if (tau < n) {
-            const float *an = aslot + (long)tau * DK;
-#pragma unroll
-            for (int j = 0; j < DK; ++j) U[j] = U[j] * an[pc ? j : 0];
-        }
-    }
-    if (!w.active) return;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     float *orow = out + (w.bh * meta.dv + w.row) * DK;
 #pragma unroll
-    for (int j = 0; j < DK; j += 4) *reinterpret_cast<f32x4 *>(orow + j) = f32x4{U[j], U[j + 1], U[j + 2], U[j + 3]};
+    for (int j0 = 0; j0 < DK; j0 += CB) {
+        float U[CB];
+        // token 1: fl(c fl(s alpha_1,j)), with the row's or column j's scale s
+        // and the token's decay of column j (a scalar decay: every column alike)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const float a1 = (KEY ? scales[w.unit * DK + j0 + j] : s) * aslot[pc ? j0 + j : 0];
+            float na1 = 0.0f;
+            if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
+            U[j] = scaled_code<PREC>(cw, j0 + j, a1, na1);
+        }
+        for (int tau = 1; tau <= n; ++tau) {
+            const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
+            float kt[NVB];
+#pragma unroll
+            for (int i = 0; i < NVB; ++i)
+                kt[i] = kslot[(long)(tau - 1) * DK + j0 + 16 * i + (lane & 15)];
+#pragma unroll
+            for (int gi = 0; gi < NVB; ++gi) axpy16(&U[16 * gi], gt, kt[gi]);
+            if (tau < n) {
+                const float *an = aslot + (long)tau * DK;
+#pragma unroll
+                for (int j = 0; j < CB; ++j) U[j] = U[j] * an[pc ? j0 + j : 0];
+            }
+        }
+        if (w.active) {
+#pragma unroll
+            for (int j = 0; j < CB; j += 4)
+                *reinterpret_cast<f32x4 *>(orow + j0 + j) = f32x4{U[j], U[j + 1], U[j + 2], U[j + 3]};
+        }
+    }
 }
 
 // Inside a window: one task per wavefront (a read-only pass, many waves per
@@ -295,7 +306,7 @@ static hipError_t window_dk(bool delta, bool bf16, const StepPtrs &p, const Step
         return bf16 ? launch_one<DK, PC, false, true, PREC, -1, KEY, true>(p, m, s)
                     : launch_one<DK, PC, false, false, PREC, -1, KEY, true>(p, m, s);
     }
-    const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
+    const dim3 grid((m.cls[0].Hc * (m.dv_pad / 64) + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
 #define LORES_WIN_LAUNCH(D, BF)                                                                 \
     hipLaunchKernelGGL((lores_window_read_kernel<DK, PREC, D, BF, KEY, PC>), grid, block, 0, s,    \
@@ -322,6 +333,10 @@ static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, bool pc,
         case 64: return LORES_WIN_KEY_PC(64);
         case 96: return LORES_WIN_KEY_PC(96);
         case 128: return LORES_WIN_KEY_PC(128);
+        case 256:                                       // value rows
+            if (key) return hipErrorInvalidValue;
+            return pc ? window_dk<256, PREC, false, true>(delta, bf16, p, m, s)
+                      : window_dk<256, PREC, false, false>(delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 #undef LORES_WIN_KEY_PC
@@ -333,7 +348,7 @@ template <int PREC>
 static hipError_t window_dequant_prec(int dk, bool key, const uint8_t *codes, const float *scales,
                                       const float *win, float *out, const StepMeta &m,
                                       hipStream_t s) {
-    const dim3 grid((m.cls[0].Hc * m.n_rb + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
+    const dim3 grid((m.cls[0].Hc * (m.dv_pad / 64) + kWavesPerGroup - 1) / kWavesPerGroup, m.B);
     const dim3 block(64 * kWavesPerGroup);
 #define LORES_WD(DK, KEY)                                                                       \
     hipLaunchKernelGGL((lores_window_dequant_kernel<DK, PREC, KEY>), grid, block, 0, s, codes,   \
@@ -343,6 +358,7 @@ static hipError_t window_dequant_prec(int dk, bool key, const uint8_t *codes, co
         case 64: if (key) LORES_WD(64, true); else LORES_WD(64, false); break;
         case 96: if (key) LORES_WD(96, true); else LORES_WD(96, false); break;
         case 128: if (key) LORES_WD(128, true); else LORES_WD(128, false); break;
+        case 256: if (key) return hipErrorInvalidValue; LORES_WD(256, false); break;
         default: return hipErrorInvalidValue;
     }
 #undef LORES_WD

@@ -109,7 +109,7 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
         assert L.lores_state_alloc(B, H, dk, dv, hp, None, ctypes.byref(nb), None, None) == -1
         assert lores.lores_last_error()
     # d_k in (128, 256) is not built; d_k = 256 (split rows) takes value-row
-    # scales and steps every token
+    # scales, with or without windows
     for dk in (160, 192, 224):
         assert L.lores_state_alloc(1, 4, dk, 64, hp, None, ctypes.byref(nb), None, None) == -2
     assert L.lores_state_alloc(1, 4, 288, 64, hp, None, ctypes.byref(nb), None, None) == -1
@@ -118,8 +118,9 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
                                     None) == -2
     assert "key-column" in lores.lores_last_error()
     assert L.lores_state_alloc_window(1, 4, 256, 64, hp, 0, 4, None, ctypes.byref(nb), None,
+                                      None) == 0
+    assert L.lores_state_alloc_window(1, 4, 256, 64, hp, 1, 4, None, ctypes.byref(nb), None,
                                       None) == -2
-    assert "windows" in lores.lores_last_error()
     assert L.lores_state_alloc_window(1, 4, 256, 64, hp, 0, 1, None, ctypes.byref(nb), None,
                                       None) == 0
     bad = (ctypes.c_uint8 * 4)(2, 2, 9, 2)
