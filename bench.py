@@ -190,6 +190,7 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, "key"][, window
     ("int8, d_k 256 (split rows)", 1024, 32, 256, 128, [2] * 32, 1),
     ("int4, d_k 256 (split rows)", 1024, 32, 256, 128, [3] * 32, 1),
     ("int8+int4, d_k 256 (one launch per class)", 1024, 32, 256, 128, [2] * 16 + [3] * 16, 1),
+    ("int8, d_k 256, key columns", 1024, 32, 256, 128, [2] * 32, 1, "key"),
 ]
 
 

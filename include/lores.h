@@ -155,9 +155,8 @@ typedef struct {
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
  *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128, 256}
  *               (160, 192 and 224 return LORES_EUNSUPPORTED, other values
- *               LORES_EINVAL), 1 <= d_v <= LORES_MAX_DV.  At d_k = 256 a
- *               state has value-row scales (key-column scales return
- *               LORES_EUNSUPPORTED) and its classes run one launch each.
+ *               LORES_EINVAL), 1 <= d_v <= LORES_MAX_DV.  At d_k = 256 the
+ *               classes of a state run one launch each.
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and
@@ -179,8 +178,8 @@ int lores_state_alloc(int32_t B, int32_t H, int32_t d_k, int32_t d_v,
  * and the same codes, rounding and draws otherwise (the comparison grouping
  * of "Intra-State Quantization (Section 4)", Scale Grouping and Proposition
  * 1).  A step then dequantizes S'_ij = fl(c_ij * fl(s_j * alpha_j)).
- * LORES_SCALE_KEY is built for d_k <= 128 and every d_v that
- * lores_state_alloc accepts.  A key-column state runs one launch per precision class (no
+ * LORES_SCALE_KEY is built for every d_k and d_v that lores_state_alloc
+ * accepts.  A key-column state runs one launch per precision class (no
  * fused pairs).  LORES_EINVAL for any other scale_axis.
  */
 int lores_state_alloc_axis(int32_t B, int32_t H, int32_t d_k, int32_t d_v,

@@ -233,10 +233,6 @@ static int alloc_impl(int32_t B, int32_t H, int32_t d_k, int32_t d_v, const uint
         if (scale_axis != LORES_SCALE_VALUE && scale_axis != LORES_SCALE_KEY)
             return fail(LORES_EINVAL, "scale_axis must be LORES_SCALE_VALUE (0) or "
                                       "LORES_SCALE_KEY (1), got %d", scale_axis);
-        // rows split across lane pairs (d_k = 256) carry value-row scales
-        if (d_k > 128 && scale_axis == LORES_SCALE_KEY)
-            return fail(LORES_EUNSUPPORTED, "key-column scales are built for d_k <= 128 (got %d)",
-                        d_k);
         lores_state tmp;
         tmp.B = B;
         tmp.H = H;

@@ -16,7 +16,6 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                      float *__restrict__ out, const StepMeta meta) {
     constexpr bool SPLIT = DK > 128;
-    static_assert(!SPLIT || !KEY, "split rows carry value-row scales");
     constexpr int CPL = SPLIT ? DK / 2 : DK, RPW = SPLIT ? 32 : 64;
     constexpr int E = Prec<PREC>::E;
     constexpr int NCH = row_chunks<CPL, PREC>();     // chunks of the lane's columns
@@ -41,7 +40,7 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
     if constexpr (has_scale<PREC>() && !KEY) s = scales[unit * dv_pad + row];
     // the scale of element j (wave-uniform loads for key columns)
     auto sc = [&](int j) {
-        if constexpr (KEY) return scales[unit * DK + j];
+        if constexpr (KEY) return scales[unit * DK + half * CPL + j];
         else return s;
     };
     float *orow = out + (bh * meta.dv + row) * DK + half * CPL;
@@ -94,11 +93,10 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
 // KEY: key-column scales from the column maxima of the unit's rows (the
 // unit's row blocks are consecutive wavefronts of one work-group).
 template <int DK, int PREC, bool KEY = false>
-__global__ void __launch_bounds__(64 * kWavesPerGroup)
+__global__ void __launch_bounds__(64 * (KEY && DK > 128 ? kMaxKeyGroupWaves : kWavesPerGroup))
 lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
                    float *__restrict__ scales, const StepMeta meta) {
     constexpr bool SPLIT = DK > 128;
-    static_assert(!SPLIT || !KEY, "split rows carry value-row scales");
     constexpr int CPL = SPLIT ? DK / 2 : DK, RPW = SPLIT ? 32 : 64;
     const int lane = threadIdx.x & 63;
     const int half = SPLIT ? lane >> 5 : 0;
@@ -136,20 +134,24 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
     const CodeRows io(codes + unit * cd.unit_bytes, cd.unit_bytes, row, dv_pad,
                       half * row_chunks<CPL, PREC>());
     if constexpr (KEY) {
-        constexpr int DKP = 64 * key_groups<DK>();          // padded to whole 64-column groups
-        __shared__ float cmax[2 * kWavesPerGroup * DKP];    // maxima, staging
-        float cm[key_groups<DK>()], snew[key_groups<DK>()], inv[DK / 16];
-        col_absmax<DK>(U, cm);
-        key_scales<DK>(cm, cmax, cmax + kWavesPerGroup * DKP, wv, rb, meta.n_rb, Prec<PREC>::R,
-                       snew, inv);
+        constexpr int SLOT = key_slot<DK>(), LW = key_lds_waves<DK>();
+        constexpr int NCM = SPLIT ? 4 : key_groups<DK>();
+        __shared__ float cmax[2 * LW * SLOT];               // maxima, staging
+        float cm[NCM], snew[NCM], inv[CPL / 16];
+        if constexpr (SPLIT) col_absmax_split(U, cm);
+        else col_absmax<DK>(U, cm);
+        auto col_of = [](int j, int L) { return SPLIT ? key_col_split(j, L) : key_col(j, L); };
+        key_scales(cm, cmax, cmax + LW * SLOT, wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv,
+                   col_of, half * CPL);
         if (rb == 0) {
 #pragma unroll
-            for (int t = 0; t < key_groups<DK>(); ++t) {
-                const int col = key_col(t, lane);
+            for (int t = 0; t < NCM; ++t) {
+                const int col = col_of(t, lane);
                 if (col < DK) scales[unit * DK + col] = snew[t];
             }
         }
-        requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr, inv);
+        requantize_row<CPL, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr, inv,
+                                        half * CPL);
     } else {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) m = fmaxf(m, fabsf(U[j]));
@@ -174,6 +176,7 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
                 case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 256: hipLaunchKernelGGL((lores_quant_kernel<256, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 default: return hipErrorInvalidValue;
             }
             return hipGetLastError();
@@ -215,6 +218,7 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
                 case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 256: hipLaunchKernelGGL((lores_dequant_kernel<256, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 default: return hipErrorInvalidValue;
             }
             return hipGetLastError();

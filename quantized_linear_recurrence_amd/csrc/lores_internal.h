@@ -121,9 +121,13 @@ constexpr int kPairWavesPerGroup = 8;
 // Wavefronts per work-group of the launches whose wavefronts exchange
 // key-column maxima (key-column steps and quantization): a unit's n_rb row
 // blocks must share one work-group, so units of three row blocks run in
-// three-wavefront groups and all others in kWavesPerGroup.
+// three-wavefront groups, units of more than four (32-row tasks at d_k =
+// 256) in groups of their own size, and all others in kWavesPerGroup.
 __host__ __device__ constexpr int key_group_waves(int n_rb) {
-    return n_rb == 3 ? 3 : kWavesPerGroup;
+    return n_rb == 3 ? 3 : n_rb <= kWavesPerGroup ? kWavesPerGroup : n_rb;
 }
+// wavefronts of the largest key-column work-group: a unit of 32-row tasks
+// (d_k = 256) has up to 8 row blocks
+constexpr int kMaxKeyGroupWaves = 8;
 
 }  // namespace lores

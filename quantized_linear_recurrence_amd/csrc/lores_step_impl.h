@@ -534,6 +534,12 @@ __device__ __forceinline__ float xmax_pair(float a, float b, bool hi) {
 // Depth first, 16 columns at a time, so only a few partial results are live.
 // Register t of lane L then holds the maximum of column key_col(t, L).
 template <int DK> constexpr int key_groups() { return (DK + 63) / 64; }
+// LDS of the key-column launches: floats per wavefront slot (64 per maximum
+// register of a lane) and wavefront slots per buffer (the largest group)
+template <int DK> constexpr int key_slot() { return DK > 128 ? 256 : 64 * key_groups<DK>(); }
+template <int DK> constexpr int key_lds_waves() {
+    return DK > 128 ? kMaxKeyGroupWaves : kWavesPerGroup;
+}
 
 __device__ __forceinline__ int key_col(int t, int L) {
     return 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + (L & 1) * 8 +
@@ -581,6 +587,50 @@ __device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[key
         cm[t] = xmax_pair<6>(xmax_pair<5>(g[0], g[1], h1), xmax_pair<5>(g[2], g[3], h1), h3);
     }
 }
+// The same over the 32 rows of a split-row task (d_k = 256: lane L and
+// L + 32 hold the two halves of one row, so lane bit 5 is not a row bit):
+// U holds the lane's 128 columns, the levels across lane bits 2, 4, 0, 1
+// and 3 leave two registers per 64-column group, and register 2 t + s of
+// lane L holds the maximum of column key_col_split(2 t + s, L).
+__device__ __forceinline__ int key_col_split(int j, int L) {
+    const int t = j >> 1, s = j & 1;
+    return ((L >> 5) & 1) * 128 + 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + s * 8 +
+           (L & 1) * 4 + ((L >> 4) & 1) * 2 + ((L >> 2) & 1);
+}
+
+__device__ __forceinline__ void col_absmax_split(const float (&U)[128], float (&cm)[4]) {
+    const int lane = threadIdx.x & 63;
+    const bool h0 = lane & 1, h1 = lane & 2, h2 = lane & 4, h3 = lane & 8;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        float g[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float *u = &U[64 * t + 16 * q];
+            float s[8], o[8], y[8];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                s[p] = h2 ? u[2 * p + 1] : u[2 * p];
+                o[p] = h2 ? u[2 * p] : u[2 * p + 1];
+            }
+            LORES_XMAX8(LORES_DPP_HALF_MIRROR);
+            float y2[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[2 * p]),
+                                                                 __float_as_uint(y[2 * p + 1]),
+                                                                 false, false);
+                y2[p] = absmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) g[q][p] = xmax_pair<4>(y2[2 * p], y2[2 * p + 1], h0);
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            cm[2 * t + p] = xmax_pair<6>(xmax_pair<5>(g[0][p], g[1][p], h1),
+                                         xmax_pair<5>(g[2][p], g[3][p], h1), h3);
+    }
+}
 #undef LORES_XMAX8
 #undef LORES_XMAX1
 
@@ -606,40 +656,39 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Column scales of a unit from its wavefronts' column maxima.  Wavefront wv
 // (row block rb of n_rb; the unit's blocks are wavefronts wv - rb ..
-// wv - rb + n_rb - 1 of the work-group) publishes its maxima in part[wv][.]
-// and, after the barrier, combines the unit's: lane L then holds column
-// key_col(t, L) of snew = fl(m / r) and of inv = the largest fp32 <= r / m
-// (0 for a zero column).  inv goes through the wavefront's own slot of
-// `stage` to the row-vector form the requantization reads: register i of
-// invrow holds column 16 i + lane % 16.
-// `part` and `stage` hold 64 key_groups<DK>() columns per wavefront (the
-// padding columns of d_k = 32, 96 read as zero columns).
-template <int DK>
-__device__ __forceinline__ void key_scales(const float (&cm)[key_groups<DK>()], float *part,
-                                           float *stage, int wv, int rb, int n_rb, float R,
-                                           float (&snew)[key_groups<DK>()],
-                                           float (&invrow)[DK / 16]) {
-    constexpr int DKP = 64 * key_groups<DK>();
+// wv - rb + n_rb - 1 of the work-group) publishes its NCM maxima per lane in
+// part[wv][.] and, after the barrier, combines the unit's: register j of
+// lane L then holds column col_of(j, L) of snew = fl(m / r) and of inv = the
+// largest fp32 <= r / m (0 for a zero column).  inv goes through the
+// wavefront's own slot of `stage` to the row-vector form the requantization
+// reads: register i of invrow holds column c0 + 16 i + lane % 16.  Each
+// wavefront's slots hold 64 NCM values.
+template <int NCM, int NVR, class ColOf>
+__device__ __forceinline__ void key_scales(const float (&cm)[NCM], float *part, float *stage,
+                                           int wv, int rb, int n_rb, float R,
+                                           float (&snew)[NCM], float (&invrow)[NVR],
+                                           ColOf &&col_of, int c0 = 0) {
+    constexpr int SLOT = 64 * NCM;
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < key_groups<DK>(); ++t) part[wv * DKP + 64 * t + lane] = cm[t];
+    for (int t = 0; t < NCM; ++t) part[wv * SLOT + 64 * t + lane] = cm[t];
     // a unit of one row block reads back only its own maxima
     if (n_rb > 1) lds_barrier();
     else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const float *base = part + (wv - rb) * DKP + lane;
-    float *mine = stage + wv * DKP;
+    const float *base = part + (wv - rb) * SLOT + lane;
+    float *mine = stage + wv * SLOT;
 #pragma unroll
-    for (int t = 0; t < key_groups<DK>(); ++t) {
+    for (int t = 0; t < NCM; ++t) {
         float m = base[64 * t];
-        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * DKP + 64 * t]);
+        for (int w = 1; w < n_rb; ++w) m = fmaxf(m, base[w * SLOT + 64 * t]);
         snew[t] = m / R;
-        mine[key_col(t, lane)] = rd_div(R, m);
+        mine[col_of(t, lane)] = rd_div(R, m);
     }
     // this wavefront's own writes, read back by its other lanes: LDS keeps a
     // wavefront's accesses in order, the compiler must not reorder them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < DK / 16; ++i) invrow[i] = mine[16 * i + (lane & 15)];
+    for (int i = 0; i < NVR; ++i) invrow[i] = mine[c0 + 16 * i + (lane & 15)];
 }
 
 // u[e] = fma(g, row element e of kv, u[e]) for e < 16
@@ -951,12 +1000,12 @@ constexpr int kMaxPrefetchChunks = 8;    // int8 and int4 rows of d_k <= 128
 // WPC: the end of a window whose tokens carry one decay per key channel:
 // av (al with key-column scales) holds the window's first token's decays and
 // avt this step's, as row vectors.
-template <int NV, bool KEY = false, bool WPC = false>
+template <int NV, bool KEY = false, bool WPC = false, int KG = 1>
 struct TaskSide {
     float s = 0.0f, v = 0.0f, alpha = 1.0f, beta = 0.0f;
     float alpha_t = 1.0f;              // window end: this step's decay (alpha is token 1's)
     float kv[NV], qv[NV], av[KEY ? 1 : NV];
-    float sl[KEY ? (NV + 3) / 4 : 1], al[KEY ? (NV + 3) / 4 : 1];
+    float sl[KEY ? KG : 1], al[KEY ? KG : 1];   // KG: 64-column groups of the row
     float avt[WPC ? NV : 1];
 };
 
@@ -980,7 +1029,7 @@ struct TaskStream {
     static constexpr bool SPLIT = DK > 128;
     static constexpr int CPL = SPLIT ? DK / 2 : DK;   // columns per lane
     static constexpr int RPW = SPLIT ? 32 : 64;       // rows per wavefront task
-    static_assert(!SPLIT || (DK == 256 && !KEY), "split rows: d_k = 256, value-row scales");
+    static_assert(!SPLIT || DK == 256, "split rows: d_k = 256");
     static constexpr int E = Prec<PREC>::E;
     static constexpr int NCH = row_chunks<CPL, PREC>();   // chunks of the lane's columns
     static_assert(PREC == LORES_INT6 || CPL % E == 0, "d_k must be a whole number of 16-byte chunks");
@@ -1022,7 +1071,7 @@ struct TaskStream {
     }
 
     static constexpr int NV = CPL / 16;           // row-vector registers per vector
-    using Side = TaskSide<NV, KEY, WEND && PC>;
+    using Side = TaskSide<NV, KEY, WEND && PC, key_groups<DK>()>;
 
     // Loads of task b: chunks [C0, C1) and, with C0 = 0, the per-task values.
     template <int C0 = 0, int C1 = NCH>
@@ -1103,15 +1152,14 @@ struct TaskStream {
         float sig[KEY ? NV : 1];
         if constexpr (KEY) {
             const int lane = threadIdx.x & 63;
-            constexpr int DKP = 64 * key_groups<DK>();
-            float *mine = lds + 2 * kWavesPerGroup * DKP +
-                          __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DKP;
+            constexpr int SLOT = key_slot<DK>(), LW = key_lds_waves<DK>();
+            float *mine = lds + 2 * LW * SLOT + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * SLOT;
 #pragma unroll
             for (int t = 0; t < key_groups<DK>(); ++t)
                 mine[64 * t + lane] = in.sl[t] * (PC ? in.al[t] : alpha_s);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < NV; ++i) sig[i] = mine[16 * i + (lane & 15)];
+            for (int i = 0; i < NV; ++i) sig[i] = mine[half * CPL + 16 * i + (lane & 15)];
         } else if constexpr (is_int<PREC>() && !PC) {
             a = s * alpha_s;
             na = a * -Prec<PREC>::OFF;
@@ -1319,21 +1367,24 @@ struct TaskStream {
         // ---- pass 3: requantize and store in place
         if constexpr (KEY) {
             // column maxima of the unit's rows, fresh column scales
-            constexpr int DKP = 64 * key_groups<DK>();
-            float cm[key_groups<DK>()], snew[key_groups<DK>()], inv[NV];
-            col_absmax<DK>(U, cm);
+            constexpr int SLOT = key_slot<DK>(), LW = key_lds_waves<DK>();
+            constexpr int NCM = SPLIT ? 4 : key_groups<DK>();
+            float cm[NCM], snew[NCM], inv[NV];
+            if constexpr (SPLIT) col_absmax_split(U, cm);
+            else col_absmax<DK>(U, cm);
+            auto col_of = [](int j, int L) { return SPLIT ? key_col_split(j, L) : key_col(j, L); };
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-            key_scales<DK>(cm, lds + buf * (kWavesPerGroup * DKP), lds + 2 * kWavesPerGroup * DKP,
-                           wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv);
+            key_scales(cm, lds + buf * (LW * SLOT), lds + 2 * LW * SLOT, wv, rb, meta.n_rb,
+                       Prec<PREC>::R, snew, inv, col_of, half * CPL);
             if (rb == 0) {
 #pragma unroll
-                for (int t = 0; t < key_groups<DK>(); ++t) {
-                    const int col = key_col(t, threadIdx.x & 63);
+                for (int t = 0; t < NCM; ++t) {
+                    const int col = col_of(t, threadIdx.x & 63);
                     if (col < DK) scales[unit * DK + col] = snew[t];
                 }
             }
-            requantize_row<DK, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr,
-                                           inv);
+            requantize_row<CPL, PREC, true>(U, 0.0f, meta, b, h, row, active, io, nullptr,
+                                            inv, half * CPL);
         } else {
             requantize_row<CPL, PREC>(U, m, meta, b, h, row, active, io,
                                       has_scale<PREC>() ? scales + unit * dv_pad + row : nullptr,
@@ -1426,7 +1477,7 @@ __device__ __forceinline__ void run_queue(const WorkQueue &wq, Make &&make) {
     constexpr int P = TS::NCH;                   // whole rows are prefetched
     static_assert(P <= kMaxPrefetchChunks, "queued streams hold prefetchable rows");
     u32x4 cw[TS::NCH];
-    TaskSide<TS::NV> in0, in1;
+    typename TS::Side in0, in1;
     int n = wq.take();
     if (n < 0) return;
     make(wq.task(n)).issue(wq.seq(n), cw, in0);
@@ -1466,8 +1517,8 @@ __device__ __forceinline__ void run_queue_paired(const WorkQueue &wq, Make0 &&ma
     static_assert(T0::NCH <= kMaxPrefetchChunks && T1::NCH <= kMaxPrefetchChunks,
                   "paired streams need prefetchable rows");
     u32x4 cw[kMaxPrefetchChunks];
-    TaskSide<T0::NV> in0;
-    TaskSide<T1::NV> in1;
+    typename T0::Side in0;
+    typename T1::Side in1;
     int n = wq.take();
     if (n < 0) return;
     make0(wq.task(n)).issue(wq.seq(n), cw, in0);
@@ -1508,14 +1559,16 @@ constexpr bool pairable() {
 
 // Wavefronts per work-group of a launch: fused int pairs run one queued
 // group per CU.
-template <int P0, int P1, int DK>
+template <int P0, int P1, int DK, bool KEY = false>
 constexpr int group_waves() {
-    return pairable<P0, P1, DK>() ? kPairWavesPerGroup : kWavesPerGroup;
+    return pairable<P0, P1, DK>()   ? kPairWavesPerGroup
+           : KEY && DK > 128        ? kMaxKeyGroupWaves
+                                    : kWavesPerGroup;
 }
 
 template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
           bool WEND = false>
-__global__ void __launch_bounds__((64 * group_waves<P0, P1, DK>()))
+__global__ void __launch_bounds__((64 * group_waves<P0, P1, DK, KEY>()))
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
@@ -1534,14 +1587,14 @@ lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
             qp, kp, vp, alphap, betap, op, codes0, scales0, meta, meta.cls[0], task, nullptr,
             win0));
     } else if constexpr (KEY) {
-        // one class (a step, or with WEND a window's end); the n_rb (1, 2
-        // or 4) row blocks of a unit are consecutive tasks, so whole units
-        // share a work-group.  A wave past
+        // one class (a step, or with WEND a window's end); the n_rb row
+        // blocks of a unit are consecutive tasks, so whole units share a
+        // work-group (key_group_waves).  A wave past
         // the last task still takes part in the work-group's barriers: one
         // per sequence of its stride, as a working wave does (units of one
         // row block take no barrier at all).
         static_assert(P1 < 0, "key-column scales run one class per launch");
-        __shared__ float cmax[3 * kWavesPerGroup * 64 * key_groups<DK>()];  // two maxima buffers, staging
+        __shared__ float cmax[3 * key_lds_waves<DK>() * key_slot<DK>()];  // two maxima buffers, staging
         const int task = gx * key_group_waves(n_rb) + wv;
         if (task >= meta.cls[0].Hc * n_rb) {
             if (n_rb > 1)
@@ -1638,8 +1691,8 @@ template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = f
 hipError_t launch_one(const StepPtrs &p, const StepMeta &m, hipStream_t s) {
     auto kern = lores_step_kernel<DK, PC, DELTA, BF16IN, P0, P1, KEY, WEND>;
     const int W = KEY ? key_group_waves(m.n_rb) : group_waves<P0, P1, DK>();
-    static int per_cu_of[kWavesPerGroup + 1] = {0};      // resident work-groups per CU, by W
-    int &per_cu = per_cu_of[W <= kWavesPerGroup ? W : 0];
+    static int per_cu_of[kMaxKeyGroupWaves + 1] = {0};   // resident work-groups per CU, by W
+    int &per_cu = per_cu_of[W <= kMaxKeyGroupWaves ? W : 0];
     if (!per_cu) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern),
@@ -1715,6 +1768,7 @@ hipError_t launch_classes_key(int dk, bool pc, bool delta, bool bf16, const Step
         case 64: return launch_dk<64, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 256: return launch_dk<256, P0, -1, true>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -333,10 +333,7 @@ static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, bool pc,
         case 64: return LORES_WIN_KEY_PC(64);
         case 96: return LORES_WIN_KEY_PC(96);
         case 128: return LORES_WIN_KEY_PC(128);
-        case 256:                                       // value rows
-            if (key) return hipErrorInvalidValue;
-            return pc ? window_dk<256, PREC, false, true>(delta, bf16, p, m, s)
-                      : window_dk<256, PREC, false, false>(delta, bf16, p, m, s);
+        case 256: return LORES_WIN_KEY_PC(256);
         default: return hipErrorInvalidValue;
     }
 #undef LORES_WIN_KEY_PC
@@ -358,7 +355,7 @@ static hipError_t window_dequant_prec(int dk, bool key, const uint8_t *codes, co
         case 64: if (key) LORES_WD(64, true); else LORES_WD(64, false); break;
         case 96: if (key) LORES_WD(96, true); else LORES_WD(96, false); break;
         case 128: if (key) LORES_WD(128, true); else LORES_WD(128, false); break;
-        case 256: if (key) return hipErrorInvalidValue; LORES_WD(256, false); break;
+        case 256: if (key) LORES_WD(256, true); else LORES_WD(256, false); break;
         default: return hipErrorInvalidValue;
     }
 #undef LORES_WD

@@ -74,10 +74,6 @@ int main() {
                         size_t n = 0;
                         int rc = lores_state_alloc_window(B, H, dk, dv, mix.data(), axis, W, nullptr,
                                                           &n, nullptr, nullptr);
-                        if (dk > 128 && axis == 1) {    // split rows: value-row scales only
-                            CHECK(rc == LORES_EUNSUPPORTED);
-                            continue;
-                        }
                         CHECK(rc == LORES_OK);
                         Buf buf(n);
                         lores_state *st = nullptr;

@@ -50,7 +50,7 @@ def test_longest_window(prec, dk, dv):
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256), (3, 128, 180),
-                                    (4, 32, 100), (3, 96, 200)])
+                                    (4, 32, 100), (3, 96, 200), (3, 256, 100), (4, 256, 200)])
 def test_key_column_windows(prec, W, dk, dv):
     """Windows over key-column scales (the PACE combination): the window end
     takes the column maxima of the replayed state."""
@@ -123,7 +123,8 @@ def test_full_size_c5_window4(axis):
                                                (4, 128, 128, 0, "value"), (3, 128, 100, 1, "key"),
                                                (5, 64, 200, 1, "key"), (3, 96, 64, 1, "value"),
                                                (4, 32, 128, 1, "value"), (3, 96, 100, 1, "key"),
-                                               (4, 32, 64, 0, "key"), (3, 256, 70, 1, "value")])
+                                               (4, 32, 64, 0, "key"), (3, 256, 70, 1, "value"),
+                                               (3, 256, 100, 1, "key")])
 def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
     """Windows whose tokens carry one decay per key channel (the diagonal
     decay of the recurrence): the in-window readouts from the stored state
@@ -172,8 +173,6 @@ def test_window_one_is_the_plain_state():
                                         ("value", "kda_channel"), ("key", "kda_channel")])
 @pytest.mark.parametrize("dk", [128, 96, 256])
 def test_dequant_replays_the_buffer(prec, axis, decay, dk):
-    if dk > 128 and axis == "key":
-        pytest.skip("key-column scales are built for d_k <= 128")
     """Inside a window lores_dequant_state returns the current state: the
     stored state followed by the buffered tokens' fp32 recurrence, bit for
     bit against the oracle's replay of the same (oracle-written) buffer, for
