@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 6
+#define LORES_SPEC_VERSION 7
 
 /* Per-head state precision. */
 enum {
@@ -121,6 +121,9 @@ typedef struct lores_state lores_state;
  * holds row bytes 16c .. 16c + 15): element j is bits 6j .. 6j + 5, value
  * code + 32 (offset binary, 1..63); n_chunk = ceil(6 d_k / 128), the bits
  * after the last element are zero.
+ * A row of d_k > 128 is stored as two half rows of d_k / 2 columns, each laid
+ * out as above from its own first chunk (n_chunk = 2 n_chunk(d_k / 2): an
+ * int4 or int6 half that ends inside a chunk is zero-padded to its end).
  * The value of an int element is scale[row] * code (scale[column] * code
  * with key-column scales).  A row of all-zero bytes with scale 0 also reads
  * as zero, so a zero-filled buffer is S = 0.
@@ -153,10 +156,9 @@ typedef struct {
  * "Intra-State Quantization (Section 4)") with one scale per value row (the
  * same section, scale grouping), starting from S_0 = 0.
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
- *   d_k, d_v    key and value dimensions; d_k in {32, 64, 96, 128, 256}
- *               (160, 192 and 224 return LORES_EUNSUPPORTED, other values
- *               LORES_EINVAL), 1 <= d_v <= LORES_MAX_DV.  At d_k = 256 the
- *               classes of a state run one launch each.
+ *   d_k, d_v    key and value dimensions; d_k a multiple of 32, at most 256
+ *               (LORES_EINVAL otherwise), 1 <= d_v <= LORES_MAX_DV.  Above
+ *               d_k = 128 the classes of a state run one launch each.
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and

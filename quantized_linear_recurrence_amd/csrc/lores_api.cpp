@@ -57,8 +57,11 @@ bool has_scales(int p) { return is_int_prec(p) || p == LORES_FP8; }
 
 // Bytes per stored row: d_k elements of 32, 16, 8, 4 or 6 bits in whole
 // 16-byte chunks (only int6 rows can end in a partly used chunk).
+// 16-byte chunks of a stored row; a row of d_k > 128 is two halves of d_k / 2
+// columns, each padded to whole chunks (the step splits it across two lanes)
 int64_t row_bytes(int prec, int dk) {
     static const int bits[LORES_NUM_PREC] = {32, 16, 8, 4, 6, 8};
+    if (dk > 128) return 2 * row_bytes(prec, dk / 2);
     return (int64_t)((dk * bits[prec] + 127) / 128) * 16;
 }
 
@@ -73,8 +76,6 @@ int check_dims(int32_t B, int32_t H, int32_t dk, int32_t dv) {
     if (dk < 32 || dk % 32 != 0)
         return fail(LORES_EINVAL, "d_k must be a positive multiple of 32 (got %d)", dk);
     if (dk > 256) return fail(LORES_EINVAL, "d_k must be at most 256 (got %d)", dk);
-    if (dk > 128 && dk != 256)
-        return fail(LORES_EUNSUPPORTED, "d_k in (128, 256) is not built (got %d)", dk);
     if (dv < 1 || dv > LORES_MAX_DV)
         return fail(LORES_EINVAL, "d_v must be in [1, %d] (got %d)", LORES_MAX_DV, dv);
     return LORES_OK;
@@ -97,7 +98,7 @@ int plan(lores_state *st, const uint8_t *head_prec) {
         st->heads[p][st->n_class[p]++] = (uint16_t)h;
     }
     st->dv_pad = (st->dv + LORES_ROW_BLOCK - 1) / LORES_ROW_BLOCK * LORES_ROW_BLOCK;
-    // tasks of 64 rows, or of 32 rows split across lane pairs at d_k = 256
+    // tasks of 64 rows, or of 32 rows split across lane pairs at d_k > 128
     st->n_rb = st->dk > 128 ? (st->dv + 31) / 32 : st->dv_pad / LORES_ROW_BLOCK;
     uint64_t off = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c) {

@@ -64,6 +64,10 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
             float x[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
+                if (c * E + e >= CPL) {              // the padding of a half chunk
+                    x[e] = 0.0f;
+                    continue;
+                }
                 if constexpr (PREC == LORES_FP8) {
                     x[e] = sc(c * E + e) * fp8_value(wd[e >> 2], e & 3);
                 } else if constexpr (PREC == LORES_INT8) {
@@ -81,7 +85,8 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
             }
 #pragma unroll
             for (int e = 0; e < E; e += 4) {
-                *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
+                if (c * E + e < CPL)
+                    *reinterpret_cast<f32x4 *>(orow + c * E + e) = f32x4{x[e], x[e + 1], x[e + 2], x[e + 3]};
             }
         }
     }
@@ -140,7 +145,10 @@ lores_quant_kernel(const float *__restrict__ X, uint8_t *__restrict__ codes,
         float cm[NCM], snew[NCM], inv[CPL / 16];
         if constexpr (SPLIT) col_absmax_split(U, cm);
         else col_absmax<DK>(U, cm);
-        auto col_of = [](int j, int L) { return SPLIT ? key_col_split(j, L) : key_col(j, L); };
+        auto col_of = [](int j, int L) {
+            if constexpr (SPLIT) return key_col_split<CPL>(j, L);
+            else return key_col(j, L);
+        };
         key_scales(cm, cmax, cmax + LW * SLOT, wv, rb, meta.n_rb, Prec<PREC>::R, snew, inv,
                    col_of, half * CPL);
         if (rb == 0) {
@@ -176,6 +184,9 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
                 case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 160: hipLaunchKernelGGL((lores_quant_kernel<160, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 192: hipLaunchKernelGGL((lores_quant_kernel<192, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
+                case 224: hipLaunchKernelGGL((lores_quant_kernel<224, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 case 256: hipLaunchKernelGGL((lores_quant_kernel<256, PREC, true>), kgrid, kblock, 0, s, X, codes, scales, m); break;
                 default: return hipErrorInvalidValue;
             }
@@ -187,6 +198,9 @@ static hipError_t quant_prec(int dk, const float *X, uint8_t *codes, float *scal
         case 64: hipLaunchKernelGGL((lores_quant_kernel<64, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 96: hipLaunchKernelGGL((lores_quant_kernel<96, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 128: hipLaunchKernelGGL((lores_quant_kernel<128, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 160: hipLaunchKernelGGL((lores_quant_kernel<160, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 192: hipLaunchKernelGGL((lores_quant_kernel<192, PREC>), grid, block, 0, s, X, codes, scales, m); break;
+        case 224: hipLaunchKernelGGL((lores_quant_kernel<224, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         case 256: hipLaunchKernelGGL((lores_quant_kernel<256, PREC>), grid, block, 0, s, X, codes, scales, m); break;
         default: return hipErrorInvalidValue;
     }
@@ -218,6 +232,9 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
                 case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 160: hipLaunchKernelGGL((lores_dequant_kernel<160, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 192: hipLaunchKernelGGL((lores_dequant_kernel<192, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
+                case 224: hipLaunchKernelGGL((lores_dequant_kernel<224, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 case 256: hipLaunchKernelGGL((lores_dequant_kernel<256, PREC, true>), grid, block, 0, s, codes, scales, out, m); break;
                 default: return hipErrorInvalidValue;
             }
@@ -229,6 +246,9 @@ static hipError_t dequant_prec(int dk, const uint8_t *codes, const float *scales
         case 64: hipLaunchKernelGGL((lores_dequant_kernel<64, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 96: hipLaunchKernelGGL((lores_dequant_kernel<96, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 128: hipLaunchKernelGGL((lores_dequant_kernel<128, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 160: hipLaunchKernelGGL((lores_dequant_kernel<160, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 192: hipLaunchKernelGGL((lores_dequant_kernel<192, PREC>), grid, block, 0, s, codes, scales, out, m); break;
+        case 224: hipLaunchKernelGGL((lores_dequant_kernel<224, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         case 256: hipLaunchKernelGGL((lores_dequant_kernel<256, PREC>), grid, block, 0, s, codes, scales, out, m); break;
         default: return hipErrorInvalidValue;
     }

@@ -592,21 +592,27 @@ __device__ __forceinline__ void col_absmax(const float (&U)[DK], float (&cm)[key
 // U holds the lane's 128 columns, the levels across lane bits 2, 4, 0, 1
 // and 3 leave two registers per 64-column group, and register 2 t + s of
 // lane L holds the maximum of column key_col_split(2 t + s, L).
+// With CPL < 128 columns per half (d_k = 160, 192, 224) the columns past
+// CPL read as zeros and their maxima go to the stage slots past d_k.
+template <int CPL>
 __device__ __forceinline__ int key_col_split(int j, int L) {
-    const int t = j >> 1, s = j & 1;
-    return ((L >> 5) & 1) * 128 + 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + s * 8 +
-           (L & 1) * 4 + ((L >> 4) & 1) * 2 + ((L >> 2) & 1);
+    const int t = j >> 1, s = j & 1, half = (L >> 5) & 1;
+    const int c = 64 * t + ((L >> 3) & 1) * 32 + ((L >> 1) & 1) * 16 + s * 8 + (L & 1) * 4 +
+                  ((L >> 4) & 1) * 2 + ((L >> 2) & 1);
+    return c < CPL ? half * CPL + c : 2 * CPL + half * (128 - CPL) + (c - CPL);
 }
 
-__device__ __forceinline__ void col_absmax_split(const float (&U)[128], float (&cm)[4]) {
+template <int CPL>
+__device__ __forceinline__ void col_absmax_split(const float (&U)[CPL], float (&cm)[4]) {
     const int lane = threadIdx.x & 63;
     const bool h0 = lane & 1, h1 = lane & 2, h2 = lane & 4, h3 = lane & 8;
+    const float zeros[16] = {};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         float g[4][2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float *u = &U[64 * t + 16 * q];
+            const float *u = 64 * t + 16 * q < CPL ? &U[64 * t + 16 * q] : zeros;
             float s[8], o[8], y[8];
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -895,6 +901,10 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 8;
+                    if (j >= DK) {                   // the padding of a half chunk
+                        ow[q4] = 0u;
+                        continue;
+                    }
                     float ze[4], zo[4];
                     if constexpr (KEY) {
                         float z[8];
@@ -1019,20 +1029,22 @@ struct TaskSide {
 // SPLIT (d_k > 128): a row of d_k fp32 values does not fit one lane's
 // registers beside the rest, so two lanes share it: lane L < 32 holds
 // columns [0, d_k / 2) of row 32 rb + L and lane L + 32 the other half
-// (each half whole 16-byte chunks of every class at d_k = 256).  Each lane
-// runs the per-lane code on its CPL = d_k / 2 columns; r, o and the row
-// maximum are combined across the pair with one v_permlane32_swap each (in
-// the same order in both lanes, so both hold the same values), and the
-// second lane's draws start at column CPL.
+// (each half of a stored row starts on a chunk: the layout pads the first
+// half to whole 16-byte chunks).  Each lane runs the per-lane code on its
+// CPL = d_k / 2 columns (an int4 half of 80 or 112 columns ends inside its
+// last chunk); r, o and the row maximum are combined across the pair with
+// one v_permlane32_swap each (in the same order in both lanes, so both hold
+// the same values), and the second lane's draws start at column CPL.
 template <int DK, int PREC, bool PC, bool DELTA, bool BF16IN, bool KEY = false, bool WEND = false>
 struct TaskStream {
     static constexpr bool SPLIT = DK > 128;
     static constexpr int CPL = SPLIT ? DK / 2 : DK;   // columns per lane
     static constexpr int RPW = SPLIT ? 32 : 64;       // rows per wavefront task
-    static_assert(!SPLIT || DK == 256, "split rows: d_k = 256");
+    static_assert(DK % 32 == 0 && DK <= 256, "d_k a multiple of 32, at most 256");
     static constexpr int E = Prec<PREC>::E;
     static constexpr int NCH = row_chunks<CPL, PREC>();   // chunks of the lane's columns
-    static_assert(PREC == LORES_INT6 || CPL % E == 0, "d_k must be a whole number of 16-byte chunks");
+    static_assert(PREC == LORES_INT6 || CPL % E == 0 || (PREC == LORES_INT4 && CPL % 16 == 0),
+                  "a lane's columns end on a chunk (int4 halves: on a half chunk)");
 
     const void *__restrict__ qp;
     const void *__restrict__ kp;
@@ -1232,6 +1244,7 @@ struct TaskStream {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int j = c * E + e;
+                if (j >= CPL) break;                     // the padding of a half chunk
                 if constexpr (PC && has_scale<PREC>() && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
@@ -1372,7 +1385,10 @@ struct TaskStream {
             float cm[NCM], snew[NCM], inv[NV];
             if constexpr (SPLIT) col_absmax_split(U, cm);
             else col_absmax<DK>(U, cm);
-            auto col_of = [](int j, int L) { return SPLIT ? key_col_split(j, L) : key_col(j, L); };
+            auto col_of = [](int j, int L) {
+                if constexpr (SPLIT) return key_col_split<CPL>(j, L);
+                else return key_col(j, L);
+            };
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
             key_scales(cm, lds + buf * (LW * SLOT), lds + 2 * LW * SLOT, wv, rb, meta.n_rb,
                        Prec<PREC>::R, snew, inv, col_of, half * CPL);
@@ -1751,10 +1767,11 @@ hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs
         case 64: return launch_dk<64, P0, P1>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, P1>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, P1>(pc, delta, bf16, p, m, s);
-        case 256:
-            // split rows run one class per launch
-            if constexpr (P1 < 0) return launch_dk<256, P0, P1>(pc, delta, bf16, p, m, s);
-            else return hipErrorInvalidValue;
+        // split rows run one class per launch
+        case 160: if constexpr (P1 < 0) return launch_dk<160, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
+        case 192: if constexpr (P1 < 0) return launch_dk<192, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
+        case 224: if constexpr (P1 < 0) return launch_dk<224, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
+        case 256: if constexpr (P1 < 0) return launch_dk<256, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -1768,6 +1785,9 @@ hipError_t launch_classes_key(int dk, bool pc, bool delta, bool bf16, const Step
         case 64: return launch_dk<64, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 160: return launch_dk<160, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 192: return launch_dk<192, P0, -1, true>(pc, delta, bf16, p, m, s);
+        case 224: return launch_dk<224, P0, -1, true>(pc, delta, bf16, p, m, s);
         case 256: return launch_dk<256, P0, -1, true>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }

@@ -73,12 +73,28 @@ __device__ __forceinline__ float stored(const u32x4 *cw, int j) {
     }
 }
 
+// A stored row of d_k > 128 columns is two halves, the second starting on a
+// chunk: its chunks, and element j of it.
+template <int DK, int PREC>
+constexpr int stored_chunks() {
+    return DK > 128 ? 2 * row_chunks<DK / 2, PREC>() : row_chunks<DK, PREC>();
+}
+template <int DK, int PREC>
+__device__ __forceinline__ float stored_at(const u32x4 *cw, int j) {
+    if constexpr (DK > 128) {
+        constexpr int H = DK / 2, NH = row_chunks<H, PREC>();
+        return j < H ? stored<PREC>(cw, j) : stored<PREC>(cw + NH, j - H);
+    } else {
+        return stored<PREC>(cw, j);
+    }
+}
+
 // fl(code * a): int rows as fma(code + off, a, -off a), exact since off * a is
 // a power-of-two multiple of a
-template <int PREC>
+template <int DK, int PREC>
 __device__ __forceinline__ float scaled_code(const u32x4 *cw, int j, float a, float na) {
-    if constexpr (PREC == LORES_FP8) return stored<PREC>(cw, j) * a;
-    else return __builtin_fmaf(stored<PREC>(cw, j), a, na);
+    if constexpr (PREC == LORES_FP8) return stored_at<DK, PREC>(cw, j) * a;
+    else return __builtin_fmaf(stored_at<DK, PREC>(cw, j), a, na);
 }
 
 struct WindowTask {
@@ -120,7 +136,7 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
                          const float *__restrict__ betap, float *__restrict__ op,
                          const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                          float *__restrict__ win, const StepMeta meta) {
-    constexpr int NCH = row_chunks<DK, PREC>(), NV = DK / 16;
+    constexpr int NCH = stored_chunks<DK, PREC>(), NV = DK / 16;
     WindowTask w;
     if (!window_task(meta, w)) return;
     const int lane = threadIdx.x & 63;
@@ -192,7 +208,7 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     for (int gi = 0; gi < NV; ++gi) {
         float x[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = stored<PREC>(cw, 16 * gi + e);
+        for (int e = 0; e < 16; ++e) x[e] = stored_at<DK, PREC>(cw, 16 * gi + e);
         if constexpr (DELTA) dot16(A, x, wk[gi]);
         dot16(Bq, x, wq[gi]);
     }
@@ -242,7 +258,7 @@ __global__ void __launch_bounds__(64 * kWavesPerGroup)
 lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict__ scales,
                             const float *__restrict__ win, float *__restrict__ out,
                             const StepMeta meta) {
-    constexpr int NCH = row_chunks<DK, PREC>();
+    constexpr int NCH = stored_chunks<DK, PREC>();
     WindowTask w;
     if (!window_task(meta, w)) return;
     const int lane = threadIdx.x & 63;
@@ -254,8 +270,10 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
     const int nslot = meta.window - 1, n = meta.wpos;
     const float *ub = win + w.unit * window_unit_floats(meta.window, meta.dv_pad, DK);
     const float *gslot = ub, *kslot = ub + (long)nslot * dv_pad, *aslot = kslot + (long)nslot * DK;
-    // columns are independent in the replay: blocks of at most 128 of them
-    constexpr int CB = DK < 128 ? DK : 128, NVB = CB / 16;
+    // columns are independent in the replay: blocks of at most 128 of them,
+    // which tile the row exactly (two halves above d_k = 128)
+    constexpr int CB = DK > 128 ? DK / 2 : DK, NVB = CB / 16;
+    static_assert(DK % CB == 0 && CB <= 128, "column blocks tile the row");
     const bool pc = meta.win_pc != 0;
     const float s = KEY ? 0.0f : scales[w.unit * dv_pad + w.lrow];
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -270,7 +288,7 @@ lores_window_dequant_kernel(const uint8_t *__restrict__ codes, const float *__re
             const float a1 = (KEY ? scales[w.unit * DK + j0 + j] : s) * aslot[pc ? j0 + j : 0];
             float na1 = 0.0f;
             if constexpr (PREC != LORES_FP8) na1 = a1 * -Prec<PREC>::OFF;
-            U[j] = scaled_code<PREC>(cw, j0 + j, a1, na1);
+            U[j] = scaled_code<DK, PREC>(cw, j0 + j, a1, na1);
         }
         for (int tau = 1; tau <= n; ++tau) {
             const float gt = gslot[(long)(tau - 1) * dv_pad + w.lrow];
@@ -333,6 +351,9 @@ static hipError_t window_prec(int dk, bool delta, bool bf16, bool key, bool pc,
         case 64: return LORES_WIN_KEY_PC(64);
         case 96: return LORES_WIN_KEY_PC(96);
         case 128: return LORES_WIN_KEY_PC(128);
+        case 160: return LORES_WIN_KEY_PC(160);
+        case 192: return LORES_WIN_KEY_PC(192);
+        case 224: return LORES_WIN_KEY_PC(224);
         case 256: return LORES_WIN_KEY_PC(256);
         default: return hipErrorInvalidValue;
     }
@@ -355,6 +376,9 @@ static hipError_t window_dequant_prec(int dk, bool key, const uint8_t *codes, co
         case 64: if (key) LORES_WD(64, true); else LORES_WD(64, false); break;
         case 96: if (key) LORES_WD(96, true); else LORES_WD(96, false); break;
         case 128: if (key) LORES_WD(128, true); else LORES_WD(128, false); break;
+        case 160: if (key) LORES_WD(160, true); else LORES_WD(160, false); break;
+        case 192: if (key) LORES_WD(192, true); else LORES_WD(192, false); break;
+        case 224: if (key) LORES_WD(224, true); else LORES_WD(224, false); break;
         case 256: if (key) LORES_WD(256, true); else LORES_WD(256, false); break;
         default: return hipErrorInvalidValue;
     }

@@ -60,9 +60,13 @@ int main() {
     CHECK(size_of(1, 1, 128, 64, {LORES_INT8}, LORES_SCALE_KEY) == 8192 + 512);
     CHECK(size_of(1, 1, 64, 64, {LORES_INT8}, 0, 3) == 4096 + 256 + 1536);   // 2*(64+2*64)*4 = 1536
     CHECK(size_of(1, 1, 64, 1, {LORES_INT6}) == 48 * 64 + 256);             // 3 chunks of 16 B per row
+    // d_k > 128: two half rows, each whole chunks (int4 at 160: 2 x 48 B, int6 at 224: 2 x 96 B)
+    CHECK(size_of(1, 1, 160, 64, {LORES_INT4}) == 96 * 64 + 256);
+    CHECK(size_of(1, 1, 224, 64, {LORES_INT6}) == 192 * 64 + 256);
+    CHECK(size_of(1, 1, 256, 64, {LORES_INT4}) == 128 * 64 + 256);
 
     // plans over many shapes: segments in bounds, disjoint, 256-aligned
-    const int dks[] = {32, 64, 96, 128, 256};
+    const int dks[] = {32, 64, 96, 128, 160, 192, 224, 256};
     const int dvs[] = {1, 64, 65, 128, 150, 200, 256};
     std::vector<std::vector<uint8_t>> mixes = {{2}, {3, 2}, {0, 1, 2, 3, 4, 5}, {5, 5, 4}, {1, 3}};
     for (int dk : dks)

@@ -19,9 +19,21 @@ SCALED_CLASSES = (2, 3, 4, 5)        # classes with fp32 scales (per value row o
 
 def n_chunks(c, dk):
     """16-byte chunks per row: d_k elements of 32, 16, 8, 4 or 6 bits, the
-    last chunk zero-padded."""
+    last chunk zero-padded; a row of d_k > 128 is two halves of d_k / 2
+    columns, each padded to whole chunks."""
+    if dk > 128:
+        return 2 * n_chunks(c, dk // 2)
     bits = {0: 32, 1: 16, 2: 8, 3: 4, 4: 6, 5: 8}[c]
     return (dk * bits + 127) // 128
+
+
+def _halves(state_unit, h, dk):
+    """The columns [h dk/2, (h + 1) dk/2) of a unit's per-element arrays."""
+    sl = slice(h * (dk // 2), (h + 1) * (dk // 2))
+    out = {k: np.asarray(v)[:, sl] for k, v in state_unit.items() if k != "scales"}
+    if "scales" in state_unit:                   # stored once, by the caller
+        out["scales"] = np.zeros(next(iter(out.values())).shape[0], np.float32)
+    return out
 
 
 def _pack6(vals):
@@ -56,6 +68,20 @@ def pack_unit(c, dk, dv, dv_pad, state_unit, key=False):
     The stored scales are [dv_pad] (value rows) or, with key=True, the
     unit's [dk] key-column scales.
     """
+    if dk > 128:
+        if c == 5:
+            fp8 = np.asarray(state_unit["fp8"], np.uint8).reshape(dv, dk)
+            su = dict(state_unit, fp8=fp8)
+        else:
+            su = state_unit
+        parts = [pack_unit(c, dk // 2, dv, dv_pad, _halves(su, h, dk), key=False)[0]
+                 .reshape(-1, dv_pad, 16) for h in (0, 1)]
+        sc = None
+        if c in SCALED_CLASSES:
+            ns, nv = (dk, dk) if key else (dv_pad, dv)
+            sc = np.zeros(ns, np.float32)
+            sc[:nv] = state_unit["scales"]
+        return np.concatenate(parts, axis=0).reshape(-1), sc
     n_chunk = n_chunks(c, dk)
     out = np.zeros((n_chunk, dv_pad, 16), np.uint8)
     sc = None
@@ -79,7 +105,9 @@ def pack_unit(c, dk, dv, dv_pad, state_unit, key=False):
             row[:, :packed.shape[1]] = packed
             out[:, :dv, :] = row.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
         else:
-            pairs = off.reshape(dv, n_chunk, 16, 2)
+            padded = np.zeros((dv, n_chunk * 32), np.uint8)     # a half chunk at the end stays 0
+            padded[:, :dk] = off
+            pairs = padded.reshape(dv, n_chunk, 16, 2)
             by = (pairs[..., 0] | (pairs[..., 1] << 4)).astype(np.uint8)
             out[:, :dv, :] = by.transpose(1, 0, 2)
     elif c == 1:
@@ -93,6 +121,20 @@ def pack_unit(c, dk, dv, dv_pad, state_unit, key=False):
 
 def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None, key=False):
     """Inverse of pack_unit."""
+    if dk > 128:
+        nh = n_chunks(c, dk // 2)
+        raw = np.asarray(code_bytes, np.uint8).reshape(2 * nh, dv_pad, 16)
+        halves = [unpack_unit(c, dk // 2, dv, dv_pad, raw[h * nh:(h + 1) * nh].reshape(-1), scales)
+                  for h in (0, 1)]
+        out = {}
+        for k in halves[0]:
+            if k == "scales":
+                continue
+            out[k] = np.concatenate([halves[0][k], halves[1][k]], axis=1)
+        if c in SCALED_CLASSES:
+            nv = dk if key else dv
+            out["scales"] = np.asarray(scales, np.float32)[:nv].copy()
+        return out
     n_chunk = n_chunks(c, dk)
     nv = dk if key else dv
     raw = np.asarray(code_bytes, np.uint8).reshape(n_chunk, dv_pad, 16)[:, :dv, :]
@@ -108,7 +150,7 @@ def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None, key=False):
     if c == 3:
         lo = (rows & 0x0F).astype(np.int32)
         hi = (rows >> 4).astype(np.int32)
-        codes = np.stack([lo, hi], axis=-1).reshape(dv, dk) - 8
+        codes = np.stack([lo, hi], axis=-1).reshape(dv, -1)[:, :dk] - 8
         return {"codes": codes, "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 1:
         return {"bits": rows.view(np.uint16).reshape(dv, dk).copy()}

@@ -302,7 +302,9 @@ def test_error_paths_live_handle():
 
 @pytest.mark.parametrize("dk,dv,rounding", [(128, 128, "sr"), (96, 65, "sr"), (32, 1, "sr"),
                                              (64, 200, "nearest"), (128, 64, "nearest"),
-                                             (256, 100, "sr"), (256, 33, "nearest")])
+                                             (256, 100, "sr"), (256, 33, "nearest"),
+                                             (160, 70, "sr"), (192, 100, "nearest"),
+                                             (224, 33, "sr")])
 def test_quant_state_matches_oracle(dk, dv, rounding):
     """lores_quant_state equals the oracle's quantization of the same fp32
     state bit for bit (no summation is involved), for every precision, with

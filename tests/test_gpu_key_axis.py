@@ -35,7 +35,8 @@ def _sample_units(B, H, n, seed=0):
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 100), (64, 256), (128, 200), (128, 150),
                                    (64, 192), (32, 64), (96, 100), (32, 200), (96, 150),
-                                   (256, 100), (256, 256), (256, 33), (256, 160)])
+                                   (256, 100), (256, 256), (256, 33), (256, 160), (160, 100),
+                                   (192, 70), (224, 256)])
 def test_each_scaled_class(prec, dk, dv):
     w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=4, delta=1)
     log(f"case: key columns prec={prec} B=3 H=4 dk={dk} dv={dv} delta=1, random initial state")
@@ -46,7 +47,7 @@ def test_each_scaled_class(prec, dk, dv):
 
 @pytest.mark.parametrize("delta", [0, 1])
 @pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
-@pytest.mark.parametrize("dk", [128, 256])
+@pytest.mark.parametrize("dk", [128, 256, 160])
 def test_mixed_heads_from_zero(delta, decay, dk):
     w = C1.scaled(B=2, H=6, dk=dk, dv=128, T=10, delta=delta, decay=decay)
     log(f"case: key columns, heads fp32/bf16/int8/int4/int6/fp8, from S_0 = 0, delta={delta} "
@@ -82,7 +83,7 @@ def test_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 200), (64, 1), (128, 160), (32, 70),
-                                   (96, 256), (256, 100), (256, 256)])
+                                   (96, 256), (256, 100), (256, 256), (224, 100), (160, 33)])
 def test_quant_and_dequant_match_oracle(dk, dv):
     """lores_quant_state with key columns equals the oracle bit for bit (the
     column maxima span every row block of a unit), and lores_dequant_state

@@ -41,7 +41,7 @@ def test_small_each_precision(prec, delta):
 
 
 @pytest.mark.parametrize("dk,dv", [(96, 100), (32, 1), (128, 65), (64, 128), (256, 100),
-                                   (256, 33)])
+                                   (256, 33), (160, 70), (192, 100), (224, 33)])
 @pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
 def test_ragged_mixed_precisions(dk, dv, decay):
     w = C1.scaled(B=3, H=6, dk=dk, dv=dv, T=5, decay=decay)
@@ -54,11 +54,13 @@ def test_ragged_mixed_precisions(dk, dv, decay):
 
 @pytest.mark.parametrize("prec", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("delta", [0, 1])
-def test_split_rows_each_precision(prec, delta):
-    """d_k = 256: each row split across a lane pair (r, o and the row maximum
-    combined across the pair, the second lane's draws from column 128)."""
-    w = C1.scaled(B=2, H=3, dk=256, dv=70, T=8, delta=delta)
-    log(f"case: split rows B=2 H=3 d_k=256 d_v=70 prec={prec} delta={delta}, random initial state")
+@pytest.mark.parametrize("dk", [256, 160, 224])
+def test_split_rows_each_precision(prec, delta, dk):
+    """d_k > 128: each row split across a lane pair (r, o and the row maximum
+    combined across the pair, the second lane's draws from column d_k / 2;
+    at 160 and 224 the int4 and int6 half rows end inside a chunk)."""
+    w = C1.scaled(B=2, H=3, dk=dk, dv=70, T=8, delta=delta)
+    log(f"case: split rows B=2 H=3 d_k={dk} d_v=70 prec={prec} delta={delta}, random initial state")
     s = run_parity(w, T=w.T, head_prec=[prec] * w.H, init="random")
     log(s.summary())
     s.check()

@@ -25,7 +25,8 @@ DEV = "cuda"
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("W,dk,dv,delta", [(2, 64, 64, 1), (4, 128, 100, 1), (3, 128, 128, 0),
-                                           (3, 256, 100, 1), (4, 256, 33, 0),
+                                           (3, 256, 100, 1), (4, 256, 33, 0), (3, 160, 100, 1),
+                                           (4, 224, 70, 0),
                                            (5, 64, 200, 1), (3, 32, 70, 1), (4, 96, 128, 1)])
 def test_each_scaled_class(prec, W, dk, dv, delta):
     w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, delta=delta)
@@ -50,7 +51,8 @@ def test_longest_window(prec, dk, dv):
 
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("W,dk,dv", [(3, 64, 64), (4, 128, 100), (4, 64, 256), (3, 128, 180),
-                                    (4, 32, 100), (3, 96, 200), (3, 256, 100), (4, 256, 200)])
+                                    (4, 32, 100), (3, 96, 200), (3, 256, 100), (4, 256, 200),
+                                    (3, 192, 100), (4, 160, 70)])
 def test_key_column_windows(prec, W, dk, dv):
     """Windows over key-column scales (the PACE combination): the window end
     takes the column maxima of the replayed state."""
@@ -124,7 +126,8 @@ def test_full_size_c5_window4(axis):
                                                (5, 64, 200, 1, "key"), (3, 96, 64, 1, "value"),
                                                (4, 32, 128, 1, "value"), (3, 96, 100, 1, "key"),
                                                (4, 32, 64, 0, "key"), (3, 256, 70, 1, "value"),
-                                               (3, 256, 100, 1, "key")])
+                                               (3, 256, 100, 1, "key"), (3, 224, 70, 1, "key"),
+                                               (4, 160, 100, 1, "value")])
 def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
     """Windows whose tokens carry one decay per key channel (the diagonal
     decay of the recurrence): the in-window readouts from the stored state
@@ -171,7 +174,7 @@ def test_window_one_is_the_plain_state():
 @pytest.mark.parametrize("prec", [2, 3, 4, 5])
 @pytest.mark.parametrize("axis,decay", [("value", "softplus_step"), ("key", "softplus_step"),
                                         ("value", "kda_channel"), ("key", "kda_channel")])
-@pytest.mark.parametrize("dk", [128, 96, 256])
+@pytest.mark.parametrize("dk", [128, 96, 256, 160, 224])
 def test_dequant_replays_the_buffer(prec, axis, decay, dk):
     """Inside a window lores_dequant_state returns the current state: the
     stored state followed by the buffered tokens' fp32 recurrence, bit for

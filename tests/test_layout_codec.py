@@ -7,7 +7,8 @@ from tests import layout_codec as lc
 
 
 @pytest.mark.parametrize("c,r", [(2, 127), (3, 7), (4, 31)])
-@pytest.mark.parametrize("dk,dv", [(32, 1), (64, 64), (96, 70), (128, 128)])
+@pytest.mark.parametrize("dk,dv", [(32, 1), (64, 64), (96, 70), (128, 128), (160, 33),
+                                   (192, 70), (224, 1), (256, 100)])
 def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
     dv_pad = (dv + 63) // 64 * 64
     vals = np.arange(-r, r + 1)
@@ -15,7 +16,9 @@ def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
     codes = np.roll(codes, 3, axis=1)                 # every value reaches every column
     scales = np.linspace(0.5, 2, dv).astype(np.float32)
     by, sc = lc.pack_unit(c, dk, dv, dv_pad, {"codes": codes, "scales": scales})
-    assert by.size == dv_pad * 16 * -(-(dk * {2: 8, 3: 4, 4: 6}[c]) // 128)
+    bits = {2: 8, 3: 4, 4: 6}[c]
+    row_chunks = 2 * -(-(dk // 2 * bits) // 128) if dk > 128 else -(-(dk * bits) // 128)
+    assert by.size == dv_pad * 16 * row_chunks
     back = lc.unpack_unit(c, dk, dv, dv_pad, by, sc)
     assert np.array_equal(back["codes"], codes) and np.array_equal(back["scales"], scales)
 
@@ -74,3 +77,35 @@ def test_fp8_bytes_roundtrip():
     back = lc.unpack_unit(5, dk, dv, 128, packed, psc)
     assert np.array_equal(back["fp8"], by) and np.array_equal(back["scales"], sc)
     assert packed.reshape(dk // 16, 128, 16)[1, 3, 5] == by[3, 16 + 5]   # chunk 1, row 3, byte 5
+
+
+def test_split_row_halves_start_on_a_chunk():
+    """Above d_k = 128 a row is two half rows, the second starting on its own
+    chunk: int4 at d_k = 160 keeps 80 columns per half, so half 0 fills 2.5
+    chunks (the rest of its third chunk zero) and column 80 is the low nibble
+    of byte 0 of chunk 3."""
+    dk, dv = 160, 1
+    codes = np.zeros((dv, dk), np.int64)
+    codes[0, 79] = 7                                  # half 0, last column: chunk 2, byte 7, high nibble
+    codes[0, 80] = -7                                 # half 1, first column: chunk 3, byte 0, low nibble
+    by, _ = lc.pack_unit(3, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
+    ch = by.reshape(6, 64, 16)[:, 0, :]
+    assert ch[2, 7] == (8 | (15 << 4)) and (ch[2, 8:] == 0).all()
+    assert ch[3, 0] == (1 | (8 << 4))
+
+
+def test_split_row_roundtrip_float_and_fp8():
+    g = np.random.default_rng(5)
+    for dk, dv in [(160, 3), (224, 65), (256, 64)]:
+        dvp = (dv + 63) // 64 * 64
+        bits = g.integers(0, 65536, (dv, dk), dtype=np.uint16)
+        by, _ = lc.pack_unit(1, dk, dv, dvp, {"bits": bits})
+        assert np.array_equal(lc.unpack_unit(1, dk, dv, dvp, by)["bits"], bits)
+        X = g.standard_normal((dv, dk)).astype(np.float32)
+        by, _ = lc.pack_unit(0, dk, dv, dvp, {"X": X})
+        assert np.array_equal(lc.unpack_unit(0, dk, dv, dvp, by)["X"], X)
+        f8 = g.integers(0, 256, (dv, dk)).astype(np.uint8)
+        sc = np.linspace(0.1, 3, dk).astype(np.float32)         # key-column scales
+        by, psc = lc.pack_unit(5, dk, dv, dvp, {"fp8": f8, "scales": sc}, key=True)
+        back = lc.unpack_unit(5, dk, dv, dvp, by, psc, key=True)
+        assert np.array_equal(back["fp8"], f8) and np.array_equal(back["scales"], sc)

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lores_lib):
 def test_spec_version(lores_lib):
     hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
     v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
-    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 6
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 7
 
 
 def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
@@ -53,7 +53,9 @@ def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
         if not hc:
             continue
         off = (off + 255) // 256 * 256
-        off += B * hc * -(-(dk * bits[c]) // 128) * 16 * dvp     # whole 16-byte chunks per row
+        # whole 16-byte chunks per row; above d_k = 128 per half row
+        chunks = 2 * -(-(dk // 2 * bits[c]) // 128) if dk > 128 else -(-(dk * bits[c]) // 128)
+        off += B * hc * chunks * 16 * dvp
         if c in (2, 3, 4, 5):                      # one fp32 scale per value row / key column
             off = (off + 255) // 256 * 256
             off += B * hc * (dk if key else dvp) * 4
@@ -68,7 +70,9 @@ def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):
     (128, 32, 128, 128, [1] * 8 + [2] * 24), (2048, 32, 128, 128, [2] * 16 + [3] * 16),
     (3, 4, 96, 100, [0, 1, 2, 3]), (1, 1, 32, 1, [3]), (2048, 32, 128, 128, [4] * 16 + [3] * 16),
     (3, 5, 96, 65, [4, 0, 1, 2, 3]), (2, 1, 32, 1, [4]), (4, 6, 64, 100, [5, 4, 3, 2, 1, 0]),
-    (3, 6, 256, 100, [5, 4, 3, 2, 1, 0]), (2, 2, 256, 1, [2, 3])])
+    (3, 6, 256, 100, [5, 4, 3, 2, 1, 0]), (2, 2, 256, 1, [2, 3]),
+    (3, 6, 160, 100, [5, 4, 3, 2, 1, 0]), (3, 6, 192, 65, [5, 4, 3, 2, 1, 0]),
+    (3, 6, 224, 33, [5, 4, 3, 2, 1, 0])])
 def test_size_query_matches_documented_layout(lores_lib, B, H, dk, dv, prec):
     assert lores.lores_state_alloc(B, H, dk, dv, prec) == _layout_bytes(B, H, dk, dv, prec)
 
@@ -108,10 +112,9 @@ def test_invalid_arguments_return_codes_without_gpu(lores_lib):
     for B, H, dk, dv in bad_dims:
         assert L.lores_state_alloc(B, H, dk, dv, hp, None, ctypes.byref(nb), None, None) == -1
         assert lores.lores_last_error()
-    # d_k in (128, 256) is not built; d_k = 256 (split rows) takes either
-    # scale axis, with or without windows
+    # d_k above 128 (split rows) takes either scale axis, with or without windows
     for dk in (160, 192, 224):
-        assert L.lores_state_alloc(1, 4, dk, 64, hp, None, ctypes.byref(nb), None, None) == -2
+        assert L.lores_state_alloc(1, 4, dk, 64, hp, None, ctypes.byref(nb), None, None) == 0
     assert L.lores_state_alloc(1, 4, 288, 64, hp, None, ctypes.byref(nb), None, None) == -1
     assert L.lores_state_alloc(1, 4, 256, 64, hp, None, ctypes.byref(nb), None, None) == 0
     assert L.lores_state_alloc_axis(1, 4, 256, 64, hp, 1, None, ctypes.byref(nb), None,
