@@ -77,7 +77,7 @@ enum {
 enum {
     LORES_OK = 0,
     LORES_EINVAL = -1,      /* invalid argument (NULL, misaligned, out of range)  */
-    LORES_EUNSUPPORTED = -2,/* valid but not built (e.g. an unsupported d_k)      */
+    LORES_EUNSUPPORTED = -2,/* valid but not built (kept for the ABI; no current case) */
     LORES_ESIZE = -3,       /* buffer too small                                     */
     LORES_EHIP = -4,        /* a HIP runtime call failed                           */
     LORES_ENOMEM = -5       /* host allocation failed                              */
