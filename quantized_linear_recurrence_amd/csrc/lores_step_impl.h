@@ -1029,8 +1029,8 @@ struct TaskSide {
 // SPLIT (d_k > 128): a row of d_k fp32 values does not fit one lane's
 // registers beside the rest, so two lanes share it: lane L < 32 holds
 // columns [0, d_k / 2) of row 32 rb + L and lane L + 32 the other half
-// (each half of a stored row starts on a chunk: the layout pads the first
-// half to whole 16-byte chunks).  Each lane runs the per-lane code on its
+// (each half of a stored row starts on a chunk: the layout pads each half to
+// whole 16-byte chunks).  Each lane runs the per-lane code on its
 // CPL = d_k / 2 columns (an int4 half of 80 or 112 columns ends inside its
 // last chunk); r, o and the row maximum are combined across the pair with
 // one v_permlane32_swap each (in the same order in both lanes, so both hold
