@@ -92,6 +92,8 @@ def parse(argv=None):
                     help="worker processes of the oracle baseline (at most the host's cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy", "error", "sweep"])
+    ap.add_argument("--sweep-only", default="",
+                    help="--mode sweep: only the rows whose label contains this text")
     ap.add_argument("--error-steps", type=int, default=2048,
                     help="horizon of the error-accumulation harness (--mode error)")
     ap.add_argument("--copy-mib", type=int, default=2048)
@@ -189,8 +191,10 @@ SWEEP = [  # (label, B, H, d_k, d_v, per-head precision, delta[, "key"][, window
     ("int8+int4 (C5), key columns, window 4", 2048, 32, 128, 128, [2] * 16 + [3] * 16, 1, "key", 4),
     ("int8, d_k 256 (split rows)", 1024, 32, 256, 128, [2] * 32, 1),
     ("int4, d_k 256 (split rows)", 1024, 32, 256, 128, [3] * 32, 1),
-    ("int8+int4, d_k 256 (one launch per class)", 1024, 32, 256, 128, [2] * 16 + [3] * 16, 1),
+    ("int8+int4, d_k 256 (split rows, fused pair)", 1024, 32, 256, 128, [2] * 16 + [3] * 16, 1),
     ("int8, d_k 256, key columns", 1024, 32, 256, 128, [2] * 32, 1, "key"),
+    ("bf16, d_k 256 (split rows)", 512, 32, 256, 128, [1] * 32, 1),
+    ("bf16+int8, d_k 256 (split rows, side by side)", 1024, 32, 256, 128, [1] * 8 + [2] * 24, 1),
 ]
 
 
@@ -203,6 +207,8 @@ def sweep_mode(args, torch):
     dev = torch.device("cuda:0")
     rows = []
     for label, B, H, dk, dv, prec, delta, *ax in SWEEP:
+        if args.sweep_only and args.sweep_only not in label:
+            continue
         key = "key" in ax
         window = next((a for a in ax if isinstance(a, int)), 1)
         g = torch.Generator(device=dev)

@@ -157,8 +157,7 @@ typedef struct {
  * same section, scale grouping), starting from S_0 = 0.
  *   B, H        sequences and heads (1 <= B <= 65535, 1 <= H <= LORES_MAX_HEADS)
  *   d_k, d_v    key and value dimensions; d_k a multiple of 32, at most 256
- *               (LORES_EINVAL otherwise), 1 <= d_v <= LORES_MAX_DV.  Above
- *               d_k = 128 the classes of a state run one launch each.
+ *               (LORES_EINVAL otherwise), 1 <= d_v <= LORES_MAX_DV.
  *   head_prec   host [H] precision per head (LORES_FP32 .. LORES_FP8)
  *   d_buf       device buffer, 256-byte aligned, >= *bytes; or NULL
  *   bytes       host in/out.  d_buf == NULL: size query, writes the size and

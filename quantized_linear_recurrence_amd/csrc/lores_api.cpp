@@ -404,7 +404,7 @@ static int plan_launches(const lores_state *st, int groups[LORES_NUM_PREC][2],
     int present[LORES_NUM_PREC], n = 0;
     for (int c = 0; c < LORES_NUM_PREC; ++c)
         if (st->n_class[c]) present[n++] = c;
-    if (n == 2 && st->axis == LORES_SCALE_VALUE && st->window == 1 && st->dk <= 128 &&
+    if (n == 2 && st->axis == LORES_SCALE_VALUE && st->window == 1 &&
         lores::fusable_pair(present[0], present[1])) {
         groups[0][0] = present[0];
         groups[0][1] = present[1];

@@ -1569,7 +1569,8 @@ constexpr bool pairable() {
     if constexpr (P1 < 0 || !is_int<P0>() || !is_int<P1>()) {
         return false;
     } else {
-        return row_chunks<DK, P0>() <= kMaxPrefetchChunks && row_chunks<DK, P1>() <= kMaxPrefetchChunks;
+        constexpr int C = DK > 128 ? DK / 2 : DK;       // a lane's columns (split rows: half)
+        return row_chunks<C, P0>() <= kMaxPrefetchChunks && row_chunks<C, P1>() <= kMaxPrefetchChunks;
     }
 }
 
@@ -1582,9 +1583,25 @@ constexpr int group_waves() {
                                     : kWavesPerGroup;
 }
 
+// Wavefronts per SIMD the compiler must leave room for.  Left to itself it
+// gives a few window ends and the per-channel key-column steps 257-294
+// registers, so one wavefront per SIMD; held to 256 (two per SIMD) these
+// spill 0-26 registers and measured 4-30 % faster.  The per-channel window
+// ends of int8 and E4M3 at d_k = 128 and 256 would spill 36-44 registers and
+// measured 8-10 % slower held to two; they, and everything the compiler
+// already fits in 256, keep its own choice.
+template <int DK, int P0, bool PC, bool KEY, bool WEND>
+constexpr int min_waves_per_simd() {
+    if constexpr (KEY && !WEND) return 2;
+    else if constexpr (WEND && !PC) return 2;
+    else if constexpr (WEND && PC && (P0 == LORES_INT4 || P0 == LORES_INT6 || DK == 224)) return 2;
+    else return 1;
+}
+
 template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
           bool WEND = false>
 __global__ void __launch_bounds__((64 * group_waves<P0, P1, DK, KEY>()))
+__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<DK, P0, PC, KEY, WEND>())))
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
@@ -1767,11 +1784,10 @@ hipError_t launch_classes(int dk, bool pc, bool delta, bool bf16, const StepPtrs
         case 64: return launch_dk<64, P0, P1>(pc, delta, bf16, p, m, s);
         case 96: return launch_dk<96, P0, P1>(pc, delta, bf16, p, m, s);
         case 128: return launch_dk<128, P0, P1>(pc, delta, bf16, p, m, s);
-        // split rows run one class per launch
-        case 160: if constexpr (P1 < 0) return launch_dk<160, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
-        case 192: if constexpr (P1 < 0) return launch_dk<192, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
-        case 224: if constexpr (P1 < 0) return launch_dk<224, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
-        case 256: if constexpr (P1 < 0) return launch_dk<256, P0, P1>(pc, delta, bf16, p, m, s); else return hipErrorInvalidValue;
+        case 160: return launch_dk<160, P0, P1>(pc, delta, bf16, p, m, s);
+        case 192: return launch_dk<192, P0, P1>(pc, delta, bf16, p, m, s);
+        case 224: return launch_dk<224, P0, P1>(pc, delta, bf16, p, m, s);
+        case 256: return launch_dk<256, P0, P1>(pc, delta, bf16, p, m, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -7,6 +7,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/lores.h"
@@ -113,8 +115,8 @@ int main() {
                     }
 
     Args x;
-    // d_k = 256: rows split across lane pairs, 32 rows per task, one launch
-    // per class (no fused pairs)
+    // d_k = 256: rows split across lane pairs, 32 rows per task; three
+    // classes, one launch each
     for (int dv : {1, 32, 33, 100, 256}) {
         const std::vector<uint8_t> prec = {2, 3, 1, 3};
         const int B = 2, H = (int)prec.size();
@@ -137,17 +139,19 @@ int main() {
     // only the unpaired rest of either class, in groups of kPairWavesPerGroup
     // wavefronts; other launches count all tasks of a class in groups of
     // kWavesPerGroup
+    // (split rows at d_k > 128 as well: 32-row tasks)
     {
         const std::vector<std::vector<uint8_t>> mixes = {
             {2, 3}, {2, 2, 2, 3}, {3, 3, 3, 3, 3, 2}, {3, 4, 4}, {1, 2, 2}, {1, 3, 3, 3},
             {2, 3, 4}, {0, 1, 2, 3, 4, 5}, {2, 2, 2, 2, 2, 2, 2, 2, 2, 3}};
+        for (int dk : {128, 160, 256})
         for (auto &prec : mixes)
             for (int dv : {1, 64, 100, 128, 256}) {
                 const int B = 2, H = (int)prec.size();
-                size_t n = size_of(B, H, 128, dv, prec);
+                size_t n = size_of(B, H, dk, dv, prec);
                 Buf buf(n);
                 lores_state *st = nullptr;
-                CHECK(lores_state_alloc(B, H, 128, dv, prec.data(), buf.p, &n, nullptr, &st) ==
+                CHECK(lores_state_alloc(B, H, dk, dv, prec.data(), buf.p, &n, nullptr, &st) ==
                       LORES_OK);
                 g_launches.clear();
                 CHECK(step(st, x, 1) == LORES_OK);
@@ -156,7 +160,7 @@ int main() {
                     const bool pair = l.p1 == LORES_INT4 || l.p1 == LORES_INT6;
                     const bool pair_ints = pair && l.p0 != LORES_BF16;
                     const int n0 = l.Hc[0] * l.n_rb, n1 = l.p1 >= 0 ? l.Hc[1] * l.n_rb : 0;
-                    CHECK(l.n_rb == (dv + 63) / 64);
+                    CHECK(l.n_rb == (dk > 128 ? (dv + 31) / 32 : (dv + 63) / 64));
                     heads += l.Hc[0] + (l.p1 >= 0 ? l.Hc[1] : 0);
                     if (pair_ints) {
                         const int paired = n0 < n1 ? n0 : n1, w = lores::kPairWavesPerGroup;
@@ -171,6 +175,26 @@ int main() {
                 CHECK(heads == H);
                 lores_state_free(st);
             }
+    }
+    // split rows fuse the same pairs
+    for (int dk : {160, 192, 224, 256}) {
+        const std::vector<std::pair<std::vector<uint8_t>, std::string>> cases = {
+            {{2, 3, 2, 3}, "launch_step_int8_int4"}, {{4, 3}, "launch_step_int4_int6"},
+            {{1, 2, 2}, "launch_step_bf16_int8"}, {{3, 1}, "launch_step_bf16_int4"}};
+        for (auto &c : cases) {
+            const int H = (int)c.first.size();
+            size_t n = size_of(2, H, dk, 100, c.first);
+            Buf buf(n);
+            lores_state *st = nullptr;
+            CHECK(lores_state_alloc(2, H, dk, 100, c.first.data(), buf.p, &n, nullptr, &st) ==
+                  LORES_OK);
+            g_launches.clear();
+            CHECK(step(st, x, 1) == LORES_OK);
+            CHECK(g_launches.v.size() == 1 && g_launches.v[0].kind == c.second);
+            int32_t nl = 0;
+            CHECK(lores_step_launches(st, &nl) == LORES_OK && nl == 1);
+            lores_state_free(st);
+        }
     }
     // launch grouping: a fused pair for value rows, one launch per class for key columns
     {

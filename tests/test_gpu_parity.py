@@ -66,8 +66,26 @@ def test_split_rows_each_precision(prec, delta, dk):
     s.check()
 
 
+@pytest.mark.parametrize("mix", [[2, 3, 2, 2, 3], [3, 4, 4, 3, 3], [1, 2, 2, 1, 2],
+                                 [3, 1, 3, 3, 1]])
+@pytest.mark.parametrize("decay", ["softplus_step", "kda_channel"])
+@pytest.mark.parametrize("dk", [256, 160, 192, 224])
+def test_split_rows_fused_pairs(mix, decay, dk):
+    """d_k > 128 with two classes in one launch: int8 + int4 and int4 + int6
+    through the pair work queue (unequal class sizes, so the unpaired rest of
+    one class runs after the pairs), bf16 + int8 and bf16 + int4 side by
+    side; d_v = 70 gives three 32-row tasks per unit, the last one ragged."""
+    w = C1.scaled(B=3, H=len(mix), dk=dk, dv=70, T=6, decay=decay)
+    log(f"case: split-row pair B=3 H={w.H} d_k={dk} d_v=70 heads {mix} decay={decay}")
+    st = lores.lores_state_alloc(w.B, w.H, dk, w.dv, mix, device=torch.device("cuda:0"))
+    assert lores.lores_step_launches(st) == 1
+    s = run_parity(w, T=w.T, head_prec=mix, init="random")
+    log(s.summary())
+    s.check()
+
+
 def test_split_rows_sampled_batch():
-    """d_k = 256 at a large batch (one launch per class), sampled units."""
+    """d_k = 256 at a large batch (int8 + int4 in one fused launch), sampled units."""
     w = get_workload("C5").scaled(B=256, dk=256, T=8)
     units = _sample_units(w.B, w.H, 48, seed=256)
     log(f"case: split rows B={w.B} H={w.H} d_k=256 d_v=128 int8 + int4, {len(units)} units, "
