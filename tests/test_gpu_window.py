@@ -37,6 +37,18 @@ def test_each_scaled_class(prec, W, dk, dv, delta):
     s.check()
 
 
+@pytest.mark.parametrize("prec", [2, 3, 4, 5])
+@pytest.mark.parametrize("W,dk,dv,decay", [(4, 128, 100, "softplus_step"), (3, 256, 70, "softplus_step"),
+                                           (4, 128, 100, "kda_channel"), (3, 224, 70, "kda_channel")])
+def test_bf16_inputs(prec, W, dk, dv, decay):
+    """Windows fed bf16 q, k and v (the window-end kernels with bf16 inputs)."""
+    w = C1.scaled(B=3, H=4, dk=dk, dv=dv, T=2 * W + 1, decay=decay, in_bf16=True)
+    log(f"case: window W={W} prec={prec} B=3 H=4 dk={dk} dv={dv} decay={decay}, bf16 inputs")
+    s = run_window_parity(w, T=w.T, W=W, head_prec=[prec] * w.H)
+    log(s.summary())
+    s.check()
+
+
 @pytest.mark.parametrize("prec,dk,dv", [(2, 128, 128), (3, 64, 1)])
 def test_longest_window(prec, dk, dv):
     """W = LORES_MAX_WINDOW (15 buffered tokens replayed at the window end),
@@ -127,7 +139,8 @@ def test_full_size_c5_window4(axis):
                                                (4, 32, 128, 1, "value"), (3, 96, 100, 1, "key"),
                                                (4, 32, 64, 0, "key"), (3, 256, 70, 1, "value"),
                                                (3, 256, 100, 1, "key"), (3, 224, 70, 1, "key"),
-                                               (4, 160, 100, 1, "value")])
+                                               (4, 160, 100, 1, "value"), (3, 224, 70, 1, "value"),
+                                               (4, 192, 100, 0, "value")])
 def test_channel_decay_windows(prec, W, dk, dv, delta, axis):
     """Windows whose tokens carry one decay per key channel (the diagonal
     decay of the recurrence): the in-window readouts from the stored state
