@@ -1421,8 +1421,12 @@ __device__ __forceinline__ void run_single(
     const TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY, WEND> &ts) {
     using TS = TaskStream<DK, PREC, PC, DELTA, BF16IN, KEY, WEND>;
     // fp32 rows (32 chunks at d_k = 128) leave no registers for a prefetch
-    // beside U: only their per-task values are loaded ahead
-    constexpr int P = TS::NCH <= kMaxPrefetchChunks ? TS::NCH
+    // beside U: only their per-task values are loaded ahead.  A window end
+    // with channel decays holds the replay's row vectors as well, so its
+    // 8-chunk rows (int8, E4M3) prefetch half their chunks, which leaves
+    // room for two wavefronts per SIMD.
+    constexpr int P = WEND && PC && TS::NCH == 8 ? 4
+                    : TS::NCH <= kMaxPrefetchChunks ? TS::NCH
                     : PREC == LORES_BF16 ? kMaxPrefetchChunks : 0;
     const int bstep = gridDim.y;
     u32x4 cw[TS::NCH];
@@ -1584,24 +1588,20 @@ constexpr int group_waves() {
 }
 
 // Wavefronts per SIMD the compiler must leave room for.  Left to itself it
-// gives a few window ends and the per-channel key-column steps 257-294
-// registers, so one wavefront per SIMD; held to 256 (two per SIMD) these
-// spill 0-26 registers and measured 4-30 % faster.  The per-channel window
-// ends of int8 and E4M3 at d_k = 128 and 256 would spill 36-44 registers and
-// measured 8-10 % slower held to two; they, and everything the compiler
-// already fits in 256, keep its own choice.
-template <int DK, int P0, bool PC, bool KEY, bool WEND>
+// gives the window ends and the per-channel key-column steps up to 294
+// registers, so one wavefront per SIMD; held to 256 (two per SIMD) they
+// spill 0-32 registers and measured 1-30 % faster.  Everything else keeps
+// the compiler's own choice (bf16 rows at d_k = 256 take 259-270 registers
+// and measured the same at one or two wavefronts per SIMD).
+template <bool KEY, bool WEND>
 constexpr int min_waves_per_simd() {
-    if constexpr (KEY && !WEND) return 2;
-    else if constexpr (WEND && !PC) return 2;
-    else if constexpr (WEND && PC && (P0 == LORES_INT4 || P0 == LORES_INT6 || DK == 224)) return 2;
-    else return 1;
+    return KEY || WEND ? 2 : 1;
 }
 
 template <int DK, bool PC, bool DELTA, bool BF16IN, int P0, int P1, bool KEY = false,
           bool WEND = false>
 __global__ void __launch_bounds__((64 * group_waves<P0, P1, DK, KEY>()))
-__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<DK, P0, PC, KEY, WEND>())))
+__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<KEY, WEND>())))
 lores_step_kernel(const void *__restrict__ qp, const void *__restrict__ kp,
                   const void *__restrict__ vp, const float *__restrict__ alphap,
                   const float *__restrict__ betap, float *__restrict__ op,
