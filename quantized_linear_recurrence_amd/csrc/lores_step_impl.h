@@ -1194,22 +1194,41 @@ struct TaskStream {
             // chunk registers are free when `mid` reuses them
             else pin16(&U[j - 15]);
         };
-        // Value-row int8 and int4 codes under a scalar decay take the code
-        // and the dequantization in one v_fma_mix_f32 (MIX): the code's bits as an
-        // f16 half times a 2^24, plus -off a.  a 2^24 must be finite, so a
-        // wavefront with a row scale near the top of the fp32 range takes the
-        // conversion and fma instead (the same values).
-        constexpr bool kMixable = (PREC == LORES_INT8 || PREC == LORES_INT4) && !KEY && !PC;
+        // Value-row int8, int4 and int6 codes under a scalar decay take the
+        // code and the dequantization in one v_fma_mix_f32 (MIX): the code's
+        // bits as an f16 half times a 2^24, plus -off a (an int6 field is
+        // extracted into the low bits of a dword first; int6 only on lanes of
+        // 128 columns, where it measured faster: elsewhere it did not).
+        // a 2^24 must be finite, so a wavefront with a row scale near the top
+        // of the fp32 range takes the conversion and fma instead (the same
+        // values).
+        constexpr bool kMixable =
+            (PREC == LORES_INT8 || PREC == LORES_INT4 || (PREC == LORES_INT6 && CPL == 128)) &&
+            !KEY && !PC;
         const float A0 = a * 0x1p24f, A1 = a * 0x1p20f;
         auto pass1 = [&](auto mix_flag) {
         constexpr bool MIX = decltype(mix_flag)::value;
         if constexpr (PREC == LORES_INT6) {
+            // MIX reads the chunks through an opaque copy, so that the two
+            // forms' field extracts are not shared and hoisted above the
+            // branch between them (which would hold every field at once)
+            u32x4 cv[NCH];
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                cv[c] = cw[c];
+                if constexpr (MIX) asm volatile("" : "+v"(cv[c]));
+            }
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 if constexpr (PC && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
-                const float ub = (float)int6_field(cw, j);
+                if constexpr (MIX) {
+                    U[j] = mix_f16(int6_field(cv, j), 0, A0, na);
+                    if ((j & 15) == 15) group_done(j);
+                    continue;
+                }
+                const float ub = (float)int6_field(cv, j);
                 if constexpr (KEY) U[j] = ub - Prec<PREC>::OFF;     // times sig_j per group
                 else if constexpr (PC) U[j] = (ub - Prec<PREC>::OFF) * aj[j & 15];
                 else U[j] = __builtin_fmaf(ub, a, na);
