@@ -940,11 +940,15 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                 // y = U * inv in [-448, 448]; fl(y * 2^-120) puts the E4M3
                 // grid on the fp32 pattern with its low 20 bits dropped (E4M3
                 // subnormals on fp32 denormals): add the draw at bits 4..19,
-                // keep the sign and the next 7 bits
+                // keep the sign (bit 31) and the next 7 bits (20..26; bits
+                // 27..30 are 0 since |y| <= 448).  Two elements at a time:
+                // their high halves side by side, shifted right by 4 in each
+                // half (v_pk_lshrrev_b16) for bits 20..26, merged (v_bfi)
+                // with their top bytes for the signs.
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int j = c * E + q4 * 4;
-                    uint32_t by[4];
+                    uint32_t t[4], pr[2];
                     float yk[4];
                     if constexpr (KEY) mul4_col(yk, invrow[j >> 4], &U[j], j & 15);
 #pragma unroll
@@ -952,14 +956,19 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                         float y;
                         if constexpr (KEY) y = yk[e];
                         else y = U[j + e] * inv;
-                        const uint32_t t = __float_as_uint(y * 0x1p-120f) + (x << 4);
+                        t[e] = __float_as_uint(y * 0x1p-120f) + (x << 4);
                         x = step16(x, psi);
-                        const uint32_t u = t >> 20;
-                        by[e] = (u & 0x7Fu) | ((u >> 4) & 0x80u);
                     }
-                    ow[q4] = __builtin_amdgcn_perm(__builtin_amdgcn_perm(by[3], by[2], 0x0c0c0400u),
-                                                   __builtin_amdgcn_perm(by[1], by[0], 0x0c0c0400u),
-                                                   0x05040100u);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const uint32_t hi = __builtin_amdgcn_perm(t[2 * h2 + 1], t[2 * h2], 0x07060302u);
+                        const uint32_t sg = __builtin_amdgcn_perm(t[2 * h2 + 1], t[2 * h2], 0x0c070c03u);
+                        const uint32_t pl = __builtin_bit_cast(
+                            uint32_t, __builtin_bit_cast(u16x2, hi) >> (u16x2){4, 4});
+                        pr[h2] = (pl & 0x007F007Fu) | (sg & ~0x007F007Fu);
+                    }
+                    // byte 0 of each half: elements 0..3 into bytes 0..3
+                    ow[q4] = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
                 }
             } else if constexpr (PREC == LORES_BF16) {
 #pragma unroll
