@@ -126,14 +126,13 @@ template <int PREC> constexpr bool is_int() {
 template <int PREC> constexpr bool has_scale() { return is_int<PREC>() || PREC == LORES_FP8; }
 
 // E4M3 byte `sel` of w as fp32 (hardware decode; gfx950 decodes the OCP
-// E4M3 format).  sel is a constant once the callers' loops are unrolled.
+// E4M3 format).  sel is a constant once the callers' loops are unrolled; the
+// bytes are decoded in pairs (v_cvt_pk_f32_fp8, bytes 0-1 or 2-3), and the
+// two calls of a pair share one instruction.
 __device__ __forceinline__ float fp8_value(uint32_t w, int sel) {
-    switch (sel) {
-        case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
-        case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
-        case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
-        default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
-    }
+    const auto p = sel >= 2 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                            : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    return (sel & 1) ? p[1] : p[0];
 }
 
 // 16-byte chunks per stored row of d_k elements
