@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LORES_SPEC_VERSION 7
+#define LORES_SPEC_VERSION 8
 
 /* Per-head state precision. */
 enum {
@@ -112,15 +112,19 @@ typedef struct lores_state lores_state;
  * chunk-major so one wavefront's 64 rows of a chunk are 1 KiB contiguous.
  * Within a chunk, element e is:
  *   fp32: word e, IEEE binary32        bf16: halfword e, bfloat16 bits
- *   int8: byte e  = code + 128         (offset binary, 1..255)
+ *   int8: byte e  = 128 + s code       (offset binary, 1..255)
  *   fp8:  byte e  = E4M3 byte (OCP: sign, 4 exponent bits with bias 7,
  *         3 mantissa bits; never the NaN pattern), value scale * E4M3 value
  *   int4: byte e/2, low nibble for even e, high nibble for odd e,
- *         nibble = code + 8            (offset binary, 1..15)
+ *         nibble = 8 + s code          (offset binary, 1..15)
  * int6 rows are a little-endian bit stream over the row's chunks (chunk c
  * holds row bytes 16c .. 16c + 15): element j is bits 6j .. 6j + 5, value
- * code + 32 (offset binary, 1..63); n_chunk = ceil(6 d_k / 128), the bits
+ * 32 + s code (offset binary, 1..63); n_chunk = ceil(6 d_k / 128), the bits
  * after the last element are zero.
+ * s = +1 in the even columns of a row and -1 in the odd ones: an int row
+ * holds the codes of its odd columns negated (a column pair shares one
+ * rounding draw, and the odd column is requantized as -U; see
+ * lores_decode_step).
  * A row of d_k > 128 is stored as two half rows of d_k / 2 columns, each laid
  * out as above from its own first chunk (n_chunk = 2 n_chunk(d_k / 2): an
  * int4 or int6 half that ends inside a chunk is zero-padded to its end).
@@ -299,15 +303,18 @@ int lores_assign_precision(const double *stat, int32_t H, const double *tier_fra
  * checked: |q| = |k| = 1, decay in (0, 1], beta in (0, 2) when delta = 1,
  * finite inputs.  Per element of an int head, with U the updated fp32 row:
  *   scale' = fl(m / r), m = max|U_row|, r = 127 (int8), 31 (int6) or 7 (int4);
- *   code'  = floor(fl(U * inv + bias + u)) - bias, inv = the largest fp32 not
- *            above r / m (0 if m = 0), bias = 128 (int8), 160 (int6) or 136
- *            (int4),
+ *   code'  = s (floor(fl(s U * inv + bias + u)) - bias), inv = the largest
+ *            fp32 not above r / m (0 if m = 0), bias = 128 (int8), 160 (int6)
+ *            or 136 (int4), s = +1 in even and -1 in odd columns, and the
+ *            columns 2m, 2m + 1 of a row share one draw u (so the odd column
+ *            rounds U with the antithetic draw 1 - u: still unbiased),
  * fp8 heads: scale' = fl(m / 448), y = fl(U * inv) with inv the largest fp32
  *            not above 448 / m; the E4M3 byte of y is the sign and the top
  *            7 magnitude bits of f32bits(fl(y * 2^-120)) + (n << 4), which
  *            rounds stochastically on the E4M3 grid (subnormals included),
  *            u = n * 2^-16 and n a 16-bit counter-based draw keyed on
- *            (seed, t, sequence, head, row, column).
+ *            (seed, t, sequence, head, row, column) (int heads: on the
+ *            column pair).
  */
 int lores_decode_step(lores_state *st, const void *q, const void *k, const void *v,
                       int32_t in_bf16, const float *alpha, int32_t alpha_per_channel,

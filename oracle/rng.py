@@ -19,9 +19,14 @@ Keying and draws (this implementation's definition):
   unit key  K = lo32(z) ^ hi32(z),
             z = mix64(mix64(mix64(seed) ^ t) ^ ((b << 32) | h))      once per unit
   row word  w_i = fmix32(K ^ i)
-  noise     n_ij = (lo16(w_i) + j * 0x9E37) mod 2^16
+  noise     n_ij = (lo16(w_i) + j * 0x9E37) mod 2^16             (bf16, E4M3)
+            n_ij = (lo16(w_i) + floor(j / 2) * 0x9E37) mod 2^16  (int classes)
   n_ij is a 16-bit integer; the int quantizer uses u_ij = n_ij * 2^-16 in
-  [0, 1) and the bf16 rounding adds n_ij below the kept bits.
+  [0, 1) and the bf16 rounding adds n_ij below the kept bits.  The int
+  classes take one draw per pair of columns (2m, 2m + 1): the even column
+  rounds U with it, the odd column rounds -U with it, which is rounding U
+  with the antithetic draw 1 - u (step.quantize_rows), so each column is
+  still rounded without bias and one draw serves two columns.
 
 Each n_ij is exactly uniform on {0, ..., 65535} when w_i is, so every
 element's rounding is unbiased on its own; within a row the draws form a
@@ -70,12 +75,15 @@ def unit_key(seed, t, b, h):
     return ((z & U64(0xFFFFFFFF)) ^ (z >> U64(32))).astype(U32)
 
 
-def noise16(K, dv, dk):
-    """Draws n_ij for keys K [N]: uint32 array [N, dv, dk] with values < 2^16."""
+def noise16(K, dv, dk, paired=False):
+    """Draws n_ij for keys K [N]: uint32 array [N, dv, dk] with values < 2^16.
+    paired: one draw per pair of columns (the int classes' draws)."""
     K = np.asarray(K, dtype=U32).reshape(-1)
     i = np.arange(dv, dtype=U32)
     w = fmix32(K[:, None] ^ i[None, :])                       # [N, dv]
     j = np.arange(dk, dtype=U32)
+    if paired:
+        j = j >> U32(1)
     with np.errstate(over="ignore"):
         x = (w[:, :, None] & U32(0xFFFF)) + j[None, None, :] * PSI16
     return (x & U32(0xFFFF)).astype(U32)

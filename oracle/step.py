@@ -36,8 +36,11 @@ repository's design notes):
      int heads, r = 2^(b-1) - 1 = 127 (int8), 31 (int6) or 7 (int4), bias
      B = 128 (int8), 160 (int6) or 136 (int4):
        m_i = max_j |U_ij|;  s'_i = fl(m_i / r);  inv_i = largest fp32 <= r / m_i
-       (inv_i = 0 for m_i = 0);  z_ij = fl(U_ij * inv_i + (B + n_ij 2^-16))
-       in one rounding;  e_ij = floor(z_ij);  c'_ij = e_ij - B  in [-r, r]
+       (inv_i = 0 for m_i = 0);  with s_j = +1 for even and -1 for odd j,
+       z_ij = fl(s_j U_ij * inv_i + (B + n_ij 2^-16)) in one rounding;
+       e_ij = floor(z_ij);  c'_ij = s_j (e_ij - B)  in [-r, r]
+       (n_ij is shared by the columns 2m, 2m + 1, so the odd column rounds
+        U_ij up with probability P(1 - u < frac): the antithetic draw)
      bf16 heads: bf16 bits of (f32bits(U_ij) + n_ij) >> 16   (rounding by noise)
      fp32 heads: X'_ij = U_ij
      (key-column scales: m_j = max_i |U_ij| over the unit's d_v rows, and
@@ -165,9 +168,12 @@ def quantize_rows(U, prec, n=None, rounding="sr", axis="value"):
     d_v rows of each column).
 
     n: noise draws [N, dv, dk] (uint32 < 2^16), needed for rounding="sr".
+    Int classes: column j is rounded as z = fl(s_j U inv + bias + n 2^-16),
+    code = s_j (floor(z) - bias), with s_j = +1 for even and -1 for odd j.
     rounding="nearest" is the same quantizer with every draw fixed at 2^15
     (u = 1/2): round to nearest, ties upward after the fp32 rounding of the
-    sum (bf16: ties away from zero) -- the library's round-to-nearest mode.
+    sum (int odd columns: ties downward; bf16: ties away from zero) -- the
+    library's round-to-nearest mode.
     rounding="rtn" is the textbook form: fl(U * inv) rounded to nearest, ties
     to even (bf16: ties to even), used by the error-propagation checks.
     Returns the new state dict.
@@ -193,9 +199,13 @@ def quantize_rows(U, prec, n=None, rounding="sr", axis="value"):
         scales = exact.rn_div32(m, F32(r))
         inv = exact.rd_div32(F32(r), m)
         if rounding == "sr":
+            # even columns round U, odd columns -U (each with its own draw
+            # n; the int draws give a column pair one draw, so the odd
+            # column rounds U with the antithetic draw 1 - u)
+            sgn = np.where(np.arange(U.shape[-1]) % 2 == 0, 1, -1).astype(np.int32)
             bias = (F32(BIAS[prec]) + n.astype(F32) * F32(2.0 ** -16)).astype(F32)
-            z = fma32(U, _spread(inv, axis), bias)
-            codes = np.floor(z).astype(np.int32) - BIAS[prec]
+            z = fma32((U * sgn.astype(F32)).astype(F32), _spread(inv, axis), bias)
+            codes = sgn * (np.floor(z).astype(np.int32) - BIAS[prec])
         elif rounding == "rtn":
             y = (U * _spread(inv, axis)).astype(F32)
             codes = np.rint(y).astype(np.int32)
@@ -261,7 +271,7 @@ def decode_step(prec, state, q, k, v, alpha, beta, delta, seed, t, b, h,
     n = None
     if prec != PREC_FP32 and rounding == "sr":  # "nearest" and "rtn" need no draws
         K = unit_key(seed, t, b, h)
-        n = (noise16 if noise == "weyl" else noise16_iid)(K, dv, dk)
+        n = noise16(K, dv, dk, paired=prec in QMAX) if noise == "weyl" else noise16_iid(K, dv, dk)
     return quantize_rows(U, prec, n, rounding, axis), o
 
 
@@ -276,7 +286,7 @@ def quant_state(prec, X, seed, b, h, rounding="sr", axis="value"):
     N, dv, dk = X.shape
     n = None
     if prec != PREC_FP32 and rounding == "sr":
-        n = noise16(unit_key(seed, 0, b, h), dv, dk)
+        n = noise16(unit_key(seed, 0, b, h), dv, dk, paired=prec in QMAX)
     return quantize_rows(X, prec, n, rounding, axis)
 
 

@@ -121,7 +121,7 @@ def window_step(prec, state, buf, q, k, v, alpha, beta, delta, seed, t, b, h, W,
     if p == W:
         n = None
         if rounding == "sr":
-            n = noise16(unit_key(seed, t, b, h), dv, dk)
+            n = noise16(unit_key(seed, t, b, h), dv, dk, paired=prec in ostep.QMAX)
         return ostep.quantize_rows(U, prec, n, rounding, axis), empty_buffer(N, W, dv, dk), o
     nb = {kk: vv.copy() for kk, vv in buf.items()}
     nb["g"][:, p - 1] = g

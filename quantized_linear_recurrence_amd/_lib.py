@@ -8,7 +8,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblores.so")
 
-SPEC_VERSION = 7                     # LORES_SPEC_VERSION of include/lores.h
+SPEC_VERSION = 8                     # LORES_SPEC_VERSION of include/lores.h
 LORES_FP32, LORES_BF16, LORES_INT8, LORES_INT4, LORES_INT6, LORES_FP8 = 0, 1, 2, 3, 4, 5
 NUM_PREC = 6
 LORES_ROUND_STOCHASTIC, LORES_ROUND_NEAREST = 0, 1

@@ -53,7 +53,11 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
         for (int j = 0; j < CPL; j += 4) {
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = sc(j + e) * ((float)int6_field(cw, j + e) - 32.0f);
+            for (int e = 0; e < 4; ++e) {
+                // an odd column holds its code negated
+                const float f = (float)int6_field(cw, j + e);
+                x[e] = sc(j + e) * ((e & 1) ? 32.0f - f : f - 32.0f);
+            }
             *reinterpret_cast<f32x4 *>(orow + j) = f32x4{x[0], x[1], x[2], x[3]};
         }
     } else {
@@ -71,11 +75,13 @@ lores_dequant_kernel(const uint8_t *__restrict__ codes, const float *__restrict_
                 if constexpr (PREC == LORES_FP8) {
                     x[e] = sc(c * E + e) * fp8_value(wd[e >> 2], e & 3);
                 } else if constexpr (PREC == LORES_INT8) {
-                    x[e] = sc(c * E + e) * ((float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) - 128.0f);
+                    // an odd column holds its code negated
+                    const float f = (float)((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+                    x[e] = sc(c * E + e) * ((e & 1) ? 128.0f - f : f - 128.0f);
                 } else if constexpr (PREC == LORES_INT4) {
                     const uint32_t w = wd[e >> 3];
-                    const uint32_t nib = (w >> (4 * (e & 7))) & 0xFu;
-                    x[e] = sc(c * E + e) * ((float)nib - 8.0f);
+                    const float f = (float)((w >> (4 * (e & 7))) & 0xFu);
+                    x[e] = sc(c * E + e) * ((e & 1) ? 8.0f - f : f - 8.0f);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
                     x[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));

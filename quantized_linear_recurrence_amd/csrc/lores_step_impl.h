@@ -234,6 +234,19 @@ __device__ __forceinline__ float mix_f16(uint32_t h, int hi, float A, float B) {
     return r;
 }
 
+// The same for an odd column, whose stored code is negated: -(h A + B), both
+// products negated by the instruction's neg modifiers.
+__device__ __forceinline__ float mix_f16n(uint32_t h, int hi, float A, float B) {
+    float r;
+    if (hi)
+        asm("v_fma_mix_f32 %0, %1, -%2, -%3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(h), "v"(A), "v"(B));
+    else
+        asm("v_fma_mix_f32 %0, %1, -%2, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+            : "=v"(r) : "v"(h), "v"(A), "v"(B));
+    return r;
+}
+
 // Bytes 1 and 3 of w into the low bytes of its two halves, the high bytes 0.
 __device__ __forceinline__ uint32_t odd_bytes(uint32_t w) {
     return __builtin_amdgcn_perm(w, w, 0x0c030c01u);
@@ -431,6 +444,30 @@ __device__ __forceinline__ void mul16(float *x, float av) {
         : "v"(av));
 }
 
+// x[e] *= s_e times row element e of av, s_e = +1 for even e and -1 for odd
+// e (the negated codes of an int row's odd columns)
+__device__ __forceinline__ void mul16n(float *x, float av) {
+    asm("s_nop 1\n"
+        "v_mul_f32_dpp %0, %16, %0 row_newbcast:0 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %1, %16, -%1 row_newbcast:1 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %2, %16, %2 row_newbcast:2 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %3, %16, -%3 row_newbcast:3 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %4, %16, %4 row_newbcast:4 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %5, %16, -%5 row_newbcast:5 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %6, %16, %6 row_newbcast:6 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %7, %16, -%7 row_newbcast:7 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %8, %16, %8 row_newbcast:8 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %9, %16, -%9 row_newbcast:9 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %10, %16, %10 row_newbcast:10 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %11, %16, -%11 row_newbcast:11 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %12, %16, %12 row_newbcast:12 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %13, %16, -%13 row_newbcast:13 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %14, %16, %14 row_newbcast:14 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %15, %16, -%15 row_newbcast:15 row_mask:0xf bank_mask:0xf\n"
+        : LORES_PV16(x)
+        : "v"(av));
+}
+
 // ---------------------------------------------------------------------------
 // key-column scales: one scale per key column of a (sequence, head) unit,
 // s_j = max_i |U_ij| / r over all d_v rows, the comparison grouping of the
@@ -441,13 +478,15 @@ __device__ __forceinline__ void mul16(float *x, float av) {
 // vectors like k and q, consumed through DPP row_newbcast.
 // ---------------------------------------------------------------------------
 
-// z[e] += row element E0 + e of inv * u[e] for e < 4 (one rounding each)
+// z[e] += row element E0 + e of inv * s_e u[e] for e < 4 (one rounding each),
+// s_e = +1 for the even and -1 for the odd elements (E0 is even): an int row's
+// odd columns are requantized negated
 #define LORES_FMAC4(E0, E1, E2, E3)                                                          \
     asm("s_nop 1\n"                                                                          \
         "v_fmac_f32_dpp %0, %4, %5 row_newbcast:" #E0 " row_mask:0xf bank_mask:0xf\n"        \
-        "v_fmac_f32_dpp %1, %4, %6 row_newbcast:" #E1 " row_mask:0xf bank_mask:0xf\n"        \
+        "v_fmac_f32_dpp %1, %4, -%6 row_newbcast:" #E1 " row_mask:0xf bank_mask:0xf\n"       \
         "v_fmac_f32_dpp %2, %4, %7 row_newbcast:" #E2 " row_mask:0xf bank_mask:0xf\n"        \
-        "v_fmac_f32_dpp %3, %4, %8 row_newbcast:" #E3 " row_mask:0xf bank_mask:0xf\n"        \
+        "v_fmac_f32_dpp %3, %4, -%8 row_newbcast:" #E3 " row_mask:0xf bank_mask:0xf\n"       \
         : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3])                                    \
         : "v"(inv), "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]))
 __device__ __forceinline__ void fmac4_col(float *z, float inv, const float *u, int e0) {
@@ -817,7 +856,9 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
         const uint32_t K = unit_key(meta.seed, meta.t, (uint64_t)(meta.seq_base + b),
                                     (uint64_t)(meta.head_base + h));
         uint32_t n0 = fmix32(K ^ (uint32_t)row) & 0xFFFFu;
-        n0 = nearest ? 0x8000u : (n0 + (uint32_t)col0 * kPsi16) & 0xFFFFu;
+        // int classes: one draw per column pair (col0 is even)
+        n0 = nearest ? 0x8000u
+                     : (n0 + (uint32_t)(is_int<PREC>() ? col0 >> 1 : col0) * kPsi16) & 0xFFFFu;
         const uint32_t n1 = nearest ? n0 : (n0 + kPsi16) & 0xFFFFu;
         if constexpr (is_int<PREC>()) x = (Prec<PREC>::FBASE & 0xFFFF0000u) | n0;
         else if constexpr (PREC == LORES_BF16) x = n0 | (n1 << 16);
@@ -851,14 +892,15 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             zb[e] = __uint_as_float(x);
-                            x = step16(x, psi);
+                            if (e & 1) x = step16(x, psi);
                         }
                         fmac4_col(zb, invrow[j >> 4], &U[j], j & 15);
                     }
                     z = zb[j & 3];
                 } else {
-                    z = __builtin_fmaf(U[j], inv, __uint_as_float(x));
-                    x = step16(x, psi);
+                    // an odd column rounds -U with its pair's draw
+                    z = __builtin_fmaf((j & 1) ? -U[j] : U[j], inv, __uint_as_float(x));
+                    if (j & 1) x = step16(x, psi);
                 }
                 const uint32_t e = (uint32_t)z;
                 const int bit = 6 * j - 128 * c, w = bit >> 5, o = bit & 31;
@@ -883,9 +925,10 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                     float z[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
+                        // an odd column rounds -U with its pair's draw
                         if constexpr (KEY) z[e] = __uint_as_float(x);
-                        else z[e] = __builtin_fmaf(U[j + e], inv, __uint_as_float(x));
-                        x = step16(x, psi);
+                        else z[e] = __builtin_fmaf((e & 1) ? -U[j + e] : U[j + e], inv, __uint_as_float(x));
+                        if (e & 1) x = step16(x, psi);
                     }
                     if constexpr (KEY) fmac4_col(z, invrow[j >> 4], &U[j], j & 15);
                     const float z0 = z[0], z1 = z[1], z2 = z[2], z3 = z[3];
@@ -910,7 +953,7 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             z[e] = __uint_as_float(x);
-                            x = step16(x, psi);
+                            if (e & 1) x = step16(x, psi);
                         }
                         fmac4_col(z, invrow[j >> 4], &U[j], j & 15);
                         fmac4_col(z + 4, invrow[j >> 4], &U[j + 4], (j + 4) & 15);
@@ -922,9 +965,9 @@ __device__ __forceinline__ void requantize_row(const float (&U)[DK], float m, co
                     } else {
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
+                            // the odd column rounds -U with the pair's draw
                             ze[p] = __builtin_fmaf(U[j + 2 * p], inv, __uint_as_float(x));
-                            x = step16(x, psi);
-                            zo[p] = __builtin_fmaf(U[j + 2 * p + 1], inv, __uint_as_float(x));
+                            zo[p] = __builtin_fmaf(-U[j + 2 * p + 1], inv, __uint_as_float(x));
                             x = step16(x, psi);
                         }
                     }
@@ -1195,7 +1238,10 @@ struct TaskStream {
         // then the group's share of r
         auto group_done = [&](int j) {
             if constexpr (PC && !has_scale<PREC>()) mul16(&U[j - 15], in.av[j >> 4]);
-            if constexpr (KEY) mul16(&U[j - 15], sig[j >> 4]);
+            if constexpr (KEY) {
+                if constexpr (is_int<PREC>()) mul16n(&U[j - 15], sig[j >> 4]);   // odd columns negated
+                else mul16(&U[j - 15], sig[j >> 4]);
+            }
             if constexpr (DELTA && !WEND) dot16(r, &U[j - 15], kv[j >> 4]);
             // without the projection nothing orders pass 1 before the
             // next task's loads; materialize the group here so the
@@ -1231,15 +1277,17 @@ struct TaskStream {
                 if constexpr (PC && !KEY) {
                     if ((j & 15) == 0) scale16(aj, s, in.av[j >> 4]);
                 }
+                // an odd column's stored code is negated
                 if constexpr (MIX) {
-                    U[j] = mix_f16(int6_field(cv, j), 0, A0, na);
+                    U[j] = (j & 1) ? mix_f16n(int6_field(cv, j), 0, A0, na)
+                                   : mix_f16(int6_field(cv, j), 0, A0, na);
                     if ((j & 15) == 15) group_done(j);
                     continue;
                 }
                 const float ub = (float)int6_field(cv, j);
-                if constexpr (KEY) U[j] = ub - Prec<PREC>::OFF;     // times sig_j per group
-                else if constexpr (PC) U[j] = (ub - Prec<PREC>::OFF) * aj[j & 15];
-                else U[j] = __builtin_fmaf(ub, a, na);
+                if constexpr (KEY) U[j] = ub - Prec<PREC>::OFF;     // times +-sig_j per group
+                else if constexpr (PC) U[j] = ((j & 1) ? -(ub - Prec<PREC>::OFF) : ub - Prec<PREC>::OFF) * aj[j & 15];
+                else U[j] = (j & 1) ? __builtin_fmaf(ub, -a, -na) : __builtin_fmaf(ub, a, na);
                 if ((j & 15) == 15) group_done(j);
             }
         } else {
@@ -1283,9 +1331,12 @@ struct TaskStream {
                     else if constexpr (PC) sp = v * aj[j & 15];
                     else sp = v * a;
                 } else if constexpr (MIX && PREC == LORES_INT8) {
-                    sp = mix_f16(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na);
+                    // an odd column's stored code is negated
+                    sp = (e & 1) ? mix_f16n(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na)
+                                 : mix_f16(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na);
                 } else if constexpr (MIX && PREC == LORES_INT4) {
-                    sp = mix_f16(hv[e >> 3][e & 3], (e >> 2) & 1, (e & 1) ? A1 : A0, na);
+                    sp = (e & 1) ? mix_f16n(hv[e >> 3][e & 3], (e >> 2) & 1, A1, na)
+                                 : mix_f16(hv[e >> 3][e & 3], (e >> 2) & 1, A0, na);
                 } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
                     if constexpr (PREC == LORES_INT8 && (KEY || PC)) {
@@ -1302,9 +1353,10 @@ struct TaskStream {
                         ub = (float)((nib >> (8 * ((e & 7) >> 1))) & 0xFFu);
                     }
                     constexpr float OFF = PREC == LORES_INT8 && (KEY || PC) ? 0.0f : Prec<PREC>::OFF;
-                    if constexpr (KEY) sp = ub - OFF;               // times sig_j per group
-                    else if constexpr (PC) sp = (ub - OFF) * aj[j & 15];
-                    else sp = __builtin_fmaf(ub, a, na);
+                    // an odd column's stored code is negated
+                    if constexpr (KEY) sp = ub - OFF;               // times +-sig_j per group
+                    else if constexpr (PC) sp = ((e & 1) ? -(ub - OFF) : ub - OFF) * aj[j & 15];
+                    else sp = (e & 1) ? __builtin_fmaf(ub, -a, -na) : __builtin_fmaf(ub, a, na);
                 } else if constexpr (PREC == LORES_BF16) {
                     const uint32_t w = wd[e >> 1];
                     sp = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));

@@ -56,8 +56,9 @@ __device__ __forceinline__ float rowdot(const float *x, const float *y) {
 }
 
 // Element j of a stored row held in chunk registers cw: the offset-binary
-// integer (code + off) of an int row, the E4M3 value of an fp8 row.  j is a
-// constant once the callers' loops are unrolled.
+// integer of an int row (code + off, or off - code in an odd column, which
+// holds its code negated), the E4M3 value of an fp8 row.  j is a constant
+// once the callers' loops are unrolled.
 template <int PREC>
 __device__ __forceinline__ float stored(const u32x4 *cw, int j) {
     if constexpr (PREC == LORES_INT6) {
@@ -90,10 +91,11 @@ __device__ __forceinline__ float stored_at(const u32x4 *cw, int j) {
 }
 
 // fl(code * a): int rows as fma(code + off, a, -off a), exact since off * a is
-// a power-of-two multiple of a
+// a power-of-two multiple of a (an odd column: fma(off - code, -a, off a))
 template <int DK, int PREC>
 __device__ __forceinline__ float scaled_code(const u32x4 *cw, int j, float a, float na) {
     if constexpr (PREC == LORES_FP8) return stored_at<DK, PREC>(cw, j) * a;
+    else if (j & 1) return __builtin_fmaf(stored_at<DK, PREC>(cw, j), -a, -na);
     else return __builtin_fmaf(stored_at<DK, PREC>(cw, j), a, na);
 }
 
@@ -193,12 +195,14 @@ lores_window_read_kernel(const void *__restrict__ qp, const void *__restrict__ k
     // sum_j c_ij w_j over the stored row (codes unscaled) with the weights
     // w = s o k and s o q (scalar decay; s = 1 for value rows) or s o C alpha_p
     // o k and ... o q (per channel): int rows take the stored offset-binary
-    // integers c + off and subtract off * sum_j w_j once (a different
-    // rounding of the same sum)
+    // integers and subtract off * sum_j w_j once (a different rounding of the
+    // same sum).  An odd column holds off - c, so its weight enters negated
+    // (the odd lanes of a row vector hold the odd columns).
+    const float wsign = (PREC != LORES_FP8 && (lane & 1)) ? -1.0f : 1.0f;
     float wk[NV], wq[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        float f = sc[i];
+        float f = sc[i] * wsign;
         if constexpr (PC) f = f * E[i];
         wk[i] = f * kv[i];
         wq[i] = f * qv[i];

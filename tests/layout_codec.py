@@ -17,6 +17,12 @@ INT_CLASSES = (2, 3, 4)
 SCALED_CLASSES = (2, 3, 4, 5)        # classes with fp32 scales (per value row or key column)
 
 
+def _col_sign(dk):
+    """+1 for the even columns, -1 for the odd ones: an int row stores the
+    code of an odd column negated."""
+    return np.where(np.arange(dk) % 2 == 0, 1, -1).astype(np.int32)
+
+
 def n_chunks(c, dk):
     """16-byte chunks per row: d_k elements of 32, 16, 8, 4 or 6 bits, the
     last chunk zero-padded; a row of d_k > 128 is two halves of d_k / 2
@@ -96,7 +102,8 @@ def pack_unit(c, dk, dv, dv_pad, state_unit, key=False):
         assert codes.min() >= -QMAX[c] and codes.max() <= QMAX[c]
         sc = np.zeros(ns, np.float32)
         sc[:nv] = state_unit["scales"]
-        off = (codes + OFFSET[c]).astype(np.uint8)              # [dv, dk]
+        # odd columns hold the negated code (include/lores.h)
+        off = (codes * _col_sign(codes.shape[1]) + OFFSET[c]).astype(np.uint8)   # [dv, dk]
         if c == 2:
             out[:, :dv, :] = off.reshape(dv, n_chunk, 16).transpose(1, 0, 2)
         elif c == 4:
@@ -140,17 +147,17 @@ def unpack_unit(c, dk, dv, dv_pad, code_bytes, scales=None, key=False):
     raw = np.asarray(code_bytes, np.uint8).reshape(n_chunk, dv_pad, 16)[:, :dv, :]
     rows = np.ascontiguousarray(raw.transpose(1, 0, 2)).reshape(dv, n_chunk * 16)
     if c == 2:
-        return {"codes": rows.astype(np.int32) - 128,
+        return {"codes": (rows.astype(np.int32) - 128) * _col_sign(dk),
                 "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 5:
         return {"fp8": rows.copy(), "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 4:
-        return {"codes": _unpack6(rows, dk) - 32,
+        return {"codes": (_unpack6(rows, dk) - 32) * _col_sign(dk),
                 "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 3:
         lo = (rows & 0x0F).astype(np.int32)
         hi = (rows >> 4).astype(np.int32)
-        codes = np.stack([lo, hi], axis=-1).reshape(dv, -1)[:, :dk] - 8
+        codes = (np.stack([lo, hi], axis=-1).reshape(dv, -1)[:, :dk] - 8) * _col_sign(dk)
         return {"codes": codes, "scales": np.asarray(scales, np.float32)[:nv].copy()}
     if c == 1:
         return {"bits": rows.view(np.uint16).reshape(dv, dk).copy()}

@@ -26,17 +26,18 @@ def test_int_roundtrip_every_code_every_position(c, r, dk, dv):
 def test_int8_byte_positions():
     dk, dv = 32, 2
     codes = np.zeros((dv, dk), np.int64)
-    codes[1, 17] = -127                               # row 1, chunk 1, byte 1
+    codes[1, 16] = -127                               # row 1, chunk 1, byte 0
+    codes[1, 17] = -127                               # byte 1: an odd column, stored negated
     by, _ = lc.pack_unit(2, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
     chunk = by.reshape(2, 64, 16)
-    assert chunk[1, 1, 1] == 1 and chunk[0, 0, 0] == 128
+    assert chunk[1, 1, 0] == 1 and chunk[1, 1, 1] == 255 and chunk[0, 0, 0] == 128
 
 
 def test_int4_nibble_positions():
     dk, dv = 32, 1
     codes = np.zeros((dv, dk), np.int64)
     codes[0, 4] = 7                                   # byte 2, low nibble
-    codes[0, 5] = -7                                  # byte 2, high nibble
+    codes[0, 5] = 7                                   # byte 2, high nibble (odd: 8 - 7)
     by, _ = lc.pack_unit(3, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
     assert by.reshape(1, 64, 16)[0, 0, 2] == (15 | (1 << 4))
 
@@ -57,8 +58,9 @@ def test_int6_bit_positions():
     across 16-byte chunk boundaries; the padding bits stay zero."""
     dk, dv = 96, 1                                    # 576 bits: 4.5 chunks -> 5
     codes = np.full((dv, dk), -32 + 32, np.int64)     # stored 32 everywhere ...
-    codes[0, 21] = 31                                 # bits 126..131: straddles chunks 0 and 1
-    codes[0, 5] = -31                                 # bits 30..35: straddles words 0 and 1
+    codes[0, 21] = -31                                # bits 126..131: straddles chunks 0 and 1
+    codes[0, 5] = 31                                  # bits 30..35: straddles words 0 and 1
+    # (both odd columns: stored negated, 32 + 31 = 63 and 32 - 31 = 1)
     by, _ = lc.pack_unit(4, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
     row = by.reshape(5, 64, 16)[:, 0, :].reshape(-1)  # the row's 80 bytes, chunk after chunk
     bits = np.unpackbits(row, bitorder="little")
@@ -86,7 +88,8 @@ def test_split_row_halves_start_on_a_chunk():
     of byte 0 of chunk 3."""
     dk, dv = 160, 1
     codes = np.zeros((dv, dk), np.int64)
-    codes[0, 79] = 7                                  # half 0, last column: chunk 2, byte 7, high nibble
+    codes[0, 79] = -7                                 # half 0, last column: chunk 2, byte 7, high nibble
+    #                                                   (odd: stored negated, 8 + 7)
     codes[0, 80] = -7                                 # half 1, first column: chunk 3, byte 0, low nibble
     by, _ = lc.pack_unit(3, dk, dv, 64, {"codes": codes, "scales": np.ones(dv, np.float32)})
     ch = by.reshape(6, 64, 16)[:, 0, :]

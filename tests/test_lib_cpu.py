@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lores_lib):
 def test_spec_version(lores_lib):
     hdr = open(os.path.join(ROOT, "include", "lores.h")).read()
     v = int(re.search(r"#define LORES_SPEC_VERSION (\d+)", hdr).group(1))
-    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 7
+    assert lores.lores_spec_version() == v == lores._lib.SPEC_VERSION == 8
 
 
 def _layout_bytes(B, H, dk, dv, head_prec, key=False, window=1):

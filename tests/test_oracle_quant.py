@@ -5,8 +5,12 @@ r = 2^(b-1) - 1 ([LoReS] Section 4, scale grouping and Proposition 1), and
 rounding that is stochastic so errors do not reinforce across steps ([LoReS]
 Section 4, Rounding / Proposition 3).  The checks below follow from those
 definitions and from probability, not from the oracle's code:
-  * exhaustive enumeration of all 2^16 noise values: a value y rounds only to
+  * exhaustive enumeration of all 2^16 noise values, in an even and in an odd
+    column (the odd column rounds -U with its draw): a value y rounds only to
     floor(y) or floor(y)+1, up with probability frac(y) (to the 2^-16 grid),
+  * a column pair sharing one draw rounds antithetically: two equal values
+    with fraction f both round up with probability max(0, 2f - 1) and both
+    down with probability max(0, 1 - 2f),
   * bf16 rounding: the mean over all 2^16 noise values is the input, exactly,
   * zero rows, code range, one-step error bound, mean over seeds,
   * Proposition 1's readout-error variances for value-axis and key-axis
@@ -28,11 +32,14 @@ QM = {step.PREC_INT8: 127, step.PREC_INT4: 7, step.PREC_INT6: 31}    # 2^(b-1) -
 
 
 def _row_with_all_noise(x, m):
-    """U [1, 1, 65537]: element 0 fixes the row max m, the rest all equal x."""
-    U = np.full((1, 1, 65537), x, F32)
+    """U [1, 1, 2 * 65536 + 2]: element 0 fixes the row max m, the rest all
+    equal x; the odd columns 1, 3, ... and the even columns 2, 4, ... each
+    see every draw once."""
+    U = np.full((1, 1, 2 * 65536 + 2), x, F32)
     U[0, 0, 0] = m
-    n = np.zeros((1, 1, 65537), np.uint32)
-    n[0, 0, 1:] = np.arange(65536, dtype=np.uint32)
+    n = np.zeros(U.shape, np.uint32)
+    n[0, 0, 1:-1:2] = np.arange(65536, dtype=np.uint32)
+    n[0, 0, 2::2] = np.arange(65536, dtype=np.uint32)
     return U, n
 
 
@@ -53,15 +60,41 @@ def test_sr_exhaustive_probability(prec):
         y = Fraction(float(x)) * Fraction(float(inv))
         fl = y.numerator // y.denominator
         frac = y - fl
-        codes = st["codes"][0, 0, 1:]
-        assert codes.min() >= -r and codes.max() <= r
-        assert set(np.unique(codes).tolist()) <= {fl, fl + 1}
-        p_up = Fraction(int((codes == fl + 1).sum()), 65536)
-        assert abs(p_up - frac) <= Fraction(2, 65536), (x, m, float(p_up), float(frac))
-        mean = Fraction(int(codes.astype(np.int64).sum()), 65536)
-        assert abs(mean - y) <= Fraction(2, 65536)
+        for codes in (st["codes"][0, 0, 1:-1:2], st["codes"][0, 0, 2::2]):   # odd, even
+            assert codes.size == 65536
+            assert codes.min() >= -r and codes.max() <= r
+            assert set(np.unique(codes).tolist()) <= {fl, fl + 1}
+            p_up = Fraction(int((codes == fl + 1).sum()), 65536)
+            assert abs(p_up - frac) <= Fraction(2, 65536), (x, m, float(p_up), float(frac))
+            mean = Fraction(int(codes.astype(np.int64).sum()), 65536)
+            assert abs(mean - y) <= Fraction(2, 65536)
         # the stored scale is the correctly rounded m / r
         assert st["scales"][0, 0] == exact.rn_div32(m, F32(r))
+
+
+@pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
+def test_column_pair_rounds_antithetically(prec):
+    """Columns 2m and 2m + 1 share their draw; with equal values the two
+    roundings are complementary: over all 2^16 draws, both round up with
+    probability max(0, 2f - 1) and both down with max(0, 1 - 2f)."""
+    r = QM[prec]
+    g = np.random.default_rng(30 + prec)
+    for trial in range(30):
+        m = F32(np.exp(g.uniform(-6, 3)))
+        x = F32(g.uniform(-1, 1) * m)
+        U = np.full((1, 65536, 4), x, F32)
+        U[:, :, 2] = m                    # the row maximum, in the second pair
+        n = np.repeat(np.arange(65536, dtype=np.uint32)[:, None], 4, axis=1)[None]
+        c = step.quantize_rows(U, prec, n)["codes"][0]
+        inv = exact.rd_div32(F32(r), np.array([m], F32))[0]
+        y = Fraction(float(x)) * Fraction(float(inv))
+        fl = y.numerator // y.denominator
+        f = y - fl
+        up0, up1 = c[:, 0] == fl + 1, c[:, 1] == fl + 1
+        both_up = Fraction(int((up0 & up1).sum()), 65536)
+        both_down = Fraction(int((~up0 & ~up1).sum()), 65536)
+        assert abs(both_up - max(0, 2 * f - 1)) <= Fraction(3, 65536), (trial, float(f), float(both_up))
+        assert abs(both_down - max(0, 1 - 2 * f)) <= Fraction(3, 65536), (trial, float(f), float(both_down))
 
 
 def test_bf16_rounding_exactly_unbiased():
@@ -111,7 +144,7 @@ def test_mean_over_seeds_is_unbiased(prec):
     acc2 = np.zeros(U.shape, np.float64)
     S = 3000
     for seed in range(S):
-        n = rng.noise16(rng.unit_key(seed, 1, 0, 0), 16, 64)
+        n = rng.noise16(rng.unit_key(seed, 1, 0, 0), 16, 64, paired=prec in QM)
         X = step.dequant(prec, step.quantize_rows(U, prec, n)).astype(np.float64)
         acc += X
         acc2 += X * X
@@ -145,11 +178,16 @@ def test_proposition1_readout_error_variances():
     ratio_key = np.mean(e_key ** 2) / np.mean(np.broadcast_to(pred_key, e_key.shape))
     assert abs(ratio_key - 1) < 0.05, ratio_key
 
-    n = rng.noise16(rng.unit_key(0, 1, np.arange(N), 0), dv, dk)
+    n = rng.noise16(rng.unit_key(0, 1, np.arange(N), 0), dv, dk, paired=True)
     sr = step.dequant(step.PREC_INT8, step.quantize_rows(U, step.PREC_INT8, n))
     e_sr = np.einsum("nij,nj->ni", (sr - U).astype(np.float64), q)
     ratio_sr = np.mean(e_sr ** 2) / np.mean(M ** 2 / (6 * r * r))
     assert abs(ratio_sr - 1) < 0.05, ratio_sr
+
+
+def _paired(K, dv, dk):
+    """The int classes' draws: one Weyl draw per column pair."""
+    return rng.noise16(K, dv, dk, paired=True)
 
 
 @pytest.mark.parametrize("prec", [step.PREC_INT8, step.PREC_INT4, step.PREC_INT6])
@@ -161,7 +199,7 @@ def test_weyl_noise_matches_independent_noise_readout_error(prec):
     q /= np.linalg.norm(q, axis=1, keepdims=True)
     K = rng.unit_key(9, 4, np.arange(N), 2)
     errs = {}
-    for name, fn in (("weyl", rng.noise16), ("iid", rng.noise16_iid)):
+    for name, fn in (("weyl", _paired), ("iid", rng.noise16_iid)):
         X = step.dequant(prec, step.quantize_rows(U, prec, fn(K, dv, dk)))
         e = np.einsum("nij,nj->ni", (X - U).astype(np.float64), q)
         errs[name] = float(np.mean(e ** 2))
@@ -204,7 +242,7 @@ def test_weyl_noise_readout_error_on_recurrent_states(shape, prec):
     q = g.standard_normal((N, dk))
     q /= np.linalg.norm(q, axis=1, keepdims=True)
     errs = {}
-    for name, fn in (("weyl", rng.noise16), ("iid", rng.noise16_iid)):
+    for name, fn in (("weyl", _paired), ("iid", rng.noise16_iid)):
         tot = []
         for t in range(8):
             X = step.dequant(prec, step.quantize_rows(U, prec, fn(rng.unit_key(9, t + 1, np.arange(N), 2), dv, dk)))
@@ -233,11 +271,12 @@ def test_nearest_mode_is_round_to_nearest(prec):
     rtn = step.quantize_rows(U, prec, rounding="rtn")["codes"]
     near_tie = np.abs(np.abs(y - np.floor(y)) - 0.5) <= 2.0 ** -15
     assert np.array_equal(st["codes"][~near_tie], rtn[~near_tie])
-    # exact ties go up
-    U2 = np.zeros((1, 1, 4), F32)
-    U2[0, 0] = [r, 0.5 * r / r * 1.0, -0.5, 0.0]        # y = r, 0.5, -0.5, 0
+    # exact ties go up in even columns and down in odd ones (an odd column
+    # rounds -y)
+    U2 = np.zeros((1, 1, 6), F32)
+    U2[0, 0] = [r, 0.5, 0.5, -0.5, -0.5, 0.0]          # y = U (inv = 1)
     c2 = step.quantize_rows(U2, prec, rounding="nearest")["codes"][0, 0]
-    assert list(c2) == [r, 1, 0, 0]
+    assert list(c2) == [r, 0, 1, -1, 0, 0]
 
 
 def test_nearest_mode_bf16_is_round_to_nearest():

@@ -87,3 +87,13 @@ def test_noise16_fresh_each_step():
 def test_noise16_iid_reference_range():
     n = rng.noise16_iid(rng.unit_key(0, 1, 0, 0), 8, 16)
     assert n.shape == (1, 8, 16) and n.max() < 65536
+
+
+def test_noise16_paired_one_draw_per_column_pair():
+    """The int classes' draws: columns 2m and 2m + 1 share draw m of the
+    column sequence, so a row of d_k columns spends d_k / 2 draws."""
+    K = rng.unit_key(4, 2, np.arange(6), 1)
+    n = rng.noise16(K, 8, 64)
+    p = rng.noise16(K, 8, 64, paired=True)
+    assert np.array_equal(p[:, :, 0::2], p[:, :, 1::2])
+    assert np.array_equal(p[:, :, 0::2], n[:, :, :32])

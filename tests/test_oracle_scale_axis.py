@@ -12,10 +12,12 @@ definition and from probability, not from the oracle's code:
   * in nearest mode every nonzero column reaches a code of magnitude r,
     zero columns stay zero, and each value is within half a code of U,
   * quantizing a state by columns equals quantizing its transpose by rows
-    (with the draws transposed),
+    (with the draws transposed; an int state's odd columns, which round -U,
+    enter the transpose negated),
   * the mean over seeds is U (stochastic rounding is unbiased), and the
     readout error variance is sum_j q_j^2 C_j^2 / 6r^2 (the stochastic
-    rounding counterpart of Proposition 1's key-axis formula),
+    rounding counterpart of Proposition 1's key-axis formula) times
+    (d_v - 1) / d_v, since each column's maximum is stored exactly,
   * a decode step from S_0 = 0 with alpha = 1 and delta = 0 stores beta v k^T
     to within one code of each column.
 """
@@ -104,10 +106,24 @@ def test_key_grouping_is_value_grouping_of_the_transpose(prec):
     U = (g.standard_normal((4, 24, 40)) * np.exp(g.uniform(-2, 2, (4, 1, 40)))).astype(F32)
     n = g.integers(0, 1 << 16, U.shape).astype(np.uint32)
     a = step.quantize_rows(U, prec, n, axis="key")
-    b = step.quantize_rows(np.ascontiguousarray(U.transpose(0, 2, 1)), prec,
-                           np.ascontiguousarray(n.transpose(0, 2, 1)), axis="value")
     field = "fp8" if prec == step.PREC_FP8 else "codes"
-    assert np.array_equal(a[field], b[field].transpose(0, 2, 1))
+    if prec == step.PREC_FP8:
+        b = step.quantize_rows(np.ascontiguousarray(U.transpose(0, 2, 1)), prec,
+                               np.ascontiguousarray(n.transpose(0, 2, 1)), axis="value")
+        assert np.array_equal(a[field], b[field].transpose(0, 2, 1))
+    else:
+        # an int column j rounds sgn_j U (sgn_j = -1 for odd j): the value
+        # rows of V[j, 2i] = sgn_j U[i, j] (zeros between, in the odd columns
+        # of V, so that every V entry that counts is rounded as is) give the
+        # key-column codes of U times sgn_j
+        N, dv, dk = U.shape
+        sgn = np.where(np.arange(dk) % 2 == 0, 1, -1)
+        V = np.zeros((N, dk, 2 * dv), F32)
+        V[:, :, 0::2] = U.transpose(0, 2, 1) * sgn[None, :, None].astype(F32)
+        nv = np.zeros(V.shape, np.uint32)
+        nv[:, :, 0::2] = n.transpose(0, 2, 1)
+        b = step.quantize_rows(V, prec, nv, axis="value")
+        assert np.array_equal(a[field], (b[field][:, :, 0::2] * sgn[None, :, None]).transpose(0, 2, 1))
     assert np.array_equal(a["scales"], b["scales"])
 
 
@@ -119,7 +135,7 @@ def test_key_grouping_mean_over_seeds_is_unbiased(prec):
     acc2 = np.zeros(U.shape, np.float64)
     S = 3000
     for seed in range(S):
-        n = rng.noise16(rng.unit_key(seed, 1, 0, 0), 16, 32)
+        n = rng.noise16(rng.unit_key(seed, 1, 0, 0), 16, 32, paired=True)
         X = step.dequant(prec, step.quantize_rows(U, prec, n, axis="key"), axis="key")
         acc += X
         acc2 += X.astype(np.float64) ** 2
@@ -140,11 +156,13 @@ def test_key_grouping_sr_readout_error_variance():
     q = g.standard_normal((N, dk))
     q /= np.linalg.norm(q, axis=1, keepdims=True)
     C = np.max(np.abs(U), axis=1).astype(np.float64)
-    n = rng.noise16(rng.unit_key(3, 1, np.arange(N), 0), dv, dk)
+    n = rng.noise16(rng.unit_key(3, 1, np.arange(N), 0), dv, dk, paired=True)
     X = step.dequant(step.PREC_INT8, step.quantize_rows(U, step.PREC_INT8, n, axis="key"),
                      axis="key")
     e = np.einsum("nij,nj->ni", (X - U).astype(np.float64), q)
-    pred = np.einsum("nj,nj->n", q ** 2, C ** 2) / (6 * r * r)
+    # each column's maximum is stored exactly (its y is +-r), so one row in
+    # d_v contributes no error to that column
+    pred = np.einsum("nj,nj->n", q ** 2, C ** 2) / (6 * r * r) * (dv - 1) / dv
     ratio = np.mean(e ** 2) / np.mean(np.broadcast_to(pred[:, None], e.shape))
     assert abs(ratio - 1) < 0.05, ratio
 
