@@ -26,8 +26,8 @@ Parity status per function (what pins it is listed in each module):
        (the pages fix no generator; only distribution tests apply)
   step.reference_step64 ............................ pinned (closed forms, Fraction)
   step.decode_step (fp32 heads) .................... pinned (closed forms, bounds)
-  step.decode_step (int8 / int4 / bf16 heads) ...... pinned (exhaustive SR, bounds,
-       Propositions 1-3)
+  step.decode_step (int8 / int4 / bf16 heads) ...... pinned (exhaustive SR in even and
+       odd columns, the antithetic pair probabilities, bounds, Propositions 1-3)
   step.quantize_rows / decode_step, axis="key" ..... pinned (hand-worked codes,
        rank-one structure, transpose identity, unbiasedness, variance)
   assign.decay_stat / assign.assign_precision ...... pinned (hand-worked cases)
