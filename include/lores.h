@@ -238,9 +238,10 @@ int lores_state_layout(const lores_state *st, lores_layout *out);
  *   LORES_ROUND_STOCHASTIC  stochastic rounding (the default), as described
  *                           at lores_decode_step
  *   LORES_ROUND_NEAREST     the same formula with u = 1/2 (n = 2^15): codes
- *                           floor(fl(U * inv + bias + 1/2)) - bias, i.e. round
- *                           to nearest, ties upward, after the fp32 rounding of
- *                           the sum; bf16 heads keep the high half of
+ *                           s (floor(fl(s U * inv + bias + 1/2)) - bias), i.e.
+ *                           round to nearest, ties upward in even and downward
+ *                           in odd columns, after the fp32 rounding of the
+ *                           sum; bf16 heads keep the high half of
  *                           f32bits(U) + 2^15 (nearest, ties away from zero)
  * Round-to-nearest is the deterministic baseline the stochastic rounding is
  * compared with ("Intra-State Quantization (Section 4)", Rounding and
