@@ -1259,6 +1259,17 @@ struct TaskStream {
         constexpr bool kMixable =
             (PREC == LORES_INT8 || PREC == LORES_INT4 || (PREC == LORES_INT6 && CPL == 128)) &&
             !KEY && !PC;
+        // Key-column int4 rows take the bare code the same way,
+        // fma_mix(P 2^-24, 2^24, -off) = P - off, exact, in place of a
+        // conversion and a subtraction; the column factor (and the odd
+        // column's sign) follows per group of 16 (mul16n).  int8 keeps its
+        // one-instruction sign-extending conversion; key-column int6 rows
+        // compiled this way spilled 46 registers and ran 61 % slower.
+        constexpr bool kKeyMix = KEY && PREC == LORES_INT4;
+        if constexpr (kKeyMix) {
+            a = 1.0f;
+            na = -Prec<PREC>::OFF;
+        }
         const float A0 = a * 0x1p24f, A1 = a * 0x1p20f;
         auto pass1 = [&](auto mix_flag) {
         constexpr bool MIX = decltype(mix_flag)::value;
@@ -1279,8 +1290,9 @@ struct TaskStream {
                 }
                 // an odd column's stored code is negated
                 if constexpr (MIX) {
-                    U[j] = (j & 1) ? mix_f16n(int6_field(cv, j), 0, A0, na)
-                                   : mix_f16(int6_field(cv, j), 0, A0, na);
+                    // (key columns: the sign comes with the column factor)
+                    U[j] = (!KEY && (j & 1)) ? mix_f16n(int6_field(cv, j), 0, A0, na)
+                                             : mix_f16(int6_field(cv, j), 0, A0, na);
                     if ((j & 15) == 15) group_done(j);
                     continue;
                 }
@@ -1335,8 +1347,10 @@ struct TaskStream {
                     sp = (e & 1) ? mix_f16n(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na)
                                  : mix_f16(hv[e >> 2][e & 1], (e >> 1) & 1, A0, na);
                 } else if constexpr (MIX && PREC == LORES_INT4) {
-                    sp = (e & 1) ? mix_f16n(hv[e >> 3][e & 3], (e >> 2) & 1, A1, na)
-                                 : mix_f16(hv[e >> 3][e & 3], (e >> 2) & 1, A0, na);
+                    // (key columns: the sign comes with the column factor)
+                    sp = (!KEY && (e & 1)) ? mix_f16n(hv[e >> 3][e & 3], (e >> 2) & 1, A1, na)
+                                           : mix_f16(hv[e >> 3][e & 3], (e >> 2) & 1,
+                                                     (e & 1) ? A1 : A0, na);
                 } else if constexpr (PREC == LORES_INT8 || PREC == LORES_INT4) {
                     float ub;
                     if constexpr (PREC == LORES_INT8 && (KEY || PC)) {
@@ -1371,7 +1385,9 @@ struct TaskStream {
         }
         }
         };
-        if constexpr (kMixable) {
+        if constexpr (kKeyMix) {
+            pass1(Flag<true>{});
+        } else if constexpr (kMixable) {
             if (__builtin_amdgcn_ballot_w64(!(a < 0x1p100f)) == 0) pass1(Flag<true>{});
             else pass1(Flag<false>{});
             // Both branches have waited for this task's loads, but the
